@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+A step is one chunkwise forward pass (gate scan, gated Gram, UT transform, chunk operators,
+state propagation and output: gdn_chunk_prepare + gdn_chunk_propagate, exactly the two
+launches gdn_chunk_fwd makes) over the training-shape workload B4 H16 T2048 d_k=d_v=128,
+bf16 q/k/v/o, fp32 gates and state, chunk 64. Inputs are resident in HBM before timing
+and rotate over 4 independent sets (~540 MB) so that no step is served from the 256 MB
+Infinity Cache. The decode step (256 sequences x H32, d128, fp32 state, 64 chained
+steps) is timed in the same run and reported under "decode".
+
+Prints one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunk-fwd tokens/s + %MFMA peak (B4 H16 T2048 d128); decode %HBM BW"
+PEAK_BF16_FLOPS = 2516.6e12   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (MI355X, ~2.5 PF)
+PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+CHUNK = 64
+
+
+def fwd_counts(dk, dv, C=CHUNK, elem=2):
+    """Algorithmic counts per token-head of the chunkwise forward: FLOP of the method's
+    eight chunk matmuls at full tile size, and the bytes it must move (q, k, v, o, g, beta).
+    The bytes split by kernel: stage 2 moves q, k, v, o; stage 1 moves g, beta."""
+    flops = 6 * dk * dv + 2 * C * (3 * dk + 2 * dv)
+    stage2_bytes = (2 * dk + dv) * elem + dv * elem
+    stage1_bytes = 8
+    # FLOP actually issued per token-head by each stage of this implementation
+    stage1_flops = 2 * C * dk * 2 + 2 * C * C          # K K^T, Q K^T, Nmat = P Mmat
+    stage2_flops = 6 * dk * dv + 4 * C * dv            # K S^T, Q S^T, Delta^T K, Mmat R, Nmat R
+    return dict(flops=flops, bytes=stage1_bytes + stage2_bytes, stage1_bytes=stage1_bytes,
+                stage2_bytes=stage2_bytes, stage1_flops=stage1_flops, stage2_flops=stage2_flops)
+
+
+def decode_bytes(dk, dv, elem=2):
+    """Bytes one decode step moves per (sequence, head): the fp32 state read and written,
+    plus q, k, v, o and the two gates."""
+    return 2 * dk * dv * 4 + (2 * dk + dv) * elem + dv * elem + 8
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--only", choices=["all", "fwd", "decode"], default="all")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run plain device copies of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if xs else float("nan")
+
+
+def bench_forward(args, torch, gb, SY):
+    w = SY.WORKLOADS[1]
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(4):
+        x = SY.make_forward_inputs(1, seed=1 + 100 * s)
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+        t["o"] = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        t["hT"] = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        sets.append(t)
+    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, B, False)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record()
+        gb.gdn_chunk_prepare(t["q"], t["k"], t["g"], t["beta"], ws, dv=dv)
+        if ev is not None:
+            ev[1].record()
+        gb.gdn_chunk_propagate(t["q"], t["k"], t["v"], ws, o=t["o"], hT=t["hT"])
+        if ev is not None:
+            ev[2].record()
+
+    # the two stage calls are exactly gdn_chunk_fwd
+    step(sets[0])
+    o_ref, h_ref = gb.gdn_chunk_fwd(*(sets[0][n] for n in ("q", "k", "v", "g", "beta")))
+    torch.cuda.synchronize()
+    assert torch.equal(o_ref, sets[0]["o"]) and torch.equal(h_ref, sets[0]["hT"])
+
+    for i in range(args.warmup):
+        step(sets[i % 4])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % 4], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prep_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    prop_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=t1 - t0, prep_ms=prep_ms, prop_ms=prop_ms)
+
+
+def bench_decode(args, torch, gb, SY):
+    w = SY.WORKLOADS[4]
+    d = SY.make_decode_inputs(4, steps=args.decode_steps)
+    dev = torch.device("cuda:0")
+    N, H, dk, dv = w.decode_seqs, w.H, w.dk, w.dv
+    toks = [{n: d[n][s].to(dev) for n in ("q", "k", "v", "g", "beta")} for s in range(args.decode_steps)]
+    state = d["state"].to(dev)
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    warm = state.clone()
+    for s in range(min(3, args.decode_steps)):
+        gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), warm, o)
+    del warm
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.decode_steps):
+        evs[s][0].record()
+        gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), state, o)
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(N=N, H=H, dk=dk, dv=dv, wall_s=t1 - t0, step_ms=step_ms)
+
+
+def cpu_baseline(seconds):
+    """The CPU fp64 oracle (C twin, OpenMP over (sequence, head) pairs) on the same
+    training-shape workload, repeated until `seconds` of wall clock have passed."""
+    from gated_delta_rule_42_amd import synthetic as SY
+    from oracle import ctwin
+
+    x = SY.make_forward_inputs(1)
+    p = ctwin.prepare_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    reps, used = 0, 1
+    t0 = time.perf_counter()
+    while True:
+        _, _, used = ctwin.forward_prepared(p)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el / reps * (reps + 1) > 3 * seconds:
+            break
+    tokens = reps * p["B"] * p["T"]
+    return {"value": tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"full B4 H16 T2048 d128 workload x{reps} (fp64 token recurrence, "
+                      f"{el:.1f} s wall, {os.cpu_count()} host CPUs visible)"}
+
+
+def calib_copy(torch, mb):
+    n = mb * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
+              "shards over (sequence, head) pairs with no exchange; see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from gated_delta_rule_42_amd import binding as gb
+    from gated_delta_rule_42_amd import synthetic as SY
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gb.lib()
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; q,k unit-norm, v ~ N(0,1), g = -softplus(N(0,1)), "
+                   "beta = sigmoid(N(0,1)))",
+           "config": {"workload": "chunkwise forward B4 H16 T2048 d_k=d_v=128 chunk 64, bf16 "
+                                  "q/k/v/o, fp32 gates and state, h0 = 0",
+                      "B": 4, "T": 2048, "H": 16, "d_k": 128, "d_v": 128, "chunk": 64,
+                      "global_batch": 4, "seq_len": 2048, "parallelism": "single GPU"}}
+    if args.calib_copy_mb:
+        calib_copy(torch, args.calib_copy_mb)
+    if args.only in ("all", "fwd"):
+        f = bench_forward(args, torch, gb, SY)
+        c = fwd_counts(f["dk"], f["dv"])
+        th = f["B"] * f["T"] * f["H"]
+        ms_step = f["wall_s"] / args.steps * 1e3
+        tokens = f["B"] * f["T"]
+        prep, prop = sum(f["prep_ms"]) / args.steps, sum(f["prop_ms"]) / args.steps
+        out["value"] = tokens / (ms_step / 1e3)
+        out["ms_per_step"] = ms_step
+        out["mfma_frac"] = c["flops"] * th / (ms_step / 1e3) / PEAK_BF16_FLOPS
+        out["tflops"] = c["flops"] * th / (ms_step / 1e3) / 1e12
+        out["hbm_frac_algorithmic"] = c["bytes"] * th / (ms_step / 1e3) / PEAK_HBM_BPS
+        out["stages_ms"] = {"chunk_prepare": prep, "chunk_propagate": prop,
+                            "chunk_prepare_median": median(f["prep_ms"]),
+                            "chunk_propagate_median": median(f["prop_ms"])}
+        if prop >= prep:
+            ach = c["stage2_bytes"] * th / (prop / 1e3)
+            out["roofline"] = {"kernel": "chunk_propagate_kernel", "bound": "hbm",
+                               "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                               "frac": ach / PEAK_HBM_BPS, "traffic": None,
+                               "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
+        else:
+            ach = c["stage1_flops"] * th / (prep / 1e3)
+            out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
+                               "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS, "traffic": None,
+                               "algorithmic_flops_per_launch": c["stage1_flops"] * th}
+    if args.only in ("all", "decode"):
+        d = bench_decode(args, torch, gb, SY)
+        per = decode_bytes(d["dk"], d["dv"]) * d["N"] * d["H"]
+        med = median(d["step_ms"])
+        mean = sum(d["step_ms"]) / len(d["step_ms"])
+        out["decode"] = {"workload": "decode 256 seq x H32 d128, fp32 state, bf16 q/k/v/o, "
+                                     f"{len(d['step_ms'])} chained steps",
+                         "ms_per_step_median": med, "ms_per_step_mean": mean,
+                         "tokens_per_s": d["N"] / (mean / 1e3),
+                         "hbm_GBps": per / (mean / 1e3) / 1e9,
+                         "hbm_frac": per / (mean / 1e3) / PEAK_HBM_BPS,
+                         "bytes_per_step": per}
+        if args.only == "decode":
+            out["value"] = d["N"] / (mean / 1e3)
+            out["ms_per_step"] = mean
+            out["metric"] = METRIC
+            out["unit"] = "tokens/s"
+            out["roofline"] = {"kernel": "decode_kernel", "bound": "hbm",
+                               "achieved": per / (mean / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                               "unit": "GB/s", "frac": per / (mean / 1e3) / PEAK_HBM_BPS,
+                               "traffic": None, "algorithmic_bytes_per_launch": per}
+    if args.cpu_seconds > 0 and args.only != "decode":
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+"""Python binding of libgdn.so (C ABI in include/gdn.h), with the same entry-point names.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels of the
+library. torch supplies device memory and the current stream. There is no CPU path: a
+missing library, or a tensor that is not on a GPU, raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+_DTYPE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+CHUNK = 64
+
+# (name, restype, argtypes) of every function declared in include/gdn.h
+_P, _I, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGNATURES = [
+    ("gdn_version", _I, []),
+    ("gdn_status_string", ctypes.c_char_p, [_I]),
+    ("gdn_chunk_fwd_workspace_bytes", _SZ, [_I] * 9),
+    ("gdn_chunk_fwd", _I, [_P] * 9 + [_I] * 8 + [_P, _SZ, _P]),
+    ("gdn_chunk_prepare", _I, [_P] * 5 + [_I] * 8 + [_P, _SZ, _P]),
+    ("gdn_chunk_propagate", _I, [_P] * 7 + [_I] * 8 + [_P, _SZ, _P]),
+    ("gdn_decode_step", _I, [_P] * 7 + [_I] * 5 + [_P]),
+]
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    """A call into libgdn.so returned a negative gdn_status."""
+
+
+def lib():
+    """Load libgdn.so (built in-tree by gated_delta_rule_42_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_delta_rule_42_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in _SIGNATURES:
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def gdn_version() -> int:
+    return lib().gdn_version()
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise GDNError(f"{what}: {gdn_status_string(status)} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("gdn: every tensor must be a contiguous tensor on a GPU")
+
+
+def gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, varlen, chunk=CHUNK, dtype=torch.bfloat16) -> int:
+    return lib().gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, int(bool(varlen)), chunk,
+                                               _DTYPE[dtype])
+
+
+def _shapes(q, v, cu_seqlens):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return B, T, H, dk, dv, N
+
+
+def _workspace(B, T, H, dk, dv, N, cu_seqlens, dtype, device, workspace):
+    need = gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, cu_seqlens is not None, CHUNK, dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None, hT=None,
+                  output_final_state=True, workspace=None, stream=None):
+    """Chunkwise forward pass. q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16); g, beta
+    [B,T,H] fp32; h0 [N,H,dv,dk] fp32 or None; cu_seqlens int32 [N+1] or None.
+    Returns (o [B,T,H,dv], hT [N,H,dv,dk] fp32 or None)."""
+    _need_gpu(q, k, v, g, beta, h0, cu_seqlens, o, hT, workspace)
+    B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    workspace, need = _workspace(B, T, H, dk, dv, N, cu_seqlens, q.dtype, q.device, workspace)
+    st = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                             _ptr(hT), _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
+                             _DTYPE.get(q.dtype, -1), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0,
+                             _stream(q.device, stream))
+    _check(st, "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_chunk_prepare(q, k, g, beta, workspace, cu_seqlens=None, chunk=CHUNK, *, dv=None, stream=None):
+    """Stage 1 (per-chunk gate scan, gated Gram, UT transform, chunk operators) into
+    `workspace` (uint8 tensor of gdn_chunk_fwd_workspace_bytes bytes)."""
+    _need_gpu(q, k, g, beta, cu_seqlens, workspace)
+    B, T, H, dk = q.shape
+    dv = dk if dv is None else dv
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    st = lib().gdn_chunk_prepare(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), chunk, B, T,
+                                 H, dk, dv, N, _DTYPE.get(q.dtype, -1), _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0,
+                                 _stream(q.device, stream))
+    _check(st, "gdn_chunk_prepare")
+
+
+def gdn_chunk_propagate(q, k, v, workspace, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None,
+                        hT=None, output_final_state=True, stream=None):
+    """Stage 2 (state carried across chunks, chunk outputs) from a prepared workspace."""
+    _need_gpu(q, k, v, h0, cu_seqlens, o, hT, workspace)
+    B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    st = lib().gdn_chunk_propagate(_ptr(q), _ptr(k), _ptr(v), _ptr(h0), _ptr(o), _ptr(hT),
+                                   _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
+                                   _DTYPE.get(q.dtype, -1), _ptr(workspace),
+                                   workspace.numel() if workspace is not None else 0,
+                                   _stream(q.device, stream))
+    _check(st, "gdn_chunk_propagate")
+    return o, hT
+
+
+def gdn_decode_step(q, k, v, g, beta, state, o=None, *, stream=None):
+    """One decode step: q, k [N,H,dk], v [N,H,dv] (fp32 or bf16), g, beta [N,H] fp32,
+    state [N,H,dv,dk] fp32 updated in place. Returns o [N,H,dv]."""
+    _need_gpu(q, k, v, g, beta, state, o)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                               N, H, dk, dv, _DTYPE.get(q.dtype, -1), _stream(q.device, stream))
+    _check(st, "gdn_decode_step")
+    return o

@@ -1,0 +1,144 @@
+// C ABI of libgdn.so (declared in include/gdn.h): argument checks, workspace layout and
+// kernel dispatch. Every check runs before any HIP call, so a rejected call launches
+// nothing and touches no device state.
+#include "gdn.h"
+#include "gdn_internal.h"
+
+#define GDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Shared checks of the chunked forward entry points. `need` flags: 1 = q,k,g,beta;
+// 2 = v,o. Fills the problem description on success.
+int check_chunk(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                const float* h0, const void* o, const float* hT, const int32_t* cu, int chunk,
+                int B, int T, int H, int dk, int dv, int N, int dtype, const void* ws,
+                size_t ws_bytes, int need, gdn::ChunkProblem* p) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || T < 0) return GDN_ERR_SHAPE;
+    if (cu) {
+        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
+    } else if (N != B) {
+        return GDN_ERR_SHAPE;
+    }
+    const long long tokens = (long long)B * T;
+    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
+        return GDN_ERR_SHAPE;
+    if (tokens > 0) {
+        if ((need & 1) && (!q || !k || !g || !beta)) return GDN_ERR_NULL;
+        if ((need & 2) && (!q || !k || !v || !o)) return GDN_ERR_NULL;
+    }
+    const void* al16[] = {q, k, v, o};
+    for (const void* x : al16)
+        if (x && !aligned(x, 16)) return GDN_ERR_ALIGN;
+    const void* al4[] = {h0, hT, g, beta, cu};
+    for (const void* x : al4)
+        if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
+    const int elem = dtype == GDN_BF16 ? 2 : 4;
+    const gdn::WorkspaceLayout w = gdn::workspace_layout(B, T, H, N, cu != nullptr, elem);
+    if (w.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
+    if (w.total > 0 && (!ws || ws_bytes < w.total)) return GDN_ERR_WORKSPACE;
+    if (ws && !aligned(ws, 256)) return GDN_ERR_ALIGN;
+
+    gdn::ChunkProblem& P = *p;
+    P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0;
+    P.o = const_cast<void*>(o); P.hT = const_cast<float*>(hT); P.cu_seqlens = cu;
+    P.B = B; P.T = T; P.H = H; P.dk = dk; P.dv = dv; P.N = N;
+    P.bf16 = dtype == GDN_BF16;
+    P.nc_bound = w.nc_bound;
+    P.nc_per_seq = (T + 63) / 64;
+    char* base = static_cast<char*>(const_cast<void*>(ws));
+    P.chunk_base = cu ? reinterpret_cast<int32_t*>(base + w.off_base) : nullptr;
+    P.gamma = w.nc_bound ? reinterpret_cast<float*>(base + w.off_gamma) : nullptr;
+    P.mmat = w.nc_bound ? base + w.off_m : nullptr;
+    P.nmat = w.nc_bound ? base + w.off_n : nullptr;
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_EXPORT int gdn_version(void) { return 100; }
+
+GDN_EXPORT const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case GDN_ERR_DTYPE: return "unknown dtype code";
+        case GDN_ERR_ALIGN: return "a pointer is misaligned (tensors 16 B, workspace 256 B)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported chunk size or head dimension (chunk 64; d_k, d_v in {64, 128})";
+        case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_chunk_fwd_workspace_bytes()";
+        case GDN_ERR_HIP: return "a HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+GDN_EXPORT size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                int varlen, int chunk, int dtype) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
+    if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
+    if (B < 1 || H < 1 || T < 0) return 0;
+    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    return gdn::workspace_layout(B, T, H, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
+}
+
+GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
+                                 int dv, int N, int dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    gdn::ChunkProblem p{};
+    int st = check_chunk(q, k, nullptr, g, beta, nullptr, nullptr, nullptr, cu_seqlens, chunk, B, T,
+                         H, dk, dv, N, dtype, workspace, workspace_bytes, 1, &p);
+    if (st != GDN_OK) return st;
+    return gdn::launch_chunk_prepare(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                      : GDN_ERR_HIP;
+}
+
+GDN_EXPORT int gdn_chunk_propagate(const void* q, const void* k, const void* v, const float* h0,
+                                   void* o, float* hT, const int32_t* cu_seqlens, int chunk, int B,
+                                   int T, int H, int dk, int dv, int N, int dtype,
+                                   const void* workspace, size_t workspace_bytes, void* stream) {
+    gdn::ChunkProblem p{};
+    int st = check_chunk(q, k, v, nullptr, nullptr, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
+                         N, dtype, workspace, workspace_bytes, 2, &p);
+    if (st != GDN_OK) return st;
+    return gdn::launch_chunk_propagate(p, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+GDN_EXPORT int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                             const float* beta, const float* h0, void* o, float* hT,
+                             const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
+                             int dv, int N, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    gdn::ChunkProblem p{};
+    int st = check_chunk(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
+                         N, dtype, workspace, workspace_bytes, 3, &p);
+    if (st != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::launch_chunk_prepare(p, s) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_chunk_propagate(p, s) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
+}
+
+GDN_EXPORT int gdn_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                               const float* beta, float* state, void* o, int N, int H, int dk,
+                               int dv, int dtype, void* stream) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || (long long)N * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    if (!q || !k || !v || !g_log_alpha || !beta || !state || !o) return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, o, state};
+    for (const void* x : al16)
+        if (!aligned(x, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(g_log_alpha, 4) || !aligned(beta, 4)) return GDN_ERR_ALIGN;
+    gdn::DecodeProblem p{q, k, v, g_log_alpha, beta, state, o, N, H, dk, dv, dtype == GDN_BF16};
+    return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                : GDN_ERR_HIP;
+}

@@ -1,0 +1,121 @@
+// Recurrent decode step of the gated delta rule for gfx950: one new token per
+// (sequence, head), applied to the fp32 state in place.
+//
+// One token of the recurrence (paper note "Gated Delta Networks: Improving Mamba2 with
+// Delta Rule", mechanism paragraph; module page "Gated DeltaNet", "How It Works"):
+//   S <- alpha S + beta (v - alpha S k) k^T,     o = S q   (the updated state)
+// Each state row s_i (one v index) is independent:
+//   a_i = s_i . k,  b_i = s_i . q,  c_i = beta (v_i - alpha a_i),
+//   s_i <- alpha s_i + c_i k,        o_i = alpha b_i + c_i (k . q)
+// so every row is read once and written once: the step streams the state through HBM.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// One DPP lane permutation within each 16-lane row (control word fixed at compile time).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row (all 16 lanes receive the total):
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    return x;
+}
+
+template <typename TS, int EPL>
+__device__ __forceinline__ void load_vec(const TS* p, float (&x)[EPL]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = to_f32(p[e]);
+}
+
+// One work-group per (sequence, head). Its 256 lanes form 16 groups of 16; group g owns
+// rows g, g+16, ...; within a group, lane l16 owns columns [l16*EPL, l16*EPL + EPL) so that
+// one group reads a whole row contiguously.
+template <typename TS, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
+    constexpr int EPL = DK / 16;   // state columns per lane
+    constexpr int RPG = DV / 16;   // rows per lane group
+    const long pr = blockIdx.x;
+    const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+
+    float kf[EPL], qf[EPL];
+    load_vec<TS, EPL>(static_cast<const TS*>(p.k) + pr * DK + l16 * EPL, kf);
+    load_vec<TS, EPL>(static_cast<const TS*>(p.q) + pr * DK + l16 * EPL, qf);
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kq += kf[e] * qf[e];
+    kq = row16_sum(kq);
+    const float alpha = __expf(p.g[pr]);
+    const float beta = p.beta[pr];
+
+    float* st = p.state + pr * (long)DV * DK + l16 * EPL;
+    const TS* vp = static_cast<const TS*>(p.v) + pr * DV;
+    TS* op = static_cast<TS*>(p.o) + pr * DV;
+
+    float s[RPG][EPL];
+    float vr[RPG];
+#pragma unroll
+    for (int it = 0; it < RPG; ++it) {
+        const int row = grp + 16 * it;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(st + (long)row * DK + e);
+            s[it][e] = x.x; s[it][e + 1] = x.y; s[it][e + 2] = x.z; s[it][e + 3] = x.w;
+        }
+        vr[it] = to_f32(vp[row]);
+    }
+#pragma unroll
+    for (int it = 0; it < RPG; ++it) {
+        const int row = grp + 16 * it;
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            sk += s[it][e] * kf[e];
+            sq += s[it][e] * qf[e];
+        }
+        sk = row16_sum(sk);
+        sq = row16_sum(sq);
+        const float c = beta * (vr[it] - alpha * sk);
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            float4 x;
+            x.x = alpha * s[it][e] + c * kf[e];
+            x.y = alpha * s[it][e + 1] + c * kf[e + 1];
+            x.z = alpha * s[it][e + 2] + c * kf[e + 2];
+            x.w = alpha * s[it][e + 3] + c * kf[e + 3];
+            *reinterpret_cast<float4*>(st + (long)row * DK + e) = x;
+        }
+        if (l16 == 0) op[row] = from_f32<TS>(alpha * sq + c * kq);
+    }
+}
+
+template <typename TS, int DK, int DV>
+static void decode_launch(const DecodeProblem& p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_kernel<TS, DK, DV>), dim3((unsigned)((long)p.N * p.H)), dim3(256), 0,
+                       s, p);
+}
+
+template <typename TS>
+static void decode_dispatch(const DecodeProblem& p, hipStream_t s) {
+    if (p.dk == 64) {
+        if (p.dv == 64) decode_launch<TS, 64, 64>(p, s); else decode_launch<TS, 64, 128>(p, s);
+    } else {
+        if (p.dv == 64) decode_launch<TS, 128, 64>(p, s); else decode_launch<TS, 128, 128>(p, s);
+    }
+}
+
+hipError_t launch_decode(const DecodeProblem& p, hipStream_t s) {
+    if ((long)p.N * p.H > 0) {
+        if (p.bf16) decode_dispatch<uint16_t>(p, s); else decode_dispatch<float>(p, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,56 @@
+// Host-side launch descriptors shared by the C ABI layer and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Resolved problem description for the chunked forward pass.
+struct ChunkProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* h0;
+    void* o;
+    float* hT;
+    const int32_t* cu_seqlens;   // NULL: fixed-length rows
+    int B, T, H, dk, dv, N;
+    int bf16;                    // 1: q,k,v,o are bf16; 0: fp32
+    long nc_bound;               // upper bound on the number of chunks (workspace rows)
+    int nc_per_seq;              // chunks per row when cu_seqlens is NULL
+    // workspace regions
+    int32_t* chunk_base;         // [N + 1] (varlen only)
+    float* gamma;                // [nc_bound, H, 64]
+    void* mmat;                  // [nc_bound, H, 64, 64] element type of q
+    void* nmat;                  // [nc_bound, H, 64, 64]
+};
+
+struct WorkspaceLayout {
+    size_t off_base, off_gamma, off_m, off_n, total;
+    long nc_bound;
+};
+
+WorkspaceLayout workspace_layout(int B, int T, int H, int N, int varlen, int elem_bytes);
+
+hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
+hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
+
+struct DecodeProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* o;
+    int N, H, dk, dv;
+    int bf16;
+};
+
+hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,163 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) gated delta rule library, libgdn.so.
+ *
+ * The operator, per sequence and head, with a matrix state S of shape [d_v, d_k]:
+ *
+ *     S_t = S_{t-1} . alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,     o_t = S_t q_t
+ *
+ * Sources: paper note "Gated Delta Networks: Improving Mamba2 with Delta Rule"
+ * (phantomic12 inference-research), mechanism paragraph (the recurrence, the parallel
+ * WY / UT-transform training algorithm, a fixed-size per-head state with no KV cache);
+ * record "LIT-137" (anthology-of-the-sota), "Standing in the anthology" (the same
+ * recurrence; the WY-based chunkwise algorithm extended to carry the gate); module page
+ * "Gated DeltaNet" (ai-model-reference), "How It Works" and "Math Or Compute Schema"
+ * (the gate decays the old memory before the delta write; the query reads the updated
+ * memory).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers allocated and owned by the caller. The
+ *    library allocates nothing, keeps no pointer after a call returns and holds no
+ *    global state; calls on distinct streams may run concurrently.
+ *  - Layouts are dense, row-major, with the feature dimension innermost:
+ *      q, k [B, T, H, d_k]     v, o [B, T, H, d_v]     g, beta [B, T, H]
+ *      states (h0, hT, decode state) [N, H, d_v, d_k] fp32 (d_k contiguous)
+ *    The pages list the state as (heads, d_k, d_v); the product v k^T makes it d_v x d_k,
+ *    which is the stored order here.
+ *  - dtype: GDN_F32 (q, k, v, o fp32) or GDN_BF16 (q, k, v, o bfloat16). g, beta and all
+ *    states are fp32 in both cases.
+ *  - g is log(alpha) and must be <= 0 (alpha in (0, 1]); beta is used as given. Neither is
+ *    checked on the device. There is no query scale (o_t = S_t q_t exactly).
+ *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and the call
+ *    returns at once. The return code reports host-side argument checks, which all run
+ *    before any HIP call, and launch errors; faults during execution surface at the
+ *    caller's next synchronisation.
+ *  - Alignment: q, k, v, o and the decode state 16 bytes; g, beta, h0, hT and cu_seqlens
+ *    4 bytes; the workspace 256 bytes. A misaligned pointer gives GDN_ERR_ALIGN.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    GDN_ERR_DTYPE = -3,       /* unknown dtype code */
+    GDN_ERR_ALIGN = -4,       /* a pointer is misaligned */
+    GDN_ERR_UNSUPPORTED = -5, /* chunk size or head dimension not built */
+    GDN_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+    GDN_ERR_HIP = -7          /* a HIP launch reported an error */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int gdn_version(void);
+
+/* Human-readable text for a gdn_status value (static storage, never NULL). */
+const char *gdn_status_string(int status);
+
+/*
+ * Workspace size in bytes needed by gdn_chunk_fwd / gdn_chunk_prepare /
+ * gdn_chunk_propagate for the given problem (0 when no chunk exists). Pure host
+ * function. `varlen` != 0 means cu_seqlens will be passed (then B must be 1 and N is
+ * the number of packed sequences); otherwise N must equal B. Returns 0 for arguments
+ * that the chunk entry points would reject.
+ *
+ * Workspace contents (all regions 256-byte aligned, in this order; `nc` is an upper
+ * bound on the number of chunks, ceil(T/64)*B without cu_seqlens and
+ * floor((T + N*63)/64) with them):
+ *   chunk_base  int32 [N + 1]        first chunk index of each sequence (varlen only)
+ *   gamma       fp32  [nc, H, 64]    in-chunk inclusive cumulative sum of g
+ *   Mmat        dtype [nc, H, 64, 64] T diag(beta), T = (I + A)^{-1} (UT transform)
+ *   Nmat        dtype [nc, H, 64, 64] P Mmat, P = (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]
+ * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
+                                     int chunk, int dtype);
+
+/*
+ * Chunkwise-parallel forward pass (WY representation / UT transform carrying the
+ * gate): computes o for every token and, optionally, the final state of every
+ * sequence. Equals gdn_chunk_prepare followed by gdn_chunk_propagate on `stream`.
+ *
+ *   q, k        [B, T, H, dk]  dtype                     (required)
+ *   v           [B, T, H, dv]  dtype                     (required)
+ *   g_log_alpha [B, T, H] fp32, log of the decay, <= 0   (required)
+ *   beta        [B, T, H] fp32, write strength           (required)
+ *   h0          [N, H, dv, dk] fp32 initial states, or NULL for zeros
+ *   o           [B, T, H, dv]  dtype, written            (required)
+ *   hT          [N, H, dv, dk] fp32 final states, written, or NULL. hT may be the same
+ *               pointer as h0 (each state is read before it is overwritten); other
+ *               overlaps are undefined.
+ *   cu_seqlens  int32 [N + 1] device array of packed-sequence offsets, or NULL. With it,
+ *               B must be 1 and sequence n covers tokens [cu[n], cu[n+1]) of the T axis;
+ *               it must satisfy 0 = cu[0] <= cu[1] <= ... <= cu[N] = T (not checked on the
+ *               device). Each sequence starts from h0[n] (or zeros); a zero-length one
+ *               yields hT[n] = h0[n]. Without it, N must equal B and row b is sequence b.
+ *   chunk       chunk length; 64 is the only one built
+ *   B, T, H, dk, dv, N: sizes; dk, dv in {64, 128}; B, H >= 1; T >= 0
+ *   dtype       gdn_dtype of q, k, v and o
+ *   workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes,
+ *               owned by the caller; may be NULL only when that size is 0
+ *   stream      hipStream_t to enqueue on
+ * Returns GDN_OK or a negative gdn_status; nothing is launched on error.
+ */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                  const float *beta, const float *h0, void *o, float *hT,
+                  const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                  int N, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stage 1 of gdn_chunk_fwd, independent across chunks (no state dependency): per
+ * (chunk, head) the in-chunk gate scan, the gated Gram matrix A, the UT transform
+ * T = (I + A)^{-1} and the two chunk-local operators Mmat and Nmat described above,
+ * written to the workspace. Arguments as in gdn_chunk_fwd; v, h0, o and hT are not
+ * used. Source: the WY / UT-transform chunkwise algorithm carrying the gate (paper note,
+ * mechanism paragraph; record "LIT-137", "Standing in the anthology").
+ */
+int gdn_chunk_prepare(const void *q, const void *k, const float *g_log_alpha, const float *beta,
+                      const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                      int N, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stage 2 of gdn_chunk_fwd: for every (sequence, head) the state is carried through
+ * the chunks in order, and each chunk's output is formed from the entering state and
+ * the stage-1 operators:
+ *     R = V - diag(e^gamma) K S^T,   Delta = Mmat R,   o = diag(e^gamma) Q S^T + Nmat R,
+ *     S <- e^{gamma_last} S + Delta^T diag(e^{gamma_last - gamma}) K.
+ * Reads the workspace written by gdn_chunk_prepare with the same arguments on the same
+ * stream. Arguments as in gdn_chunk_fwd; g_log_alpha and beta are not used.
+ */
+int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float *h0, void *o,
+                        float *hT, const int32_t *cu_seqlens, int chunk, int B, int T, int H,
+                        int dk, int dv, int N, int dtype, const void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step: one new token for each of N sequences and H heads,
+ * applied to the states in place, with the readout of the updated state
+ * (the recurrence above for a single t; the state is the whole memory, so decode
+ * memory does not grow with context - paper note, mechanism paragraph).
+ *
+ *   q, k   [N, H, dk] dtype        v [N, H, dv] dtype
+ *   g_log_alpha, beta  [N, H] fp32
+ *   state  [N, H, dv, dk] fp32, read and overwritten in place
+ *   o      [N, H, dv] dtype, written
+ * dk, dv in {64, 128}; N, H >= 1. Returns GDN_OK or a negative gdn_status.
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                    const float *beta, float *state, void *o, int N, int H, int dk, int dv,
+                    int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,136 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every function
+that include/gdn.h declares, sizes workspaces as documented, and rejects bad arguments
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_42_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUP, ERR_WS = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gb.LIB_PATH):
+        from gated_delta_rule_42_amd import build
+        build.build()
+    return gb.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_chunk_fwd", "gdn_decode_step", "gdn_chunk_prepare", "gdn_chunk_propagate",
+              "gdn_chunk_fwd_workspace_bytes", "gdn_status_string", "gdn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    bound = {n for n, _, _ in gb._SIGNATURES}
+    assert bound == set(declared_functions())
+
+
+def test_only_c_abi_is_exported():
+    """The shared object exports the gdn_* C functions and no C++ symbols of its own."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", gb.LIB_PATH], capture_output=True, text=True).stdout
+    mine = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert set(declared_functions()) <= set(mine)
+    assert not [m for m in mine if m.startswith("_ZN3gdn")]
+
+
+def test_version_and_status_strings(L):
+    assert gb.gdn_version() >= 100
+    for s in range(-7, 1):
+        assert len(gb.gdn_status_string(s)) >= 2
+    assert gb.gdn_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # B4 H16 T2048 bf16: 128 chunks x 16 heads
+    nc, H = 4 * 32, 16
+    expect = al(nc * H * 64 * 4) + al(nc * H * 4096 * 2) + nc * H * 4096 * 2
+    assert gb.gdn_chunk_fwd_workspace_bytes(4, 2048, 16, 128, 128, 4, False) == expect
+    # packed: bound floor((T + N*63)/64), plus the chunk table
+    T, N, H = 1000, 5, 2
+    ncb = (T + N * 63) // 64
+    expect = al((N + 1) * 4) + al(ncb * H * 64 * 4) + al(ncb * H * 4096 * 4) + ncb * H * 4096 * 4
+    import torch
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, T, H, 64, 64, N, True, dtype=torch.float32) == expect
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 0, 2, 64, 64, 1, False) == 0
+    # rejected arguments give 0
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 10, 2, 96, 64, 1, 0, 64, 1) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 10, 2, 64, 64, 1, 0, 32, 1) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(2, 10, 2, 64, 64, 3, 0, 64, 1) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(2, 10, 2, 64, 64, 3, 1, 64, 1) == 0
+
+
+FAKE = 1 << 20  # an aligned, never dereferenced address: every call below fails validation
+
+
+def fwd(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, h0=None, o=FAKE, hT=None, cu=None, chunk=64,
+        B=1, T=128, H=2, dk=64, dv=64, N=1, dtype=1, ws=None, wsb=0):
+    return L.gdn_chunk_fwd(q, k, v, g, b, h0, o, hT, cu, chunk, B, T, H, dk, dv, N, dtype, ws, wsb, None)
+
+
+def test_chunk_fwd_rejects_before_any_launch(L):
+    assert fwd(L, dtype=7) == ERR_DTYPE
+    assert fwd(L, chunk=32) == ERR_UNSUP
+    assert fwd(L, dk=96) == ERR_UNSUP
+    assert fwd(L, dv=256) == ERR_UNSUP
+    assert fwd(L, H=0) == ERR_SHAPE
+    assert fwd(L, T=-1) == ERR_SHAPE
+    assert fwd(L, B=2, N=1) == ERR_SHAPE
+    assert fwd(L, B=2, N=2, cu=FAKE) == ERR_SHAPE          # packed sequences need B == 1
+    assert fwd(L, q=None) == ERR_NULL
+    assert fwd(L, o=None) == ERR_NULL
+    assert fwd(L, g=None) == ERR_NULL
+    assert fwd(L, v=FAKE + 2) == ERR_ALIGN
+    assert fwd(L, h0=FAKE + 2) == ERR_ALIGN
+    assert fwd(L) == ERR_WS                                # workspace required
+    assert fwd(L, ws=FAKE, wsb=100) == ERR_WS              # too small
+    need = L.gdn_chunk_fwd_workspace_bytes(1, 128, 2, 64, 64, 1, 0, 64, 1)
+    assert fwd(L, ws=FAKE + 16, wsb=need) == ERR_ALIGN     # workspace needs 256 B alignment
+
+
+def test_stage_entry_points_validate(L):
+    assert L.gdn_chunk_prepare(None, FAKE, FAKE, FAKE, None, 64, 1, 128, 2, 64, 64, 1, 1, None, 0, None) == ERR_NULL
+    assert L.gdn_chunk_prepare(FAKE, FAKE, FAKE, FAKE, None, 64, 1, 128, 2, 64, 64, 1, 1, None, 0, None) == ERR_WS
+    assert L.gdn_chunk_propagate(FAKE, FAKE, None, None, FAKE, None, None, 64, 1, 128, 2, 64, 64, 1, 1,
+                                 None, 0, None) == ERR_NULL
+    assert L.gdn_chunk_propagate(FAKE, FAKE, FAKE, None, FAKE, None, None, 64, 1, 128, 2, 64, 64, 1, 3,
+                                 None, 0, None) == ERR_DTYPE
+
+
+def test_decode_rejects_before_any_launch(L):
+    def dec(q=FAKE, state=FAKE, N=4, H=2, dk=128, dv=128, dtype=1):
+        return L.gdn_decode_step(q, FAKE, FAKE, FAKE, FAKE, state, FAKE, N, H, dk, dv, dtype, None)
+    assert dec(dtype=2) == ERR_DTYPE
+    assert dec(dk=32) == ERR_UNSUP
+    assert dec(N=0) == ERR_SHAPE
+    assert dec(q=None) == ERR_NULL
+    assert dec(state=FAKE + 4) == ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(1, 64, 2, 64)
+    g = torch.zeros(1, 64, 2)
+    with pytest.raises(ValueError):
+        gb.gdn_chunk_fwd(x, x, x, g, g)
+    with pytest.raises(ValueError):
+        gb.gdn_decode_step(x[0], x[0], x[0], g[0], g[0], torch.zeros(1, 64, 2, 64, 64))
