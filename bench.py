@@ -43,10 +43,10 @@ def fwd_counts(dk, dv, C=CHUNK, elem=2):
                 stage2_bytes=stage2_bytes, stage1_flops=stage1_flops, stage2_flops=stage2_flops)
 
 
-def decode_bytes(dk, dv, elem=2):
+def decode_bytes(dk, dv, elem=2, o_elem=4):
     """Bytes one decode step moves per (sequence, head): the fp32 state read and written,
-    plus q, k, v, o and the two gates."""
-    return 2 * dk * dv * 4 + (2 * dk + dv) * elem + dv * elem + 8
+    plus q, k, v (elem bytes), o (o_elem bytes) and the two gates."""
+    return 2 * dk * dv * 4 + (2 * dk + dv) * elem + dv * o_elem + 8
 
 
 def parse():
@@ -119,7 +119,7 @@ def bench_decode(args, torch, gb, SY):
     N, H, dk, dv = w.decode_seqs, w.H, w.dk, w.dv
     toks = [{n: d[n][s].to(dev) for n in ("q", "k", "v", "g", "beta")} for s in range(args.decode_steps)]
     state = d["state"].to(dev)
-    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     warm = state.clone()
     for s in range(min(3, args.decode_steps)):
         gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), warm, o)
@@ -227,7 +227,7 @@ def main():
         per = decode_bytes(d["dk"], d["dv"]) * d["N"] * d["H"]
         med = median(d["step_ms"])
         mean = sum(d["step_ms"]) / len(d["step_ms"])
-        out["decode"] = {"workload": "decode 256 seq x H32 d128, fp32 state, bf16 q/k/v/o, "
+        out["decode"] = {"workload": "decode 256 seq x H32 d128, fp32 state, bf16 q/k/v, fp32 o, "
                                      f"{len(d['step_ms'])} chained steps",
                          "ms_per_step_median": med, "ms_per_step_mean": mean,
                          "tokens_per_s": d["N"] / (mean / 1e3),

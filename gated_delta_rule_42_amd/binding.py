@@ -24,10 +24,10 @@ _SIGNATURES = [
     ("gdn_version", _I, []),
     ("gdn_status_string", ctypes.c_char_p, [_I]),
     ("gdn_chunk_fwd_workspace_bytes", _SZ, [_I] * 9),
-    ("gdn_chunk_fwd", _I, [_P] * 9 + [_I] * 8 + [_P, _SZ, _P]),
+    ("gdn_chunk_fwd", _I, [_P] * 9 + [_I] * 9 + [_P, _SZ, _P]),
     ("gdn_chunk_prepare", _I, [_P] * 5 + [_I] * 8 + [_P, _SZ, _P]),
-    ("gdn_chunk_propagate", _I, [_P] * 7 + [_I] * 8 + [_P, _SZ, _P]),
-    ("gdn_decode_step", _I, [_P] * 7 + [_I] * 5 + [_P]),
+    ("gdn_chunk_propagate", _I, [_P] * 7 + [_I] * 9 + [_P, _SZ, _P]),
+    ("gdn_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
 ]
 
 _lib = None
@@ -101,20 +101,21 @@ def _workspace(B, T, H, dk, dv, N, cu_seqlens, dtype, device, workspace):
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None, hT=None,
-                  output_final_state=True, workspace=None, stream=None):
+                  o_dtype=None, output_final_state=True, workspace=None, stream=None):
     """Chunkwise forward pass. q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16); g, beta
     [B,T,H] fp32; h0 [N,H,dv,dk] fp32 or None; cu_seqlens int32 [N+1] or None.
+    o is written in o_dtype (default: the dtype of q; fp32 is allowed for bf16 inputs).
     Returns (o [B,T,H,dv], hT [N,H,dv,dk] fp32 or None)."""
     _need_gpu(q, k, v, g, beta, h0, cu_seqlens, o, hT, workspace)
     B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
     if hT is None and output_final_state:
         hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
     workspace, need = _workspace(B, T, H, dk, dv, N, cu_seqlens, q.dtype, q.device, workspace)
     st = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
                              _ptr(hT), _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
-                             _DTYPE.get(q.dtype, -1), _ptr(workspace),
+                             _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1), _ptr(workspace),
                              workspace.numel() if workspace is not None else 0,
                              _stream(q.device, stream))
     _check(st, "gdn_chunk_fwd")
@@ -136,32 +137,34 @@ def gdn_chunk_prepare(q, k, g, beta, workspace, cu_seqlens=None, chunk=CHUNK, *,
 
 
 def gdn_chunk_propagate(q, k, v, workspace, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None,
-                        hT=None, output_final_state=True, stream=None):
+                        hT=None, o_dtype=None, output_final_state=True, stream=None):
     """Stage 2 (state carried across chunks, chunk outputs) from a prepared workspace."""
     _need_gpu(q, k, v, h0, cu_seqlens, o, hT, workspace)
     B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
     if hT is None and output_final_state:
         hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
     st = lib().gdn_chunk_propagate(_ptr(q), _ptr(k), _ptr(v), _ptr(h0), _ptr(o), _ptr(hT),
                                    _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
-                                   _DTYPE.get(q.dtype, -1), _ptr(workspace),
+                                   _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1), _ptr(workspace),
                                    workspace.numel() if workspace is not None else 0,
                                    _stream(q.device, stream))
     _check(st, "gdn_chunk_propagate")
     return o, hT
 
 
-def gdn_decode_step(q, k, v, g, beta, state, o=None, *, stream=None):
+def gdn_decode_step(q, k, v, g, beta, state, o=None, *, o_dtype=torch.float32, stream=None):
     """One decode step: q, k [N,H,dk], v [N,H,dv] (fp32 or bf16), g, beta [N,H] fp32,
-    state [N,H,dv,dk] fp32 updated in place. Returns o [N,H,dv]."""
+    state [N,H,dv,dk] fp32 updated in place. Returns o [N,H,dv] in o_dtype (fp32 by
+    default; bf16 gives the fp32 result rounded to nearest even)."""
     _need_gpu(q, k, v, g, beta, state, o)
     N, H, dk = q.shape
     dv = v.shape[-1]
     if o is None:
-        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((N, H, dv), dtype=o_dtype, device=q.device)
     st = lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
-                               N, H, dk, dv, _DTYPE.get(q.dtype, -1), _stream(q.device, stream))
+                               N, H, dk, dv, _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1),
+                               _stream(q.device, stream))
     _check(st, "gdn_decode_step")
     return o

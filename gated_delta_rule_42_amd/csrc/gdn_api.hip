@@ -15,9 +15,10 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 // 2 = v,o. Fills the problem description on success.
 int check_chunk(const void* q, const void* k, const void* v, const float* g, const float* beta,
                 const float* h0, const void* o, const float* hT, const int32_t* cu, int chunk,
-                int B, int T, int H, int dk, int dv, int N, int dtype, const void* ws,
-                size_t ws_bytes, int need, gdn::ChunkProblem* p) {
+                int B, int T, int H, int dk, int dv, int N, int dtype, int o_dtype,
+                const void* ws, size_t ws_bytes, int need, gdn::ChunkProblem* p) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return GDN_ERR_SHAPE;
@@ -50,6 +51,7 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     P.o = const_cast<void*>(o); P.hT = const_cast<float*>(hT); P.cu_seqlens = cu;
     P.B = B; P.T = T; P.H = H; P.dk = dk; P.dv = dv; P.N = N;
     P.bf16 = dtype == GDN_BF16;
+    P.o_bf16 = o_dtype == GDN_BF16;
     P.nc_bound = w.nc_bound;
     P.nc_per_seq = (T + 63) / 64;
     char* base = static_cast<char*>(const_cast<void*>(ws));
@@ -93,7 +95,7 @@ GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, c
                                  void* stream) {
     gdn::ChunkProblem p{};
     int st = check_chunk(q, k, nullptr, g, beta, nullptr, nullptr, nullptr, cu_seqlens, chunk, B, T,
-                         H, dk, dv, N, dtype, workspace, workspace_bytes, 1, &p);
+                         H, dk, dv, N, dtype, GDN_F32, workspace, workspace_bytes, 1, &p);
     if (st != GDN_OK) return st;
     return gdn::launch_chunk_prepare(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                       : GDN_ERR_HIP;
@@ -101,11 +103,11 @@ GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, c
 
 GDN_EXPORT int gdn_chunk_propagate(const void* q, const void* k, const void* v, const float* h0,
                                    void* o, float* hT, const int32_t* cu_seqlens, int chunk, int B,
-                                   int T, int H, int dk, int dv, int N, int dtype,
+                                   int T, int H, int dk, int dv, int N, int dtype, int o_dtype,
                                    const void* workspace, size_t workspace_bytes, void* stream) {
     gdn::ChunkProblem p{};
     int st = check_chunk(q, k, v, nullptr, nullptr, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
-                         N, dtype, workspace, workspace_bytes, 2, &p);
+                         N, dtype, o_dtype, workspace, workspace_bytes, 2, &p);
     if (st != GDN_OK) return st;
     return gdn::launch_chunk_propagate(p, static_cast<hipStream_t>(stream)) == hipSuccess
                ? GDN_OK
@@ -115,11 +117,11 @@ GDN_EXPORT int gdn_chunk_propagate(const void* q, const void* k, const void* v, 
 GDN_EXPORT int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
                              const float* beta, const float* h0, void* o, float* hT,
                              const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
-                             int dv, int N, int dtype, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int dv, int N, int dtype, int o_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     gdn::ChunkProblem p{};
     int st = check_chunk(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
-                         N, dtype, workspace, workspace_bytes, 3, &p);
+                         N, dtype, o_dtype, workspace, workspace_bytes, 3, &p);
     if (st != GDN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::launch_chunk_prepare(p, s) != hipSuccess) return GDN_ERR_HIP;
@@ -129,8 +131,9 @@ GDN_EXPORT int gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
 
 GDN_EXPORT int gdn_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
                                const float* beta, float* state, void* o, int N, int H, int dk,
-                               int dv, int dtype, void* stream) {
+                               int dv, int dtype, int o_dtype, void* stream) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
     if (N < 1 || H < 1 || (long long)N * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
     if (!q || !k || !v || !g_log_alpha || !beta || !state || !o) return GDN_ERR_NULL;
@@ -138,7 +141,8 @@ GDN_EXPORT int gdn_decode_step(const void* q, const void* k, const void* v, cons
     for (const void* x : al16)
         if (!aligned(x, 16)) return GDN_ERR_ALIGN;
     if (!aligned(g_log_alpha, 4) || !aligned(beta, 4)) return GDN_ERR_ALIGN;
-    gdn::DecodeProblem p{q, k, v, g_log_alpha, beta, state, o, N, H, dk, dv, dtype == GDN_BF16};
+    gdn::DecodeProblem p{q,  k, v,  g_log_alpha, beta,           state,
+                         o,  N, H,  dk,          dv,   dtype == GDN_BF16, o_dtype == GDN_BF16};
     return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                 : GDN_ERR_HIP;
 }

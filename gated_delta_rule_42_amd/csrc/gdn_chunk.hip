@@ -98,26 +98,27 @@ __device__ __forceinline__ bool locate_chunk(const ChunkProblem& p, long c, long
 }
 
 // ------------------------------------------------------------------- stage 1
-template <typename TS, int DK>
+template <typename TM, int DK>
 struct alignas(16) PrepSmem {
-    static constexpr int PK = DK + 16 / (int)sizeof(TS);  // K, Q row pitch (elements)
-    static constexpr int PC = 64 + 16 / (int)sizeof(TS);  // P, Mt row pitch
+    static constexpr int PK = DK + 16 / (int)sizeof(TM);  // K, Q row pitch (elements)
+    static constexpr int PC = 64 + 16 / (int)sizeof(TM);  // P, Mt row pitch
     static constexpr int PF = 68;                          // fp32 A, T row pitch
     union {
-        struct { TS K[64 * PK]; TS Q[64 * PK]; } in;
+        struct { TM K[64 * PK]; TM Q[64 * PK]; } in;
         struct { float A[64 * PF]; float T[64 * PF]; } tri;
     } u;
-    TS P[64 * PC];
-    TS Mt[64 * PC];
+    TM P[64 * PC];
+    TM Mt[64 * PC];
     float gam[64];
     float beta[64];
 };
 
-template <typename TS, int DK>
+template <typename TIn, int DK>
 __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
-    using SM = PrepSmem<TS, DK>;
+    using TM = typename Operand<TIn>::type;
+    using SM = PrepSmem<TM, DK>;
     constexpr int PK = SM::PK, PC = SM::PC, PF = SM::PF;
-    constexpr int EPV = 16 / (int)sizeof(TS);  // elements per 16-byte vector
+    constexpr int EPV = 16 / (int)sizeof(TM);  // elements per 16-byte vector
     constexpr int VPR = DK / EPV;              // vectors per K / Q row
     __shared__ SM sm;
 
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
     const long widx = c * H + h;
 
     // -- load K, Q (rows past the chunk end are zero), g, beta; scan g
-    const TS* kp = static_cast<const TS*>(p.k);
-    const TS* qp = static_cast<const TS*>(p.q);
+    const TIn* kp = static_cast<const TIn*>(p.k);
+    const TIn* qp = static_cast<const TIn*>(p.q);
 #pragma unroll
     for (int it = 0; it < 64 * VPR / 256; ++it) {
         const int vi = tid + 256 * it;
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
         uint4 kv = zero16(), qv = zero16();
         if (r < len) {
             const long off = ((bos + r) * H + h) * DK + cv * EPV;
-            kv = *reinterpret_cast<const uint4*>(kp + off);
-            qv = *reinterpret_cast<const uint4*>(qp + off);
+            kv = to_operand16<TIn>(*reinterpret_cast<const uint4*>(kp + off));
+            qv = to_operand16<TIn>(*reinterpret_cast<const uint4*>(qp + off));
         }
         *reinterpret_cast<uint4*>(&sm.u.in.K[r * PK + cv * EPV]) = kv;
         *reinterpret_cast<uint4*>(&sm.u.in.Q[r * PK + cv * EPV]) = qv;
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
         G[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         P0[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (cb <= rb) {
-            const TS* brow = &sm.u.in.K[(16 * cb + l16) * PK];
-            mma_nt<TS, DK>(G[cb], &sm.u.in.K[(16 * rb + l16) * PK], brow);
-            mma_nt<TS, DK>(P0[cb], &sm.u.in.Q[(16 * rb + l16) * PK], brow);
+            const TM* brow = &sm.u.in.K[(16 * cb + l16) * PK];
+            mma_nt<TM, DK>(G[cb], &sm.u.in.K[(16 * rb + l16) * PK], brow);
+            mma_nt<TM, DK>(P0[cb], &sm.u.in.Q[(16 * rb + l16) * PK], brow);
         }
     }
     __syncthreads();  // K and Q are dead; their space becomes A and T
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 pp = P0[cb][v] * e;
             }
             sm.u.tri.A[r * PF + i] = a;
-            sm.P[r * PC + i] = from_f32<TS>(pp);
+            sm.P[r * PC + i] = from_f32<TM>(pp);
         }
     }
     __syncthreads();
@@ -257,60 +258,62 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             const int ci = c0 + e;
             const float t = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
             mv[e] = t * sm.beta[ci];
-            sm.Mt[ci * PC + r] = from_f32<TS>(mv[e]);
+            sm.Mt[ci * PC + r] = from_f32<TM>(mv[e]);
         }
-        store16<TS>(static_cast<TS*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+        store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
     }
     __syncthreads();
 
-    // -- Nmat = P Mmat (lower triangular); staged through LDS for a coalesced store
+    // -- Nmat = P Mmat, staged through LDS for a coalesced store. P and Mmat are lower
+    //    triangular, so the tiles above the diagonal come out exactly zero; computing all
+    //    four costs no time (wave 3 needs four anyway) and needs no masking.
     f32x4_t Nacc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         Nacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (cb <= rb) mma_nt<TS, 64>(Nacc[cb], &sm.P[(16 * rb + l16) * PC], &sm.Mt[(16 * cb + l16) * PC]);
+        mma_nt<TM, 64>(Nacc[cb], &sm.P[(16 * rb + l16) * PC], &sm.Mt[(16 * cb + l16) * PC]);
     }
     float* F = sm.u.tri.A;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            F[(16 * rb + 4 * lq + v) * PF + 16 * cb + l16] = (cb <= rb) ? Nacc[cb][v] : 0.f;
+        for (int v = 0; v < 4; ++v) F[(16 * rb + 4 * lq + v) * PF + 16 * cb + l16] = Nacc[cb][v];
     __syncthreads();
     {
         const int r = tid >> 2, c0 = (tid & 3) * 16;
         float nv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) nv[e] = F[r * PF + c0 + e];
-        store16<TS>(static_cast<TS*>(p.nmat) + widx * 4096 + r * 64 + c0, nv);
+        store16<TM>(static_cast<TM*>(p.nmat) + widx * 4096 + r * 64 + c0, nv);
     }
 }
 
 // ------------------------------------------------------------------- stage 2
-template <typename TS, int DK, int DVT>
+template <typename TM, int DK, int DVT>
 struct alignas(16) PropSmem {
-    static constexpr int PK = DK + 16 / (int)sizeof(TS);
-    static constexpr int PC = 64 + 16 / (int)sizeof(TS);
-    TS K[64 * PK];
-    TS Q[64 * PK];
-    TS V[64 * DVT];
-    TS M[64 * PC];
-    TS Nm[64 * PC];
-    TS S[DVT * PK];    // operand copy of the state tile, rows = d_v
-    TS Rt[DVT * PC];   // R^T, rows = d_v, columns = tokens
-    TS Dt[DVT * PC];   // (diag(e^{gamma_last - gamma}) Delta)^T
+    static constexpr int PK = DK + 16 / (int)sizeof(TM);
+    static constexpr int PC = 64 + 16 / (int)sizeof(TM);
+    TM K[64 * PK];
+    TM Q[64 * PK];
+    TM V[64 * DVT];
+    TM M[64 * PC];
+    TM Nm[64 * PC];
+    TM S[DVT * PK];    // operand copy of the state tile, rows = d_v
+    TM Rt[DVT * PC];   // R^T, rows = d_v, columns = tokens
+    TM Dt[DVT * PC];   // (diag(e^{gamma_last - gamma}) Delta)^T
     float gam[64];
 };
 
 // Global -> register -> LDS staging of one chunk's inputs (K, Q, the V tile, Mmat, Nmat,
 // gamma), so that the loads for chunk c+1 are in flight while chunk c is computed.
-template <typename TS, int DK, int DV, int DVT>
+template <typename TIn, int DK, int DV, int DVT>
 struct ChunkStage {
-    static constexpr int EPV = 16 / (int)sizeof(TS);
+    using TM = typename Operand<TIn>::type;
+    static constexpr int EPV = 16 / (int)sizeof(TM);
     static constexpr int VPR_K = DK / EPV, NV_K = 64 * VPR_K / 256;
     static constexpr int VPR_V = DVT / EPV, NV_V = (64 * VPR_V + 255) / 256;
     static constexpr int VPR_M = 64 / EPV, NV_M = 64 * VPR_M / 256;
-    using SM = PropSmem<TS, DK, DVT>;
+    using SM = PropSmem<TM, DK, DVT>;
     uint4 rk[NV_K], rq[NV_K], rv[NV_V], rm[NV_M], rn[NV_M];
     float rg;
 
@@ -321,9 +324,9 @@ struct ChunkStage {
         const long lrem = seos - bos;
         const int len = (int)(lrem < kChunk ? lrem : kChunk);
         const long widx = (cbase + jc) * H + h;
-        const TS* kp = static_cast<const TS*>(p.k);
-        const TS* qp = static_cast<const TS*>(p.q);
-        const TS* vp = static_cast<const TS*>(p.v);
+        const TIn* kp = static_cast<const TIn*>(p.k);
+        const TIn* qp = static_cast<const TIn*>(p.q);
+        const TIn* vp = static_cast<const TIn*>(p.v);
 #pragma unroll
         for (int it = 0; it < NV_K; ++it) {
             const int vi = tid + 256 * it, r = vi / VPR_K, cv = vi % VPR_K;
@@ -342,8 +345,8 @@ struct ChunkStage {
             if (vi < 64 * VPR_V && r < len)
                 rv[it] = *reinterpret_cast<const uint4*>(vp + ((bos + r) * H + h) * DV + dv0 + cv * EPV);
         }
-        const uint4* mp = reinterpret_cast<const uint4*>(static_cast<const TS*>(p.mmat) + widx * 4096);
-        const uint4* np = reinterpret_cast<const uint4*>(static_cast<const TS*>(p.nmat) + widx * 4096);
+        const uint4* mp = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.mmat) + widx * 4096);
+        const uint4* np = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.nmat) + widx * 4096);
 #pragma unroll
         for (int it = 0; it < NV_M; ++it) {
             rm[it] = mp[tid + 256 * it];
@@ -357,13 +360,13 @@ struct ChunkStage {
 #pragma unroll
         for (int it = 0; it < NV_K; ++it) {
             const int vi = tid + 256 * it, r = vi / VPR_K, cv = vi % VPR_K;
-            *reinterpret_cast<uint4*>(&sm.K[r * PK + cv * EPV]) = rk[it];
-            *reinterpret_cast<uint4*>(&sm.Q[r * PK + cv * EPV]) = rq[it];
+            *reinterpret_cast<uint4*>(&sm.K[r * PK + cv * EPV]) = to_operand16<TIn>(rk[it]);
+            *reinterpret_cast<uint4*>(&sm.Q[r * PK + cv * EPV]) = to_operand16<TIn>(rq[it]);
         }
 #pragma unroll
         for (int it = 0; it < NV_V; ++it) {
             const int vi = tid + 256 * it;
-            if (vi < 64 * VPR_V) *reinterpret_cast<uint4*>(&sm.V[vi * EPV]) = rv[it];
+            if (vi < 64 * VPR_V) *reinterpret_cast<uint4*>(&sm.V[vi * EPV]) = to_operand16<TIn>(rv[it]);
         }
 #pragma unroll
         for (int it = 0; it < NV_M; ++it) {
@@ -375,14 +378,15 @@ struct ChunkStage {
     }
 };
 
-template <typename TS, int DK, int DV, int DVT>
+template <typename TIn, typename TO, int DK, int DV, int DVT>
 __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
-    using SM = PropSmem<TS, DK, DVT>;
+    using TM = typename Operand<TIn>::type;
+    using SM = PropSmem<TM, DK, DVT>;
     constexpr int PK = SM::PK, PC = SM::PC;
     constexpr int NDB = DVT / 16;                       // d_v blocks in the tile
     constexpr int NKB = DK / 16;                        // d_k blocks
     constexpr int TPW = NDB * NKB / 4;                  // state tiles per wave
-    static_assert(TPW >= 1 && ChunkStage<TS, DK, DV, DVT>::NV_K >= 1, "tile shape");
+    static_assert(TPW >= 1 && ChunkStage<TIn, DK, DV, DVT>::NV_K >= 1, "tile shape");
     __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -424,13 +428,13 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
             const int row = 16 * a + 4 * lq + v, col = 16 * b + l16;
             const float x = p.h0 ? p.h0[(pair * DV + dv0 + row) * DK + col] : 0.f;
             S[u][v] = x;
-            sm.S[row * PK + col] = from_f32<TS>(x);
+            sm.S[row * PK + col] = from_f32<TM>(x);
         }
     }
 
     // -- chunk inputs staged through registers one chunk ahead
-    ChunkStage<TS, DK, DV, DVT> stage;
-    TS* op = static_cast<TS*>(p.o);
+    ChunkStage<TIn, DK, DV, DVT> stage;
+    TO* op = static_cast<TO*>(p.o);
     if (nchunks > 0) stage.load(p, sbos, seos, cbase, 0, h, dv0, tid);
     for (long jc = 0; jc < nchunks; ++jc) {
         __syncthreads();  // all reads of the previous chunk's LDS data are done
@@ -447,9 +451,9 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-            const TS* srow = &sm.S[(16 * db + l16) * PK];
-            mma_nt<TS, DK>(x, &sm.K[(16 * wave + l16) * PK], srow);
-            mma_nt<TS, DK>(y, &sm.Q[(16 * wave + l16) * PK], srow);
+            const TM* srow = &sm.S[(16 * db + l16) * PK];
+            mma_nt<TM, DK>(x, &sm.K[(16 * wave + l16) * PK], srow);
+            mma_nt<TM, DK>(y, &sm.Q[(16 * wave + l16) * PK], srow);
             float r4[4];
             const int col = 16 * db + l16;
 #pragma unroll
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
                 r4[v] = to_f32(sm.V[r * DVT + col]) - e * x[v];
                 Yg[db][v] = e * y[v];
             }
-            store4<TS>(&sm.Rt[col * PC + 16 * wave + 4 * lq], r4[0], r4[1], r4[2], r4[3]);
+            store4<TM>(&sm.Rt[col * PC + 16 * wave + 4 * lq], r4[0], r4[1], r4[2], r4[3]);
         }
         __syncthreads();
 
@@ -467,18 +471,18 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             f32x4_t dl = {0.f, 0.f, 0.f, 0.f}, oi = {0.f, 0.f, 0.f, 0.f};
-            const TS* rrow = &sm.Rt[(16 * db + l16) * PC];
-            mma_nt<TS, 64>(dl, &sm.M[(16 * wave + l16) * PC], rrow);
-            mma_nt<TS, 64>(oi, &sm.Nm[(16 * wave + l16) * PC], rrow);
+            const TM* rrow = &sm.Rt[(16 * db + l16) * PC];
+            mma_nt<TM, 64>(dl, &sm.M[(16 * wave + l16) * PC], rrow);
+            mma_nt<TM, 64>(oi, &sm.Nm[(16 * wave + l16) * PC], rrow);
             float d4[4];
             const int col = 16 * db + l16;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * wave + 4 * lq + v;
-                if (r < len) op[((bos + r) * H + h) * DV + dv0 + col] = from_f32<TS>(Yg[db][v] + oi[v]);
+                if (r < len) op[((bos + r) * H + h) * DV + dv0 + col] = from_f32<TO>(Yg[db][v] + oi[v]);
                 d4[v] = dl[v] * __expf(glast - sm.gam[r]);
             }
-            store4<TS>(&sm.Dt[col * PC + 16 * wave + 4 * lq], d4[0], d4[1], d4[2], d4[3]);
+            store4<TM>(&sm.Dt[col * PC + 16 * wave + 4 * lq], d4[0], d4[1], d4[2], d4[3]);
         }
         __syncthreads();
 
@@ -490,13 +494,13 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
             f32x4_t acc = S[u] * eg;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const Frag<TS> fa = load_frag<TS>(&sm.Dt[(16 * a + l16) * PC + 32 * ks + 8 * lq]);
-                const Frag<TS> fb = gather_frag<TS>(&sm.K[(32 * ks + 8 * lq) * PK + 16 * b + l16], PK);
+                const Frag<TM> fa = load_frag<TM>(&sm.Dt[(16 * a + l16) * PC + 32 * ks + 8 * lq]);
+                const Frag<TM> fb = gather_frag<TM>(&sm.K[(32 * ks + 8 * lq) * PK + 16 * b + l16], PK);
                 mma_k32(acc, fa, fb);
             }
             S[u] = acc;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sm.S[(16 * a + 4 * lq + v) * PK + 16 * b + l16] = from_f32<TS>(acc[v]);
+            for (int v = 0; v < 4; ++v) sm.S[(16 * a + 4 * lq + v) * PK + 16 * b + l16] = from_f32<TM>(acc[v]);
         }
     }
 
@@ -527,10 +531,10 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int N, int varlen, int ele
     return w;
 }
 
-template <typename TS, int DK>
+template <typename TIn, int DK>
 static void prep_launch(const ChunkProblem& p, hipStream_t s) {
     const long blocks = p.nc_bound * p.H;
-    hipLaunchKernelGGL((chunk_prepare_kernel<TS, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
 }
 
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
@@ -547,27 +551,29 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TS, int DK, int DV>
+template <typename TIn, typename TO, int DK, int DV>
 static void prop_launch(const ChunkProblem& p, hipStream_t s) {
     // d_v rows per work-group; fp32 operands with d_k = 128 use 16 to stay inside 160 KB of LDS
-    constexpr int DVT = (sizeof(TS) == 4 && DK == 128) ? 16 : 32;
+    constexpr int DVT = (sizeof(TIn) == 4 && DK == 128) ? 16 : 32;
     const long blocks = (long)p.N * p.H * (DV / DVT);
-    hipLaunchKernelGGL((chunk_propagate_kernel<TS, DK, DV, DVT>), dim3((unsigned)blocks), dim3(256),
-                       0, s, p);
+    hipLaunchKernelGGL((chunk_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, p);
 }
 
-template <typename TS>
+template <typename TIn, typename TO>
 static void prop_dispatch(const ChunkProblem& p, hipStream_t s) {
     if (p.dk == 64) {
-        if (p.dv == 64) prop_launch<TS, 64, 64>(p, s); else prop_launch<TS, 64, 128>(p, s);
+        if (p.dv == 64) prop_launch<TIn, TO, 64, 64>(p, s); else prop_launch<TIn, TO, 64, 128>(p, s);
     } else {
-        if (p.dv == 64) prop_launch<TS, 128, 64>(p, s); else prop_launch<TS, 128, 128>(p, s);
+        if (p.dv == 64) prop_launch<TIn, TO, 128, 64>(p, s); else prop_launch<TIn, TO, 128, 128>(p, s);
     }
 }
 
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s) {
     if ((long)p.N * p.H > 0) {
-        if (p.bf16) prop_dispatch<uint16_t>(p, s); else prop_dispatch<float>(p, s);
+        if (!p.bf16) prop_dispatch<float, float>(p, s);
+        else if (p.o_bf16) prop_dispatch<uint16_t, uint16_t>(p, s);
+        else prop_dispatch<uint16_t, float>(p, s);
     }
     return hipGetLastError();
 }

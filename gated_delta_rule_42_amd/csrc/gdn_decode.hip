@@ -38,7 +38,7 @@ __device__ __forceinline__ void load_vec(const TS* p, float (&x)[EPL]) {
 // One work-group per (sequence, head). Its 256 lanes form 16 groups of 16; group g owns
 // rows g, g+16, ...; within a group, lane l16 owns columns [l16*EPL, l16*EPL + EPL) so that
 // one group reads a whole row contiguously.
-template <typename TS, int DK, int DV>
+template <typename TS, typename TO, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     constexpr int EPL = DK / 16;   // state columns per lane
     constexpr int RPG = DV / 16;   // rows per lane group
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
 
     float* st = p.state + pr * (long)DV * DK + l16 * EPL;
     const TS* vp = static_cast<const TS*>(p.v) + pr * DV;
-    TS* op = static_cast<TS*>(p.o) + pr * DV;
+    TO* op = static_cast<TO*>(p.o) + pr * DV;
 
     float s[RPG][EPL];
     float vr[RPG];
@@ -92,28 +92,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
             x.w = alpha * s[it][e + 3] + c * kf[e + 3];
             *reinterpret_cast<float4*>(st + (long)row * DK + e) = x;
         }
-        if (l16 == 0) op[row] = from_f32<TS>(alpha * sq + c * kq);
+        if (l16 == 0) op[row] = from_f32<TO>(alpha * sq + c * kq);
     }
 }
 
-template <typename TS, int DK, int DV>
+template <typename TS, typename TO, int DK, int DV>
 static void decode_launch(const DecodeProblem& p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<TS, DK, DV>), dim3((unsigned)((long)p.N * p.H)), dim3(256), 0,
-                       s, p);
+    hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
+                       0, s, p);
 }
 
-template <typename TS>
+template <typename TS, typename TO>
 static void decode_dispatch(const DecodeProblem& p, hipStream_t s) {
     if (p.dk == 64) {
-        if (p.dv == 64) decode_launch<TS, 64, 64>(p, s); else decode_launch<TS, 64, 128>(p, s);
+        if (p.dv == 64) decode_launch<TS, TO, 64, 64>(p, s); else decode_launch<TS, TO, 64, 128>(p, s);
     } else {
-        if (p.dv == 64) decode_launch<TS, 128, 64>(p, s); else decode_launch<TS, 128, 128>(p, s);
+        if (p.dv == 64) decode_launch<TS, TO, 128, 64>(p, s); else decode_launch<TS, TO, 128, 128>(p, s);
     }
 }
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s) {
     if ((long)p.N * p.H > 0) {
-        if (p.bf16) decode_dispatch<uint16_t>(p, s); else decode_dispatch<float>(p, s);
+        if (p.bf16) {
+            if (p.o_bf16) decode_dispatch<uint16_t, uint16_t>(p, s); else decode_dispatch<uint16_t, float>(p, s);
+        } else {
+            if (p.o_bf16) decode_dispatch<float, uint16_t>(p, s); else decode_dispatch<float, float>(p, s);
+        }
     }
     return hipGetLastError();
 }

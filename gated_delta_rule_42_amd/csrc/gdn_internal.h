@@ -19,7 +19,8 @@ struct ChunkProblem {
     float* hT;
     const int32_t* cu_seqlens;   // NULL: fixed-length rows
     int B, T, H, dk, dv, N;
-    int bf16;                    // 1: q,k,v,o are bf16; 0: fp32
+    int bf16;                    // 1: q, k, v are bf16; 0: fp32
+    int o_bf16;                  // 1: o is bf16; 0: fp32
     long nc_bound;               // upper bound on the number of chunks (workspace rows)
     int nc_per_seq;              // chunks per row when cu_seqlens is NULL
     // workspace regions
@@ -48,7 +49,8 @@ struct DecodeProblem {
     float* state;
     void* o;
     int N, H, dk, dv;
-    int bf16;
+    int bf16;     // q, k, v are bf16 (else fp32)
+    int o_bf16;   // o is bf16 (else fp32)
 };
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);

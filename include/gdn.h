@@ -23,8 +23,12 @@
  *      states (h0, hT, decode state) [N, H, d_v, d_k] fp32 (d_k contiguous)
  *    The pages list the state as (heads, d_k, d_v); the product v k^T makes it d_v x d_k,
  *    which is the stored order here.
- *  - dtype: GDN_F32 (q, k, v, o fp32) or GDN_BF16 (q, k, v, o bfloat16). g, beta and all
- *    states are fp32 in both cases.
+ *  - dtype: GDN_F32 (q, k, v fp32) or GDN_BF16 (q, k, v bfloat16); o_dtype: GDN_F32 or
+ *    GDN_BF16 (bf16 o only with bf16 inputs). g, beta and all states are fp32 in every
+ *    case. Products run on the matrix cores with fp32 accumulation; bf16 inputs are
+ *    multiplied as fp16 (exact for bf16 values of magnitude 2^-14..65504), which also
+ *    carries the fp32 intermediates that become operands at 11 significant bits. A bf16 o
+ *    is the fp32 result rounded to nearest even.
  *  - g is log(alpha) and must be <= 0 (alpha in (0, 1]); beta is used as given. Neither is
  *    checked on the device. There is no query scale (o_t = S_t q_t exactly).
  *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and the call
@@ -75,8 +79,10 @@ const char *gdn_status_string(int status);
  * floor((T + N*63)/64) with them):
  *   chunk_base  int32 [N + 1]        first chunk index of each sequence (varlen only)
  *   gamma       fp32  [nc, H, 64]    in-chunk inclusive cumulative sum of g
- *   Mmat        dtype [nc, H, 64, 64] T diag(beta), T = (I + A)^{-1} (UT transform)
- *   Nmat        dtype [nc, H, 64, 64] P Mmat, P = (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]
+ *   Mmat        op    [nc, H, 64, 64] T diag(beta), T = (I + A)^{-1} (UT transform)
+ *   Nmat        op    [nc, H, 64, 64] P Mmat, P = (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]
+ * with op = fp16 for bf16 inputs and fp32 for fp32 inputs, rows and columns past a
+ * chunk's last token zero.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
@@ -92,7 +98,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  *   g_log_alpha [B, T, H] fp32, log of the decay, <= 0   (required)
  *   beta        [B, T, H] fp32, write strength           (required)
  *   h0          [N, H, dv, dk] fp32 initial states, or NULL for zeros
- *   o           [B, T, H, dv]  dtype, written            (required)
+ *   o           [B, T, H, dv]  o_dtype, written          (required)
  *   hT          [N, H, dv, dk] fp32 final states, written, or NULL. hT may be the same
  *               pointer as h0 (each state is read before it is overwritten); other
  *               overlaps are undefined.
@@ -103,7 +109,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  *               yields hT[n] = h0[n]. Without it, N must equal B and row b is sequence b.
  *   chunk       chunk length; 64 is the only one built
  *   B, T, H, dk, dv, N: sizes; dk, dv in {64, 128}; B, H >= 1; T >= 0
- *   dtype       gdn_dtype of q, k, v and o
+ *   dtype       gdn_dtype of q, k and v
+ *   o_dtype     gdn_dtype of o (GDN_F32, or GDN_BF16 when dtype is GDN_BF16)
  *   workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes,
  *               owned by the caller; may be NULL only when that size is 0
  *   stream      hipStream_t to enqueue on
@@ -112,7 +119,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g_log_alpha,
                   const float *beta, const float *h0, void *o, float *hT,
                   const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
-                  int N, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+                  int N, int dtype, int o_dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /*
  * Stage 1 of gdn_chunk_fwd, independent across chunks (no state dependency): per
@@ -137,7 +145,7 @@ int gdn_chunk_prepare(const void *q, const void *k, const float *g_log_alpha, co
  */
 int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float *h0, void *o,
                         float *hT, const int32_t *cu_seqlens, int chunk, int B, int T, int H,
-                        int dk, int dv, int N, int dtype, const void *workspace,
+                        int dk, int dv, int N, int dtype, int o_dtype, const void *workspace,
                         size_t workspace_bytes, void *stream);
 
 /*
@@ -149,12 +157,13 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  *   q, k   [N, H, dk] dtype        v [N, H, dv] dtype
  *   g_log_alpha, beta  [N, H] fp32
  *   state  [N, H, dv, dk] fp32, read and overwritten in place
- *   o      [N, H, dv] dtype, written
+ *   o      [N, H, dv] in o_dtype (GDN_F32 or GDN_BF16), written. All arithmetic is
+ *          fp32; a bf16 o is the fp32 result rounded to nearest even.
  * dk, dv in {64, 128}; N, H >= 1. Returns GDN_OK or a negative gdn_status.
  */
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_log_alpha,
                     const float *beta, float *state, void *o, int N, int H, int dk, int dv,
-                    int dtype, void *stream);
+                    int dtype, int o_dtype, void *stream);
 
 #ifdef __cplusplus
 }

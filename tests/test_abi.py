@@ -83,12 +83,15 @@ FAKE = 1 << 20  # an aligned, never dereferenced address: every call below fails
 
 
 def fwd(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, h0=None, o=FAKE, hT=None, cu=None, chunk=64,
-        B=1, T=128, H=2, dk=64, dv=64, N=1, dtype=1, ws=None, wsb=0):
-    return L.gdn_chunk_fwd(q, k, v, g, b, h0, o, hT, cu, chunk, B, T, H, dk, dv, N, dtype, ws, wsb, None)
+        B=1, T=128, H=2, dk=64, dv=64, N=1, dtype=1, o_dtype=1, ws=None, wsb=0):
+    return L.gdn_chunk_fwd(q, k, v, g, b, h0, o, hT, cu, chunk, B, T, H, dk, dv, N, dtype, o_dtype,
+                           ws, wsb, None)
 
 
 def test_chunk_fwd_rejects_before_any_launch(L):
     assert fwd(L, dtype=7) == ERR_DTYPE
+    assert fwd(L, o_dtype=3) == ERR_DTYPE
+    assert fwd(L, dtype=0, o_dtype=1) == ERR_DTYPE        # bf16 o needs bf16 inputs
     assert fwd(L, chunk=32) == ERR_UNSUP
     assert fwd(L, dk=96) == ERR_UNSUP
     assert fwd(L, dv=256) == ERR_UNSUP
@@ -111,15 +114,16 @@ def test_stage_entry_points_validate(L):
     assert L.gdn_chunk_prepare(None, FAKE, FAKE, FAKE, None, 64, 1, 128, 2, 64, 64, 1, 1, None, 0, None) == ERR_NULL
     assert L.gdn_chunk_prepare(FAKE, FAKE, FAKE, FAKE, None, 64, 1, 128, 2, 64, 64, 1, 1, None, 0, None) == ERR_WS
     assert L.gdn_chunk_propagate(FAKE, FAKE, None, None, FAKE, None, None, 64, 1, 128, 2, 64, 64, 1, 1,
-                                 None, 0, None) == ERR_NULL
+                                 1, None, 0, None) == ERR_NULL
     assert L.gdn_chunk_propagate(FAKE, FAKE, FAKE, None, FAKE, None, None, 64, 1, 128, 2, 64, 64, 1, 3,
-                                 None, 0, None) == ERR_DTYPE
+                                 0, None, 0, None) == ERR_DTYPE
 
 
 def test_decode_rejects_before_any_launch(L):
-    def dec(q=FAKE, state=FAKE, N=4, H=2, dk=128, dv=128, dtype=1):
-        return L.gdn_decode_step(q, FAKE, FAKE, FAKE, FAKE, state, FAKE, N, H, dk, dv, dtype, None)
+    def dec(q=FAKE, state=FAKE, N=4, H=2, dk=128, dv=128, dtype=1, o_dtype=0):
+        return L.gdn_decode_step(q, FAKE, FAKE, FAKE, FAKE, state, FAKE, N, H, dk, dv, dtype, o_dtype, None)
     assert dec(dtype=2) == ERR_DTYPE
+    assert dec(o_dtype=5) == ERR_DTYPE
     assert dec(dk=32) == ERR_UNSUP
     assert dec(N=0) == ERR_SHAPE
     assert dec(q=None) == ERR_NULL

@@ -4,8 +4,11 @@ Tolerances, per tensor:
   * fp32 q/k/v:  max|x - ref| / max|ref|        <= 1e-4
   * bf16 q/k/v (fp32 gates and state):  max|x - ref| <= 2e-2 * RMS(ref)
 The oracle reads back exactly the values the GPU receives (bf16 widened exactly), so input
-rounding is not counted as error. Full-size workloads are checked on sampled heads, which
-the oracle computes independently of the others.
+rounding is not counted as error. Outputs are compared in fp32 (o_dtype=fp32): for these
+heavy-tailed outputs (max|o| / RMS(o) reaches 12-19) a single bf16 rounding of the exact
+result already exceeds 2e-2 * RMS, so the bf16-output path is instead checked bit for bit
+against the fp32 output rounded to nearest even. Full-size workloads are checked on sampled
+heads, which the oracle computes independently of the others.
 """
 import numpy as np
 import pytest
@@ -44,13 +47,13 @@ def to_np(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def gpu_fwd(x, h0=None, hT=True):
+def gpu_fwd(x, h0=None, hT=True, o_dtype=torch.float32):
     dev = "cuda"
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     g, b = x["g"].to(dev), x["beta"].to(dev)
     h = None if h0 is None else h0.to(dev)
     cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(dev)
-    o, hTt = gb.gdn_chunk_fwd(q, k, v, g, b, h, cu, output_final_state=hT)
+    o, hTt = gb.gdn_chunk_fwd(q, k, v, g, b, h, cu, output_final_state=hT, o_dtype=o_dtype)
     torch.cuda.synchronize()
     return to_np(o), (None if hTt is None else to_np(hTt))
 
@@ -132,6 +135,22 @@ def test_fwd_empty_sequence_axis():
     assert o.shape == (2, 0, 2, 128) and np.array_equal(hT, x["h0"].double().numpy())
 
 
+@pytest.mark.parametrize("wid,kw", [(1, dict(T=300, B=2, H=3)), (3, dict(lengths=[100, 1, 64, 250], H=2))])
+def test_bf16_output_is_rounded_fp32_output(wid, kw):
+    """The bf16-output kernels compute the same fp32 values as the fp32-output kernels and
+    round them to nearest even: bit-for-bit equal to torch's rounding of the fp32 output."""
+    x = SY.make_forward_inputs(wid, **kw)
+    dev = "cuda"
+    q, k, v, g, b = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(dev)
+    h = None if x["h0"] is None else x["h0"].to(dev)
+    o32, h32 = gb.gdn_chunk_fwd(q, k, v, g, b, h, cu, o_dtype=torch.float32)
+    o16, h16 = gb.gdn_chunk_fwd(q, k, v, g, b, h, cu, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(h16, h32)
+
+
 def test_h0_none_equals_explicit_zeros():
     x = SY.make_forward_inputs(1, T=200, B=2, H=2)
     o1, h1 = gpu_fwd(x, None)
@@ -192,6 +211,7 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
     x = SY.make_forward_inputs(w, seed=11, gate_scale=0.2)
     dev = "cuda"
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    opdt = torch.float32 if dtype == "f32" else torch.float16   # operator storage type
     need = gb.gdn_chunk_fwd_workspace_bytes(1, T, H, dk, dk, 1, False, dtype=tdt)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     gb.gdn_chunk_prepare(x["q"].to(dev), x["k"].to(dev), x["g"].to(dev), x["beta"].to(dev), ws)
@@ -202,8 +222,8 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
     gam = ws[:nc * H * 64 * 4].view(torch.float32).view(nc, H, 64).cpu().double().numpy()
     off_m = al(nc * H * 64 * 4)
     off_n = al(off_m + nc * H * 4096 * el)
-    M = ws[off_m:off_m + nc * H * 4096 * el].view(tdt).view(nc, H, 64, 64).float().cpu().double().numpy()
-    Nm = ws[off_n:off_n + nc * H * 4096 * el].view(tdt).view(nc, H, 64, 64).float().cpu().double().numpy()
+    M = ws[off_m:off_m + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
+    Nm = ws[off_n:off_n + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
     f64 = lambda t: R._f64(t)[0]  # noqa: E731
     q, k, v, g, b = (f64(x[n]) for n in ("q", "k", "v", "g", "beta"))
     for c in range(nc):
@@ -214,7 +234,7 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
             m_ref = f["T"] * b[c0:c1, h][None, :]
             n_ref = ((q[c0:c1, h] @ k[c0:c1, h].T) * f["ratio"]) @ m_ref
             assert np.max(np.abs(gam[c, h, :n] - f["gamma"])) < 1e-5 * max(1, np.abs(f["gamma"]).max())
-            t = 1e-5 if dtype == "f32" else 2e-2
+            t = 1e-5 if dtype == "f32" else 2e-3
             assert np.max(np.abs(M[c, h, :n, :n] - m_ref)) <= t * max(np.abs(m_ref).max(), 1)
             assert np.max(np.abs(Nm[c, h, :n, :n] - n_ref)) <= t * max(np.abs(n_ref).max(), 1)
             assert not M[c, h, n:, :].any() and not M[c, h, :, n:].any()
@@ -254,6 +274,22 @@ def test_decode_small(dtype, dk, dv):
     w = SY.Workload(94, "decode_small", H=3, dk=dk, dv=dv, dtype=dtype, decode_seqs=5,
                     decode_steps=12)
     check_decode(SY.make_decode_inputs(w, seed=12))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_bf16_output_is_rounded_fp32_output(dtype):
+    """o written as bf16 is bit-for-bit the fp32 o rounded to nearest even (torch's rule)."""
+    w = SY.Workload(93, "decode_odtype", H=4, dk=128, dv=128, dtype=dtype, decode_seqs=7,
+                    decode_steps=1)
+    d = SY.make_decode_inputs(w, seed=13)
+    dev = "cuda"
+    tok = [d[n][0].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    s1, s2 = d["state"].to(dev), d["state"].to(dev)
+    o32 = gb.gdn_decode_step(*tok, s1, o_dtype=torch.float32)
+    o16 = gb.gdn_decode_step(*tok, s2, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(s1, s2)
 
 
 def test_decode_matches_forward_pass():
