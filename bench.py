@@ -49,6 +49,22 @@ def decode_bytes(dk, dv, elem=2, o_elem=4):
     return 2 * dk * dv * 4 + (2 * dk + dv) * elem + dv * o_elem + 8
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch (read + write) that rocprofv3 counters measured for `kernel` on
+    the benchmark workload (profiles/traffic.json), or None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    csrc = os.path.join(ROOT, "gated_delta_rule_42_amd", "csrc")
+    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in rec["sources"])).hexdigest()
+    return rec["read_bytes"] + rec["write_bytes"] if h == rec["source_sha256"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,13 +230,15 @@ def main():
             ach = c["stage2_bytes"] * th / (prop / 1e3)
             out["roofline"] = {"kernel": "chunk_propagate_kernel", "bound": "hbm",
                                "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                               "frac": ach / PEAK_HBM_BPS, "traffic": None,
+                               "frac": ach / PEAK_HBM_BPS,
+                               "traffic": measured_traffic("chunk_propagate_kernel"),
                                "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
         else:
             ach = c["stage1_flops"] * th / (prep / 1e3)
             out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
                                "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
-                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS, "traffic": None,
+                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
+                               "traffic": measured_traffic("chunk_prepare_kernel"),
                                "algorithmic_flops_per_launch": c["stage1_flops"] * th}
     if args.only in ("all", "decode"):
         d = bench_decode(args, torch, gb, SY)
@@ -233,7 +251,8 @@ def main():
                          "tokens_per_s": d["N"] / (mean / 1e3),
                          "hbm_GBps": per / (mean / 1e3) / 1e9,
                          "hbm_frac": per / (mean / 1e3) / PEAK_HBM_BPS,
-                         "bytes_per_step": per}
+                         "bytes_per_step": per,
+                         "traffic": measured_traffic("decode_kernel")}
         if args.only == "decode":
             out["value"] = d["N"] / (mean / 1e3)
             out["ms_per_step"] = mean
@@ -242,7 +261,8 @@ def main():
             out["roofline"] = {"kernel": "decode_kernel", "bound": "hbm",
                                "achieved": per / (mean / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                                "unit": "GB/s", "frac": per / (mean / 1e3) / PEAK_HBM_BPS,
-                               "traffic": None, "algorithmic_bytes_per_launch": per}
+                               "traffic": measured_traffic("decode_kernel"),
+                               "algorithmic_bytes_per_launch": per}
     if args.cpu_seconds > 0 and args.only != "decode":
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
