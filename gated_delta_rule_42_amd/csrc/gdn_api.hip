@@ -21,7 +21,9 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || T < 0) return GDN_ERR_SHAPE;
+    // H bound: one chunk of one head spans 64 token rows of H heads, addressed with 32-bit
+    // byte offsets inside the kernels
+    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
     if (cu) {
         if (B != 1 || N < 1) return GDN_ERR_SHAPE;
     } else if (N != B) {
@@ -34,14 +36,14 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
         if ((need & 1) && (!q || !k || !g || !beta)) return GDN_ERR_NULL;
         if ((need & 2) && (!q || !k || !v || !o)) return GDN_ERR_NULL;
     }
-    const void* al16[] = {q, k, v, o};
+    const void* al16[] = {q, k, v, o, h0, hT};
     for (const void* x : al16)
         if (x && !aligned(x, 16)) return GDN_ERR_ALIGN;
-    const void* al4[] = {h0, hT, g, beta, cu};
+    const void* al4[] = {g, beta, cu};
     for (const void* x : al4)
         if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
     const int elem = dtype == GDN_BF16 ? 2 : 4;
-    const gdn::WorkspaceLayout w = gdn::workspace_layout(B, T, H, N, cu != nullptr, elem);
+    const gdn::WorkspaceLayout w = gdn::workspace_layout(B, T, H, dk, N, cu != nullptr, elem);
     if (w.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
     if (w.total > 0 && (!ws || ws_bytes < w.total)) return GDN_ERR_WORKSPACE;
     if (ws && !aligned(ws, 256)) return GDN_ERR_ALIGN;
@@ -56,9 +58,11 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     P.nc_per_seq = (T + 63) / 64;
     char* base = static_cast<char*>(const_cast<void*>(ws));
     P.chunk_base = cu ? reinterpret_cast<int32_t*>(base + w.off_base) : nullptr;
-    P.gamma = w.nc_bound ? reinterpret_cast<float*>(base + w.off_gamma) : nullptr;
+    P.gates = w.nc_bound ? reinterpret_cast<float*>(base + w.off_gates) : nullptr;
     P.mmat = w.nc_bound ? base + w.off_m : nullptr;
-    P.nmat = w.nc_bound ? base + w.off_n : nullptr;
+    P.pmat = w.nc_bound ? base + w.off_p : nullptr;
+    P.k16 = (w.nc_bound && P.bf16) ? reinterpret_cast<_Float16*>(base + w.off_k16) : nullptr;
+    P.q16 = (w.nc_bound && P.bf16) ? reinterpret_cast<_Float16*>(base + w.off_q16) : nullptr;
     return GDN_OK;
 }
 
@@ -72,7 +76,7 @@ GDN_EXPORT const char* gdn_status_string(int status) {
         case GDN_ERR_NULL: return "a required pointer is NULL";
         case GDN_ERR_SHAPE: return "a size is out of range or inconsistent";
         case GDN_ERR_DTYPE: return "unknown dtype code";
-        case GDN_ERR_ALIGN: return "a pointer is misaligned (tensors 16 B, workspace 256 B)";
+        case GDN_ERR_ALIGN: return "a pointer is misaligned (q/k/v/o/states 16 B, gates 4 B, workspace 256 B)";
         case GDN_ERR_UNSUPPORTED: return "unsupported chunk size or head dimension (chunk 64; d_k, d_v in {64, 128})";
         case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_chunk_fwd_workspace_bytes()";
         case GDN_ERR_HIP: return "a HIP launch failed";
@@ -86,7 +90,7 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
     if (B < 1 || H < 1 || T < 0) return 0;
     if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
-    return gdn::workspace_layout(B, T, H, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
+    return gdn::workspace_layout(B, T, H, dk, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
 }
 
 GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, const float* beta,

@@ -10,16 +10,15 @@
 //   T     = (I + A)^{-1}                                                UT transform
 //   Mmat  = T diag(beta)             (so U = Mmat V and W = Mmat diag(e^gamma) K)
 //   P     = (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]    (read after the write)
-//   Nmat  = P Mmat
 //   R     = V - diag(e^gamma) K S^T
 //   Delta = Mmat R  (= U - W S^T)                                       effective writes
-//   O     = diag(e^gamma) Q S^T + Nmat R  (= diag(e^gamma) Q S^T + P Delta)
+//   O     = diag(e^gamma) Q S^T + P Delta
 //   S'    = e^{gamma_last} S + Delta^T diag(e^{gamma_last - gamma}) K
 //
-// Stage 1 (chunk_prepare_kernel) computes gamma, Mmat and Nmat for every chunk in
-// parallel. Stage 2 (chunk_propagate_kernel) walks the chunks of one (sequence, head,
-// d_v tile) in order, keeping the fp32 state tile in registers, and writes O.
-// Every gate factor is exp of a non-positive difference, masked before the exp.
+// Stage 1 (chunk_prepare_kernel) computes, for every chunk in parallel, the gate tables
+// e^gamma and e^{gamma_last - gamma}, Mmat and P. Stage 2 (chunk_propagate_kernel) walks the
+// chunks of one (sequence, head, d_v tile) in order with the fp32 state in registers and
+// writes O. Every gate factor is exp of a non-positive difference, masked before the exp.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -98,238 +97,37 @@ __device__ __forceinline__ bool locate_chunk(const ChunkProblem& p, long c, long
 }
 
 // ------------------------------------------------------------------- stage 1
-template <typename TM, int DK>
+template <typename TIn, int DK>
 struct alignas(16) PrepSmem {
-    static constexpr int PK = DK + 16 / (int)sizeof(TM);  // K, Q row pitch (elements)
-    static constexpr int PC = 64 + 16 / (int)sizeof(TM);  // P, Mt row pitch
-    static constexpr int PF = 68;                          // fp32 A, T row pitch
+    using TM = typename Operand<TIn>::type;
+    static constexpr int PK = DK + 16 / (int)sizeof(TIn);  // raw K, Q row pitch (elements)
+    static constexpr int PC = 64 + 16 / (int)sizeof(TM);   // P row pitch
+    static constexpr int PF = 68;                           // fp32 A, T row pitch
     union {
-        struct { TM K[64 * PK]; TM Q[64 * PK]; } in;
+        struct { TIn K[64 * PK]; TIn Q[64 * PK]; } in;
         struct { float A[64 * PF]; float T[64 * PF]; } tri;
     } u;
     TM P[64 * PC];
-    TM Mt[64 * PC];
     float gam[64];
     float beta[64];
 };
 
+// Register staging of one chunk's K, Q, g, beta (raw input elements).
 template <typename TIn, int DK>
-__global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
-    using TM = typename Operand<TIn>::type;
-    using SM = PrepSmem<TM, DK>;
-    constexpr int PK = SM::PK, PC = SM::PC, PF = SM::PF;
-    constexpr int EPV = 16 / (int)sizeof(TM);  // elements per 16-byte vector
-    constexpr int VPR = DK / EPV;              // vectors per K / Q row
-    __shared__ SM sm;
+struct PrepStage {
+    static constexpr int EPV = 16 / (int)sizeof(TIn);
+    static constexpr int VPR = DK / EPV;
+    static constexpr int NV = 64 * VPR / 256;
+    uint4 rk[NV], rq[NV];
+    float rg, rb;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
-    const int H = p.H;
-    const int h = (int)(blockIdx.x % H);
-    const long c = blockIdx.x / H;
-    long bos;
-    int len;
-    if (!locate_chunk(p, c, bos, len)) return;
-    const long widx = c * H + h;
-
-    // -- load K, Q (rows past the chunk end are zero), g, beta; scan g
-    const TIn* kp = static_cast<const TIn*>(p.k);
-    const TIn* qp = static_cast<const TIn*>(p.q);
-#pragma unroll
-    for (int it = 0; it < 64 * VPR / 256; ++it) {
-        const int vi = tid + 256 * it;
-        const int r = vi / VPR, cv = vi % VPR;
-        uint4 kv = zero16(), qv = zero16();
-        if (r < len) {
-            const long off = ((bos + r) * H + h) * DK + cv * EPV;
-            kv = to_operand16<TIn>(*reinterpret_cast<const uint4*>(kp + off));
-            qv = to_operand16<TIn>(*reinterpret_cast<const uint4*>(qp + off));
-        }
-        *reinterpret_cast<uint4*>(&sm.u.in.K[r * PK + cv * EPV]) = kv;
-        *reinterpret_cast<uint4*>(&sm.u.in.Q[r * PK + cv * EPV]) = qv;
-    }
-    if (wave == 0) {
-        float gg = 0.f, bb = 0.f;
-        if (lane < len) {
-            const long o = (bos + lane) * H + h;
-            gg = p.g[o];
-            bb = p.beta[o];
-        }
-        float x = gg;  // inclusive prefix sum over the 64 positions
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        sm.gam[lane] = x;
-        sm.beta[lane] = bb;
-        p.gamma[widx * 64 + lane] = x;
-    }
-    __syncthreads();
-
-    // -- K K^T and Q K^T on MFMA; wave w owns row block w, column blocks <= w
-    const int rb = wave;
-    f32x4_t G[4], P0[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        G[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        P0[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (cb <= rb) {
-            const TM* brow = &sm.u.in.K[(16 * cb + l16) * PK];
-            mma_nt<TM, DK>(G[cb], &sm.u.in.K[(16 * rb + l16) * PK], brow);
-            mma_nt<TM, DK>(P0[cb], &sm.u.in.Q[(16 * rb + l16) * PK], brow);
-        }
-    }
-    __syncthreads();  // K and Q are dead; their space becomes A and T
-
-    // -- gate the products: A (strictly lower, fp32) and P (lower incl. diagonal)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 16 * rb + 4 * lq + v, i = 16 * cb + l16;
-            float a = 0.f, pp = 0.f;
-            if (cb <= rb && i <= r) {
-                const float e = __expf(sm.gam[r] - sm.gam[i]);
-                if (i < r) a = sm.beta[r] * G[cb][v] * e;
-                pp = P0[cb][v] * e;
-            }
-            sm.u.tri.A[r * PF + i] = a;
-            sm.P[r * PC + i] = from_f32<TM>(pp);
-        }
-    }
-    __syncthreads();
-
-    // -- T = (I + A)^{-1}: the four 16x16 diagonal blocks by forward substitution, one
-    //    column per lane (wave 0) ...
-    float* At = sm.u.tri.A;
-    float* Tt = sm.u.tri.T;
-    if (wave == 0) {
-        const int b = lq, jc = l16;
-        const float* Ab = At + 16 * b * PF + 16 * b;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= Ab[r * PF + i] * x[i];
-            x[r] = acc;
-        }
-        float* Tb = Tt + 16 * b * PF + 16 * b;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tb[r * PF + jc] = x[r];
-    }
-    __syncthreads();
-    // ... then the blocks below the diagonal, one sub-diagonal at a time:
-    //    T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA, 16x16x4)
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        if (wave < 4 - d) {
-            const int ib = d + wave, jb = ib - d;
-            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            for (int m = jb; m < ib; ++m) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float a = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
-                    const float bb = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
-                    z = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, z, 0, 0, 0);
-                }
-            }
-            // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it as
-            // the right operand with k relabelled to 4*lq + s in step s.
-            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float a = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
-                t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[s], t, 0, 0, 0);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
-        }
-        __syncthreads();
-    }
-
-    // -- Mmat = T diag(beta): to the workspace (row-major) and, transposed, to LDS
-    {
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
-        float mv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int ci = c0 + e;
-            const float t = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
-            mv[e] = t * sm.beta[ci];
-            sm.Mt[ci * PC + r] = from_f32<TM>(mv[e]);
-        }
-        store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
-    }
-    __syncthreads();
-
-    // -- Nmat = P Mmat, staged through LDS for a coalesced store. P and Mmat are lower
-    //    triangular, so the tiles above the diagonal come out exactly zero; computing all
-    //    four costs no time (wave 3 needs four anyway) and needs no masking.
-    f32x4_t Nacc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        Nacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        mma_nt<TM, 64>(Nacc[cb], &sm.P[(16 * rb + l16) * PC], &sm.Mt[(16 * cb + l16) * PC]);
-    }
-    float* F = sm.u.tri.A;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) F[(16 * rb + 4 * lq + v) * PF + 16 * cb + l16] = Nacc[cb][v];
-    __syncthreads();
-    {
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
-        float nv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) nv[e] = F[r * PF + c0 + e];
-        store16<TM>(static_cast<TM*>(p.nmat) + widx * 4096 + r * 64 + c0, nv);
-    }
-}
-
-// ------------------------------------------------------------------- stage 2
-template <typename TM, int DK, int DVT>
-struct alignas(16) PropSmem {
-    static constexpr int PK = DK + 16 / (int)sizeof(TM);
-    static constexpr int PC = 64 + 16 / (int)sizeof(TM);
-    TM K[64 * PK];
-    TM Q[64 * PK];
-    TM V[64 * DVT];
-    TM M[64 * PC];
-    TM Nm[64 * PC];
-    TM S[DVT * PK];    // operand copy of the state tile, rows = d_v
-    TM Rt[DVT * PC];   // R^T, rows = d_v, columns = tokens
-    TM Dt[DVT * PC];   // (diag(e^{gamma_last - gamma}) Delta)^T
-    float gam[64];
-};
-
-// Global -> register -> LDS staging of one chunk's inputs (K, Q, the V tile, Mmat, Nmat,
-// gamma), so that the loads for chunk c+1 are in flight while chunk c is computed.
-template <typename TIn, int DK, int DV, int DVT>
-struct ChunkStage {
-    using TM = typename Operand<TIn>::type;
-    static constexpr int EPV = 16 / (int)sizeof(TM);
-    static constexpr int VPR_K = DK / EPV, NV_K = 64 * VPR_K / 256;
-    static constexpr int VPR_V = DVT / EPV, NV_V = (64 * VPR_V + 255) / 256;
-    static constexpr int VPR_M = 64 / EPV, NV_M = 64 * VPR_M / 256;
-    using SM = PropSmem<TM, DK, DVT>;
-    uint4 rk[NV_K], rq[NV_K], rv[NV_V], rm[NV_M], rn[NV_M];
-    float rg;
-
-    __device__ __forceinline__ void load(const ChunkProblem& p, long sbos, long seos, long cbase,
-                                         long jc, int h, int dv0, int tid) {
+    __device__ __forceinline__ void load(const ChunkProblem& p, long bos, int len, int h, int tid) {
         const int H = p.H;
-        const long bos = sbos + jc * kChunk;
-        const long lrem = seos - bos;
-        const int len = (int)(lrem < kChunk ? lrem : kChunk);
-        const long widx = (cbase + jc) * H + h;
         const TIn* kp = static_cast<const TIn*>(p.k);
         const TIn* qp = static_cast<const TIn*>(p.q);
-        const TIn* vp = static_cast<const TIn*>(p.v);
 #pragma unroll
-        for (int it = 0; it < NV_K; ++it) {
-            const int vi = tid + 256 * it, r = vi / VPR_K, cv = vi % VPR_K;
+        for (int it = 0; it < NV; ++it) {
+            const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
             rk[it] = zero16();
             rq[it] = zero16();
             if (r < len) {
@@ -338,70 +136,397 @@ struct ChunkStage {
                 rq[it] = *reinterpret_cast<const uint4*>(qp + off);
             }
         }
-#pragma unroll
-        for (int it = 0; it < NV_V; ++it) {
-            const int vi = tid + 256 * it, r = vi / VPR_V, cv = vi % VPR_V;
-            rv[it] = zero16();
-            if (vi < 64 * VPR_V && r < len)
-                rv[it] = *reinterpret_cast<const uint4*>(vp + ((bos + r) * H + h) * DV + dv0 + cv * EPV);
+        rg = 0.f;
+        rb = 0.f;
+        if (tid < len) {
+            const long o = (bos + tid) * H + h;
+            rg = p.g[o];
+            rb = p.beta[o];
         }
-        const uint4* mp = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.mmat) + widx * 4096);
-        const uint4* np = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.nmat) + widx * 4096);
-#pragma unroll
-        for (int it = 0; it < NV_M; ++it) {
-            rm[it] = mp[tid + 256 * it];
-            rn[it] = np[tid + 256 * it];
-        }
-        rg = tid < 64 ? p.gamma[widx * 64 + tid] : 0.f;
     }
 
-    __device__ __forceinline__ void store(SM& sm, int tid) const {
-        constexpr int PK = SM::PK, PC = SM::PC;
+    __device__ __forceinline__ void store(PrepSmem<TIn, DK>& sm, int tid) const {
+        constexpr int PK = PrepSmem<TIn, DK>::PK;
 #pragma unroll
-        for (int it = 0; it < NV_K; ++it) {
-            const int vi = tid + 256 * it, r = vi / VPR_K, cv = vi % VPR_K;
-            *reinterpret_cast<uint4*>(&sm.K[r * PK + cv * EPV]) = to_operand16<TIn>(rk[it]);
-            *reinterpret_cast<uint4*>(&sm.Q[r * PK + cv * EPV]) = to_operand16<TIn>(rq[it]);
+        for (int it = 0; it < NV; ++it) {
+            const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
+            *reinterpret_cast<uint4*>(&sm.u.in.K[r * PK + cv * EPV]) = rk[it];
+            *reinterpret_cast<uint4*>(&sm.u.in.Q[r * PK + cv * EPV]) = rq[it];
         }
+        if (tid < 64) {
+            sm.gam[tid] = rg;
+            sm.beta[tid] = rb;
+        }
+    }
+
+    // bf16 inputs: the chunk's K as fp16 rows [64, DK] (zero past the chunk's end), from the
+    // staged registers
+    __device__ __forceinline__ void write_k16(_Float16* dst, int tid) const {
+        if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
-        for (int it = 0; it < NV_V; ++it) {
-            const int vi = tid + 256 * it;
-            if (vi < 64 * VPR_V) *reinterpret_cast<uint4*>(&sm.V[vi * EPV]) = to_operand16<TIn>(rv[it]);
+            for (int it = 0; it < NV; ++it) {
+                const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
+                *reinterpret_cast<uint4*>(dst + r * DK + cv * EPV) = to_operand16<TIn>(rk[it]);
+            }
         }
-#pragma unroll
-        for (int it = 0; it < NV_M; ++it) {
-            const int vi = tid + 256 * it, r = vi / VPR_M, cv = vi % VPR_M;
-            *reinterpret_cast<uint4*>(&sm.M[r * PC + cv * EPV]) = rm[it];
-            *reinterpret_cast<uint4*>(&sm.Nm[r * PC + cv * EPV]) = rn[it];
-        }
-        if (tid < 64) sm.gam[tid] = rg;
     }
 };
 
-template <typename TIn, typename TO, int DK, int DV, int DVT>
-__global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
-    using TM = typename Operand<TIn>::type;
-    using SM = PropSmem<TM, DK, DVT>;
-    constexpr int PK = SM::PK, PC = SM::PC;
-    constexpr int NDB = DVT / 16;                       // d_v blocks in the tile
-    constexpr int NKB = DK / 16;                        // d_k blocks
-    constexpr int TPW = NDB * NKB / 4;                  // state tiles per wave
-    static_assert(TPW >= 1 && ChunkStage<TIn, DK, DV, DVT>::NV_K >= 1, "tile shape");
+// bf16 inputs: the chunk's diag(e^gamma) Q as fp16 rows [64, DK], from the raw Q in LDS and
+// the scanned gamma.
+template <typename TIn, int DK>
+__device__ __forceinline__ void write_q16(const PrepSmem<TIn, DK>& sm, _Float16* dst, int tid) {
+    if constexpr (sizeof(TIn) == 2) {
+        constexpr int PK = PrepSmem<TIn, DK>::PK, VPR = DK / 8, NV = 64 * VPR / 256;
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
+            const uint4 w = *reinterpret_cast<const uint4*>(&sm.u.in.Q[r * PK + cv * 8]);
+            const float e = __expf(sm.gam[r]);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = pack_f16x2(e * __uint_as_float(u[i] << 16), e * __uint_as_float(u[i] & 0xffff0000u));
+            *reinterpret_cast<uint4*>(dst + r * DK + cv * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// Persistent work-groups: each walks (chunk, head) units with a stride of the grid, keeping
+// the next unit's inputs in flight in registers while the current one is computed.
+template <typename TIn, int DK>
+__global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
+    using SM = PrepSmem<TIn, DK>;
+    using TM = typename SM::TM;
+    constexpr int PK = SM::PK, PC = SM::PC, PF = SM::PF;
     __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
+    const long nunits = p.nc_bound * H;
+
+    PrepStage<TIn, DK> stage;
+    long unit = blockIdx.x;
+    long bos = 0;
+    int len = 0;
+    bool ok = unit < nunits && locate_chunk(p, unit / H, bos, len);
+    if (ok) stage.load(p, bos, len, (int)(unit % H), tid);
+
+    while (unit < nunits) {
+        const long nxt = unit + gridDim.x;
+        long nbos = 0;
+        int nlen = 0;
+        const bool nok = nxt < nunits && locate_chunk(p, nxt / H, nbos, nlen);
+        if (ok) {
+            const long c = unit / H;
+            const int h = (int)(unit % H);
+            const long widx = c * H + h;
+            __syncthreads();  // the previous unit is done with LDS
+            stage.store(sm, tid);
+            if (p.k16) stage.write_k16(p.k16 + widx * 64 * DK, tid);
+            __syncthreads();
+            if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
+
+            // -- gate scan and gate tables (wave 0)
+            if (wave == 0) {
+                float x = sm.gam[lane];  // inclusive prefix sum of g over the 64 positions
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(x, off, 64);
+                    if (lane >= off) x += y;
+                }
+                const float last = __shfl(x, 63, 64);
+                sm.gam[lane] = x;
+                p.gates[widx * 128 + lane] = __expf(x);
+                p.gates[widx * 128 + 64 + lane] = __expf(last - x);
+            }
+            __syncthreads();
+            if (p.q16) write_q16<TIn, DK>(sm, p.q16 + widx * 64 * DK, tid);
+
+            // -- K K^T and Q K^T (exact products of the inputs); wave w owns row block w
+            const int rb = wave;
+            f32x4_t G[4], P0[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                G[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                P0[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                const TIn* brow = &sm.u.in.K[(16 * cb + l16) * PK];
+                mma_nt_in<TIn, DK>(G[cb], &sm.u.in.K[(16 * rb + l16) * PK], brow);
+                mma_nt_in<TIn, DK>(P0[cb], &sm.u.in.Q[(16 * rb + l16) * PK], brow);
+            }
+            __syncthreads();  // K and Q are dead; their space becomes A and T
+
+            // -- gate the products: A (strictly lower, fp32) and P (lower incl. diagonal)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * rb + 4 * lq + v, i = 16 * cb + l16;
+                    float a = 0.f, pp = 0.f;
+                    if (i <= r) {
+                        const float e = __expf(sm.gam[r] - sm.gam[i]);
+                        if (i < r) a = sm.beta[r] * G[cb][v] * e;
+                        pp = P0[cb][v] * e;
+                    }
+                    sm.u.tri.A[r * PF + i] = a;
+                    sm.P[r * PC + i] = from_f32<TM>(pp);
+                }
+            }
+            __syncthreads();
+
+            // -- T = (I + A)^{-1}. Diagonal 16x16 blocks: wave w inverts block w by forward
+            //    substitution, lane l16 computing column l16 with the block's strictly lower
+            //    entries held in registers.
+            float* At = sm.u.tri.A;
+            float* Tt = sm.u.tri.T;
+            {
+                const float* Ab = At + 16 * wave * PF + 16 * wave;
+                float a[16][16];
+#pragma unroll
+                for (int r = 1; r < 16; ++r)
+#pragma unroll
+                    for (int i = 0; i < r; ++i) a[r][i] = Ab[r * PF + i];
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc0 = (r == l16) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < r; i += 2) {
+                        acc0 -= a[r][i] * x[i];
+                        if (i + 1 < r) acc1 -= a[r][i + 1] * x[i + 1];
+                    }
+                    x[r] = acc0 + acc1;
+                }
+                if (lq == 0) {
+                    float* Tb = Tt + 16 * wave * PF + 16 * wave;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) Tb[r * PF + l16] = x[r];
+                }
+            }
+            __syncthreads();
+            // ... then the blocks below the diagonal, one sub-diagonal at a time:
+            //    T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA, 16x16x4)
+#pragma unroll
+            for (int d = 1; d < 4; ++d) {
+                if (wave < 4 - d) {
+                    const int ib = d + wave, jb = ib - d;
+                    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                    for (int m = jb; m < ib; ++m) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const float av = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
+                            const float bv = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
+                            z = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, z, 0, 0, 0);
+                        }
+                    }
+                    // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it
+                    // as the right operand with k relabelled to 4*lq + s in step s.
+                    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float av = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
+                        t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, z[s], t, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
+                }
+                __syncthreads();
+            }
+
+            // -- Mmat = T diag(beta) and P to the workspace, row-major, 16-byte stores
+            {
+                const int r = tid >> 2, c0 = (tid & 3) * 16;
+                float mv[16], pv[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int ci = c0 + e;
+                    mv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] * sm.beta[ci] : 0.f;
+                    pv[e] = to_f32(sm.P[r * PC + ci]);
+                }
+                store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+                store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+            }
+        } else if (nok) {
+            stage.load(p, nbos, nlen, (int)(nxt % H), tid);
+        }
+        unit = nxt;
+        ok = nok;
+    }
+}
+
+// ------------------------------------------------------------------- stage 2
+// Element offset of (row, col) in the LDS copy of K or Q. 16-bit operands with d_k = 128 use
+// an unpadded 256-byte row with its 8-byte granules XOR-swizzled by the row, so that both
+// ways the kernel reads K are free of bank conflicts: row fragments (16 rows x 8 bytes per
+// half-wave) and transposing reads (8 rows x 32 bytes per half-wave). The swizzle keeps each
+// even/odd granule pair adjacent, so 16-byte staging stores stay contiguous. Other shapes use
+// a padded row.
+template <typename TM, int DK>
+struct KQLayout {
+    static constexpr bool kSwizzle = sizeof(TM) == 2 && DK == 128;
+    static constexpr int kPitch = kSwizzle ? DK : DK + 16 / (int)sizeof(TM);
+    __device__ __forceinline__ static int off(int row, int col) {
+        if constexpr (kSwizzle) {
+            const int g = (col >> 2) ^ (4 * (row & 7) + 2 * ((row >> 3) & 1));
+            return row * DK + 4 * g + (col & 3);
+        } else {
+            return row * kPitch + col;
+        }
+    }
+};
+
+template <typename TIn, int DK, int DVT>
+struct alignas(16) PropSmem {
+    using TM = typename Operand<TIn>::type;
+    static constexpr int PK = KQLayout<TM, DK>::kPitch;    // K, Q row pitch (operand type)
+    static constexpr int PC = 64 + 16 / (int)sizeof(TM);   // Mmat, P row pitch
+    static constexpr int PV = DVT + 32 / (int)sizeof(TIn); // V tile row pitch (raw input)
+    TM K[64 * PK];
+    TM Q[64 * PK];
+    TM M[64 * PC];
+    TM P[64 * PC];
+    TIn V[64 * PV];
+    float eg[64];   // e^{gamma_r}
+    float ed[64];   // e^{gamma_last - gamma_r}
+};
+
+// Global -> register -> LDS staging of one chunk's inputs, so that the loads for chunk c+1
+// are in flight while chunk c is computed. K and Q are converted to the operand type on the
+// way into LDS; V stays in the input type (it is only used elementwise).
+template <typename TIn, int DK, int DV, int DVT>
+struct PropStage {
+    using TM = typename Operand<TIn>::type;
+    using SM = PropSmem<TIn, DK, DVT>;
+    using KL = KQLayout<TM, DK>;
+    static constexpr int NT = DVT / 16 * 64;                // threads
+    static constexpr int EPV = 16 / (int)sizeof(TIn);
+    static constexpr int VPR_K = DK / EPV, NV_K = 64 * VPR_K / NT;
+    static constexpr int VPR_V = DVT / EPV, NV_V = 64 * VPR_V / NT;
+    static constexpr int EPM = 16 / (int)sizeof(TM);
+    static constexpr int VPR_M = 64 / EPM, NV_M = 64 * VPR_M / NT;
+    static_assert(NV_K * NT == 64 * VPR_K && NV_V * NT == 64 * VPR_V && NV_M * NT == 64 * VPR_M,
+                  "staging shape");
+    uint4 rk[NV_K], rq[NV_K], rv[NV_V], rm[NV_M], rp[NV_M];
+    float4 rgt;
+
+    // Loads chunk (first token bos, len tokens) of head h; rows past len read as zeros. The
+    // loads are numbered in a fixed order and only those with number % nparts == part are
+    // issued, so that a caller can spread them over its compute (part and nparts fold to
+    // constants where the caller's loop is unrolled).
+    __device__ __forceinline__ void load(const ChunkProblem& p, long bos, int len, long widx, int h,
+                                         int dv0, int tid, int part = 0, int nparts = 1) {
+        const int H = p.H;
+        const long tok0 = bos * H + h;
+        constexpr int E = (int)sizeof(TIn);
+        const unsigned kbytes = (unsigned)((len - 1) * H * DK + DK) * E;
+        const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * E;
+        const auto kr = make_rsrc(static_cast<const TIn*>(p.k) + tok0 * DK, kbytes);
+        const auto qr = make_rsrc(static_cast<const TIn*>(p.q) + tok0 * DK, kbytes);
+        const auto vr = make_rsrc(static_cast<const TIn*>(p.v) + tok0 * DV + dv0, vbytes);
+        int n = 0;
+#pragma unroll
+        for (int it = 0; it < NV_K; ++it) {
+            const int vi = tid + NT * it, r = vi / VPR_K, cv = vi % VPR_K;
+            const int off = (r * H * DK + cv * EPV) * E;
+            if (n++ % nparts == part) rk[it] = buf_load16(kr, off);
+            if (n++ % nparts == part) rq[it] = buf_load16(qr, off);
+        }
+#pragma unroll
+        for (int it = 0; it < NV_V; ++it) {
+            const int vi = tid + NT * it, r = vi / VPR_V, cv = vi % VPR_V;
+            if (n++ % nparts == part) rv[it] = buf_load16(vr, (r * H * DV + cv * EPV) * E);
+        }
+        const uint4* mp = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.mmat) + widx * 4096);
+        const uint4* pp = reinterpret_cast<const uint4*>(static_cast<const TM*>(p.pmat) + widx * 4096);
+#pragma unroll
+        for (int it = 0; it < NV_M; ++it) {
+            if (n++ % nparts == part) rm[it] = mp[tid + NT * it];
+            if (n++ % nparts == part) rp[it] = pp[tid + NT * it];
+        }
+        if (n % nparts == part) rgt = reinterpret_cast<const float4*>(p.gates + widx * 128)[tid & 31];
+    }
+
+    __device__ __forceinline__ void store(SM& sm, int tid) const {
+#pragma unroll
+        for (int it = 0; it < NV_K; ++it) {
+            const int vi = tid + NT * it, r = vi / VPR_K, cv = vi % VPR_K;
+            const int o = KL::off(r, cv * EPV);
+            *reinterpret_cast<uint4*>(&sm.K[o]) = to_operand16<TIn>(rk[it]);
+            *reinterpret_cast<uint4*>(&sm.Q[o]) = to_operand16<TIn>(rq[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NV_V; ++it) {
+            const int vi = tid + NT * it, r = vi / VPR_V, cv = vi % VPR_V;
+            *reinterpret_cast<uint4*>(&sm.V[r * SM::PV + cv * EPV]) = rv[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NV_M; ++it) {
+            const int vi = tid + NT * it, r = vi / VPR_M, cv = vi % VPR_M;
+            *reinterpret_cast<uint4*>(&sm.M[r * SM::PC + cv * EPM]) = rm[it];
+            *reinterpret_cast<uint4*>(&sm.P[r * SM::PC + cv * EPM]) = rp[it];
+        }
+        if (tid < 32) reinterpret_cast<float4*>(sm.eg)[tid] = rgt;  // eg then ed, contiguous
+    }
+};
+
+// Operand fragment of K^T (rows d_k 16j + l16, k = tokens) read transposed from the LDS
+// copy of K: slots 0-3 are tokens t0 + 0..3, slots 4-7 tokens t1 + 0..3 (t0, t1 multiples
+// of 4). 16-bit operands use the gfx950 transposing read, lane s of each 16-lane group
+// addressing row t + s/4, columns 16j + 4*(s%4) .. +3.
+template <typename TM, int DK>
+__device__ __forceinline__ Frag<TM> load_kt(const TM* K, int t0, int t1, int j) {
+    using KL = KQLayout<TM, DK>;
+    const int l16 = threadIdx.x & 15;
+    if constexpr (sizeof(TM) == 2) {
+        const int rr = l16 >> 2, cc = 16 * j + 4 * (l16 & 3);
+        const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(K + KL::off(t0 + rr, cc)));
+        const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(K + KL::off(t1 + rr, cc)));
+        const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+        Frag<TM> f;
+        f.v = make_uint4(ua.x, ua.y, ub.x, ub.y);
+        return f;
+    } else {
+        const int c = 16 * j + l16;
+        Frag<TM> f;
+        f.lo = make_float4(K[KL::off(t0, c)], K[KL::off(t0 + 1, c)], K[KL::off(t0 + 2, c)], K[KL::off(t0 + 3, c)]);
+        f.hi = make_float4(K[KL::off(t1, c)], K[KL::off(t1 + 1, c)], K[KL::off(t1 + 2, c)], K[KL::off(t1 + 3, c)]);
+        return f;
+    }
+}
+
+// One work-group per (sequence, head, d_v tile of DVT columns); wave w owns the 16 columns
+// dv0 + 16w .. +15 for all 64 tokens of every chunk, so the waves only meet at the input
+// staging. The state is held transposed, S^T [d_k, 16], as d_k/16 accumulator tiles (lane
+// holds S[dv0 + 16w + l16][16j + 4*lq + 0..3]). Each product's accumulator feeds the next
+// product's right operand directly from registers (pack_frag); only the left operands (rows
+// of K, Q, Mmat, P, and K^T through transposing reads) come from LDS. A chunk's outputs are
+// written at the start of the next chunk, before its prefetch, so that waiting for the
+// prefetched inputs never waits for output stores.
+template <typename TIn, typename TO, int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkProblem p) {
+    using SM = PropSmem<TIn, DK, DVT>;
+    using TM = typename SM::TM;
+    using KL = KQLayout<TM, DK>;
+    constexpr int PC = SM::PC, PV = SM::PV;
+    constexpr int NKB = DK / 16;   // d_k tiles of the state
+    constexpr int NKS = DK / 32;   // 32-wide d_k slices
     constexpr int NTILE = DV / DVT;
+    __shared__ SM sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
 
     // (sequence, head) pair and d_v tile. When the pair count allows it, the NTILE tiles
     // of one pair get block ids that are equal modulo 8, i.e. land on the same XCD and
-    // share its L2 for K, Q and the chunk operators.
-    const long P = (long)p.N * H;
+    // share its L2 for K, Q, Mmat and P.
+    const long NP = (long)p.N * H;
     const long bid = blockIdx.x;
     long pair;
     int tile;
-    if (P % 8 == 0) {
+    if (NP % 8 == 0) {
         const long x = bid % 8, i = bid / 8;
         tile = (int)(i % NTILE);
         pair = (i / NTILE) * 8 + x;
@@ -411,129 +536,482 @@ __global__ __launch_bounds__(256) void chunk_propagate_kernel(ChunkProblem p) {
     }
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int dv0 = tile * DVT;
+    const int dvw = dv0 + 16 * wave;  // this wave's first d_v column
 
     long sbos, seos;
     seq_range(p, n, sbos, seos);
-    long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
     long nchunks = (seos - sbos + kChunk - 1) / kChunk;
     if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
 
-    // -- state tile: registers (fp32, accumulator layout) + operand copy in LDS
-    f32x4_t S[TPW];
+    // -- state S^T in accumulator tiles
+    f32x4_t ST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int ti = wave * TPW + u, a = ti / NKB, b = ti % NKB;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = 16 * a + 4 * lq + v, col = 16 * b + l16;
-            const float x = p.h0 ? p.h0[(pair * DV + dv0 + row) * DK + col] : 0.f;
-            S[u][v] = x;
-            sm.S[row * PK + col] = from_f32<TM>(x);
+    for (int j = 0; j < NKB; ++j) {
+        if (p.h0) {
+            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
+            ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    // -- chunk inputs staged through registers one chunk ahead
-    ChunkStage<TIn, DK, DV, DVT> stage;
-    TO* op = static_cast<TO*>(p.o);
-    if (nchunks > 0) stage.load(p, sbos, seos, cbase, 0, h, dv0, tid);
+    PropStage<TIn, DK, DV, DVT> stage;
+    auto chunk_len = [&](long jc) {
+        const long l = seos - (sbos + jc * kChunk);
+        return (int)(l < kChunk ? l : kChunk);
+    };
+    if (nchunks > 0) stage.load(p, sbos, chunk_len(0), cbase * H + h, h, dv0, tid);
+    // Outputs of the previous chunk, transposed (lane holds o[token 16t + l16][dvw + 4lq + v]),
+    // written one iteration late through a resource sized to the chunk's valid rows.
+    f32x4_t O[4];
+    long obos = 0;
+    int olen = 0;
+    auto store_out = [&]() {
+        constexpr int E = (int)sizeof(TO);
+        const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV,
+                                   (unsigned)((olen - 1) * H * DV + DV) * E);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + dvw + 4 * lq) * E, O[t]);
+    };
+
     for (long jc = 0; jc < nchunks; ++jc) {
-        __syncthreads();  // all reads of the previous chunk's LDS data are done
+        __syncthreads();  // every wave is done with the previous chunk's LDS data
         stage.store(sm, tid);
         __syncthreads();
-        if (jc + 1 < nchunks) stage.load(p, sbos, seos, cbase, jc + 1, h, dv0, tid);
-        const long bos = sbos + jc * kChunk;
-        const long lrem = seos - bos;
-        const int len = (int)(lrem < kChunk ? lrem : kChunk);
-        const float glast = sm.gam[63];
+        if (jc > 0) store_out();
+        // the next chunk's loads are issued a quarter at a time between the token tiles below
+        const bool more = jc + 1 < nchunks;
+        const long nbos = sbos + (jc + 1) * kChunk, nwidx = (cbase + jc + 1) * H + h;
+        const int nlen = more ? chunk_len(jc + 1) : 1;
 
-        // step 1-2: X = K S^T, Y = Q S^T (token block = wave); R = V - e^gamma X -> R^T
-        f32x4_t Yg[NDB];
+        // X = K S^T and Y = Q S^T: [64 tokens x 16 columns] as 4 token tiles
+        Frag<TM> BS[NKS];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-            const TM* srow = &sm.S[(16 * db + l16) * PK];
-            mma_nt<TM, DK>(x, &sm.K[(16 * wave + l16) * PK], srow);
-            mma_nt<TM, DK>(y, &sm.Q[(16 * wave + l16) * PK], srow);
-            float r4[4];
-            const int col = 16 * db + l16;
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_frag<TM>(ST[2 * s], ST[2 * s + 1]);
+        // Y^T = S Q^T is computed transposed ([16 columns x 64 tokens]) so that the output
+        // lands as runs of 4 consecutive columns per lane.
+        f32x4_t X[4], Y[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * wave + 4 * lq + v;
-                const float e = __expf(sm.gam[r]);
-                r4[v] = to_f32(sm.V[r * DVT + col]) - e * x[v];
-                Yg[db][v] = e * y[v];
+        for (int t = 0; t < 4; ++t) {
+            if (more) stage.load(p, nbos, nlen, nwidx, h, dv0, tid, t, 4);
+            X[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * t + l16;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int c0 = 32 * s + 4 * lq, c1 = c0 + 16;
+                mma_k32(X[t], load_frag2<TM>(&sm.K[KL::off(row, c0)], &sm.K[KL::off(row, c1)]), BS[s]);
+                mma_k32(Y[t], BS[s], load_frag2<TM>(&sm.Q[KL::off(row, c0)], &sm.Q[KL::off(row, c1)]));
             }
-            store4<TM>(&sm.Rt[col * PC + 16 * wave + 4 * lq], r4[0], r4[1], r4[2], r4[3]);
         }
-        __syncthreads();
 
-        // step 3: Delta = Mmat R, O = e^gamma Q S^T + Nmat R; Delta scaled for the state
+        // R = V - e^gamma X (fp32); Y^T scaled by e^gamma (one token per lane) for the output
+        f32x4_t R[4];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            f32x4_t dl = {0.f, 0.f, 0.f, 0.f}, oi = {0.f, 0.f, 0.f, 0.f};
-            const TM* rrow = &sm.Rt[(16 * db + l16) * PC];
-            mma_nt<TM, 64>(dl, &sm.M[(16 * wave + l16) * PC], rrow);
-            mma_nt<TM, 64>(oi, &sm.Nm[(16 * wave + l16) * PC], rrow);
-            float d4[4];
-            const int col = 16 * db + l16;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * wave + 4 * lq + v;
-                if (r < len) op[((bos + r) * H + h) * DV + dv0 + col] = from_f32<TO>(Yg[db][v] + oi[v]);
-                d4[v] = dl[v] * __expf(glast - sm.gam[r]);
-            }
-            store4<TM>(&sm.Dt[col * PC + 16 * wave + 4 * lq], d4[0], d4[1], d4[2], d4[3]);
+        for (int t = 0; t < 4; ++t) {
+            const float4 eg = *reinterpret_cast<const float4*>(&sm.eg[16 * t + 4 * lq]);
+            const float4 v4 = load4_t<TIn>(&sm.V[(16 * t + 4 * lq) * PV + 16 * wave], PV);
+            R[t] = f32x4_t{v4.x - eg.x * X[t][0], v4.y - eg.y * X[t][1], v4.z - eg.z * X[t][2],
+                           v4.w - eg.w * X[t][3]};
+            Y[t] *= sm.eg[16 * t + l16];
         }
-        __syncthreads();
 
-        // step 4: S = e^{gamma_last} S + Dt K   (contraction over the chunk's tokens)
-        const float eg = __expf(glast);
+        // Delta = Mmat R  (contraction over the chunk's tokens)
+        const Frag<TM> BR0 = pack_frag<TM>(R[0], R[1]), BR1 = pack_frag<TM>(R[2], R[3]);
+        f32x4_t D[4];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int ti = wave * TPW + u, a = ti / NKB, b = ti % NKB;
-            f32x4_t acc = S[u] * eg;
+        for (int t = 0; t < 4; ++t) {
+            D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const TM* mrow = &sm.M[(16 * t + l16) * PC + 4 * lq];
+            mma_k32(D[t], load_frag2<TM>(mrow, mrow + 16), BR0);
+            mma_k32(D[t], load_frag2<TM>(mrow + 32, mrow + 48), BR1);
+        }
+
+        // O^T = e^gamma S Q^T + Delta^T P^T (kept in registers until the next iteration)
+        const Frag<TM> BD0 = pack_frag<TM>(D[0], D[1]), BD1 = pack_frag<TM>(D[2], D[3]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const Frag<TM> fa = load_frag<TM>(&sm.Dt[(16 * a + l16) * PC + 32 * ks + 8 * lq]);
-                const Frag<TM> fb = gather_frag<TM>(&sm.K[(32 * ks + 8 * lq) * PK + 16 * b + l16], PK);
-                mma_k32(acc, fa, fb);
-            }
-            S[u] = acc;
+        for (int t = 0; t < 4; ++t) {
+            O[t] = Y[t];
+            const TM* prow = &sm.P[(16 * t + l16) * PC + 4 * lq];
+            mma_k32(O[t], BD0, load_frag2<TM>(prow, prow + 16));
+            mma_k32(O[t], BD1, load_frag2<TM>(prow + 32, prow + 48));
+        }
+        obos = sbos + jc * kChunk;
+        olen = chunk_len(jc);
+
+        // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
+        f32x4_t Dd[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sm.S[(16 * a + 4 * lq + v) * PK + 16 * b + l16] = from_f32<TM>(acc[v]);
+        for (int t = 0; t < 4; ++t) {
+            const float4 ed = *reinterpret_cast<const float4*>(&sm.ed[16 * t + 4 * lq]);
+            Dd[t] = f32x4_t{ed.x * D[t][0], ed.y * D[t][1], ed.z * D[t][2], ed.w * D[t][3]};
+        }
+        const Frag<TM> BT0 = pack_frag<TM>(Dd[0], Dd[1]), BT1 = pack_frag<TM>(Dd[2], Dd[3]);
+        const float elast = sm.eg[63];
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            f32x4_t acc = ST[j] * elast;
+            mma_k32(acc, load_kt<TM, DK>(sm.K, 4 * lq, 16 + 4 * lq, j), BT0);
+            mma_k32(acc, load_kt<TM, DK>(sm.K, 32 + 4 * lq, 48 + 4 * lq, j), BT1);
+            ST[j] = acc;
         }
     }
+    if (nchunks > 0) store_out();
 
     if (p.hT) {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int ti = wave * TPW + u, a = ti / NKB, b = ti % NKB;
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    }
+}
+
+// ------------------------------------------------------- stage 2, bf16 inputs (DMA)
+// Stage 2 for bf16 inputs. Each chunk's operands are copied global -> LDS by the DMA path of
+// the buffer loads (no registers, no conversion), double-buffered so that chunk c+1 is in
+// flight while chunk c is computed, with one barrier per chunk. Stage 1 leaves every matrix
+// operand in fp16 (K, diag(e^gamma) Q, Mmat, P; rows past the chunk's end zero); V stays bf16
+// and enters only the fp32 residual. All products run on the fp16 matrix core.
+//
+// 16-byte pieces of each LDS row are permuted by the row (XOR with swz_kq / swz_mp) so that
+// the row-fragment reads (16 rows x 8 bytes per half-wave) and the transposing reads of K
+// (8 rows x 32 bytes) hit distinct banks. The DMA applies the permutation on the global side.
+template <int DK>
+__device__ __forceinline__ int swz_kq(int r) {
+    if constexpr (DK == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return (r >> 1) & 7;
+}
+__device__ __forceinline__ int swz_mp(int r) { return (r >> 1) & 7; }
+template <int DK>
+__device__ __forceinline__ int off_kq(int r, int c) { return r * DK + 8 * ((c >> 3) ^ swz_kq<DK>(r)) + (c & 7); }
+__device__ __forceinline__ int off_mp(int r, int c) { return r * 64 + 8 * ((c >> 3) ^ swz_mp(r)) + (c & 7); }
+
+template <int DK, int DVT>
+struct alignas(1024) DmaChunk {
+    _Float16 K[64 * DK];
+    _Float16 Q[64 * DK];   // diag(e^gamma) Q
+    _Float16 M[64 * 64];   // Mmat
+    _Float16 P[64 * 64];
+    uint16_t V[64 * DVT];  // bf16, the work-group's d_v columns
+    float eg[64];          // e^{gamma_r}
+    float ed[64];          // e^{gamma_last - gamma_r}
+};
+
+// Which 1 KB DMA blocks of a chunk each wave copies, and in which of `nparts` slices of the
+// compute it issues them. Wave w copies blocks w*n .. w*n + n-1 of each array.
+template <int DK, int DV, int DVT>
+struct DmaPlan {
+    static constexpr int NW = DVT / 16;
+    static constexpr int NB_KQ = 64 * DK * 2 / 1024;
+    static constexpr int NB_MP = 8;
+    static constexpr int NB_V = 64 * DVT * 2 / 1024;
+    static constexpr int W_KQ = NB_KQ / NW, W_MP = NB_MP / NW, W_V = NB_V / NW;
+    static_assert(W_KQ * NW == NB_KQ && W_MP * NW == NB_MP && W_V * NW == NB_V && W_V > 0, "DMA split");
+    static constexpr int ROW_KQ = DK * 2, ROW_V = DVT * 2;  // LDS row bytes
+
+    // Issues this wave's share of slice `part` for chunk (bos, len) of head h into `dst`.
+    __device__ __forceinline__ static void issue(DmaChunk<DK, DVT>& dst, const ChunkProblem& p,
+                                                 long bos, int len, long widx, int h, int dv0,
+                                                 int wave, int lane, int part, int nparts) {
+        const int H = p.H;
+        const long tok0 = bos * H + h;
+        const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
+        const auto kr = make_rsrc(p.k16 + widx * 64 * DK, 64 * DK * 2);
+        const auto qr = make_rsrc(p.q16 + widx * 64 * DK, 64 * DK * 2);
+        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + tok0 * DV + dv0, vbytes);
+        const auto mr = make_rsrc(static_cast<const _Float16*>(p.mmat) + widx * 4096, 8192);
+        const auto pr = make_rsrc(static_cast<const _Float16*>(p.pmat) + widx * 4096, 8192);
+        int n = 0;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                p.hT[(pair * DV + dv0 + 16 * a + 4 * lq + v) * DK + 16 * b + l16] = S[u][v];
+        for (int j = 0; j < W_KQ; ++j) {
+            const int b = wave * W_KQ + j;
+            const int byte = 1024 * b + 16 * lane, r = byte / ROW_KQ;
+            const int piece = ((byte % ROW_KQ) >> 4) ^ swz_kq<DK>(r);
+            const int off = r * DK * 2 + 16 * piece;
+            if (n++ % nparts == part) dma16(kr, reinterpret_cast<const char*>(dst.K) + 1024 * b, off);
+            if (n++ % nparts == part) dma16(qr, reinterpret_cast<const char*>(dst.Q) + 1024 * b, off);
         }
+#pragma unroll
+        for (int j = 0; j < W_MP; ++j) {
+            const int b = wave * W_MP + j;
+            const int byte = 1024 * b + 16 * lane, r = byte >> 7;
+            const int off = 128 * r + 16 * (((byte & 127) >> 4) ^ swz_mp(r));
+            if (n++ % nparts == part) dma16(mr, reinterpret_cast<const char*>(dst.M) + 1024 * b, off);
+            if (n++ % nparts == part) dma16(pr, reinterpret_cast<const char*>(dst.P) + 1024 * b, off);
+        }
+#pragma unroll
+        for (int j = 0; j < W_V; ++j) {
+            const int b = wave * W_V + j;
+            const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
+            const int off = r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4);
+            if (n++ % nparts == part) dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, off);
+        }
+        if (n % nparts == part && wave == 0 && lane < 32) {
+            const auto gr = make_rsrc(p.gates + widx * 128, 512);
+            dma16(gr, dst.eg, 16 * lane);
+        }
+    }
+};
+
+// One work-group per (sequence, head, DVT-column tile); wave w owns columns dv0 + 16w .. +15
+// for all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
+// S[dv0 + 16w + l16][16j + 4*lq + 0..3]). The products are those of the generic stage-2 kernel
+// (chunk_propagate_kernel), with the operand formats described above.
+template <typename TO, int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
+    using Plan = DmaPlan<DK, DV, DVT>;
+    using Buf = DmaChunk<DK, DVT>;
+    constexpr int NKB = DK / 16;   // d_k tiles of the state
+    constexpr int NKS = DK / 32;   // 32-wide d_k slices
+    constexpr int NTILE = DV / DVT;
+    __shared__ Buf buf0;
+    __shared__ Buf buf1;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+
+    // (sequence, head) pair and column tile; with a pair count divisible by 8 the tiles of one
+    // pair get block ids equal modulo 8 (same XCD, shared L2 for K, Q, Mmat and P)
+    const long NP = (long)p.N * H;
+    const long bid = blockIdx.x;
+    long pair;
+    int tile;
+    if (NP % 8 == 0) {
+        const long x = bid % 8, i = bid / 8;
+        tile = (int)(i % NTILE);
+        pair = (i / NTILE) * 8 + x;
+    } else {
+        pair = bid / NTILE;
+        tile = (int)(bid % NTILE);
+    }
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT;
+    const int dvw = dv0 + 16 * wave;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + kChunk - 1) / kChunk;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+    auto chunk_len = [&](long jc) {
+        const long l = seos - (sbos + jc * kChunk);
+        return (int)(l < kChunk ? l : kChunk);
+    };
+
+    f32x4_t ST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        if (p.h0) {
+            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
+            ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // outputs of the previous chunk, transposed (lane: o[token 16t + l16][dvw + 4lq + v]),
+    // written at the start of the next chunk through a resource sized to its valid rows
+    f32x4_t O[4];
+    long obos = 0;
+    int olen = 0;
+    auto store_out = [&]() {
+        constexpr int E = (int)sizeof(TO);
+        const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV,
+                                   (unsigned)((olen - 1) * H * DV + DV) * E);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + dvw + 4 * lq) * E, O[t]);
+    };
+
+    // The next chunk's copies are issued in kParts slices spread over the phases of a chunk.
+    // LDS operands are read ahead of the products that use them (those that do not depend on
+    // the state right after the barrier, the X/Y fragments one 32-wide slice ahead, K^T during
+    // the output product), and each product phase cycles over independent accumulators; the
+    // scheduling fences keep that order.
+    constexpr int kParts = 8;
+    auto step = [&](Buf& cur, Buf& nxt, long jc) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into cur have landed
+        __syncthreads();                // ... and every wave's; nobody reads nxt any more
+        if (jc > 0) store_out();
+        const bool more = jc + 1 < nchunks;
+        const long nbos = sbos + (jc + 1) * kChunk, nwidx = (cbase + jc + 1) * H + h;
+        const int nlen = more ? chunk_len(jc + 1) : 1;
+        auto dma = [&](int part) {
+            if (more) Plan::issue(nxt, p, nbos, nlen, nwidx, h, dv0, wave, lane, part, kParts);
+        };
+
+        // operands read one phase ahead of their products
+        uint4 MF[4][2], PF[4][2];
+        float4 V4[4], EG4[4];
+        auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int row = 16 * t + l16, c = 32 * hf + 4 * lq;
+                    f[t][hf] = lds_frag2(&src[off_mp(row, c)], &src[off_mp(row, c + 16)]);
+                }
+        };
+        auto load_r = [&]() {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                V4[t] = load4_t<uint16_t>(&cur.V[(16 * t + 4 * lq) * DVT + 16 * wave], DVT);
+                EG4[t] = *reinterpret_cast<const float4*>(&cur.eg[16 * t + 4 * lq]);
+            }
+        };
+
+        // X = K S^T [64 tokens x 16 columns] and Y^T = S (diag(e^gamma) Q)^T [16 columns x 64 tokens]
+        uint4 BS[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_f16_frag(ST[2 * s], ST[2 * s + 1]);
+        uint4 KF[2][4], QF[2][4];  // fragments of slice s in [s % 2]
+        auto load_xy = [&](int s, uint4 (&kf)[4], uint4 (&qf)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int row = 16 * t + l16, c0 = 32 * s + 4 * lq;
+                kf[t] = lds_frag2(&cur.K[off_kq<DK>(row, c0)], &cur.K[off_kq<DK>(row, c0 + 16)]);
+                qf[t] = lds_frag2(&cur.Q[off_kq<DK>(row, c0)], &cur.Q[off_kq<DK>(row, c0 + 16)]);
+            }
+        };
+        load_xy(0, KF[0], QF[0]);
+        f32x4_t X[4], Y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            X[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int b = s & 1;
+            if (s + 1 < NKS) load_xy(s + 1, KF[b ^ 1], QF[b ^ 1]);
+            else {
+                load_r();
+                load_mp(cur.M, MF);
+            }
+            dma(s % 4);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                X[t] = mfma_f16(KF[b][t], BS[s], X[t]);
+                Y[t] = mfma_f16(BS[s], QF[b][t], Y[t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (NKS < 4) {
+#pragma unroll
+            for (int part = NKS; part < 4; ++part) dma(part);
+        }
+
+        // R = V - e^gamma X
+        dma(4);
+        f32x4_t R[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            R[t] = f32x4_t{V4[t].x - EG4[t].x * X[t][0], V4[t].y - EG4[t].y * X[t][1],
+                           V4[t].z - EG4[t].z * X[t][2], V4[t].w - EG4[t].w * X[t][3]};
+
+        // Delta = Mmat R
+        load_mp(cur.P, PF);
+        const uint4 BR[2] = {pack_f16_frag(R[0], R[1]), pack_f16_frag(R[2], R[3])};
+        f32x4_t D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) D[t] = mfma_f16(MF[t][hf], BR[hf], D[t]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // K^T fragments for the state update, read while the output product runs
+        const int tr = l16 >> 2, tc = 4 * (l16 & 3);
+        uint4 KT[NKB][2];
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            const int c = 16 * j + tc;
+            KT[j][0] = lds_frag2_t(&cur.K[off_kq<DK>(4 * lq + tr, c)], &cur.K[off_kq<DK>(16 + 4 * lq + tr, c)]);
+            KT[j][1] = lds_frag2_t(&cur.K[off_kq<DK>(32 + 4 * lq + tr, c)], &cur.K[off_kq<DK>(48 + 4 * lq + tr, c)]);
+        }
+        dma(5);
+
+        // O^T = e^gamma S Q^T + Delta^T P^T
+        const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) O[t] = Y[t];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+        obos = sbos + jc * kChunk;
+        olen = chunk_len(jc);
+        dma(6);
+
+        // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
+        f32x4_t Dd[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 ed = *reinterpret_cast<const float4*>(&cur.ed[16 * t + 4 * lq]);
+            Dd[t] = f32x4_t{ed.x * D[t][0], ed.y * D[t][1], ed.z * D[t][2], ed.w * D[t][3]};
+        }
+        const float elast = cur.eg[63];
+        const uint4 BT[2] = {pack_f16_frag(Dd[0], Dd[1]), pack_f16_frag(Dd[2], Dd[3])};
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) ST[j] *= elast;
+        dma(7);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
+    };
+
+    if (nchunks > 0) {
+#pragma unroll
+        for (int part = 0; part < kParts; ++part)
+            Plan::issue(buf0, p, sbos, chunk_len(0), cbase * H + h, h, dv0, wave, lane, part, kParts);
+    }
+    for (long jc = 0; jc < nchunks; jc += 2) {
+        step(buf0, buf1, jc);
+        if (jc + 1 < nchunks) step(buf1, buf0, jc + 1);
+    }
+    if (nchunks > 0) store_out();
+
+    if (p.hT) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
     }
 }
 
 // -------------------------------------------------------------------- launchers
-WorkspaceLayout workspace_layout(int B, int T, int H, int N, int varlen, int elem_bytes) {
+WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     WorkspaceLayout w{};
     w.nc_bound = varlen ? ((long)T + (long)N * (kChunk - 1)) / kChunk
                         : (long)B * (((long)T + kChunk - 1) / kChunk);
+    const size_t units = (size_t)w.nc_bound * H;
     w.off_base = 0;
     const size_t base_bytes = varlen ? (size_t)(N + 1) * 4 : 0;
-    w.off_gamma = al(base_bytes);
-    w.off_m = al(w.off_gamma + (size_t)w.nc_bound * H * 64 * 4);
-    w.off_n = al(w.off_m + (size_t)w.nc_bound * H * 4096 * elem_bytes);
-    w.total = w.off_n + (size_t)w.nc_bound * H * 4096 * elem_bytes;
+    w.off_gates = al(base_bytes);
+    w.off_m = al(w.off_gates + units * 128 * 4);
+    w.off_p = al(w.off_m + units * 4096 * elem_bytes);
+    w.total = w.off_p + units * 4096 * elem_bytes;
+    if (elem_bytes == 2) {  // fp16 copies of K and of diag(e^gamma) Q
+        w.off_k16 = al(w.total);
+        w.off_q16 = al(w.off_k16 + units * 64 * dk * 2);
+        w.total = w.off_q16 + units * 64 * dk * 2;
+    }
     if (w.nc_bound == 0) w.total = al(base_bytes);
     return w;
 }
 
 template <typename TIn, int DK>
 static void prep_launch(const ChunkProblem& p, hipStream_t s) {
-    const long blocks = p.nc_bound * p.H;
+    // persistent grid: up to 3 resident work-groups per CU on 256 CUs
+    const long units = p.nc_bound * p.H;
+    const long blocks = units < 768 ? units : 768;
     hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
 }
 
@@ -553,11 +1031,18 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
 
 template <typename TIn, typename TO, int DK, int DV>
 static void prop_launch(const ChunkProblem& p, hipStream_t s) {
-    // d_v rows per work-group; fp32 operands with d_k = 128 use 16 to stay inside 160 KB of LDS
-    constexpr int DVT = (sizeof(TIn) == 4 && DK == 128) ? 16 : 32;
-    const long blocks = (long)p.N * p.H * (DV / DVT);
-    hipLaunchKernelGGL((chunk_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)blocks),
-                       dim3(256), 0, s, p);
+    if constexpr (sizeof(TIn) == 2) {
+        // bf16: two waves (32 columns) per work-group
+        constexpr int DVT = 32;
+        const long blocks = (long)p.N * p.H * (DV / DVT);
+        hipLaunchKernelGGL((chunk_propagate_bf16_kernel<TO, DK, DV, DVT>), dim3((unsigned)blocks),
+                           dim3(DVT / 16 * 64), 0, s, p);
+    } else {
+        constexpr int DVT = 32;  // two waves of 16 columns (LDS size)
+        const long blocks = (long)p.N * p.H * (DV / DVT);
+        hipLaunchKernelGGL((chunk_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)blocks),
+                           dim3(DVT / 16 * 64), 0, s, p);
+    }
 }
 
 template <typename TIn, typename TO>

@@ -25,17 +25,19 @@ struct ChunkProblem {
     int nc_per_seq;              // chunks per row when cu_seqlens is NULL
     // workspace regions
     int32_t* chunk_base;         // [N + 1] (varlen only)
-    float* gamma;                // [nc_bound, H, 64]
-    void* mmat;                  // [nc_bound, H, 64, 64] element type of q
-    void* nmat;                  // [nc_bound, H, 64, 64]
+    float* gates;                // [nc_bound, H, 128]: e^gamma (64), e^{gamma_last - gamma} (64)
+    void* mmat;                  // [nc_bound, H, 64, 64] operand type (fp16 or fp32)
+    void* pmat;                  // [nc_bound, H, 64, 64] operand type
+    _Float16* k16;               // [nc_bound, H, 64, dk] fp16 K (bf16 inputs only)
+    _Float16* q16;               // [nc_bound, H, 64, dk] fp16 diag(e^gamma) Q (bf16 inputs only)
 };
 
 struct WorkspaceLayout {
-    size_t off_base, off_gamma, off_m, off_n, total;
+    size_t off_base, off_gates, off_m, off_p, off_k16, off_q16, total;
     long nc_bound;
 };
 
-WorkspaceLayout workspace_layout(int B, int T, int H, int N, int varlen, int elem_bytes);
+WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes);
 
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);

@@ -35,7 +35,7 @@
  *    returns at once. The return code reports host-side argument checks, which all run
  *    before any HIP call, and launch errors; faults during execution surface at the
  *    caller's next synchronisation.
- *  - Alignment: q, k, v, o and the decode state 16 bytes; g, beta, h0, hT and cu_seqlens
+ *  - Alignment: q, k, v, o, h0, hT and the decode state 16 bytes; g, beta and cu_seqlens
  *    4 bytes; the workspace 256 bytes. A misaligned pointer gives GDN_ERR_ALIGN.
  */
 #ifndef GDN_H_
@@ -77,12 +77,15 @@ const char *gdn_status_string(int status);
  * Workspace contents (all regions 256-byte aligned, in this order; `nc` is an upper
  * bound on the number of chunks, ceil(T/64)*B without cu_seqlens and
  * floor((T + N*63)/64) with them):
- *   chunk_base  int32 [N + 1]        first chunk index of each sequence (varlen only)
- *   gamma       fp32  [nc, H, 64]    in-chunk inclusive cumulative sum of g
+ *   chunk_base  int32 [N + 1]         first chunk index of each sequence (varlen only)
+ *   gates       fp32  [nc, H, 128]    exp(gamma_r) for r < 64, then exp(gamma_last - gamma_r),
+ *                                     gamma = in-chunk inclusive cumulative sum of g
  *   Mmat        op    [nc, H, 64, 64] T diag(beta), T = (I + A)^{-1} (UT transform)
- *   Nmat        op    [nc, H, 64, 64] P Mmat, P = (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]
- * with op = fp16 for bf16 inputs and fp32 for fp32 inputs, rows and columns past a
- * chunk's last token zero.
+ *   P           op    [nc, H, 64, 64] (Q K^T) * exp(gamma_r - gamma_i) * [i <= r]
+ *   K16         fp16  [nc, H, 64, dk] the chunk's K rows          (bf16 inputs only)
+ *   Q16         fp16  [nc, H, 64, dk] diag(exp(gamma)) Q          (bf16 inputs only)
+ * with op = fp16 for bf16 inputs and fp32 for fp32 inputs; rows and columns past a chunk's
+ * last token are zero and gamma stays constant there.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
@@ -108,7 +111,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  *               device). Each sequence starts from h0[n] (or zeros); a zero-length one
  *               yields hT[n] = h0[n]. Without it, N must equal B and row b is sequence b.
  *   chunk       chunk length; 64 is the only one built
- *   B, T, H, dk, dv, N: sizes; dk, dv in {64, 128}; B, H >= 1; T >= 0
+ *   B, T, H, dk, dv, N: sizes; dk, dv in {64, 128}; B, H >= 1; T >= 0; H <= 32768
  *   dtype       gdn_dtype of q, k and v
  *   o_dtype     gdn_dtype of o (GDN_F32, or GDN_BF16 when dtype is GDN_BF16)
  *   workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes,
@@ -124,8 +127,8 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g_lo
 
 /*
  * Stage 1 of gdn_chunk_fwd, independent across chunks (no state dependency): per
- * (chunk, head) the in-chunk gate scan, the gated Gram matrix A, the UT transform
- * T = (I + A)^{-1} and the two chunk-local operators Mmat and Nmat described above,
+ * (chunk, head) the in-chunk gate scan and gate tables, the gated Gram matrix A, the UT
+ * transform T = (I + A)^{-1} and the two chunk-local operators Mmat and P described above,
  * written to the workspace. Arguments as in gdn_chunk_fwd; v, h0, o and hT are not
  * used. Source: the WY / UT-transform chunkwise algorithm carrying the gate (paper note,
  * mechanism paragraph; record "LIT-137", "Standing in the anthology").
@@ -138,7 +141,7 @@ int gdn_chunk_prepare(const void *q, const void *k, const float *g_log_alpha, co
  * Stage 2 of gdn_chunk_fwd: for every (sequence, head) the state is carried through
  * the chunks in order, and each chunk's output is formed from the entering state and
  * the stage-1 operators:
- *     R = V - diag(e^gamma) K S^T,   Delta = Mmat R,   o = diag(e^gamma) Q S^T + Nmat R,
+ *     R = V - diag(e^gamma) K S^T,   Delta = Mmat R,   o = diag(e^gamma) Q S^T + P Delta,
  *     S <- e^{gamma_last} S + Delta^T diag(e^{gamma_last - gamma}) K.
  * Reads the workspace written by gdn_chunk_prepare with the same arguments on the same
  * stream. Arguments as in gdn_chunk_fwd; g_log_alpha and beta are not used.

@@ -63,12 +63,13 @@ def test_workspace_bytes(L):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # B4 H16 T2048 bf16: 128 chunks x 16 heads
     nc, H = 4 * 32, 16
-    expect = al(nc * H * 64 * 4) + al(nc * H * 4096 * 2) + nc * H * 4096 * 2
+    expect = (al(nc * H * 128 * 4) + al(nc * H * 4096 * 2) + al(nc * H * 4096 * 2)
+              + al(nc * H * 64 * 128 * 2) + nc * H * 64 * 128 * 2)   # + fp16 K and scaled Q
     assert gb.gdn_chunk_fwd_workspace_bytes(4, 2048, 16, 128, 128, 4, False) == expect
     # packed: bound floor((T + N*63)/64), plus the chunk table
     T, N, H = 1000, 5, 2
     ncb = (T + N * 63) // 64
-    expect = al((N + 1) * 4) + al(ncb * H * 64 * 4) + al(ncb * H * 4096 * 4) + ncb * H * 4096 * 4
+    expect = al((N + 1) * 4) + al(ncb * H * 128 * 4) + al(ncb * H * 4096 * 4) + ncb * H * 4096 * 4
     import torch
     assert gb.gdn_chunk_fwd_workspace_bytes(1, T, H, 64, 64, N, True, dtype=torch.float32) == expect
     assert gb.gdn_chunk_fwd_workspace_bytes(1, 0, 2, 64, 64, 1, False) == 0
@@ -103,7 +104,8 @@ def test_chunk_fwd_rejects_before_any_launch(L):
     assert fwd(L, o=None) == ERR_NULL
     assert fwd(L, g=None) == ERR_NULL
     assert fwd(L, v=FAKE + 2) == ERR_ALIGN
-    assert fwd(L, h0=FAKE + 2) == ERR_ALIGN
+    assert fwd(L, h0=FAKE + 4) == ERR_ALIGN
+    assert fwd(L, g=FAKE + 2) == ERR_ALIGN
     assert fwd(L) == ERR_WS                                # workspace required
     assert fwd(L, ws=FAKE, wsb=100) == ERR_WS              # too small
     need = L.gdn_chunk_fwd_workspace_bytes(1, 128, 2, 64, 64, 1, 0, 64, 1)

@@ -204,8 +204,9 @@ def test_state_carry_matches_one_pass():
 # ------------------------------------------------------------------ stage 1
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prepare_stage_matches_chunkwise_model(dtype):
-    """gamma, Mmat = T diag(beta) and Nmat = P Mmat from the workspace, against the fp64
-    chunkwise model, on a ragged two-chunk sequence."""
+    """Gate tables, Mmat = T diag(beta) and P from the workspace (and, for bf16 inputs, the
+    fp16 copies of K and diag(e^gamma) Q), against the fp64 chunkwise model, on a ragged
+    two-chunk sequence."""
     H, T, dk = 2, 100, 128
     w = SY.Workload(95, "stage", H=H, dk=dk, dv=dk, dtype=dtype, B=1, T=T)
     x = SY.make_forward_inputs(w, seed=11, gate_scale=0.2)
@@ -219,11 +220,16 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
     nc = 2
     al = lambda n: (n + 255) // 256 * 256  # noqa: E731
     el = 4 if dtype == "f32" else 2
-    gam = ws[:nc * H * 64 * 4].view(torch.float32).view(nc, H, 64).cpu().double().numpy()
-    off_m = al(nc * H * 64 * 4)
-    off_n = al(off_m + nc * H * 4096 * el)
+    gates = ws[:nc * H * 128 * 4].view(torch.float32).view(nc, H, 128).cpu().double().numpy()
+    off_m = al(nc * H * 128 * 4)
+    off_p = al(off_m + nc * H * 4096 * el)
     M = ws[off_m:off_m + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
-    Nm = ws[off_n:off_n + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
+    Pm = ws[off_p:off_p + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
+    if dtype == "bf16":
+        off_k = al(off_p + nc * H * 4096 * el)
+        off_q = al(off_k + nc * H * 64 * dk * 2)
+        K16 = ws[off_k:off_k + nc * H * 64 * dk * 2].view(torch.float16).view(nc, H, 64, dk).cpu().double().numpy()
+        Q16 = ws[off_q:off_q + nc * H * 64 * dk * 2].view(torch.float16).view(nc, H, 64, dk).cpu().double().numpy()
     f64 = lambda t: R._f64(t)[0]  # noqa: E731
     q, k, v, g, b = (f64(x[n]) for n in ("q", "k", "v", "g", "beta"))
     for c in range(nc):
@@ -232,12 +238,24 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
         for h in range(H):
             f = CW.chunk_factors(k[c0:c1, h], v[c0:c1, h], g[c0:c1, h], b[c0:c1, h])
             m_ref = f["T"] * b[c0:c1, h][None, :]
-            n_ref = ((q[c0:c1, h] @ k[c0:c1, h].T) * f["ratio"]) @ m_ref
-            assert np.max(np.abs(gam[c, h, :n] - f["gamma"])) < 1e-5 * max(1, np.abs(f["gamma"]).max())
+            p_ref = (q[c0:c1, h] @ k[c0:c1, h].T) * f["ratio"]
+            gam = f["gamma"]
+            assert np.max(np.abs(gates[c, h, :n] - np.exp(gam))) < 1e-5
+            assert np.max(np.abs(gates[c, h, 64:64 + n] - np.exp(gam[-1] - gam))) < 1e-5
+            assert np.allclose(gates[c, h, n:64], np.exp(gam[-1]), rtol=1e-5)   # gamma constant past the end
             t = 1e-5 if dtype == "f32" else 2e-3
             assert np.max(np.abs(M[c, h, :n, :n] - m_ref)) <= t * max(np.abs(m_ref).max(), 1)
-            assert np.max(np.abs(Nm[c, h, :n, :n] - n_ref)) <= t * max(np.abs(n_ref).max(), 1)
+            assert np.max(np.abs(Pm[c, h, :n, :n] - p_ref)) <= t * max(np.abs(p_ref).max(), 1)
             assert not M[c, h, n:, :].any() and not M[c, h, :, n:].any()
+            assert not Pm[c, h, n:, :].any() and not Pm[c, h, :, n:].any()
+            if dtype == "bf16":
+                # bf16 values of magnitude >= 2^-14 are exact in fp16; smaller ones land on the
+                # fp16 subnormal grid (spacing 2^-24). The scaled Q is rounded once.
+                assert np.max(np.abs(K16[c, h, :n] - k[c0:c1, h])) <= 2.0 ** -25
+                assert not K16[c, h, n:].any()
+                q_ref = np.exp(gam)[:, None] * q[c0:c1, h]
+                assert np.max(np.abs(Q16[c, h, :n] - q_ref)) <= 2.0 ** -11 * np.abs(q_ref).max()
+                assert not Q16[c, h, n:].any()
 
 
 # -------------------------------------------------------------------- decode
