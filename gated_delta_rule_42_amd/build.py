@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the kernels feed every accumulator to vector
+    # instructions (packing, scaling, stores), which would otherwise first copy it out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

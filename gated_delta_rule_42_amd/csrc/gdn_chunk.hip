@@ -96,6 +96,35 @@ __device__ __forceinline__ bool locate_chunk(const ChunkProblem& p, long c, long
     return len > 0;
 }
 
+// ------------------------------------------------------- LDS images (bf16 inputs)
+// For bf16 inputs stage 1 stores the fp16 operands of stage 2 (K, diag(e^gamma) Q: W = d_k
+// columns; Mmat, P: W = 64) as byte images of the LDS tiles stage 2 reads, so that stage 2
+// copies them with plain 1 KB DMA blocks. A row is cut into 16-byte pieces; piece pc holds
+// the 8 contraction indices one lane feeds to a 16x16x32 product, columns
+// 32(pc>>2) + 4(pc&3) + 0..3 then the same + 16, and sits at position pc ^ img_swz<W>(r)
+// of row r. With that permutation the row-fragment reads (16 rows x 16 bytes per quarter
+// wave) and the transposing reads of K (4 rows x 32 bytes per quarter wave) touch distinct
+// banks.
+template <int W>
+__device__ __forceinline__ int img_swz(int r) {
+    if constexpr (W == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return (r >> 1) & 7;  // W = 64: two rows per 256-byte bank line
+}
+// element offset, in a [64, W] image, of the 4-element run at column c (c % 4 == 0) of row r
+template <int W>
+__device__ __forceinline__ int img_off(int r, int c) {
+    const int s = c >> 5, a = (c >> 4) & 1, m = (c >> 2) & 3;
+    return r * W + 8 * ((4 * s + m) ^ img_swz<W>(r)) + 4 * a;
+}
+// source columns of image piece i (pieces numbered in storage order): c0 .. c0+3, c0+16 .. c0+19
+template <int W>
+__device__ __forceinline__ void img_piece(int i, int& r, int& c0) {
+    constexpr int NP = W / 8;
+    r = i / NP;
+    const int pc = (i % NP) ^ img_swz<W>(r);
+    c0 = 32 * (pc >> 2) + 4 * (pc & 3);
+}
+
 // ------------------------------------------------------------------- stage 1
 template <typename TIn, int DK>
 struct alignas(16) PrepSmem {
@@ -158,37 +187,32 @@ struct PrepStage {
             sm.beta[tid] = rb;
         }
     }
-
-    // bf16 inputs: the chunk's K as fp16 rows [64, DK] (zero past the chunk's end), from the
-    // staged registers
-    __device__ __forceinline__ void write_k16(_Float16* dst, int tid) const {
-        if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-            for (int it = 0; it < NV; ++it) {
-                const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
-                *reinterpret_cast<uint4*>(dst + r * DK + cv * EPV) = to_operand16<TIn>(rk[it]);
-            }
-        }
-    }
 };
 
-// bf16 inputs: the chunk's diag(e^gamma) Q as fp16 rows [64, DK], from the raw Q in LDS and
-// the scanned gamma.
+// bf16 inputs: the chunk's K and diag(e^gamma) Q as fp16 images [64, DK] (rows past the
+// chunk's end zero), from the raw tiles in LDS and the scanned gamma.
 template <typename TIn, int DK>
-__device__ __forceinline__ void write_q16(const PrepSmem<TIn, DK>& sm, _Float16* dst, int tid) {
+__device__ __forceinline__ void write_kq_images(const PrepSmem<TIn, DK>& sm, _Float16* kimg,
+                                                _Float16* qimg, int tid) {
     if constexpr (sizeof(TIn) == 2) {
-        constexpr int PK = PrepSmem<TIn, DK>::PK, VPR = DK / 8, NV = 64 * VPR / 256;
+        constexpr int PK = PrepSmem<TIn, DK>::PK, NI = 64 * DK / 8 / 256;
+        auto cvt = [](uint2 a, uint2 b, float e) {
+            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+            return make_uint4(pack_f16x2(e * lo(a.x), e * hi(a.x)), pack_f16x2(e * lo(a.y), e * hi(a.y)),
+                              pack_f16x2(e * lo(b.x), e * hi(b.x)), pack_f16x2(e * lo(b.y), e * hi(b.y)));
+        };
 #pragma unroll
-        for (int it = 0; it < NV; ++it) {
-            const int vi = tid + 256 * it, r = vi / VPR, cv = vi % VPR;
-            const uint4 w = *reinterpret_cast<const uint4*>(&sm.u.in.Q[r * PK + cv * 8]);
-            const float e = __expf(sm.gam[r]);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = pack_f16x2(e * __uint_as_float(u[i] << 16), e * __uint_as_float(u[i] & 0xffff0000u));
-            *reinterpret_cast<uint4*>(dst + r * DK + cv * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        for (int it = 0; it < NI; ++it) {
+            const int i = tid + 256 * it;
+            int r, c0;
+            img_piece<DK>(i, r, c0);
+            const uint2 ka = *reinterpret_cast<const uint2*>(&sm.u.in.K[r * PK + c0]);
+            const uint2 kb = *reinterpret_cast<const uint2*>(&sm.u.in.K[r * PK + c0 + 16]);
+            const uint2 qa = *reinterpret_cast<const uint2*>(&sm.u.in.Q[r * PK + c0]);
+            const uint2 qb = *reinterpret_cast<const uint2*>(&sm.u.in.Q[r * PK + c0 + 16]);
+            reinterpret_cast<uint4*>(kimg)[i] = cvt(ka, kb, 1.f);
+            reinterpret_cast<uint4*>(qimg)[i] = cvt(qa, qb, __expf(sm.gam[r]));
         }
     }
 }
@@ -225,7 +249,6 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             const long widx = c * H + h;
             __syncthreads();  // the previous unit is done with LDS
             stage.store(sm, tid);
-            if (p.k16) stage.write_k16(p.k16 + widx * 64 * DK, tid);
             __syncthreads();
             if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
 
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 p.gates[widx * 128 + 64 + lane] = __expf(last - x);
             }
             __syncthreads();
-            if (p.q16) write_q16<TIn, DK>(sm, p.q16 + widx * 64 * DK, tid);
+            if (p.k16) write_kq_images<TIn, DK>(sm, p.k16 + widx * 64 * DK, p.q16 + widx * 64 * DK, tid);
 
             // -- K K^T and Q K^T (exact products of the inputs); wave w owns row block w
             const int rb = wave;
@@ -335,8 +358,8 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 __syncthreads();
             }
 
-            // -- Mmat = T diag(beta) and P to the workspace, row-major, 16-byte stores
-            {
+            // -- Mmat = T diag(beta) and P to the workspace: fp32 row-major, fp16 as images
+            if constexpr (sizeof(TM) == 4) {
                 const int r = tid >> 2, c0 = (tid & 3) * 16;
                 float mv[16], pv[16];
 #pragma unroll
@@ -347,6 +370,26 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 }
                 store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+            } else {
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    const int i = tid + 256 * it;
+                    int r, c0;
+                    img_piece<64>(i, r, c0);
+                    float mv[8], pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int ci = c0 + (e & 3) + 16 * (e >> 2);
+                        mv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] * sm.beta[ci] : 0.f;
+                        pv[e] = to_f32(sm.P[r * PC + ci]);
+                    }
+                    reinterpret_cast<uint4*>(static_cast<TM*>(p.mmat) + widx * 4096)[i] =
+                        make_uint4(pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
+                                   pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7]));
+                    reinterpret_cast<uint4*>(static_cast<TM*>(p.pmat) + widx * 4096)[i] =
+                        make_uint4(pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                                   pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7]));
+                }
             }
         } else if (nok) {
             stage.load(p, nbos, nlen, (int)(nxt % H), tid);
@@ -674,19 +717,8 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkPro
 // operand in fp16 (K, diag(e^gamma) Q, Mmat, P; rows past the chunk's end zero); V stays bf16
 // and enters only the fp32 residual. All products run on the fp16 matrix core.
 //
-// 16-byte pieces of each LDS row are permuted by the row (XOR with swz_kq / swz_mp) so that
-// the row-fragment reads (16 rows x 8 bytes per half-wave) and the transposing reads of K
-// (8 rows x 32 bytes) hit distinct banks. The DMA applies the permutation on the global side.
-template <int DK>
-__device__ __forceinline__ int swz_kq(int r) {
-    if constexpr (DK == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-    else return (r >> 1) & 7;
-}
-__device__ __forceinline__ int swz_mp(int r) { return (r >> 1) & 7; }
-template <int DK>
-__device__ __forceinline__ int off_kq(int r, int c) { return r * DK + 8 * ((c >> 3) ^ swz_kq<DK>(r)) + (c & 7); }
-__device__ __forceinline__ int off_mp(int r, int c) { return r * 64 + 8 * ((c >> 3) ^ swz_mp(r)) + (c & 7); }
-
+// K, Q, Mmat and P arrive as the LDS images stage 1 wrote (see img_off); V rows are copied
+// as they are, with rows past the chunk's end read as zeros.
 template <int DK, int DVT>
 struct alignas(1024) DmaChunk {
     _Float16 K[64 * DK];
@@ -708,37 +740,32 @@ struct DmaPlan {
     static constexpr int NB_V = 64 * DVT * 2 / 1024;
     static constexpr int W_KQ = NB_KQ / NW, W_MP = NB_MP / NW, W_V = NB_V / NW;
     static_assert(W_KQ * NW == NB_KQ && W_MP * NW == NB_MP && W_V * NW == NB_V && W_V > 0, "DMA split");
-    static constexpr int ROW_KQ = DK * 2, ROW_V = DVT * 2;  // LDS row bytes
+    static constexpr int ROW_V = DVT * 2;  // LDS row bytes of V
 
     // Issues this wave's share of slice `part` for chunk (bos, len) of head h into `dst`.
     __device__ __forceinline__ static void issue(DmaChunk<DK, DVT>& dst, const ChunkProblem& p,
                                                  long bos, int len, long widx, int h, int dv0,
                                                  int wave, int lane, int part, int nparts) {
         const int H = p.H;
-        const long tok0 = bos * H + h;
         const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
-        const auto kr = make_rsrc(p.k16 + widx * 64 * DK, 64 * DK * 2);
-        const auto qr = make_rsrc(p.q16 + widx * 64 * DK, 64 * DK * 2);
-        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + tok0 * DV + dv0, vbytes);
-        const auto mr = make_rsrc(static_cast<const _Float16*>(p.mmat) + widx * 4096, 8192);
-        const auto pr = make_rsrc(static_cast<const _Float16*>(p.pmat) + widx * 4096, 8192);
+        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
+        const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
+        const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
+        const char* mimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.mmat) + widx * 4096);
+        const char* pimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.pmat) + widx * 4096);
+        const unsigned lo = 16u * lane;
         int n = 0;
 #pragma unroll
         for (int j = 0; j < W_KQ; ++j) {
-            const int b = wave * W_KQ + j;
-            const int byte = 1024 * b + 16 * lane, r = byte / ROW_KQ;
-            const int piece = ((byte % ROW_KQ) >> 4) ^ swz_kq<DK>(r);
-            const int off = r * DK * 2 + 16 * piece;
-            if (n++ % nparts == part) dma16(kr, reinterpret_cast<const char*>(dst.K) + 1024 * b, off);
-            if (n++ % nparts == part) dma16(qr, reinterpret_cast<const char*>(dst.Q) + 1024 * b, off);
+            const unsigned b = wave * W_KQ + j;
+            if (n++ % nparts == part) dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
+            if (n++ % nparts == part) dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
         }
 #pragma unroll
         for (int j = 0; j < W_MP; ++j) {
-            const int b = wave * W_MP + j;
-            const int byte = 1024 * b + 16 * lane, r = byte >> 7;
-            const int off = 128 * r + 16 * (((byte & 127) >> 4) ^ swz_mp(r));
-            if (n++ % nparts == part) dma16(mr, reinterpret_cast<const char*>(dst.M) + 1024 * b, off);
-            if (n++ % nparts == part) dma16(pr, reinterpret_cast<const char*>(dst.P) + 1024 * b, off);
+            const unsigned b = wave * W_MP + j;
+            if (n++ % nparts == part) dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
+            if (n++ % nparts == part) dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
         }
 #pragma unroll
         for (int j = 0; j < W_V; ++j) {
@@ -747,10 +774,8 @@ struct DmaPlan {
             const int off = r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4);
             if (n++ % nparts == part) dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, off);
         }
-        if (n % nparts == part && wave == 0 && lane < 32) {
-            const auto gr = make_rsrc(p.gates + widx * 128, 512);
-            dma16(gr, dst.eg, 16 * lane);
-        }
+        if (n % nparts == part && wave == 0 && lane < 32)
+            dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
     }
 };
 
@@ -852,7 +877,7 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const int row = 16 * t + l16, c = 32 * hf + 4 * lq;
-                    f[t][hf] = lds_frag2(&src[off_mp(row, c)], &src[off_mp(row, c + 16)]);
+                    f[t][hf] = *reinterpret_cast<const uint4*>(&src[img_off<64>(row, c)]);
                 }
         };
         auto load_r = [&]() {
@@ -872,8 +897,8 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int row = 16 * t + l16, c0 = 32 * s + 4 * lq;
-                kf[t] = lds_frag2(&cur.K[off_kq<DK>(row, c0)], &cur.K[off_kq<DK>(row, c0 + 16)]);
-                qf[t] = lds_frag2(&cur.Q[off_kq<DK>(row, c0)], &cur.Q[off_kq<DK>(row, c0 + 16)]);
+                kf[t] = *reinterpret_cast<const uint4*>(&cur.K[img_off<DK>(row, c0)]);
+                qf[t] = *reinterpret_cast<const uint4*>(&cur.Q[img_off<DK>(row, c0)]);
             }
         };
         load_xy(0, KF[0], QF[0]);
@@ -931,8 +956,8 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
 #pragma unroll
         for (int j = 0; j < NKB; ++j) {
             const int c = 16 * j + tc;
-            KT[j][0] = lds_frag2_t(&cur.K[off_kq<DK>(4 * lq + tr, c)], &cur.K[off_kq<DK>(16 + 4 * lq + tr, c)]);
-            KT[j][1] = lds_frag2_t(&cur.K[off_kq<DK>(32 + 4 * lq + tr, c)], &cur.K[off_kq<DK>(48 + 4 * lq + tr, c)]);
+            KT[j][0] = lds_frag2_t(&cur.K[img_off<DK>(4 * lq + tr, c)], &cur.K[img_off<DK>(16 + 4 * lq + tr, c)]);
+            KT[j][1] = lds_frag2_t(&cur.K[img_off<DK>(32 + 4 * lq + tr, c)], &cur.K[img_off<DK>(48 + 4 * lq + tr, c)]);
         }
         dma(5);
 

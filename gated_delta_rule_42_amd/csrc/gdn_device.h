@@ -370,5 +370,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_block)), 16, off, 0, 0, 0);
 }
+// The same from a plain global address: wave-uniform base plus a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16g(const char* base, unsigned off, const void* lds_block) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
+                                     (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_block)),
+                                     16, 0, 0);
+}
 
 }  // namespace gdn

@@ -85,7 +85,11 @@ const char *gdn_status_string(int status);
  *   K16         fp16  [nc, H, 64, dk] the chunk's K rows          (bf16 inputs only)
  *   Q16         fp16  [nc, H, 64, dk] diag(exp(gamma)) Q          (bf16 inputs only)
  * with op = fp16 for bf16 inputs and fp32 for fp32 inputs; rows and columns past a chunk's
- * last token are zero and gamma stays constant there.
+ * last token are zero and gamma stays constant there. fp32 operators are row-major. The fp16
+ * ones (Mmat, P, K16, Q16: W = 64 or dk columns) are stored as the LDS images the propagate
+ * kernel reads: each row is W/8 pieces of 8 values, the piece at position pos of row r holds
+ * columns 32(pc>>2) + 4(pc&3) + {0..3, 16..19} with pc = pos ^ swz(r), where
+ * swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,

@@ -202,6 +202,23 @@ def test_state_carry_matches_one_pass():
 
 
 # ------------------------------------------------------------------ stage 1
+def from_image(img, W):
+    """Row-major [.., 64, W] from the fp16 operand image stage 1 writes for bf16 inputs: each
+    row holds W/8 16-byte pieces; the piece at position pos of row r carries the source piece
+    pc = pos ^ swz(r), whose 8 values are columns 32(pc>>2) + 4(pc&3) + 0..3 and the same + 16;
+    swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64."""
+    out = np.full_like(img, np.nan)
+    for r in range(64):
+        swz = 4 * (r & 3) + ((r >> 2) & 3) if W == 128 else (r >> 1) & 7
+        for pos in range(W // 8):
+            pc = pos ^ swz
+            c0 = 32 * (pc >> 2) + 4 * (pc & 3)
+            out[..., r, c0:c0 + 4] = img[..., r, 8 * pos:8 * pos + 4]
+            out[..., r, c0 + 16:c0 + 20] = img[..., r, 8 * pos + 4:8 * pos + 8]
+    assert not np.isnan(out).any()
+    return out
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prepare_stage_matches_chunkwise_model(dtype):
     """Gate tables, Mmat = T diag(beta) and P from the workspace (and, for bf16 inputs, the
@@ -226,10 +243,12 @@ def test_prepare_stage_matches_chunkwise_model(dtype):
     M = ws[off_m:off_m + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
     Pm = ws[off_p:off_p + nc * H * 4096 * el].view(opdt).view(nc, H, 64, 64).float().cpu().double().numpy()
     if dtype == "bf16":
+        M, Pm = from_image(M, 64), from_image(Pm, 64)
         off_k = al(off_p + nc * H * 4096 * el)
         off_q = al(off_k + nc * H * 64 * dk * 2)
         K16 = ws[off_k:off_k + nc * H * 64 * dk * 2].view(torch.float16).view(nc, H, 64, dk).cpu().double().numpy()
         Q16 = ws[off_q:off_q + nc * H * 64 * dk * 2].view(torch.float16).view(nc, H, 64, dk).cpu().double().numpy()
+        K16, Q16 = from_image(K16, dk), from_image(Q16, dk)
     f64 = lambda t: R._f64(t)[0]  # noqa: E731
     q, k, v, g, b = (f64(x[n]) for n in ("q", "k", "v", "g", "beta"))
     for c in range(nc):
