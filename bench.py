@@ -37,8 +37,8 @@ def fwd_counts(dk, dv, C=CHUNK, elem=2):
     stage2_bytes = (2 * dk + dv) * elem + dv * elem
     stage1_bytes = 8
     # FLOP actually issued per token-head by each stage of this implementation
-    stage1_flops = 2 * C * dk * 2 + 2 * C * C          # K K^T, Q K^T, Nmat = P Mmat
-    stage2_flops = 6 * dk * dv + 4 * C * dv            # K S^T, Q S^T, Delta^T K, Mmat R, Nmat R
+    stage1_flops = 2 * C * dk * 2                      # K K^T, Q K^T (plus the small 64x64 solve)
+    stage2_flops = 6 * dk * dv + 4 * C * dv            # K S^T, Q S^T, Delta^T K, Mmat R, P Delta
     return dict(flops=flops, bytes=stage1_bytes + stage2_bytes, stage1_bytes=stage1_bytes,
                 stage2_bytes=stage2_bytes, stage1_flops=stage1_flops, stage2_flops=stage2_flops)
 
@@ -228,10 +228,10 @@ def main():
                             "chunk_propagate_median": median(f["prop_ms"])}
         if prop >= prep:
             ach = c["stage2_bytes"] * th / (prop / 1e3)
-            out["roofline"] = {"kernel": "chunk_propagate_kernel", "bound": "hbm",
+            out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
                                "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                                "frac": ach / PEAK_HBM_BPS,
-                               "traffic": measured_traffic("chunk_propagate_kernel"),
+                               "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
                                "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
         else:
             ach = c["stage1_flops"] * th / (prep / 1e3)

@@ -281,20 +281,24 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             }
             __syncthreads();  // K and Q are dead; their space becomes A and T
 
-            // -- gate the products: A (strictly lower, fp32) and P (lower incl. diagonal)
+            // -- gate the products: A (strictly lower, fp32) and P (lower incl. diagonal). The
+            //    exponent is clamped to <= 0 before the exp, so masked entries cannot overflow.
+            {
+                const float4 gr = *reinterpret_cast<const float4*>(&sm.gam[16 * rb + 4 * lq]);
+                const float4 br = *reinterpret_cast<const float4*>(&sm.beta[16 * rb + 4 * lq]);
+                const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
+                for (int cb = 0; cb < 4; ++cb) {
+                    const float gc = sm.gam[16 * cb + l16];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * rb + 4 * lq + v, i = 16 * cb + l16;
-                    float a = 0.f, pp = 0.f;
-                    if (i <= r) {
-                        const float e = __expf(sm.gam[r] - sm.gam[i]);
-                        if (i < r) a = sm.beta[r] * G[cb][v] * e;
-                        pp = P0[cb][v] * e;
+                    for (int v = 0; v < 4; ++v) {
+                        const int r = 16 * rb + 4 * lq + v, i = 16 * cb + l16;
+                        const float e = __expf(fminf(grv[v] - gc, 0.f));
+                        const float a = (i < r) ? brv[v] * G[cb][v] * e : 0.f;
+                        const float pp = (i <= r) ? P0[cb][v] * e : 0.f;
+                        sm.u.tri.A[r * PF + i] = a;
+                        sm.P[r * PC + i] = from_f32<TM>(pp);
                     }
-                    sm.u.tri.A[r * PF + i] = a;
-                    sm.P[r * PC + i] = from_f32<TM>(pp);
                 }
             }
             __syncthreads();
@@ -730,68 +734,77 @@ struct alignas(1024) DmaChunk {
     float ed[64];          // e^{gamma_last - gamma_r}
 };
 
-// Which 1 KB DMA blocks of a chunk each wave copies, and in which of `nparts` slices of the
-// compute it issues them. Wave w copies blocks w*n .. w*n + n-1 of each array.
-template <int DK, int DV, int DVT>
-struct DmaPlan {
-    static constexpr int NW = DVT / 16;
-    static constexpr int NB_KQ = 64 * DK * 2 / 1024;
-    static constexpr int NB_MP = 8;
-    static constexpr int NB_V = 64 * DVT * 2 / 1024;
-    static constexpr int W_KQ = NB_KQ / NW, W_MP = NB_MP / NW, W_V = NB_V / NW;
-    static_assert(W_KQ * NW == NB_KQ && W_MP * NW == NB_MP && W_V * NW == NB_V && W_V > 0, "DMA split");
-    static constexpr int ROW_V = DVT * 2;  // LDS row bytes of V
-
-    // Issues this wave's share of slice `part` for chunk (bos, len) of head h into `dst`.
-    __device__ __forceinline__ static void issue(DmaChunk<DK, DVT>& dst, const ChunkProblem& p,
-                                                 long bos, int len, long widx, int h, int dv0,
-                                                 int wave, int lane, int part, int nparts) {
-        const int H = p.H;
-        const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
-        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
-        const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
-        const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
-        const char* mimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.mmat) + widx * 4096);
-        const char* pimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.pmat) + widx * 4096);
-        const unsigned lo = 16u * lane;
-        int n = 0;
-#pragma unroll
-        for (int j = 0; j < W_KQ; ++j) {
-            const unsigned b = wave * W_KQ + j;
-            if (n++ % nparts == part) dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
-            if (n++ % nparts == part) dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
-        }
-#pragma unroll
-        for (int j = 0; j < W_MP; ++j) {
-            const unsigned b = wave * W_MP + j;
-            if (n++ % nparts == part) dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
-            if (n++ % nparts == part) dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
-        }
-#pragma unroll
-        for (int j = 0; j < W_V; ++j) {
-            const int b = wave * W_V + j;
-            const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
-            const int off = r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4);
-            if (n++ % nparts == part) dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, off);
-        }
-        if (n % nparts == part && wave == 0 && lane < 32)
-            dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
-    }
+// Output staging for one chunk: the compute waves leave o^T tiles here and the store wave
+// writes them out as whole rows of the work-group's columns. Rows are padded by 16 bytes so
+// that the compute waves' 4-column writes of 16 consecutive tokens fall in distinct banks.
+template <typename TO, int DVT>
+struct alignas(16) OStage {
+    static constexpr int ROWB = DVT * (int)sizeof(TO);  // bytes of one token's columns
+    static constexpr int PITCH = ROWB + 16;
+    char b[64 * PITCH];
 };
 
-// One work-group per (sequence, head, DVT-column tile); wave w owns columns dv0 + 16w .. +15
-// for all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
-// S[dv0 + 16w + l16][16j + 4*lq + 0..3]). The products are those of the generic stage-2 kernel
-// (chunk_propagate_kernel), with the operand formats described above.
+// The DMA wave's work for one chunk: the 1 KB DMA blocks of every array of the chunk
+// (K, Q, Mmat, P and the gate tables are linear images; V rows are gathered from the input
+// with rows past the chunk's end read as zeros).
+template <int DK, int DV, int DVT>
+__device__ __forceinline__ void copy_chunk(DmaChunk<DK, DVT>& dst, const ChunkProblem& p, long bos,
+                                           int len, long widx, int h, int dv0, int lane) {
+    constexpr int NB_KQ = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
+    const int H = p.H;
+    const unsigned lo = 16u * lane;
+    const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
+    const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
+    const char* mimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.mmat) + widx * 4096);
+    const char* pimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.pmat) + widx * 4096);
+    const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
+    const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
+    if (lane < 32) dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
+#pragma unroll
+    for (int b = 0; b < NB_V; ++b) {
+        const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
+        dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
+    }
+#pragma unroll
+    for (int b = 0; b < NB_KQ; ++b) {
+        dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
+        dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
+        dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+    }
+}
+
+// Work-group barrier that orders LDS accesses only: the waves' global stores and copies are
+// not waited for (the DMA wave waits for its own copies explicitly).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One work-group per (sequence, head, DVT-column tile) with DVT/16 compute waves, one DMA wave
+// and one store wave, each on its own SIMD. Compute wave w owns columns dv0 + 16w .. +15 for
+// all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
+// S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it only reads and writes LDS and runs the matrix and
+// vector units. The DMA wave copies chunk c+1 into the other LDS buffer while chunk c is
+// computed and waits for its copies before the next barrier; the store wave writes chunk c-1's
+// outputs from the LDS staging buffer and never waits for its stores. One barrier per chunk.
+// The products are those of the generic stage-2 kernel (chunk_propagate_kernel).
 template <typename TO, int DK, int DV, int DVT>
-__global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
-    using Plan = DmaPlan<DK, DV, DVT>;
+__global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
     using Buf = DmaChunk<DK, DVT>;
+    using OS = OStage<TO, DVT>;
+    constexpr int NW = DVT / 16;   // compute waves
     constexpr int NKB = DK / 16;   // d_k tiles of the state
     constexpr int NKS = DK / 32;   // 32-wide d_k slices
     constexpr int NTILE = DV / DVT;
     __shared__ Buf buf0;
     __shared__ Buf buf1;
+    __shared__ OS ost0;
+    __shared__ OS ost1;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -814,7 +827,6 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
     }
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int dv0 = tile * DVT;
-    const int dvw = dv0 + 16 * wave;
 
     long sbos, seos;
     seq_range(p, n, sbos, seos);
@@ -826,6 +838,56 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
         return (int)(l < kChunk ? l : kChunk);
     };
 
+    if (wave == NW) {
+        // ------------------------------------------------------------------- DMA wave
+        auto step = [&](Buf& nxt, long jc) {
+            __builtin_amdgcn_s_waitcnt(0);  // chunk jc's copies have landed
+            lds_barrier();
+            if (jc + 1 < nchunks)
+                copy_chunk<DK, DV, DVT>(nxt, p, sbos + (jc + 1) * kChunk, chunk_len(jc + 1),
+                                        (cbase + jc + 1) * H + h, h, dv0, lane);
+        };
+        if (nchunks > 0) copy_chunk<DK, DV, DVT>(buf0, p, sbos, chunk_len(0), cbase * H + h, h, dv0, lane);
+        for (long jc = 0; jc < nchunks; jc += 2) {
+            step(buf1, jc);
+            if (jc + 1 < nchunks) step(buf0, jc + 1);
+        }
+        lds_barrier();
+        return;
+    }
+    if (wave == NW + 1) {
+        // ----------------------------------------------------------------- store wave
+        // outputs of chunk jc: token row `lane` through a resource sized to the valid rows
+        auto store_out = [&](const OS& os, long jc) {
+            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16;
+            const long obos = sbos + jc * kChunk;
+            const int olen = chunk_len(jc);
+            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
+                                       (unsigned)((olen - 1) * H * DV + DVT) * E);
+            uint4 row[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) row[i] = *reinterpret_cast<const uint4*>(&os.b[lane * OS::PITCH + 16 * i]);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const u32x4_t v = {row[i].x, row[i].y, row[i].z, row[i].w};
+                __builtin_amdgcn_raw_buffer_store_b128(v, orr, lane * H * DV * E + 16 * i, 0, 0);
+            }
+        };
+        for (long jc = 0; jc < nchunks; jc += 2) {
+            lds_barrier();
+            if (jc > 0) store_out(ost1, jc - 1);
+            if (jc + 1 < nchunks) {
+                lds_barrier();
+                store_out(ost0, jc);
+            }
+        }
+        lds_barrier();  // the last chunk's outputs are staged
+        if (nchunks > 0) store_out((nchunks & 1) ? ost0 : ost1, nchunks - 1);
+        return;
+    }
+
+    // ------------------------------------------------------------------- compute waves
+    const int dvw = dv0 + 16 * wave;
     f32x4_t ST[NKB];
     const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
@@ -838,47 +900,20 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
         }
     }
 
-    // outputs of the previous chunk, transposed (lane: o[token 16t + l16][dvw + 4lq + v]),
-    // written at the start of the next chunk through a resource sized to its valid rows
-    f32x4_t O[4];
-    long obos = 0;
-    int olen = 0;
-    auto store_out = [&]() {
-        constexpr int E = (int)sizeof(TO);
-        const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV,
-                                   (unsigned)((olen - 1) * H * DV + DV) * E);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + dvw + 4 * lq) * E, O[t]);
-    };
-
-    // The next chunk's copies are issued in kParts slices spread over the phases of a chunk.
-    // LDS operands are read ahead of the products that use them (those that do not depend on
-    // the state right after the barrier, the X/Y fragments one 32-wide slice ahead, K^T during
-    // the output product), and each product phase cycles over independent accumulators; the
-    // scheduling fences keep that order.
-    constexpr int kParts = 8;
-    auto step = [&](Buf& cur, Buf& nxt, long jc) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into cur have landed
-        __syncthreads();                // ... and every wave's; nobody reads nxt any more
-        if (jc > 0) store_out();
-        const bool more = jc + 1 < nchunks;
-        const long nbos = sbos + (jc + 1) * kChunk, nwidx = (cbase + jc + 1) * H + h;
-        const int nlen = more ? chunk_len(jc + 1) : 1;
-        auto dma = [&](int part) {
-            if (more) Plan::issue(nxt, p, nbos, nlen, nwidx, h, dv0, wave, lane, part, kParts);
-        };
-
-        // operands read one phase ahead of their products
+    // LDS operands are read ahead of the products that use them (the X/Y fragments one
+    // 32-wide slice ahead, Mmat and the residual terms in the last slice, P during the
+    // residual, K^T during the output product), and each product phase cycles over
+    // independent accumulators; the scheduling fences keep that order.
+    auto step = [&](const Buf& cur, OS& os) {
+        lds_barrier();  // chunk data in cur; os free
         uint4 MF[4][2], PF[4][2];
         float4 V4[4], EG4[4];
         auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int row = 16 * t + l16, c = 32 * hf + 4 * lq;
-                    f[t][hf] = *reinterpret_cast<const uint4*>(&src[img_off<64>(row, c)]);
-                }
+                for (int hf = 0; hf < 2; ++hf)
+                    f[t][hf] = *reinterpret_cast<const uint4*>(&src[img_off<64>(16 * t + l16, 32 * hf + 4 * lq)]);
         };
         auto load_r = [&]() {
 #pragma unroll
@@ -916,7 +951,6 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
                 load_r();
                 load_mp(cur.M, MF);
             }
-            dma(s % 4);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -925,13 +959,9 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (NKS < 4) {
-#pragma unroll
-            for (int part = NKS; part < 4; ++part) dma(part);
-        }
 
         // R = V - e^gamma X
-        dma(4);
+        load_mp(cur.P, PF);
         f32x4_t R[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -939,7 +969,6 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
                            V4[t].z - EG4[t].z * X[t][2], V4[t].w - EG4[t].w * X[t][3]};
 
         // Delta = Mmat R
-        load_mp(cur.P, PF);
         const uint4 BR[2] = {pack_f16_frag(R[0], R[1]), pack_f16_frag(R[2], R[3])};
         f32x4_t D[4];
 #pragma unroll
@@ -959,19 +988,25 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
             KT[j][0] = lds_frag2_t(&cur.K[img_off<DK>(4 * lq + tr, c)], &cur.K[img_off<DK>(16 + 4 * lq + tr, c)]);
             KT[j][1] = lds_frag2_t(&cur.K[img_off<DK>(32 + 4 * lq + tr, c)], &cur.K[img_off<DK>(48 + 4 * lq + tr, c)]);
         }
-        dma(5);
 
-        // O^T = e^gamma S Q^T + Delta^T P^T
+        // O^T = e^gamma S Q^T + Delta^T P^T, staged in LDS for the store wave (lane: token
+        // 16t + l16, columns 16 wave + 4 lq .. +3)
         const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
+        f32x4_t O[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) O[t] = Y[t];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
-        obos = sbos + jc * kChunk;
-        olen = chunk_len(jc);
-        dma(6);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            char* dst = &os.b[(16 * t + l16) * OS::PITCH + (16 * wave + 4 * lq) * (int)sizeof(TO)];
+            if constexpr (sizeof(TO) == 2)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(O[t][0], O[t][1]), pack_bf16x2(O[t][2], O[t][3]));
+            else
+                *reinterpret_cast<float4*>(dst) = make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+        }
 
         // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
         f32x4_t Dd[4];
@@ -984,7 +1019,6 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
         const uint4 BT[2] = {pack_f16_frag(Dd[0], Dd[1]), pack_f16_frag(Dd[2], Dd[3])};
 #pragma unroll
         for (int j = 0; j < NKB; ++j) ST[j] *= elast;
-        dma(7);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -992,16 +1026,11 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_bf16_kernel(Chu
             for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
     };
 
-    if (nchunks > 0) {
-#pragma unroll
-        for (int part = 0; part < kParts; ++part)
-            Plan::issue(buf0, p, sbos, chunk_len(0), cbase * H + h, h, dv0, wave, lane, part, kParts);
-    }
     for (long jc = 0; jc < nchunks; jc += 2) {
-        step(buf0, buf1, jc);
-        if (jc + 1 < nchunks) step(buf1, buf0, jc + 1);
+        step(buf0, ost0);
+        if (jc + 1 < nchunks) step(buf1, ost1);
     }
-    if (nchunks > 0) store_out();
+    lds_barrier();  // hand the last chunk's outputs to the store wave
 
     if (p.hT) {
 #pragma unroll
@@ -1034,9 +1063,22 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
 
 template <typename TIn, int DK>
 static void prep_launch(const ChunkProblem& p, hipStream_t s) {
-    // persistent grid: up to 3 resident work-groups per CU on 256 CUs
+    // persistent grid: as many work-groups as the device holds at once (queried once per
+    // device), so that every (chunk, head) unit is taken by an already running work-group
+    static int resident[64] = {0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int& cap = resident[dev & 63];
+    if (cap == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<TIn, DK>, 256, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            per_cu < 1 || cus < 1)
+            per_cu = 2, cus = 256;
+        cap = per_cu * cus;
+    }
     const long units = p.nc_bound * p.H;
-    const long blocks = units < 768 ? units : 768;
+    const long blocks = units < cap ? units : cap;
     hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
 }
 
@@ -1057,11 +1099,11 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
 template <typename TIn, typename TO, int DK, int DV>
 static void prop_launch(const ChunkProblem& p, hipStream_t s) {
     if constexpr (sizeof(TIn) == 2) {
-        // bf16: two waves (32 columns) per work-group
+        // bf16: two compute waves (32 columns), a DMA wave and a store wave per work-group
         constexpr int DVT = 32;
         const long blocks = (long)p.N * p.H * (DV / DVT);
         hipLaunchKernelGGL((chunk_propagate_bf16_kernel<TO, DK, DV, DVT>), dim3((unsigned)blocks),
-                           dim3(DVT / 16 * 64), 0, s, p);
+                           dim3((DVT / 16 + 2) * 64), 0, s, p);
     } else {
         constexpr int DVT = 32;  // two waves of 16 columns (LDS size)
         const long blocks = (long)p.N * p.H * (DV / DVT);

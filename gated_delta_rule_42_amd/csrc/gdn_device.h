@@ -366,15 +366,18 @@ __device__ __forceinline__ void split_bf16_frag(const f32x4_t& a, const f32x4_t&
 // Global -> LDS copy of 16 bytes per lane through a buffer resource: lane l writes LDS bytes
 // [16 l, 16 l + 16) after the wave-uniform address lds_block, reading global byte offset off
 // of the resource (zeros where that is out of range).
+// LDS address of a generic pointer to a __shared__ object: the low 32 bits of its flat
+// address (taken as an integer, which needs no null check).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ lds_void_ptr to_lds(const void* p) {
+    return (lds_void_ptr)(uint32_t)reinterpret_cast<uintptr_t>(p);
+}
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_block, int off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_block)), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_block), 16, off, 0, 0, 0);
 }
 // The same from a plain global address: wave-uniform base plus a 32-bit per-lane offset.
 __device__ __forceinline__ void dma16g(const char* base, unsigned off, const void* lds_block) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off),
-                                     (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_block)),
-                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off), to_lds(lds_block), 16, 0, 0);
 }
 
 }  // namespace gdn
