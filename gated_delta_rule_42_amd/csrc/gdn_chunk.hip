@@ -723,10 +723,15 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkPro
 //
 // K, Q, Mmat and P arrive as the LDS images stage 1 wrote (see img_off); V rows are copied
 // as they are, with rows past the chunk's end read as zeros.
-template <int DK, int DVT>
-struct alignas(1024) DmaChunk {
-    _Float16 K[64 * DK];
+// A chunk's operands in LDS, in two parts with different lifetimes: Q is copied one chunk
+// ahead (double-buffered), the rest two chunks ahead (triple-buffered).
+template <int DK>
+struct alignas(16) KQChunk {
     _Float16 Q[64 * DK];   // diag(e^gamma) Q
+};
+template <int DK, int DVT>
+struct alignas(16) MPVChunk {
+    _Float16 K[64 * DK];
     _Float16 M[64 * 64];   // Mmat
     _Float16 P[64 * 64];
     uint16_t V[64 * DVT];  // bf16, the work-group's d_v columns
@@ -744,21 +749,30 @@ struct alignas(16) OStage {
     char b[64 * PITCH];
 };
 
-// The DMA wave's work for one chunk: the 1 KB DMA blocks of every array of the chunk
-// (K, Q, Mmat, P and the gate tables are linear images; V rows are gathered from the input
-// with rows past the chunk's end read as zeros).
+// The DMA wave's copies for one chunk, as 1 KB DMA blocks: the Q image (copy_kq), and the K
+// image, Mmat, P, the gate tables and V (copy_mpv; V rows gathered from the input, rows past the
+// chunk's end read as zeros). copy_mpv issues kMpvCopies instructions.
+template <int DK>
+__device__ __forceinline__ void copy_kq(KQChunk<DK>& dst, const ChunkProblem& p, long widx, int lane) {
+    constexpr int NB_KQ = 64 * DK * 2 / 1024;
+    const unsigned lo = 16u * lane;
+    const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
+#pragma unroll
+    for (int b = 0; b < NB_KQ; ++b) dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
+}
+template <int DK, int DVT>
+constexpr int kMpvCopies = 64 * DK * 2 / 1024 + 8 + 8 + 64 * DVT * 2 / 1024 + 1;
 template <int DK, int DV, int DVT>
-__device__ __forceinline__ void copy_chunk(DmaChunk<DK, DVT>& dst, const ChunkProblem& p, long bos,
-                                           int len, long widx, int h, int dv0, int lane) {
+__device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProblem& p, long bos, int len,
+                                         long widx, int h, int dv0, int lane) {
     constexpr int NB_KQ = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
     const int H = p.H;
     const unsigned lo = 16u * lane;
-    const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
-    const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
     const char* mimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.mmat) + widx * 4096);
     const char* pimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.pmat) + widx * 4096);
     const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
     const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
+    const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
     if (lane < 32) dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
 #pragma unroll
     for (int b = 0; b < NB_V; ++b) {
@@ -766,16 +780,17 @@ __device__ __forceinline__ void copy_chunk(DmaChunk<DK, DVT>& dst, const ChunkPr
         dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
     }
 #pragma unroll
-    for (int b = 0; b < NB_KQ; ++b) {
-        dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
-        dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
-    }
+    for (int b = 0; b < NB_KQ; ++b) dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
         dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
     }
 }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Work-group barrier that orders LDS accesses only: the waves' global stores and copies are
 // not waited for (the DMA wave waits for its own copies explicitly).
@@ -789,22 +804,24 @@ __device__ __forceinline__ void lds_barrier() {
 // and one store wave, each on its own SIMD. Compute wave w owns columns dv0 + 16w .. +15 for
 // all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
 // S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it only reads and writes LDS and runs the matrix and
-// vector units. The DMA wave copies chunk c+1 into the other LDS buffer while chunk c is
-// computed and waits for its copies before the next barrier; the store wave writes chunk c-1's
-// outputs from the LDS staging buffer and never waits for its stores. One barrier per chunk.
+// vector units. While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
+// chunk c+2 into ring buffers (2 and 3 deep: memory latency is about one chunk's
+// compute time), and before the next barrier waits for exactly the copies chunk c+1 needs; the
+// store wave writes chunk c-1's outputs from the LDS staging buffer and never waits for its
+// stores. One barrier per chunk.
 // The products are those of the generic stage-2 kernel (chunk_propagate_kernel).
 template <typename TO, int DK, int DV, int DVT>
 __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
-    using Buf = DmaChunk<DK, DVT>;
+    using KQ = KQChunk<DK>;
+    using MPV = MPVChunk<DK, DVT>;
     using OS = OStage<TO, DVT>;
     constexpr int NW = DVT / 16;   // compute waves
     constexpr int NKB = DK / 16;   // d_k tiles of the state
     constexpr int NKS = DK / 32;   // 32-wide d_k slices
     constexpr int NTILE = DV / DVT;
-    __shared__ Buf buf0;
-    __shared__ Buf buf1;
-    __shared__ OS ost0;
-    __shared__ OS ost1;
+    __shared__ KQ kq[2];
+    __shared__ MPV mpv[3];
+    __shared__ OS ost[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -840,17 +857,23 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
 
     if (wave == NW) {
         // ------------------------------------------------------------------- DMA wave
-        auto step = [&](Buf& nxt, long jc) {
-            __builtin_amdgcn_s_waitcnt(0);  // chunk jc's copies have landed
-            lds_barrier();
-            if (jc + 1 < nchunks)
-                copy_chunk<DK, DV, DVT>(nxt, p, sbos + (jc + 1) * kChunk, chunk_len(jc + 1),
-                                        (cbase + jc + 1) * H + h, h, dv0, lane);
+        // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2). Loads complete
+        // in issue order, so at the top of chunk c only MPV(c+1) may still be in flight.
+        auto mpv_copy = [&](long jc) {
+            copy_mpv<DK, DV, DVT>(mpv[jc % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
+                              dv0, lane);
         };
-        if (nchunks > 0) copy_chunk<DK, DV, DVT>(buf0, p, sbos, chunk_len(0), cbase * H + h, h, dv0, lane);
-        for (long jc = 0; jc < nchunks; jc += 2) {
-            step(buf1, jc);
-            if (jc + 1 < nchunks) step(buf0, jc + 1);
+        if (nchunks > 0) {
+            copy_kq<DK>(kq[0], p, cbase * H + h, lane);
+            mpv_copy(0);
+        }
+        if (nchunks > 1) mpv_copy(1);
+        for (long jc = 0; jc < nchunks; ++jc) {
+            if (jc + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            lds_barrier();  // chunk jc's operands are in LDS; chunk jc-1's buffers are free
+            if (jc + 1 < nchunks) copy_kq<DK>(kq[(jc + 1) & 1], p, (cbase + jc + 1) * H + h, lane);
+            if (jc + 2 < nchunks) mpv_copy(jc + 2);
         }
         lds_barrier();
         return;
@@ -873,16 +896,12 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
                 __builtin_amdgcn_raw_buffer_store_b128(v, orr, lane * H * DV * E + 16 * i, 0, 0);
             }
         };
-        for (long jc = 0; jc < nchunks; jc += 2) {
+        for (long jc = 0; jc < nchunks; ++jc) {
             lds_barrier();
-            if (jc > 0) store_out(ost1, jc - 1);
-            if (jc + 1 < nchunks) {
-                lds_barrier();
-                store_out(ost0, jc);
-            }
+            if (jc > 0) store_out(ost[(jc - 1) & 1], jc - 1);
         }
         lds_barrier();  // the last chunk's outputs are staged
-        if (nchunks > 0) store_out((nchunks & 1) ? ost0 : ost1, nchunks - 1);
+        if (nchunks > 0) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
         return;
     }
 
@@ -904,8 +923,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     // 32-wide slice ahead, Mmat and the residual terms in the last slice, P during the
     // residual, K^T during the output product), and each product phase cycles over
     // independent accumulators; the scheduling fences keep that order.
-    auto step = [&](const Buf& cur, OS& os) {
-        lds_barrier();  // chunk data in cur; os free
+    auto step = [&](const KQ& ck, const MPV& cm, OS& os) {
+        lds_barrier();  // chunk data in ck, cm; os free
         uint4 MF[4][2], PF[4][2];
         float4 V4[4], EG4[4];
         auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
@@ -918,8 +937,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         auto load_r = [&]() {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                V4[t] = load4_t<uint16_t>(&cur.V[(16 * t + 4 * lq) * DVT + 16 * wave], DVT);
-                EG4[t] = *reinterpret_cast<const float4*>(&cur.eg[16 * t + 4 * lq]);
+                V4[t] = load4_t<uint16_t>(&cm.V[(16 * t + 4 * lq) * DVT + 16 * wave], DVT);
+                EG4[t] = *reinterpret_cast<const float4*>(&cm.eg[16 * t + 4 * lq]);
             }
         };
 
@@ -932,8 +951,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int row = 16 * t + l16, c0 = 32 * s + 4 * lq;
-                kf[t] = *reinterpret_cast<const uint4*>(&cur.K[img_off<DK>(row, c0)]);
-                qf[t] = *reinterpret_cast<const uint4*>(&cur.Q[img_off<DK>(row, c0)]);
+                kf[t] = *reinterpret_cast<const uint4*>(&cm.K[img_off<DK>(row, c0)]);
+                qf[t] = *reinterpret_cast<const uint4*>(&ck.Q[img_off<DK>(row, c0)]);
             }
         };
         load_xy(0, KF[0], QF[0]);
@@ -949,7 +968,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
             if (s + 1 < NKS) load_xy(s + 1, KF[b ^ 1], QF[b ^ 1]);
             else {
                 load_r();
-                load_mp(cur.M, MF);
+                load_mp(cm.M, MF);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -961,7 +980,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         }
 
         // R = V - e^gamma X
-        load_mp(cur.P, PF);
+        load_mp(cm.P, PF);
         f32x4_t R[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -985,8 +1004,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
 #pragma unroll
         for (int j = 0; j < NKB; ++j) {
             const int c = 16 * j + tc;
-            KT[j][0] = lds_frag2_t(&cur.K[img_off<DK>(4 * lq + tr, c)], &cur.K[img_off<DK>(16 + 4 * lq + tr, c)]);
-            KT[j][1] = lds_frag2_t(&cur.K[img_off<DK>(32 + 4 * lq + tr, c)], &cur.K[img_off<DK>(48 + 4 * lq + tr, c)]);
+            KT[j][0] = lds_frag2_t(&cm.K[img_off<DK>(4 * lq + tr, c)], &cm.K[img_off<DK>(16 + 4 * lq + tr, c)]);
+            KT[j][1] = lds_frag2_t(&cm.K[img_off<DK>(32 + 4 * lq + tr, c)], &cm.K[img_off<DK>(48 + 4 * lq + tr, c)]);
         }
 
         // O^T = e^gamma S Q^T + Delta^T P^T, staged in LDS for the store wave (lane: token
@@ -1012,10 +1031,10 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         f32x4_t Dd[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float4 ed = *reinterpret_cast<const float4*>(&cur.ed[16 * t + 4 * lq]);
+            const float4 ed = *reinterpret_cast<const float4*>(&cm.ed[16 * t + 4 * lq]);
             Dd[t] = f32x4_t{ed.x * D[t][0], ed.y * D[t][1], ed.z * D[t][2], ed.w * D[t][3]};
         }
-        const float elast = cur.eg[63];
+        const float elast = cm.eg[63];
         const uint4 BT[2] = {pack_f16_frag(Dd[0], Dd[1]), pack_f16_frag(Dd[2], Dd[3])};
 #pragma unroll
         for (int j = 0; j < NKB; ++j) ST[j] *= elast;
@@ -1026,10 +1045,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
             for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
     };
 
-    for (long jc = 0; jc < nchunks; jc += 2) {
-        step(buf0, ost0);
-        if (jc + 1 < nchunks) step(buf1, ost1);
-    }
+    for (long jc = 0, m3 = 0; jc < nchunks; ++jc, m3 = (m3 == 2 ? 0 : m3 + 1)) step(kq[jc & 1], mpv[m3], ost[jc & 1]);
     lds_barrier();  // hand the last chunk's outputs to the store wave
 
     if (p.hT) {
