@@ -880,20 +880,23 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     }
     if (wave == NW + 1) {
         // ----------------------------------------------------------------- store wave
-        // outputs of chunk jc: token row `lane` through a resource sized to the valid rows
+        // outputs of chunk jc through a resource sized to the valid rows; NV adjacent lanes
+        // write one token row's columns (16 bytes each), so an instruction covers 64/NV rows
         auto store_out = [&](const OS& os, long jc) {
-            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16;
+            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16, RPI = 64 / NV;
             const long obos = sbos + jc * kChunk;
             const int olen = chunk_len(jc);
             const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
                                        (unsigned)((olen - 1) * H * DV + DVT) * E);
-            uint4 row[NV];
+            const int rr = lane / NV, pc = lane % NV;
+            uint4 piece[NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) row[i] = *reinterpret_cast<const uint4*>(&os.b[lane * OS::PITCH + 16 * i]);
+            for (int i = 0; i < NV; ++i)
+                piece[i] = *reinterpret_cast<const uint4*>(&os.b[(RPI * i + rr) * OS::PITCH + 16 * pc]);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const u32x4_t v = {row[i].x, row[i].y, row[i].z, row[i].w};
-                __builtin_amdgcn_raw_buffer_store_b128(v, orr, lane * H * DV * E + 16 * i, 0, 0);
+                const u32x4_t v = {piece[i].x, piece[i].y, piece[i].z, piece[i].w};
+                __builtin_amdgcn_raw_buffer_store_b128(v, orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
             }
         };
         for (long jc = 0; jc < nchunks; ++jc) {
