@@ -78,14 +78,14 @@ def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def _token_tensors(rng, shape_qk, shape_v, shape_gate, dtype, gate_scale):
+def _token_tensors(rng, shape_qk, shape_v, shape_gate, dtype, gate_scale, beta_scale=1.0):
     q = rng.standard_normal(shape_qk, dtype=np.float32)
     k = rng.standard_normal(shape_qk, dtype=np.float32)
     v = rng.standard_normal(shape_v, dtype=np.float32)
     g_raw = rng.standard_normal(shape_gate, dtype=np.float32)
     b_raw = rng.standard_normal(shape_gate, dtype=np.float32)
     g = (-np.float32(gate_scale) * _softplus(g_raw)).astype(np.float32)
-    beta = _sigmoid(b_raw)
+    beta = (np.float32(beta_scale) * _sigmoid(b_raw)).astype(np.float32)
     return dict(q=_cast(_unit(q), dtype), k=_cast(_unit(k), dtype), v=_cast(v, dtype),
                 g=torch.from_numpy(g), beta=torch.from_numpy(beta))
 
@@ -99,13 +99,14 @@ def varlen_lengths(w: Workload, seed: int) -> np.ndarray:
 def make_forward_inputs(w: Workload | int, seed: int | None = None, *, T: int | None = None,
                         B: int | None = None, H: int | None = None, lengths=None,
                         gate_scale: float = 1.0, h0: bool | None = None,
-                        dtype: str | None = None) -> dict:
+                        dtype: str | None = None, beta_scale: float = 1.0) -> dict:
     """Draw one forward-pass input set.
 
     Returns CPU tensors: q, k [B,T,H,dk], v [B,T,H,dv] in the workload dtype; g, beta
     [B,T,H] fp32; h0 [N,H,dv,dk] fp32 or None; cu_seqlens int32 [N+1] or None.
     Overrides (T, B, H, lengths, dtype) shrink a workload for quick tests while
-    keeping its distributions. `gate_scale` multiplies -softplus (0.01 gives slow decay).
+    keeping its distributions. `gate_scale` multiplies -softplus (0.01 gives slow decay);
+    `beta_scale` multiplies the sigmoid (2 gives beta in (0, 2), the negative-eigenvalue range).
     """
     if isinstance(w, int):
         w = WORKLOADS[w]
@@ -126,21 +127,22 @@ def make_forward_inputs(w: Workload | int, seed: int | None = None, *, T: int | 
         Tn = w.T if T is None else T
         N = Bn
         cu_seqlens = None
-    out = _token_tensors(rng, (Bn, Tn, H, w.dk), (Bn, Tn, H, w.dv), (Bn, Tn, H), dtype, gate_scale)
+    out = _token_tensors(rng, (Bn, Tn, H, w.dk), (Bn, Tn, H, w.dv), (Bn, Tn, H), dtype, gate_scale,
+                         beta_scale)
     want_h0 = w.h0 if h0 is None else h0
     out["h0"] = (torch.from_numpy((rng.standard_normal((N, H, w.dv, w.dk), dtype=np.float32)
                                    * np.float32(w.state_std)).astype(np.float32))
                  if want_h0 else None)
     out["cu_seqlens"] = cu_seqlens
     out["meta"] = dict(workload=w.name, B=Bn, T=Tn, H=H, dk=w.dk, dv=w.dv, N=N, dtype=dtype,
-                       chunk=w.chunk, seed=seed, gate_scale=gate_scale,
+                       chunk=w.chunk, seed=seed, gate_scale=gate_scale, beta_scale=beta_scale,
                        lengths=None if cu_seqlens is None else [int(x) for x in np.diff(cu_seqlens.numpy())])
     return out
 
 
 def make_decode_inputs(w: Workload | int = 4, seed: int | None = None, *, N: int | None = None,
                        H: int | None = None, steps: int | None = None,
-                       dtype: str | None = None) -> dict:
+                       dtype: str | None = None, beta_scale: float = 1.0) -> dict:
     """Draw the decode workload: fp32 state [N,H,dv,dk] and `steps` stacked token sets
     q, k [steps,N,H,dk], v [steps,N,H,dv] (workload dtype), g, beta [steps,N,H] fp32."""
     if isinstance(w, int):
@@ -152,7 +154,8 @@ def make_decode_inputs(w: Workload | int = 4, seed: int | None = None, *, N: int
     steps = w.decode_steps if steps is None else steps
     dtype = w.dtype if dtype is None else dtype
     state = (rng.standard_normal((N, H, w.dv, w.dk), dtype=np.float32) * np.float32(w.state_std))
-    out = _token_tensors(rng, (steps, N, H, w.dk), (steps, N, H, w.dv), (steps, N, H), dtype, 1.0)
+    out = _token_tensors(rng, (steps, N, H, w.dk), (steps, N, H, w.dv), (steps, N, H), dtype, 1.0,
+                         beta_scale)
     out["state"] = torch.from_numpy(state.astype(np.float32))
     out["meta"] = dict(workload=w.name, N=N, H=H, dk=w.dk, dv=w.dv, steps=steps, dtype=dtype, seed=seed)
     return out

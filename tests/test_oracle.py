@@ -122,8 +122,25 @@ def pin_hand_example(fwd):
     return max(rel(o[0, :, 0], a[:, 8:10]), rel(hT[0, 0].ravel(), a[-1, 10:14]))
 
 
+def pin_reflection(fwd):
+    """beta = 2 (the negative-eigenvalue range beta in (0, 2)), alpha = 1, v = 0: the step is
+    S <- S (I - 2 k k^T), a Householder reflection. Two steps with the same unit key restore
+    h0 exactly; with q = k the readouts are -h0 k after the first step and h0 k after the
+    second."""
+    rng = np.random.default_rng(42)
+    H, dk, dv = 2, 6, 5
+    k1 = unit(rng.standard_normal((H, dk)))
+    k = np.stack([k1, k1])[None]                       # [1, 2, H, dk]
+    h0 = rng.standard_normal((1, H, dv, dk))
+    x = dict(q=k.copy(), k=k, v=np.zeros((1, 2, H, dv)), g=np.zeros((1, 2, H)),
+             beta=np.full((1, 2, H), 2.0), h0=h0)
+    o, hT = fwd(**x)
+    hk = np.einsum("hvk,hk->hv", h0[0], k1)
+    return max(rel(o[0, 0], -hk), rel(o[0, 1], hk), rel(hT, h0))
+
+
 PINS = [pin_decay_only, pin_orthonormal_recall, pin_overwrite, pin_literal_product,
-        pin_hand_example]
+        pin_hand_example, pin_reflection]
 TOL = 1e-12
 
 
@@ -151,6 +168,17 @@ def test_chunkwise_equals_recurrence(C, gate_scale):
     o_r, h_r = R.forward(**x)
     o_c, h_c = CW.forward(**x, chunk=C)
     assert rel(o_c, o_r) < 1e-12 and rel(h_c, h_r) < 1e-12
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_chunkwise_equals_recurrence_beta_to_2(C):
+    """beta in (0, 2): the chunk factors stay exact (the UT transform of a unit lower
+    triangular matrix needs no pivoting whatever the size of A's entries)."""
+    x = rand_inputs(30 + C, B=2, T=150, H=2, dk=16, dv=12, gate_scale=0.3, h0=True)
+    x["beta"] = 2.0 * x["beta"]
+    o_r, h_r = R.forward(**x)
+    o_c, h_c = CW.forward(**x, chunk=C)
+    assert rel(o_c, o_r) < 1e-11 and rel(h_c, h_r) < 1e-11
 
 
 def test_chunkwise_varlen_equals_recurrence():

@@ -109,6 +109,21 @@ def test_fwd_small(B, T, H, dk, dv, dtype, h0, gs):
     check_fwd(SY.make_forward_inputs(w, seed=1000 + T + dk + dv, gate_scale=gs, h0=h0))
 
 
+@pytest.mark.parametrize("dtype,dk,dv,T,gs", [("bf16", 128, 128, 300, 0.05), ("bf16", 64, 128, 130, 1.0),
+                                               ("f32", 128, 128, 200, 0.05), ("f32", 64, 64, 150, 1.0)])
+def test_fwd_beta_to_2(dtype, dk, dv, T, gs):
+    """beta in (0, 2), the negative-eigenvalue range: the same kernels, with A's entries up to
+    about 2 in the UT transform."""
+    w = SY.Workload(90, f"beta2_{dtype}", H=2, dk=dk, dv=dv, dtype=dtype, B=2, T=T)
+    check_fwd(SY.make_forward_inputs(w, seed=31 + T + dk, gate_scale=gs, h0=True, beta_scale=2.0))
+
+
+def test_fwd_beta_to_2_varlen():
+    w = SY.Workload(90, "beta2_varlen", H=3, dk=128, dv=128, dtype="bf16")
+    check_fwd(SY.make_forward_inputs(w, seed=33, lengths=[65, 1, 200, 0, 130], gate_scale=0.1, h0=True,
+                                     beta_scale=2.0))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fwd_varlen_edges(dtype):
     """Packed sequences of lengths 1, 64, 0, 65, 130, 7 and 200: single-token, exactly one
@@ -311,6 +326,13 @@ def test_decode_small(dtype, dk, dv):
     w = SY.Workload(94, "decode_small", H=3, dk=dk, dv=dv, dtype=dtype, decode_seqs=5,
                     decode_steps=12)
     check_decode(SY.make_decode_inputs(w, seed=12))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_beta_to_2(dtype):
+    w = SY.Workload(89, "decode_beta2", H=3, dk=128, dv=128, dtype=dtype, decode_seqs=5,
+                    decode_steps=12)
+    check_decode(SY.make_decode_inputs(w, seed=14, beta_scale=2.0))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
