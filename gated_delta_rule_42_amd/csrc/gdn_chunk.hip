@@ -126,6 +126,22 @@ __device__ __forceinline__ void img_piece(int i, int& r, int& c0) {
 }
 
 // ------------------------------------------------------------------- stage 1
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each 16-lane row, then the
+// row totals broadcast forward (DPP row_shr and row_bcast).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_src(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x = dpp_add_src<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_add_src<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_add_src<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_add_src<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 template <typename TIn, int DK>
 struct alignas(16) PrepSmem {
     using TM = typename Operand<TIn>::type;
@@ -137,7 +153,8 @@ struct alignas(16) PrepSmem {
         struct { float A[64 * PF]; float T[64 * PF]; } tri;
     } u;
     TM P[64 * PC];
-    float gam[64];
+    float graw[64];   // g as loaded
+    float gam[64];    // its in-chunk inclusive cumulative sum
     float beta[64];
 };
 
@@ -183,7 +200,7 @@ struct PrepStage {
             *reinterpret_cast<uint4*>(&sm.u.in.Q[r * PK + cv * EPV]) = rq[it];
         }
         if (tid < 64) {
-            sm.gam[tid] = rg;
+            sm.graw[tid] = rg;
             sm.beta[tid] = rb;
         }
     }
@@ -252,20 +269,18 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             __syncthreads();
             if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
 
-            // -- gate scan and gate tables (wave 0)
-            if (wave == 0) {
-                float x = sm.gam[lane];  // inclusive prefix sum of g over the 64 positions
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(x, off, 64);
-                    if (lane >= off) x += y;
-                }
-                const float last = __shfl(x, 63, 64);
+            // -- gate scan (every wave scans its own copy, so no barrier is needed before the
+            //    reads of gamma below; the identical LDS writes of the four waves are benign) and
+            //    gate tables (wave 0)
+            {
+                const float x = wave_inclusive_sum(sm.graw[lane]);
                 sm.gam[lane] = x;
-                p.gates[widx * 128 + lane] = __expf(x);
-                p.gates[widx * 128 + 64 + lane] = __expf(last - x);
+                if (wave == 0) {
+                    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+                    p.gates[widx * 128 + lane] = __expf(x);
+                    p.gates[widx * 128 + 64 + lane] = __expf(last - x);
+                }
             }
-            __syncthreads();
             if (p.k16) write_kq_images<TIn, DK>(sm, p.k16 + widx * 64 * DK, p.q16 + widx * 64 * DK, tid);
 
             // -- K K^T and Q K^T (exact products of the inputs); wave w owns row block w

@@ -370,7 +370,7 @@ __device__ __forceinline__ void split_bf16_frag(const f32x4_t& a, const f32x4_t&
 // address (taken as an integer, which needs no null check).
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ __forceinline__ lds_void_ptr to_lds(const void* p) {
-    return (lds_void_ptr)(uint32_t)reinterpret_cast<uintptr_t>(p);
+    return (lds_void_ptr)(uintptr_t)(uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_block, int off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_block), 16, off, 0, 0, 0);
