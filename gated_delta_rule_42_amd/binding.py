@@ -28,6 +28,8 @@ _SIGNATURES = [
     ("gdn_chunk_prepare", _I, [_P] * 5 + [_I] * 8 + [_P, _SZ, _P]),
     ("gdn_chunk_propagate", _I, [_P] * 7 + [_I] * 9 + [_P, _SZ, _P]),
     ("gdn_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
+    ("gdn_chunk_bwd_workspace_bytes", _SZ, [_I] * 9),
+    ("gdn_chunk_bwd", _I, [_P] * 15 + [_I] * 9 + [_P, _SZ, _P]),
 ]
 
 _lib = None
@@ -168,3 +170,37 @@ def gdn_decode_step(q, k, v, g, beta, state, o=None, *, o_dtype=torch.float32, s
                                _stream(q.device, stream))
     _check(st, "gdn_decode_step")
     return o
+
+
+def gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, varlen, chunk=CHUNK, dtype=torch.bfloat16) -> int:
+    return lib().gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, int(bool(varlen)), chunk,
+                                               _DTYPE[dtype])
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, do, h0=None, dhT=None, cu_seqlens=None, chunk=CHUNK, *,
+                  grad_dtype=None, need_dh0=True, workspace=None, stream=None):
+    """Backward pass of gdn_chunk_fwd for output gradients do [B,T,H,dv] (dtype of q) and
+    final-state gradients dhT [N,H,dv,dk] fp32 (or None). Returns dq, dk, dv (grad_dtype,
+    default the dtype of q; fp32 is allowed for bf16 inputs), dg, dbeta [B,T,H] fp32 and
+    dh0 [N,H,dv,dk] fp32 (None unless need_dh0)."""
+    _need_gpu(q, k, v, g, beta, do, h0, dhT, cu_seqlens, workspace)
+    B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
+    dev = q.device
+    gd = grad_dtype or q.dtype
+    dq = torch.empty(q.shape, dtype=gd, device=dev)
+    dk_ = torch.empty(k.shape, dtype=gd, device=dev)
+    dv_ = torch.empty(v.shape, dtype=gd, device=dev)
+    dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    db = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev) if need_dh0 else None
+    need = gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, cu_seqlens is not None, chunk, q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+                             _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dh0),
+                             _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N, _DTYPE.get(q.dtype, -1),
+                             _DTYPE.get(gd, -1), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0,
+                             _stream(dev, stream))
+    _check(st, "gdn_chunk_bwd")
+    return dq, dk_, dv_, dg, db, dh0

@@ -150,3 +150,81 @@ GDN_EXPORT int gdn_decode_step(const void* q, const void* k, const void* v, cons
     return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                 : GDN_ERR_HIP;
 }
+
+GDN_EXPORT size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                int varlen, int chunk, int dtype) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
+    if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
+    if (B < 1 || H < 1 || T < 0) return 0;
+    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    return gdn::bwd_workspace_layout(B, T, H, dk, dv, N, varlen != 0, dtype == GDN_BF16).total;
+}
+
+GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                             const float* beta, const float* h0, const void* d_o, const float* dhT,
+                             void* dq, void* dk_out, void* dv_out, float* dg, float* dbeta, float* dh0,
+                             const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                             int N, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (grad_dtype != GDN_F32 && !(grad_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
+    if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
+    } else if (N != B) {
+        return GDN_ERR_SHAPE;
+    }
+    const long long tokens = (long long)B * T;
+    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
+        return GDN_ERR_SHAPE;
+    if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !beta || !d_o || !dq || !dk_out || !dv_out ||
+                       !dg || !dbeta))
+        return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, d_o, dq, dk_out, dv_out, h0, dhT, dh0};
+    for (const void* x : al16)
+        if (x && !aligned(x, 16)) return GDN_ERR_ALIGN;
+    const void* al4[] = {g_log_alpha, beta, dg, dbeta, cu_seqlens};
+    for (const void* x : al4)
+        if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
+    const int bf16 = dtype == GDN_BF16;
+    const gdn::BwdLayout w = gdn::bwd_workspace_layout(B, T, H, dk, dv, N, cu_seqlens != nullptr, bf16);
+    if (w.fwd.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
+    if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
+
+    char* base = static_cast<char*>(workspace);
+    gdn::BwdProblem b{};
+    gdn::ChunkProblem& P = b.f;
+    b.q_in = q; b.k_in = k; b.v_in = v; b.do_in = d_o;
+    if (bf16 && tokens > 0) {
+        b.q32 = reinterpret_cast<float*>(base + w.off_q32);
+        b.k32 = reinterpret_cast<float*>(base + w.off_k32);
+        b.v32 = reinterpret_cast<float*>(base + w.off_v32);
+        b.do32w = reinterpret_cast<float*>(base + w.off_do32);
+    }
+    P.q = bf16 ? b.q32 : q;
+    P.k = bf16 ? b.k32 : k;
+    P.v = bf16 ? b.v32 : v;
+    b.do32 = bf16 ? b.do32w : static_cast<const float*>(d_o);
+    P.g = g_log_alpha; P.beta = beta; P.h0 = h0; P.o = nullptr; P.hT = nullptr;
+    P.cu_seqlens = cu_seqlens;
+    P.B = B; P.T = T; P.H = H; P.dk = dk; P.dv = dv; P.N = N;
+    P.bf16 = 0; P.o_bf16 = 0;
+    P.nc_bound = w.fwd.nc_bound;
+    P.nc_per_seq = (T + 63) / 64;
+    const bool any = w.fwd.nc_bound > 0;
+    P.chunk_base = cu_seqlens ? reinterpret_cast<int32_t*>(base + w.fwd.off_base) : nullptr;
+    P.gates = any ? reinterpret_cast<float*>(base + w.fwd.off_gates) : nullptr;
+    P.mmat = any ? base + w.fwd.off_m : nullptr;
+    P.pmat = any ? base + w.fwd.off_p : nullptr;
+    P.tmat = any ? reinterpret_cast<float*>(base + w.off_t) : nullptr;
+    P.states = any ? reinterpret_cast<float*>(base + w.off_states) : nullptr;
+    b.dstates = any ? reinterpret_cast<float*>(base + w.off_dstates) : nullptr;
+    b.dhT = dhT;
+    b.dq = dq; b.dk = dk_out; b.dv = dv_out; b.dg = dg; b.dbeta = dbeta; b.dh0 = dh0;
+    b.grad_bf16 = grad_dtype == GDN_BF16;
+    return gdn::launch_chunk_backward(b, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                       : GDN_ERR_HIP;
+}

@@ -1,0 +1,603 @@
+// Chunked backward pass of the gated delta rule for gfx950: the gradients of a loss with
+// respect to q, k, v, g = log alpha, beta and h0, given its gradients dO with respect to the
+// outputs and dhT with respect to the final states.
+//
+// The pages train the layer with the chunkwise algorithm (paper note "Gated Delta Networks:
+// Improving Mamba2 with Delta Rule", mechanism paragraph: "parallel training algorithm";
+// record "LIT-137", "Key takeaways") but print no gradient formulas. The ones below are the
+// adjoint of the chunk equations of the forward pass (gdn_chunk.hip), with E = diag(e^gamma),
+// Ed = diag(e^{gamma_last - gamma}), lam = e^{gamma_last}, X = K S^T, R = V - E X,
+// Delta = Mmat R, Y = E Q S^T, O = Y + P Delta, S' = lam S + Delta^T Ed K:
+//
+//   reverse walk over the chunks of a sequence, dS' = gradient reaching the state after the
+//   chunk (dhT for the last chunk):
+//     Z = K dS'^T,   dDelta = P^T dO + Ed Z,   dR = Mmat^T dDelta  (= dV)
+//     dS = lam dS' + (E dO)^T Q - (E dR)^T K      (dS' of the chunk before; dh0 at the start)
+//   every chunk independently, given its entering state S and its dS':
+//     dP = dO Delta^T (lower incl. diagonal),  dPg = dP * Gamma
+//     dMmat = dDelta R^T,  dT = dMmat diag(beta),  dA = strict_lower(-T^T dT T^T)
+//     dQ = E dO S + dPg K
+//     dK = -E dR S + Ed Delta dS' + dPg^T Q + (dG + dG^T) K,   dG = dA * beta_r * Gamma
+//     dbeta_i = sum_r dMmat[r,i] T[r,i] + sum_m dA[i,m] (k_i . k_m) Gamma[i,m]
+//     dgamma_r = (dO : Y)_r - (dR : E X)_r - z_r + (dP : P) row r - (dP : P) column r
+//                + (dA : A) row r - (dA : A) column r,   z_r = Ed_r (Delta : Z)_r,
+//                and the chunk's last row also gets lam (dS' : S) + sum_r z_r
+//     dg = reverse cumulative sum of dgamma within the chunk.
+// (":" is the sum of an elementwise product over the d_v columns; Gamma[r,i] = e^{gamma_r -
+// gamma_i} for i <= r.)
+//
+// Passes, all in fp32: (0) bf16 q, k, v, dO are widened into the workspace; (1) stage 1 of
+// the forward pass (gate tables, Mmat, P) also keeping T; (2) stage 2 of the forward pass
+// keeping the state entering every chunk instead of writing o; (3) chunk_bwd_state_kernel,
+// the reverse walk, keeping dS' of every chunk and writing dh0; (4) chunk_bwd_grad_kernel,
+// every (chunk, head) on its own. The products run on the fp32 matrix core (16x16x4).
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// acc (16x16 fp32 tile) += A[16 x 4] B[4 x 16]: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16]; acc holds rows 4 (l / 16) + 0..3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ widening
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src,
+                                                         float* __restrict__ dst, long n8) {
+    for (long i = blockIdx.x * 256L + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+        const uint4 raw = reinterpret_cast<const uint4*>(src)[i];
+        auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+        auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+        reinterpret_cast<float4*>(dst)[2 * i] = make_float4(lo(raw.x), hi(raw.x), lo(raw.y), hi(raw.y));
+        reinterpret_cast<float4*>(dst)[2 * i + 1] = make_float4(lo(raw.z), hi(raw.z), lo(raw.w), hi(raw.w));
+    }
+}
+
+// ------------------------------------------------------- reverse walk (pass 3)
+template <int DK, int DVT>
+struct alignas(16) BwdStateSmem {
+    static constexpr int PK = DK + 4, PC = 68, PV = DVT + 4;
+    float K[64 * PK];
+    float Q[64 * PK];
+    float M[64 * PC];
+    float P[64 * PC];
+    float dO[64 * PV];   // the work-group's d_v columns
+    float eg[64];
+    float ed[64];
+};
+
+// One work-group per (sequence, head, DVT-column tile); wave w owns d_v columns dv0 + 16w
+// .. +15 and holds dS'^T [d_k, 16] as d_k/16 accumulator tiles (lane: dS'[col l16][16j +
+// 4 lq + 0..3]), walking the chunks from the last to the first.
+template <int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state_kernel(ChunkProblem p, const float* do32,
+                                                                         const float* dhT, float* dstates,
+                                                                         float* dh0) {
+    using SM = BwdStateSmem<DK, DVT>;
+    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, NKB = DK / 16, NTILE = DV / DVT;
+    constexpr int NT = DVT / 16 * 64;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long pair = blockIdx.x / NTILE;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + 63) / 64;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+
+    f32x4_t dST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        if (dhT) {
+            const float4 x = *reinterpret_cast<const float4*>(dhT + srow + 16 * j);
+            dST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            dST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const float* kp = static_cast<const float*>(p.k);
+    const float* qp = static_cast<const float*>(p.q);
+    const float* mp = static_cast<const float*>(p.mmat);
+    const float* pp = static_cast<const float*>(p.pmat);
+
+    for (long jc = nchunks - 1; jc >= 0; --jc) {
+        const long bos = sbos + jc * 64, widx = (cbase + jc) * H + h;
+        const int len = (int)min(64L, seos - bos);
+        __syncthreads();  // the previous chunk's LDS data is dead
+        for (int i = tid; i < 64 * DK / 4; i += NT) {
+            const int r = i / (DK / 4), c = 4 * (i % (DK / 4));
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+            if (r < len) {
+                kv = *reinterpret_cast<const float4*>(kp + ((bos + r) * H + h) * DK + c);
+                qv = *reinterpret_cast<const float4*>(qp + ((bos + r) * H + h) * DK + c);
+            }
+            *reinterpret_cast<float4*>(&sm.K[r * PK + c]) = kv;
+            *reinterpret_cast<float4*>(&sm.Q[r * PK + c]) = qv;
+        }
+        for (int i = tid; i < 64 * 16; i += NT) {
+            const int r = i / 16, c = 4 * (i % 16);
+            *reinterpret_cast<float4*>(&sm.M[r * PC + c]) = *reinterpret_cast<const float4*>(mp + widx * 4096 + r * 64 + c);
+            *reinterpret_cast<float4*>(&sm.P[r * PC + c]) = *reinterpret_cast<const float4*>(pp + widx * 4096 + r * 64 + c);
+        }
+        for (int i = tid; i < 64 * DVT / 4; i += NT) {
+            const int r = i / (DVT / 4), c = 4 * (i % (DVT / 4));
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < len) x = *reinterpret_cast<const float4*>(do32 + ((bos + r) * H + h) * DV + dv0 + c);
+            *reinterpret_cast<float4*>(&sm.dO[r * PV + c]) = x;
+        }
+        if (tid < 128) (tid < 64 ? sm.eg : sm.ed)[tid & 63] = p.gates[widx * 128 + tid];
+        __syncthreads();
+
+        // dS' of this chunk, for the per-chunk gradients
+        float* ds = dstates + (widx * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(ds + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+
+        // Z = K dS'^T (k relabelled to the accumulator rows: step (j, s) takes d_k 16j + 4lq + s)
+        f32x4_t Z[4], dD[4], dR[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            Z[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKB; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Z[t] = mfma4(sm.K[(16 * t + l16) * PK + 16 * j + 4 * lq + s], dST[j][s], Z[t]);
+        }
+        // dDelta = P^T dO + Ed Z
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dD[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < 64; k0 += 4)
+                dD[t] = mfma4(sm.P[(k0 + lq) * PC + 16 * t + l16], sm.dO[(k0 + lq) * PV + 16 * wave + l16], dD[t]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dD[t][m] += sm.ed[16 * t + 4 * lq + m] * Z[t][m];
+        }
+        // dR = Mmat^T dDelta
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    dR[t] = mfma4(sm.M[(16 * t2 + 4 * lq + s) * PC + 16 * t + l16], dD[t2][s], dR[t]);
+        }
+        // dS'^T <- lam dS'^T + Q^T (E dO) - K^T (E dR)
+        const float lam = sm.eg[63];
+        f32x4_t EdR[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) EdR[t][m] = -sm.eg[16 * t + 4 * lq + m] * dR[t][m];
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            f32x4_t acc = dST[j] * lam;
+#pragma unroll 4
+            for (int k0 = 0; k0 < 64; k0 += 4)
+                acc = mfma4(sm.Q[(k0 + lq) * PK + 16 * j + l16],
+                            sm.eg[k0 + lq] * sm.dO[(k0 + lq) * PV + 16 * wave + l16], acc);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma4(sm.K[(16 * t + 4 * lq + s) * PK + 16 * j + l16], EdR[t][s], acc);
+            dST[j] = acc;
+        }
+    }
+    if (dh0) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(dh0 + srow + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+    }
+}
+
+// ------------------------------------------------------ per-chunk gradients (pass 4)
+template <int DK>
+struct alignas(16) GradSmem {
+    static constexpr int PK = DK + 4, PC = 68, PS = DK + 4, PV = 20;
+    float K[64 * PK];
+    float Q[64 * PK];
+    float T[64 * PC];
+    float P[64 * PC];          // P, then dPg
+    union {
+        struct {               // one 16-column d_v slice
+            float S[16 * PS];  // rows dv0 .. +15 of the entering state
+            float dS[16 * PS]; // the same rows of dS'
+            float V[64 * PV];
+            float dO[64 * PV];
+            float R[64 * PV];
+            float D[64 * PV];  // Delta
+            float dD[64 * PV]; // dDelta
+            float dR[64 * PV];
+        } sl;
+        struct {
+            float X1[64 * PC]; // dT, then dG
+            float X2[64 * PC]; // dT T^T
+        } cc;
+    } u;
+    float gam[64], eg[64], ed[64], beta[64];
+    // partial sums of dgamma and dbeta, added in a fixed order (results are reproducible)
+    float colg[4][64], colb[4][64];   // column terms, per wave
+    float rowg[64], rowb[64];         // row terms (each row belongs to one wave)
+    float tailw[4];                   // last-row terms, per wave
+};
+
+// Sums over the lanes of a wave that share l16 (the four lq groups), or that share lq (the
+// sixteen l16 lanes), or over all 64 lanes. Butterflies: every lane ends with the same value,
+// added in an order that does not depend on timing.
+__device__ __forceinline__ float sum_lq(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+__device__ __forceinline__ float sum_l16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    return x + __shfl_xor(x, 8);
+}
+
+template <typename TO>
+__device__ __forceinline__ void store_elem(TO* p, float x) { *p = from_f32<TO>(x); }
+
+// One work-group (4 waves) per (chunk, head); wave w owns token rows 16w .. 16w+15 of every
+// row-blocked product. The d_v-dependent terms are accumulated over 16-column slices of d_v.
+template <typename TO, int DK, int DV>
+__global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdProblem bp) {
+    using SM = GradSmem<DK>;
+    constexpr int PK = SM::PK, PC = SM::PC, PS = SM::PS, PV = SM::PV, NKB = DK / 16;
+    __shared__ SM sm;
+    const ChunkProblem& p = bp.f;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long unit = blockIdx.x, c = unit / H;
+    const int h = (int)(unit % H);
+    long bos;
+    int len;
+    if (!locate_chunk(p, c, bos, len)) return;   // uniform over the work-group
+    const long widx = c * H + h;
+    const float* kp = static_cast<const float*>(p.k);
+    const float* qp = static_cast<const float*>(p.q);
+    const float* vp = static_cast<const float*>(p.v);
+    const float* dop = bp.do32;
+
+    for (int i = tid; i < 64 * DK / 4; i += 256) {
+        const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (r < len) {
+            kv = *reinterpret_cast<const float4*>(kp + ((bos + r) * H + h) * DK + cc);
+            qv = *reinterpret_cast<const float4*>(qp + ((bos + r) * H + h) * DK + cc);
+        }
+        *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
+        *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+    }
+    for (int i = tid; i < 64 * 16; i += 256) {
+        const int r = i / 16, cc = 4 * (i % 16);
+        *reinterpret_cast<float4*>(&sm.T[r * PC + cc]) = *reinterpret_cast<const float4*>(p.tmat + widx * 4096 + r * 64 + cc);
+        *reinterpret_cast<float4*>(&sm.P[r * PC + cc]) =
+            *reinterpret_cast<const float4*>(static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc);
+    }
+    if (wave == 0) {
+        const long o = (bos + lane) * H + h;
+        const float gr = lane < len ? p.g[o] : 0.f;
+        sm.beta[lane] = lane < len ? p.beta[o] : 0.f;
+        sm.gam[lane] = wave_inclusive_sum(gr);
+        sm.eg[lane] = p.gates[widx * 128 + lane];
+        sm.ed[lane] = p.gates[widx * 128 + 64 + lane];
+    }
+
+    const int row = 16 * wave + l16;   // this lane's row as a left operand
+    f32x4_t dP[4], dM[4], dQ1[NKB], dK1[NKB];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dP[t] = dM[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) dQ1[j] = dK1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float gacc[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma of rows 16 wave + 4 lq + m, this lane's column
+    float tail = 0.f;                       // lam (dS' : S) + sum z, this thread's share
+    auto& sl = sm.u.sl;
+
+    for (int js = 0; js < DV / 16; ++js) {
+        const int dv0 = 16 * js;
+        __syncthreads();  // the previous slice is dead (first slice: the loads above are done)
+        const float lam = sm.eg[63];
+        for (int i = tid; i < 16 * DK / 4; i += 256) {
+            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const float4 s = *reinterpret_cast<const float4*>(p.states + (widx * DV + dv0 + r) * DK + cc);
+            const float4 d = *reinterpret_cast<const float4*>(bp.dstates + (widx * DV + dv0 + r) * DK + cc);
+            *reinterpret_cast<float4*>(&sl.S[r * PS + cc]) = s;
+            *reinterpret_cast<float4*>(&sl.dS[r * PS + cc]) = d;
+            tail += lam * (s.x * d.x + s.y * d.y + s.z * d.z + s.w * d.w);
+        }
+        {
+            const int r = tid >> 2, cc = 4 * (tid & 3);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f), d = v;
+            if (r < len) {
+                v = *reinterpret_cast<const float4*>(vp + ((bos + r) * H + h) * DV + dv0 + cc);
+                d = *reinterpret_cast<const float4*>(dop + ((bos + r) * H + h) * DV + dv0 + cc);
+            }
+            *reinterpret_cast<float4*>(&sl.V[r * PV + cc]) = v;
+            *reinterpret_cast<float4*>(&sl.dO[r * PV + cc]) = d;
+        }
+        __syncthreads();
+
+        // X = K S^T, Y = Q S^T, Z = K dS'^T for this wave's rows
+        f32x4_t X = {0.f, 0.f, 0.f, 0.f}, Y = X, Z = X;
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const float ak = sm.K[row * PK + k0 + lq], aq = sm.Q[row * PK + k0 + lq];
+            const float bs = sl.S[l16 * PS + k0 + lq], bd = sl.dS[l16 * PS + k0 + lq];
+            X = mfma4(ak, bs, X);
+            Y = mfma4(aq, bs, Y);
+            Z = mfma4(ak, bd, Z);
+        }
+        float EX[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            EX[m] = sm.eg[r] * X[m];
+            sl.R[r * PV + l16] = sl.V[r * PV + l16] - EX[m];
+            gacc[m] += sl.dO[r * PV + l16] * sm.eg[r] * Y[m];
+        }
+        __syncthreads();
+
+        // Delta = T diag(beta) R, dDelta = P^T dO + Ed Z
+        f32x4_t Dl = {0.f, 0.f, 0.f, 0.f}, dDl = Dl;
+#pragma unroll 4
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int i = k0 + lq;
+            Dl = mfma4(sm.T[row * PC + i], sm.beta[i] * sl.R[i * PV + l16], Dl);
+            dDl = mfma4(sm.P[i * PC + row], sl.dO[i * PV + l16], dDl);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            const float z = sm.ed[r] * Dl[m] * Z[m];
+            dDl[m] += sm.ed[r] * Z[m];
+            gacc[m] -= z;
+            tail += z;
+            sl.D[r * PV + l16] = Dl[m];
+            sl.dD[r * PV + l16] = dDl[m];
+        }
+        __syncthreads();
+
+        // dR = Mmat^T dDelta (= dV)
+        f32x4_t dRl = {0.f, 0.f, 0.f, 0.f};
+        const float brow = sm.beta[row];
+#pragma unroll 4
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int r = k0 + lq;
+            dRl = mfma4(sm.T[r * PC + row] * brow, sl.dD[r * PV + l16], dRl);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            gacc[m] -= dRl[m] * EX[m];
+            sl.dR[r * PV + l16] = dRl[m];
+            if (r < len) store_elem<TO>(static_cast<TO*>(bp.dv) + ((bos + r) * H + h) * DV + dv0 + l16, dRl[m]);
+        }
+        __syncthreads();
+
+        // dP += dO Delta^T, dMmat += dDelta R^T (contraction over the slice's 16 columns)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 4) {
+                const int v = k0 + lq;
+                dP[cb] = mfma4(sl.dO[row * PV + v], sl.D[(16 * cb + l16) * PV + v], dP[cb]);
+                dM[cb] = mfma4(sl.dD[row * PV + v], sl.R[(16 * cb + l16) * PV + v], dM[cb]);
+            }
+        // dQ1 += E dO S, dK1 += -E dR S + Ed Delta dS'
+        const float egr = sm.eg[row], edr = sm.ed[row];
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+            const int v = k0 + lq;
+            const float a1 = egr * sl.dO[row * PV + v], a2 = -egr * sl.dR[row * PV + v], a3 = edr * sl.D[row * PV + v];
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) {
+                const float bS = sl.S[v * PS + 16 * j + l16], bdS = sl.dS[v * PS + 16 * j + l16];
+                dQ1[j] = mfma4(a1, bS, dQ1[j]);
+                dK1[j] = mfma4(a2, bS, dK1[j]);
+                dK1[j] = mfma4(a3, bdS, dK1[j]);
+            }
+        }
+    }
+    __syncthreads();  // slice buffers are dead; their space becomes X1, X2
+
+    // -- dPg (into P) and the P terms of dgamma; dT (into X1) and the Mmat term of dbeta
+    float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, dbrow[4] = {0.f, 0.f, 0.f, 0.f};
+    float colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};   // column 16 cb + l16
+    auto& cc = sm.u.cc;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int col = 16 * cb + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            float dpg = 0.f;
+            if (col <= r) {
+                const float x = dP[cb][m] * sm.P[r * PC + col];
+                rowacc[m] += x;
+                colg[cb] -= x;
+                dpg = dP[cb][m] * __expf(sm.gam[r] - sm.gam[col]);
+            }
+            sm.P[r * PC + col] = dpg;
+            colb[cb] += dM[cb][m] * sm.T[r * PC + col];
+            cc.X1[r * PC + col] = dM[cb][m] * sm.beta[col];
+        }
+    }
+    __syncthreads();
+    // -- X2 = dT T^T
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k0 = 0; k0 < 64; k0 += 4)
+            acc = mfma4(cc.X1[row * PC + k0 + lq], sm.T[(16 * cb + l16) * PC + k0 + lq], acc);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cc.X2[(16 * wave + 4 * lq + m) * PC + 16 * cb + l16] = acc[m];
+    }
+    __syncthreads();
+    // -- dA = strict_lower(-T^T X2); with G = K K^T: the A terms of dbeta and dgamma, dG into X1
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        f32x4_t ta = {0.f, 0.f, 0.f, 0.f}, G = ta;
+#pragma unroll 4
+        for (int k0 = 0; k0 < 64; k0 += 4)
+            ta = mfma4(sm.T[(k0 + lq) * PC + row], cc.X2[(k0 + lq) * PC + 16 * cb + l16], ta);
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 4)
+            G = mfma4(sm.K[row * PK + k0 + lq], sm.K[(16 * cb + l16) * PK + k0 + lq], G);
+        const int col = 16 * cb + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            float dg = 0.f;
+            if (col < r) {
+                const float da = -ta[m], gm = __expf(sm.gam[r] - sm.gam[col]);
+                const float ag = G[m] * gm;
+                dbrow[m] += da * ag;
+                const float aa = da * sm.beta[r] * ag;
+                rowacc[m] += aa;
+                colg[cb] -= aa;
+                dg = da * sm.beta[r] * gm;
+            }
+            cc.X1[r * PC + col] = dg;
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const float g = sum_lq(colg[cb]), b = sum_lq(colb[cb]);
+        if (lq == 0) {
+            sm.colg[wave][16 * cb + l16] = g;
+            sm.colb[wave][16 * cb + l16] = b;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float g = sum_l16(gacc[m] + rowacc[m]), b = sum_l16(dbrow[m]);
+        if (l16 == 0) {
+            sm.rowg[16 * wave + 4 * lq + m] = g;
+            sm.rowb[16 * wave + 4 * lq + m] = b;
+        }
+    }
+    {
+        const float t = sum_l16(sum_lq(tail));
+        if (lane == 0) sm.tailw[wave] = t;
+    }
+    __syncthreads();
+
+    // -- dQ = dQ1 + dPg K, dK = dK1 + dPg^T Q + dG K + dG^T K
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        f32x4_t aq = dQ1[j], ak = dK1[j];
+        const int col = 16 * j + l16;
+#pragma unroll 4
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int i = k0 + lq;
+            const float bK = sm.K[i * PK + col], bQ = sm.Q[i * PK + col];
+            aq = mfma4(sm.P[row * PC + i], bK, aq);
+            ak = mfma4(sm.P[i * PC + row], bQ, ak);
+            ak = mfma4(cc.X1[row * PC + i], bK, ak);
+            ak = mfma4(cc.X1[i * PC + row], bK, ak);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            if (r < len) {
+                const long o = ((bos + r) * H + h) * DK + col;
+                store_elem<TO>(static_cast<TO*>(bp.dq) + o, aq[m]);
+                store_elem<TO>(static_cast<TO*>(bp.dk) + o, ak[m]);
+            }
+        }
+    }
+    // -- dg = reverse cumulative sum of dgamma; dbeta
+    if (wave == 0) {
+        const int r = 63 - lane;
+        float dgam = sm.rowg[r] + ((sm.colg[0][r] + sm.colg[1][r]) + (sm.colg[2][r] + sm.colg[3][r]));
+        if (r == 63) dgam += (sm.tailw[0] + sm.tailw[1]) + (sm.tailw[2] + sm.tailw[3]);
+        const float x = wave_inclusive_sum(dgam);
+        if (r < len) {
+            bp.dg[(bos + r) * H + h] = x;
+            bp.dbeta[(bos + r) * H + h] =
+                sm.rowb[r] + ((sm.colb[0][r] + sm.colb[1][r]) + (sm.colb[2][r] + sm.colb[3][r]));
+        }
+    }
+}
+
+// -------------------------------------------------------------------- launchers
+BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    BwdLayout w{};
+    w.fwd = workspace_layout(B, T, H, dk, N, varlen, 4);
+    const size_t units = (size_t)w.fwd.nc_bound * H;
+    w.off_t = al(w.fwd.total);
+    w.off_states = al(w.off_t + units * 4096 * 4);
+    w.off_dstates = al(w.off_states + units * dv * dk * 4);
+    size_t end = w.off_dstates + units * dv * dk * 4;
+    const size_t tok = (size_t)B * T * H;
+    if (bf16) {
+        w.off_q32 = al(end);
+        w.off_k32 = al(w.off_q32 + tok * dk * 4);
+        w.off_v32 = al(w.off_k32 + tok * dk * 4);
+        w.off_do32 = al(w.off_v32 + tok * dv * 4);
+        end = w.off_do32 + tok * dv * 4;
+    }
+    w.total = end;
+    return w;
+}
+
+template <typename TO, int DK, int DV>
+static void bwd_launch(const BwdProblem& b, hipStream_t s) {
+    const ChunkProblem& p = b.f;
+    constexpr int DVT = 32;
+    const long pairs = (long)p.N * p.H;
+    if (pairs > 0)
+        hipLaunchKernelGGL((chunk_bwd_state_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                           dim3(DVT / 16 * 64), 0, s, p, b.do32, b.dhT, b.dstates, b.dh0);
+    const long units = p.nc_bound * p.H;
+    if (units > 0)
+        hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+}
+
+template <typename TO>
+static void bwd_dispatch(const BwdProblem& b, hipStream_t s) {
+    const int dk = b.f.dk, dv = b.f.dv;
+    if (dk == 64) {
+        if (dv == 64) bwd_launch<TO, 64, 64>(b, s); else bwd_launch<TO, 64, 128>(b, s);
+    } else {
+        if (dv == 64) bwd_launch<TO, 128, 64>(b, s); else bwd_launch<TO, 128, 128>(b, s);
+    }
+}
+
+hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
+    const ChunkProblem& p = b.f;
+    const long tok = (long)p.B * p.T * p.H;
+    if (b.q32) {   // bf16 inputs: widen q, k, v, dO
+        const void* src[4] = {b.q_in, b.k_in, b.v_in, b.do_in};
+        float* dst[4] = {b.q32, b.k32, b.v32, b.do32w};
+        const long n8[4] = {tok * p.dk / 8, tok * p.dk / 8, tok * p.dv / 8, tok * p.dv / 8};
+        for (int i = 0; i < 4; ++i) {
+            if (n8[i] == 0) continue;
+            const long blocks = min(n8[i] / 256 + 1, 4096L);
+            hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                               static_cast<const uint16_t*>(src[i]), dst[i], n8[i]);
+        }
+    }
+    hipError_t e = launch_chunk_prepare(p, s);
+    if (e != hipSuccess) return e;
+    e = launch_chunk_propagate(p, s);
+    if (e != hipSuccess) return e;
+    if (b.grad_bf16) bwd_dispatch<uint16_t>(b, s); else bwd_dispatch<float>(b, s);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -57,45 +57,6 @@ __global__ __launch_bounds__(1024) void chunk_base_kernel(const int32_t* __restr
     if (tid == 1023) base[N] = part[1023];
 }
 
-// Token range of sequence n, clamped to [0, T] (see chunk_base_kernel).
-__device__ __forceinline__ void seq_range(const ChunkProblem& p, int n, long& bos, long& eos) {
-    if (p.cu_seqlens == nullptr) {
-        bos = (long)n * p.T;
-        eos = bos + p.T;
-    } else {
-        const int b0 = min(max(p.cu_seqlens[n], 0), p.T);
-        const int b1 = min(max(p.cu_seqlens[n + 1], b0), p.T);
-        bos = b0;
-        eos = b1;
-    }
-}
-
-// Global chunk index c -> first token and length; false if c is past the last chunk.
-__device__ __forceinline__ bool locate_chunk(const ChunkProblem& p, long c, long& bos, int& len) {
-    int n;
-    long j;
-    if (p.cu_seqlens == nullptr) {
-        n = (int)(c / p.nc_per_seq);
-        j = c % p.nc_per_seq;
-    } else {
-        const long total = min((long)p.chunk_base[p.N], p.nc_bound);
-        if (c >= total) return false;
-        int lo = 0, hi = p.N;  // largest n with base[n] <= c
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.chunk_base[mid] <= c) lo = mid; else hi = mid;
-        }
-        n = lo;
-        j = c - p.chunk_base[n];
-    }
-    long sb, se;
-    seq_range(p, n, sb, se);
-    bos = sb + j * kChunk;
-    const long l = se - bos;
-    len = (int)(l < kChunk ? l : kChunk);
-    return len > 0;
-}
-
 // ------------------------------------------------------- LDS images (bf16 inputs)
 // For bf16 inputs stage 1 stores the fp16 operands of stage 2 (K, diag(e^gamma) Q: W = d_k
 // columns; Mmat, P: W = 64) as byte images of the LDS tiles stage 2 reads, so that stage 2
@@ -126,22 +87,6 @@ __device__ __forceinline__ void img_piece(int i, int& r, int& c0) {
 }
 
 // ------------------------------------------------------------------- stage 1
-// Inclusive prefix sum over the 64 lanes of a wave: shifts within each 16-lane row, then the
-// row totals broadcast forward (DPP row_shr and row_bcast).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_add_src(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float wave_inclusive_sum(float x) {
-    x = dpp_add_src<0x111, 0xF>(x);  // row_shr:1
-    x = dpp_add_src<0x112, 0xF>(x);  // row_shr:2
-    x = dpp_add_src<0x114, 0xF>(x);  // row_shr:4
-    x = dpp_add_src<0x118, 0xF>(x);  // row_shr:8
-    x = dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
-
 template <typename TIn, int DK>
 struct alignas(16) PrepSmem {
     using TM = typename Operand<TIn>::type;
@@ -380,15 +325,17 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             // -- Mmat = T diag(beta) and P to the workspace: fp32 row-major, fp16 as images
             if constexpr (sizeof(TM) == 4) {
                 const int r = tid >> 2, c0 = (tid & 3) * 16;
-                float mv[16], pv[16];
+                float mv[16], pv[16], tv[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int ci = c0 + e;
-                    mv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] * sm.beta[ci] : 0.f;
+                    tv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
+                    mv[e] = tv[e] * sm.beta[ci];
                     pv[e] = to_f32(sm.P[r * PC + ci]);
                 }
                 store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+                if (p.tmat) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
             } else {
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
@@ -642,12 +589,18 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkPro
         __syncthreads();  // every wave is done with the previous chunk's LDS data
         stage.store(sm, tid);
         __syncthreads();
-        if (jc > 0) store_out();
+        if (jc > 0 && p.o) store_out();
         // the next chunk's loads are issued a quarter at a time between the token tiles below
         const bool more = jc + 1 < nchunks;
         const long nbos = sbos + (jc + 1) * kChunk, nwidx = (cbase + jc + 1) * H + h;
         const int nlen = more ? chunk_len(jc + 1) : 1;
 
+        if (p.states) {  // the state entering this chunk, for the backward pass
+            float* sp = p.states + (((cbase + jc) * H + h) * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+            for (int j = 0; j < NKB; ++j)
+                *reinterpret_cast<float4*>(sp + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+        }
         // X = K S^T and Y = Q S^T: [64 tokens x 16 columns] as 4 token tiles
         Frag<TM> BS[NKS];
 #pragma unroll
@@ -720,7 +673,7 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkPro
             ST[j] = acc;
         }
     }
-    if (nchunks > 0) store_out();
+    if (nchunks > 0 && p.o) store_out();
 
     if (p.hT) {
 #pragma unroll

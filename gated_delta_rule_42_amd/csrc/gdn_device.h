@@ -380,4 +380,21 @@ __device__ __forceinline__ void dma16g(const char* base, unsigned off, const voi
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off), to_lds(lds_block), 16, 0, 0);
 }
 
+// ------------------------------------------------------------------ wave scan
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each 16-lane row, then the
+// row totals broadcast forward (DPP row_shr and row_bcast).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_src(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x = dpp_add_src<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_add_src<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_add_src<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_add_src<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_add_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 }  // namespace gdn

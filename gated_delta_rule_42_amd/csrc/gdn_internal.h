@@ -30,7 +30,49 @@ struct ChunkProblem {
     void* pmat;                  // [nc_bound, H, 64, 64] operand type
     _Float16* k16;               // [nc_bound, H, 64, dk] fp16 K (bf16 inputs only)
     _Float16* q16;               // [nc_bound, H, 64, dk] fp16 diag(e^gamma) Q (bf16 inputs only)
+    // optional outputs of the fp32 kernels, used by the backward pass (NULL: not written)
+    float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
+    float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
 };
+
+// Token range of sequence n, clamped to [0, T] (see chunk_base_kernel).
+__device__ __forceinline__ void seq_range(const ChunkProblem& p, int n, long& bos, long& eos) {
+    if (p.cu_seqlens == nullptr) {
+        bos = (long)n * p.T;
+        eos = bos + p.T;
+    } else {
+        const int b0 = min(max(p.cu_seqlens[n], 0), p.T);
+        const int b1 = min(max(p.cu_seqlens[n + 1], b0), p.T);
+        bos = b0;
+        eos = b1;
+    }
+}
+
+// Global chunk index c -> first token and length; false if c is past the last chunk.
+__device__ __forceinline__ bool locate_chunk(const ChunkProblem& p, long c, long& bos, int& len) {
+    int n;
+    long j;
+    if (p.cu_seqlens == nullptr) {
+        n = (int)(c / p.nc_per_seq);
+        j = c % p.nc_per_seq;
+    } else {
+        const long total = min((long)p.chunk_base[p.N], p.nc_bound);
+        if (c >= total) return false;
+        int lo = 0, hi = p.N;  // largest n with base[n] <= c
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.chunk_base[mid] <= c) lo = mid; else hi = mid;
+        }
+        n = lo;
+        j = c - p.chunk_base[n];
+    }
+    long sb, se;
+    seq_range(p, n, sb, se);
+    bos = sb + j * 64;
+    const long l = se - bos;
+    len = (int)(l < 64 ? l : 64);
+    return len > 0;
+}
 
 struct WorkspaceLayout {
     size_t off_base, off_gates, off_m, off_p, off_k16, off_q16, total;
@@ -41,6 +83,39 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
 
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
+
+// Backward pass. `f` describes the forward problem over fp32 q, k, v (the caller's, or
+// widened copies in the workspace) with its stage-1 workspace and the tmat and states
+// regions set; the rest are the backward's own inputs, outputs and regions.
+struct BwdProblem {
+    ChunkProblem f;
+    const void* q_in;            // caller's q, k, v, dO in the caller's dtype
+    const void* k_in;
+    const void* v_in;
+    const void* do_in;
+    const float* do32;           // fp32 dO (the caller's, or the widened copy)
+    float* q32;                  // widening targets (bf16 inputs only, else NULL)
+    float* k32;
+    float* v32;
+    float* do32w;
+    const float* dhT;            // NULL: zero
+    void* dq;                    // [B,T,H,dk] caller's dtype
+    void* dk;
+    void* dv;                    // [B,T,H,dv] caller's dtype
+    float* dg;                   // [B,T,H]
+    float* dbeta;                // [B,T,H]
+    float* dh0;                  // [N,H,dv,dk] or NULL
+    float* dstates;              // [nc_bound, H, dv, dk] gradient leaving each chunk
+    int grad_bf16;               // 1: dq, dk, dv are bf16; 0: fp32
+};
+
+struct BwdLayout {
+    WorkspaceLayout fwd;         // stage-1 regions (fp32 operands)
+    size_t off_t, off_states, off_dstates, off_q32, off_k32, off_v32, off_do32, total;
+};
+
+BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16);
+hipError_t launch_chunk_backward(const BwdProblem& p, hipStream_t s);
 
 struct DecodeProblem {
     const void* q;

@@ -159,3 +159,14 @@ def make_decode_inputs(w: Workload | int = 4, seed: int | None = None, *, N: int
     out["state"] = torch.from_numpy(state.astype(np.float32))
     out["meta"] = dict(workload=w.name, N=N, H=H, dk=w.dk, dv=w.dv, steps=steps, dtype=dtype, seed=seed)
     return out
+
+
+def make_cotangents(x: dict, seed: int, *, dhT: bool = True) -> dict:
+    """Gradients of a synthetic loss with respect to the forward outputs of input set x:
+    dO [B,T,H,dv] ~ N(0,1) in the input dtype, dhT [N,H,dv,dk] ~ N(0,1) fp32 (or None)."""
+    m = x["meta"]
+    rng = np.random.default_rng(seed)
+    do = _cast(rng.standard_normal((m["B"], m["T"], m["H"], m["dv"]), dtype=np.float32), m["dtype"])
+    dh = (torch.from_numpy(rng.standard_normal((m["N"], m["H"], m["dv"], m["dk"]), dtype=np.float32))
+          if dhT else None)
+    return dict(do=do, dhT=dh)

@@ -156,6 +156,53 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
                         size_t workspace_bytes, void *stream);
 
 /*
+ * Workspace size in bytes needed by gdn_chunk_bwd (arguments as in
+ * gdn_chunk_fwd_workspace_bytes; 0 for arguments gdn_chunk_bwd would reject or when no
+ * chunk exists). Contents, 256-byte aligned regions in this order (nc as above):
+ *   the regions of gdn_chunk_fwd_workspace_bytes for fp32 operators (chunk_base, gates,
+ *   Mmat, P), then
+ *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major
+ *   states   fp32 [nc, H, dv, dk]  the state entering each chunk
+ *   dstates  fp32 [nc, H, dv, dk]  the gradient reaching the state after each chunk
+ *   q, k, v, dO widened to fp32 ([B, T, H, d] each; bf16 inputs only).
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
+                                     int chunk, int dtype);
+
+/*
+ * Backward pass of gdn_chunk_fwd: given the gradients of a scalar loss with respect to
+ * the outputs (d_o) and the final states (dhT), writes its gradients with respect to
+ * q, k, v, g_log_alpha, beta and h0. The pages train the layer with the chunkwise
+ * algorithm (paper note, mechanism paragraph: "parallel training algorithm") but print
+ * no gradient formulas; these are the adjoint of the chunk equations of gdn_chunk_propagate,
+ * computed chunk by chunk: stage 1 and 2 of the forward pass again (keeping T and the state
+ * entering every chunk), a reverse walk over the chunks of each sequence carrying the
+ * state gradient, then every (chunk, head) independently. All arithmetic is fp32 (bf16
+ * inputs are widened exactly); bf16 gradients are the fp32 results rounded to nearest even.
+ *
+ *   q, k, v, g_log_alpha, beta, h0, cu_seqlens, chunk, B, T, H, dk, dv, N, dtype:
+ *               the forward pass's arguments, as in gdn_chunk_fwd
+ *   d_o         [B, T, H, dv] dtype, gradient with respect to o        (required)
+ *   dhT         [N, H, dv, dk] fp32, gradient with respect to hT, or NULL for zeros
+ *   dq, dk_out  [B, T, H, dk] grad_dtype, written                       (required)
+ *   dv_out      [B, T, H, dv] grad_dtype, written                       (required)
+ *   dg, dbeta   [B, T, H] fp32, written                                 (required)
+ *   dh0         [N, H, dv, dk] fp32, written, or NULL (not written). Defined also when
+ *               h0 is NULL (the gradient with respect to a zero initial state).
+ *   grad_dtype  gdn_dtype of dq, dk_out, dv_out (GDN_F32, or GDN_BF16 when dtype is GDN_BF16)
+ *   workspace   device scratch of at least gdn_chunk_bwd_workspace_bytes(...) bytes
+ *   stream      hipStream_t to enqueue on
+ * Outputs must not overlap inputs. Returns GDN_OK or a negative gdn_status; nothing is
+ * launched on error.
+ */
+int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                  const float *beta, const float *h0, const void *d_o, const float *dhT,
+                  void *dq, void *dk_out, void *dv_out, float *dg, float *dbeta, float *dh0,
+                  const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                  int N, int dtype, int grad_dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
  * One recurrent decode step: one new token for each of N sequences and H heads,
  * applied to the states in place, with the readout of the updated state
  * (the recurrence above for a single t; the state is the whole memory, so decode

@@ -1,0 +1,112 @@
+"""GPU parity of the backward pass (gdn_chunk_bwd, through the C ABI) against the CPU fp64
+gradient oracle (oracle/backward.py: the adjoint of the token recurrence, pinned by finite
+differences).
+
+Tolerances, per gradient tensor, as for the forward pass:
+  * fp32 q/k/v:  max|x - ref| / max|ref|        <= 1e-4
+  * bf16 q/k/v:  max|x - ref| <= 2e-2 * RMS(ref)
+The oracle reads exactly the values the GPU receives (bf16 inputs and dO widened exactly).
+Gradients of bf16 inputs are compared in fp32 (grad_dtype=fp32); the bf16 gradients are
+checked bit for bit against those fp32 results rounded to nearest even.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_42_amd import binding as gb
+from gated_delta_rule_42_amd import synthetic as SY
+from oracle import backward as BW
+from test_parity import err, to_np, tol
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def gpu_bwd(x, cot, grad_dtype=torch.float32):
+    dev = "cuda"
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    g, b = x["g"].to(dev), x["beta"].to(dev)
+    h0 = None if x["h0"] is None else x["h0"].to(dev)
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(dev)
+    do = cot["do"].to(dev)
+    dhT = None if cot["dhT"] is None else cot["dhT"].to(dev)
+    out = gb.gdn_chunk_bwd(q, k, v, g, b, do, h0, dhT, cu, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_bwd(x, cot, heads=None):
+    sl = (lambda t: t) if heads is None else (lambda t: None if t is None else t[:, :, heads].contiguous())
+    slN = (lambda t: t) if heads is None else (lambda t: None if t is None else t[:, heads].contiguous())
+    return BW.backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), sl(cot["do"]),
+                       h0=slN(x["h0"]), dhT=slN(cot["dhT"]), cu_seqlens=x["cu_seqlens"])
+
+
+def check_bwd(x, cot, heads=None):
+    dt = x["meta"]["dtype"]
+    print(f"[gpu] chunk_bwd {x['meta']} dhT={cot['dhT'] is not None}", flush=True)
+    got = [to_np(t) for t in gpu_bwd(x, cot)]
+    ref = oracle_bwd(x, cot, heads)
+    errs = {}
+    for name, a, r in zip(NAMES, got, ref):
+        if heads is not None:
+            a = a[:, heads] if name == "dh0" else a[:, :, heads]
+        errs[name] = err(a, r, dt)
+    print("      " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" tol={tol(dt):.0e}", flush=True)
+    assert all(e <= tol(dt) for e in errs.values()), errs
+    return errs
+
+
+BW_SMALL = [
+    # B, T, H, dk, dv, dtype, h0, dhT, gate_scale
+    (1, 200, 2, 64, 64, "f32", True, True, 1.0),
+    (2, 130, 2, 128, 128, "f32", True, True, 0.01),
+    (1, 100, 2, 64, 128, "f32", False, False, 1.0),
+    (1, 190, 2, 128, 64, "f32", True, True, 0.05),
+    (2, 150, 2, 128, 128, "bf16", True, True, 1.0),
+    (1, 257, 2, 128, 128, "bf16", True, True, 0.01),
+    (1, 64, 3, 64, 64, "bf16", False, True, 1.0),
+    (1, 1, 2, 128, 128, "bf16", True, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,h0,dhT,gs", BW_SMALL)
+def test_bwd_small(B, T, H, dk, dv, dtype, h0, dhT, gs):
+    w = SY.Workload(99, f"small_{dtype}", H=H, dk=dk, dv=dv, dtype=dtype, B=B, T=T)
+    x = SY.make_forward_inputs(w, seed=2000 + T + dk + dv, gate_scale=gs, h0=h0)
+    check_bwd(x, SY.make_cotangents(x, 3000 + T, dhT=dhT))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_varlen(dtype):
+    """Packed sequences, one of them empty (its dh0 is dhT) and one a single token."""
+    w = SY.Workload(99, "varlen_small", H=2, dk=128, dv=128, dtype=dtype, varlen=5)
+    x = SY.make_forward_inputs(w, seed=41, lengths=[70, 0, 1, 64, 129], h0=True, gate_scale=0.05)
+    check_bwd(x, SY.make_cotangents(x, 42))
+
+
+def test_bwd_beta_to_2():
+    w = SY.Workload(99, "beta2", H=2, dk=128, dv=128, dtype="bf16", B=1, T=200)
+    x = SY.make_forward_inputs(w, seed=43, gate_scale=0.01, h0=True, beta_scale=2.0)
+    check_bwd(x, SY.make_cotangents(x, 44))
+
+
+def test_bwd_bf16_grads_are_rounded_fp32():
+    w = SY.Workload(99, "round", H=2, dk=64, dv=128, dtype="bf16", B=1, T=150)
+    x = SY.make_forward_inputs(w, seed=45, h0=True)
+    cot = SY.make_cotangents(x, 46)
+    g32 = gpu_bwd(x, cot, torch.float32)
+    g16 = gpu_bwd(x, cot, torch.bfloat16)
+    for a, b in zip(g32[:3], g16[:3]):
+        assert b.dtype == torch.bfloat16 and torch.equal(a.to(torch.bfloat16), b)
+    for a, b in zip(g32[3:], g16[3:]):
+        assert torch.equal(a, b)
+
+
+def test_bwd_train_workload_sampled_heads():
+    """The training-shape workload (B4 H16 T2048 d128, bf16) in full on the GPU; the oracle
+    computes two of the sixteen heads, which it can do on their own."""
+    x = SY.make_forward_inputs(1)
+    cot = SY.make_cotangents(x, 101)
+    check_bwd(x, cot, heads=[0, 11])
