@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 METRIC = "GDN chunk-fwd tokens/s + %MFMA peak (B4 H16 T2048 d128); decode %HBM BW"
 PEAK_BF16_FLOPS = 2516.6e12   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (MI355X, ~2.5 PF)
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+PEAK_FP32_MFMA = 157.3e12     # dense fp32 matrix (MI355X)
 CHUNK = 64
 
 
@@ -41,6 +42,17 @@ def fwd_counts(dk, dv, C=CHUNK, elem=2):
     stage2_flops = 6 * dk * dv + 4 * C * dv            # K S^T, Q S^T, Delta^T K, Mmat R, P Delta
     return dict(flops=flops, bytes=stage1_bytes + stage2_bytes, stage1_bytes=stage1_bytes,
                 stage2_bytes=stage2_bytes, stage1_flops=stage1_flops, stage2_flops=stage2_flops)
+
+
+def bwd_counts(dk, dv, C=CHUNK):
+    """FLOP per token-head of the two backward kernels of this implementation (fp32 matrix
+    core): the reverse walk (K dS'^T, P^T dO, Mmat^T dDelta, the two rank-C state-gradient
+    updates) and the per-chunk gradients (K S^T, Q S^T, K dS'^T, Mmat R, P^T dO, Mmat^T dDelta,
+    dO Delta^T, dDelta R^T, E dO S, E dR S, Ed Delta dS', dT T^T, T^T X, K K^T, dPg K,
+    dPg^T Q, dG K, dG^T K)."""
+    state = 2 * (3 * dk * dv + 2 * C * dv)
+    grad = 2 * (6 * dk * dv + 5 * C * dv + 2 * C * C + 5 * C * dk)
+    return dict(state_flops=state, grad_flops=grad)
 
 
 def decode_bytes(dk, dv, elem=2, o_elem=4):
@@ -73,7 +85,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["all", "fwd", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "bwd"], default="all")
+    ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run plain device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -126,6 +139,40 @@ def bench_forward(args, torch, gb, SY):
     prep_ms = [e[0].elapsed_time(e[1]) for e in evs]
     prop_ms = [e[1].elapsed_time(e[2]) for e in evs]
     return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=t1 - t0, prep_ms=prep_ms, prop_ms=prop_ms)
+
+
+def bench_backward(args, torch, gb, SY):
+    """gdn_chunk_bwd on the training-shape workload (bf16 q/k/v/dO and gradients, no initial
+    or final state), two rotating input sets."""
+    w = SY.WORKLOADS[1]
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        x = SY.make_forward_inputs(1, seed=1 + 100 * s)
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+        t["do"] = SY.make_cotangents(x, 7 + s, dhT=False)["do"].to(dev)
+        sets.append(t)
+    need = gb.gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, B, False)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step(t):
+        return gb.gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["do"], need_dh0=False,
+                                workspace=ws)
+
+    for i in range(2):
+        step(sets[i % 2])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.bwd_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.bwd_steps):
+        evs[i][0].record()
+        step(sets[i % 2])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=t1 - t0,
+                step_ms=[e[0].elapsed_time(e[1]) for e in evs])
 
 
 def bench_decode(args, torch, gb, SY):
@@ -263,7 +310,23 @@ def main():
                                "unit": "GB/s", "frac": per / (mean / 1e3) / PEAK_HBM_BPS,
                                "traffic": measured_traffic("decode_kernel"),
                                "algorithmic_bytes_per_launch": per}
-    if args.cpu_seconds > 0 and args.only != "decode":
+    if args.only in ("all", "bwd"):
+        b = bench_backward(args, torch, gb, SY)
+        th = b["B"] * b["T"] * b["H"]
+        ms = b["wall_s"] / args.bwd_steps * 1e3
+        c = bwd_counts(b["dk"], b["dv"])
+        out["bwd"] = {"workload": "chunkwise backward B4 H16 T2048 d_k=d_v=128 chunk 64, bf16 "
+                                  "q/k/v/dO and gradients, fp32 arithmetic, no h0 / dhT",
+                      "ms_per_step": ms, "ms_per_step_median": median(b["step_ms"]),
+                      "tokens_per_s": b["B"] * b["T"] / (ms / 1e3),
+                      "fp32_mfma_tflops_issued": (c["state_flops"] + c["grad_flops"]) * th / (ms / 1e3) / 1e12,
+                      "grad_kernel_flops_per_launch": c["grad_flops"] * th,
+                      "state_kernel_flops_per_launch": c["state_flops"] * th,
+                      "fp32_mfma_peak_tflops": PEAK_FP32_MFMA / 1e12}
+        if args.only == "bwd":
+            out["value"] = b["B"] * b["T"] / (ms / 1e3)
+            out["ms_per_step"] = ms
+    if args.cpu_seconds > 0 and args.only not in ("decode", "bwd"):
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
