@@ -30,6 +30,9 @@ _SIGNATURES = [
     ("gdn_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
     ("gdn_chunk_bwd_workspace_bytes", _SZ, [_I] * 9),
     ("gdn_chunk_bwd", _I, [_P] * 15 + [_I] * 9 + [_P, _SZ, _P]),
+    ("gdn_kda_chunk_fwd_workspace_bytes", _SZ, [_I] * 9),
+    ("gdn_kda_chunk_fwd", _I, [_P] * 9 + [_I] * 9 + [_P, _SZ, _P]),
+    ("gdn_kda_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
 ]
 
 _lib = None
@@ -204,3 +207,45 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, h0=None, dhT=None, cu_seqlens=None, chun
                              _stream(dev, stream))
     _check(st, "gdn_chunk_bwd")
     return dq, dk_, dv_, dg, db, dh0
+
+
+def gdn_kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, varlen, chunk=CHUNK, dtype=torch.bfloat16) -> int:
+    return lib().gdn_kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, int(bool(varlen)), chunk,
+                                                   _DTYPE[dtype])
+
+
+def gdn_kda_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None, hT=None,
+                      o_dtype=None, output_final_state=True, workspace=None, stream=None):
+    """Chunkwise forward pass with a channel-wise decay: as gdn_chunk_fwd, with g
+    [B,T,H,dk] fp32 (log of one decay per key channel)."""
+    _need_gpu(q, k, v, g, beta, h0, cu_seqlens, o, hT, workspace)
+    B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = gdn_kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, cu_seqlens is not None, chunk, q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().gdn_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                 _ptr(hT), _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
+                                 _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1), _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0,
+                                 _stream(q.device, stream))
+    _check(st, "gdn_kda_chunk_fwd")
+    return o, hT
+
+
+def gdn_kda_decode_step(q, k, v, g, beta, state, o=None, *, o_dtype=torch.float32, stream=None):
+    """One decode step with a channel-wise decay: g [N,H,dk] fp32; otherwise as
+    gdn_decode_step (state updated in place)."""
+    _need_gpu(q, k, v, g, beta, state, o)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype, device=q.device)
+    st = lib().gdn_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                                   N, H, dk, dv, _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1),
+                                   _stream(q.device, stream))
+    _check(st, "gdn_kda_decode_step")
+    return o

@@ -228,3 +228,81 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     return gdn::launch_chunk_backward(b, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                        : GDN_ERR_HIP;
 }
+
+GDN_EXPORT size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                    int varlen, int chunk, int dtype) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
+    if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
+    if (B < 1 || H < 1 || T < 0) return 0;
+    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    return gdn::kda_workspace_layout(B, T, H, dk, N, varlen != 0).total;
+}
+
+GDN_EXPORT int gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                                 const float* beta, const float* h0, void* o, float* hT,
+                                 const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
+                                 int dv, int N, int dtype, int o_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
+    if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
+    } else if (N != B) {
+        return GDN_ERR_SHAPE;
+    }
+    const long long tokens = (long long)B * T;
+    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
+        return GDN_ERR_SHAPE;
+    if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !beta || !o)) return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, o, h0, hT, g_log_alpha};
+    for (const void* x : al16)
+        if (x && !aligned(x, 16)) return GDN_ERR_ALIGN;
+    const void* al4[] = {beta, cu_seqlens};
+    for (const void* x : al4)
+        if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
+    const gdn::KdaLayout w = gdn::kda_workspace_layout(B, T, H, dk, N, cu_seqlens != nullptr);
+    if (w.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
+    if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
+    char* base = static_cast<char*>(workspace);
+    gdn::ChunkProblem P{};
+    P.q = q; P.k = k; P.v = v; P.g = g_log_alpha; P.beta = beta; P.h0 = h0; P.o = o; P.hT = hT;
+    P.cu_seqlens = cu_seqlens;
+    P.B = B; P.T = T; P.H = H; P.dk = dk; P.dv = dv; P.N = N;
+    P.bf16 = dtype == GDN_BF16;
+    P.o_bf16 = o_dtype == GDN_BF16;
+    P.nc_bound = w.nc_bound;
+    P.nc_per_seq = (T + 63) / 64;
+    const bool any = w.nc_bound > 0;
+    P.chunk_base = cu_seqlens ? reinterpret_cast<int32_t*>(base + w.off_base) : nullptr;
+    P.mmat = any ? base + w.off_m : nullptr;
+    P.pmat = any ? base + w.off_p : nullptr;
+    P.khat = any ? reinterpret_cast<float*>(base + w.off_kh) : nullptr;
+    P.qhat = any ? reinterpret_cast<float*>(base + w.off_qh) : nullptr;
+    P.kdec = any ? reinterpret_cast<float*>(base + w.off_kd) : nullptr;
+    P.lam = any ? reinterpret_cast<float*>(base + w.off_lam) : nullptr;
+    return gdn::launch_kda_chunk_fwd(P, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                       : GDN_ERR_HIP;
+}
+
+GDN_EXPORT int gdn_kda_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                                   const float* beta, float* state, void* o, int N, int H, int dk,
+                                   int dv, int dtype, int o_dtype, void* stream) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || (long long)N * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    if (!q || !k || !v || !g_log_alpha || !beta || !state || !o) return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, o, state, g_log_alpha};
+    for (const void* x : al16)
+        if (!aligned(x, 16)) return GDN_ERR_ALIGN;
+    if (!aligned(beta, 4)) return GDN_ERR_ALIGN;
+    gdn::DecodeProblem p{q,  k, v,  g_log_alpha, beta,           state,
+                         o,  N, H,  dk,          dv,   dtype == GDN_BF16, o_dtype == GDN_BF16};
+    p.channel_gate = 1;
+    return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                : GDN_ERR_HIP;
+}

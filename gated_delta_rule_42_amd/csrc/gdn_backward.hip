@@ -36,12 +36,6 @@
 
 namespace gdn {
 
-// acc (16x16 fp32 tile) += A[16 x 4] B[4 x 16]: lane l gives A[l % 16][l / 16] and
-// B[l / 16][l % 16]; acc holds rows 4 (l / 16) + 0..3 of column l % 16.
-__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-}
-
 // ------------------------------------------------------------------ widening
 __global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src,
                                                          float* __restrict__ dst, long n8) {

@@ -21,6 +21,7 @@
 // writes O. Every gate factor is exp of a non-positive difference, masked before the exp.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_ut.h"
 
 namespace gdn {
 
@@ -263,64 +264,10 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
             }
             __syncthreads();
 
-            // -- T = (I + A)^{-1}. Diagonal 16x16 blocks: wave w inverts block w by forward
-            //    substitution, lane l16 computing column l16 with the block's strictly lower
-            //    entries held in registers.
+            // -- T = (I + A)^{-1}
             float* At = sm.u.tri.A;
             float* Tt = sm.u.tri.T;
-            {
-                const float* Ab = At + 16 * wave * PF + 16 * wave;
-                float a[16][16];
-#pragma unroll
-                for (int r = 1; r < 16; ++r)
-#pragma unroll
-                    for (int i = 0; i < r; ++i) a[r][i] = Ab[r * PF + i];
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc0 = (r == l16) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-                    for (int i = 0; i < r; i += 2) {
-                        acc0 -= a[r][i] * x[i];
-                        if (i + 1 < r) acc1 -= a[r][i + 1] * x[i + 1];
-                    }
-                    x[r] = acc0 + acc1;
-                }
-                if (lq == 0) {
-                    float* Tb = Tt + 16 * wave * PF + 16 * wave;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) Tb[r * PF + l16] = x[r];
-                }
-            }
-            __syncthreads();
-            // ... then the blocks below the diagonal, one sub-diagonal at a time:
-            //    T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA, 16x16x4)
-#pragma unroll
-            for (int d = 1; d < 4; ++d) {
-                if (wave < 4 - d) {
-                    const int ib = d + wave, jb = ib - d;
-                    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                    for (int m = jb; m < ib; ++m) {
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const float av = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
-                            const float bv = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
-                            z = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, z, 0, 0, 0);
-                        }
-                    }
-                    // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it
-                    // as the right operand with k relabelled to 4*lq + s in step s.
-                    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float av = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
-                        t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, z[s], t, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
-                }
-                __syncthreads();
-            }
+            ut_inverse64<PF>(At, Tt, wave, lane);
 
             // -- Mmat = T diag(beta) and P to the workspace: fp32 row-major, fp16 as images
             if constexpr (sizeof(TM) == 4) {
@@ -1069,10 +1016,14 @@ static void prep_launch(const ChunkProblem& p, hipStream_t s) {
     hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
 }
 
-hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
+void launch_chunk_base(const ChunkProblem& p, hipStream_t s) {
     if (p.cu_seqlens)
         hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.N, p.T,
                            p.chunk_base);
+}
+
+hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
+    launch_chunk_base(p, s);
     if (p.nc_bound > 0) {
         if (p.bf16) {
             if (p.dk == 64) prep_launch<uint16_t, 64>(p, s); else prep_launch<uint16_t, 128>(p, s);

@@ -8,6 +8,11 @@
 //   a_i = s_i . k,  b_i = s_i . q,  c_i = beta (v_i - alpha a_i),
 //   s_i <- alpha s_i + c_i k,        o_i = alpha b_i + c_i (k . q)
 // so every row is read once and written once: the step streams the state through HBM.
+//
+// With a channel-wise decay (one alpha per key channel, g [N, H, d_k]; record "LIT-137",
+// "Standing in the anthology") the decay scales the state's columns instead:
+//   s~_i = s_i * alpha,  a_i = s~_i . k,  b_i = s~_i . q,  c_i = beta (v_i - a_i),
+//   s_i <- s~_i + c_i k,  o_i = b_i + c_i (k . q).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -38,7 +43,7 @@ __device__ __forceinline__ void load_vec(const TS* p, float (&x)[EPL]) {
 // One work-group per (sequence, head). Its 256 lanes form 16 groups of 16; group g owns
 // rows g, g+16, ...; within a group, lane l16 owns columns [l16*EPL, l16*EPL + EPL) so that
 // one group reads a whole row contiguously.
-template <typename TS, typename TO, int DK, int DV>
+template <typename TS, typename TO, int DK, int DV, bool CW>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     constexpr int EPL = DK / 16;   // state columns per lane
     constexpr int RPG = DV / 16;   // rows per lane group
@@ -52,8 +57,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) kq += kf[e] * qf[e];
     kq = row16_sum(kq);
-    const float alpha = __expf(p.g[pr]);
+    const float alpha = CW ? 1.f : __expf(p.g[pr]);
     const float beta = p.beta[pr];
+    float af[EPL];   // channel-wise decay of this lane's columns
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) af[e] = CW ? __expf(p.g[pr * DK + l16 * EPL + e]) : 1.f;
 
     float* st = p.state + pr * (long)DV * DK + l16 * EPL;
     const TS* vp = static_cast<const TS*>(p.v) + pr * DV;
@@ -68,6 +76,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
         for (int e = 0; e < EPL; e += 4) {
             const float4 x = *reinterpret_cast<const float4*>(st + (long)row * DK + e);
             s[it][e] = x.x; s[it][e + 1] = x.y; s[it][e + 2] = x.z; s[it][e + 3] = x.w;
+        }
+        if constexpr (CW) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s[it][e] *= af[e];
         }
         vr[it] = to_f32(vp[row]);
     }
@@ -98,8 +110,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
 
 template <typename TS, typename TO, int DK, int DV>
 static void decode_launch(const DecodeProblem& p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
-                       0, s, p);
+    if (p.channel_gate)
+        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
+                           0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, false>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
+                           0, s, p);
 }
 
 template <typename TS, typename TO>

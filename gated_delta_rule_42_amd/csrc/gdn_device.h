@@ -397,4 +397,10 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
+// acc (16x16 fp32 tile) += A[16 x 4] B[4 x 16] on the fp32 matrix core: lane l gives
+// A[l % 16][l / 16] and B[l / 16][l % 16]; acc holds rows 4 (l / 16) + 0..3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
 }  // namespace gdn

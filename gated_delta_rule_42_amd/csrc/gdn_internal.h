@@ -33,6 +33,11 @@ struct ChunkProblem {
     // optional outputs of the fp32 kernels, used by the backward pass (NULL: not written)
     float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
     float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
+    // channel-wise decay (g is [B,T,H,dk]): chunk operators of the fp32 kernels
+    float* khat;                 // [nc_bound, H, 64, dk] K * e^gamma
+    float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma
+    float* kdec;                 // [nc_bound, H, 64, dk] K * e^{gamma_last - gamma}
+    float* lam;                  // [nc_bound, H, dk] e^{gamma_last}
 };
 
 // Token range of sequence n, clamped to [0, T] (see chunk_base_kernel).
@@ -81,6 +86,7 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes);
 
+void launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
 
@@ -117,6 +123,14 @@ struct BwdLayout {
 BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16);
 hipError_t launch_chunk_backward(const BwdProblem& p, hipStream_t s);
 
+// Channel-wise decay: workspace layout and the two stages (chunk operators, propagation).
+struct KdaLayout {
+    size_t off_base, off_m, off_p, off_kh, off_qh, off_kd, off_lam, total;
+    long nc_bound;
+};
+KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen);
+hipError_t launch_kda_chunk_fwd(const ChunkProblem& p, hipStream_t s);
+
 struct DecodeProblem {
     const void* q;
     const void* k;
@@ -128,6 +142,7 @@ struct DecodeProblem {
     int N, H, dk, dv;
     int bf16;     // q, k, v are bf16 (else fp32)
     int o_bf16;   // o is bf16 (else fp32)
+    int channel_gate;   // g is [N, H, dk] (one decay per key channel), else [N, H]
 };
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);

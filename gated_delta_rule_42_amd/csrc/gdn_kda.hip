@@ -1,0 +1,347 @@
+// Chunkwise forward pass of the gated delta rule with a channel-wise decay (one decay per key
+// channel) for gfx950.
+//
+// The pages extend the gated delta rule "with a channel-wise forgetting gate" (record "LIT-137",
+// "Standing in the anthology"; practice "SOTA-135", "Sequence": it "replaces the scalar decay
+// with a channel-wise one") and give no formula. Reading: alpha_t becomes a vector in
+// (0,1]^{d_k} applied to the key channels (the columns of S [d_v, d_k]) where the scalar one
+// was, before the write:
+//     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t.
+// Chunk form (derived; the scalar case with the row scalings of K and Q replaced by
+// elementwise ones): with gamma_r the in-chunk cumulative log decay of every channel,
+// Kh = K * e^gamma, Qh = Q * e^gamma, Kd = K * e^{gamma_last - gamma}, lam = e^{gamma_last}:
+//     A     = strict_lower(diag(beta) [sum_c k_r k_i e^{gamma_r - gamma_i}])
+//     T     = (I + A)^{-1},   Mmat = T diag(beta)
+//     P     = lower_incl([sum_c q_r k_i e^{gamma_r - gamma_i}])
+//     Delta = Mmat (V - Kh S^T),   O = Qh S^T + P Delta,   S' = S Diag(lam) + Delta^T Kd.
+// Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head); stage 2
+// (kda_propagate_kernel) carries the state through the chunks. All arithmetic is fp32 (fp32
+// 16x16x4 matrix core); bf16 inputs are widened on load.
+//
+// A and P never form e^{-gamma} (it overflows under strong decay): blocks below the 16x16
+// diagonal use a reference at the first row of the row block, so both factors
+// e^{gamma_r - gamma_ref} and e^{gamma_ref - gamma_i} are <= 1; diagonal blocks are summed
+// over the channels with the exponent of each difference directly.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_ut.h"
+
+namespace gdn {
+
+// Four consecutive input elements as fp32.
+__device__ __forceinline__ float4 load4_in(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_in(const uint16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// ------------------------------------------------------------------- stage 1
+template <int DK>
+struct alignas(16) KdaPrepSmem {
+    static constexpr int PK = DK + 4, PF = 68;
+    float K[64 * PK];
+    float Q[64 * PK];
+    float G[64 * PK];   // g, then gamma (in-chunk inclusive cumulative sum, per channel)
+    float A[64 * PF];
+    float T[64 * PF];
+    float P[64 * PF];
+    float beta[64];
+};
+
+// One work-group (4 waves) per (chunk, head); wave w owns row block w of A and P.
+template <typename TIn, int DK>
+__global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
+    using SM = KdaPrepSmem<DK>;
+    constexpr int PK = SM::PK, PF = SM::PF;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long c = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    long bos;
+    int len;
+    if (!locate_chunk(p, c, bos, len)) return;   // uniform over the work-group
+    const long widx = c * H + h;
+    const TIn* kp = static_cast<const TIn*>(p.k);
+    const TIn* qp = static_cast<const TIn*>(p.q);
+
+    for (int i = tid; i < 64 * DK / 4; i += 256) {
+        const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
+        if (r < len) {
+            const long o = ((bos + r) * H + h) * DK + cc;
+            kv = load4_in(kp + o);
+            qv = load4_in(qp + o);
+            gv = *reinterpret_cast<const float4*>(p.g + o);
+        }
+        *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
+        *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+        *reinterpret_cast<float4*>(&sm.G[r * PK + cc]) = gv;
+    }
+    if (tid < 64) sm.beta[tid] = tid < len ? p.beta[(bos + tid) * H + h] : 0.f;
+    __syncthreads();
+    if (tid < DK) {   // gamma, one channel per thread (rows past the chunk's end add 0)
+        float run = 0.f;
+        for (int r = 0; r < 64; ++r) {
+            run += sm.G[r * PK + tid];
+            sm.G[r * PK + tid] = run;
+        }
+    }
+    __syncthreads();
+
+    // -- Kh, Qh, Kd and lam to the workspace
+    for (int i = tid; i < 64 * DK / 4; i += 256) {
+        const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+        const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
+        const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
+        const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
+        const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
+        const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
+        const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
+        const long o = (widx * 64 + r) * DK + cc;
+        *reinterpret_cast<float4*>(p.khat + o) = make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w);
+        *reinterpret_cast<float4*>(p.qhat + o) = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
+        *reinterpret_cast<float4*>(p.kdec + o) = make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w);
+    }
+    if (tid < DK) p.lam[widx * DK + tid] = __expf(sm.G[63 * PK + tid]);
+
+    // -- A and P, row block I = wave
+    const int I = wave;
+    for (int J = 0; J < I; ++J) {   // below the diagonal: reference gamma at row 16 I
+        f32x4_t ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const int ch = k0 + lq;
+            const float gref = sm.G[16 * I * PK + ch];
+            const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
+            const float er = __expf(gref - sm.G[(16 * J + l16) * PK + ch]);
+            const float b = sm.K[(16 * J + l16) * PK + ch] * er;
+            ak = mfma4(sm.K[(16 * I + l16) * PK + ch] * el, b, ak);
+            aq = mfma4(sm.Q[(16 * I + l16) * PK + ch] * el, b, aq);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
+            sm.A[r * PF + i] = sm.beta[r] * ak[m];
+            sm.P[r * PF + i] = aq[m];
+        }
+    }
+    // the diagonal block: exact sums over the channels
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r = 16 * I + 4 * lq + m, i = 16 * I + l16;
+        float sk = 0.f, sq = 0.f;
+        if (i <= r) {
+            for (int ch = 0; ch < DK; ++ch) {
+                const float e = __expf(fminf(sm.G[r * PK + ch] - sm.G[i * PK + ch], 0.f)) * sm.K[i * PK + ch];
+                sk += sm.K[r * PK + ch] * e;
+                sq += sm.Q[r * PK + ch] * e;
+            }
+        }
+        sm.A[r * PF + i] = i < r ? sm.beta[r] * sk : 0.f;
+        sm.P[r * PF + i] = sq;
+    }
+    __syncthreads();
+
+    ut_inverse64<PF>(sm.A, sm.T, wave, lane);
+
+    // -- Mmat = T diag(beta) and P (lower incl. diagonal), fp32 row-major
+    {
+        const int r = tid >> 2, c0 = (tid & 3) * 16;
+        float mv[16], pv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int ci = c0 + e;
+            mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * sm.beta[ci] : 0.f;
+            pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
+        }
+        store16<float>(static_cast<float*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+        store16<float>(static_cast<float*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+    }
+}
+
+// ------------------------------------------------------------------- stage 2
+template <int DK, int DVT>
+struct alignas(16) KdaPropSmem {
+    static constexpr int PK = DK + 4, PC = 68, PV = DVT + 4;
+    float Kh[64 * PK];
+    float Qh[64 * PK];
+    float Kd[64 * PK];
+    float M[64 * PC];
+    float P[64 * PC];
+    float V[64 * PV];
+    float lam[DK];
+};
+
+// One work-group per (sequence, head, DVT-column tile); wave w owns d_v columns dv0 + 16w ..
+// +15 and holds S^T [d_k, 16] as d_k/16 accumulator tiles (lane: S[col l16][16j + 4lq + 0..3]).
+template <typename TIn, typename TO, int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate_kernel(ChunkProblem p) {
+    using SM = KdaPropSmem<DK, DVT>;
+    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, NKB = DK / 16, NTILE = DV / DVT;
+    constexpr int NT = DVT / 16 * 64;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long pair = blockIdx.x / NTILE;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + 63) / 64;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+
+    f32x4_t ST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        if (p.h0) {
+            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
+            ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const TIn* vp = static_cast<const TIn*>(p.v);
+    const float* mp = static_cast<const float*>(p.mmat);
+    const float* pp = static_cast<const float*>(p.pmat);
+
+    for (long jc = 0; jc < nchunks; ++jc) {
+        const long bos = sbos + jc * 64, widx = (cbase + jc) * H + h;
+        const int len = (int)min(64L, seos - bos);
+        __syncthreads();  // the previous chunk's LDS data is dead
+        for (int i = tid; i < 64 * DK / 4; i += NT) {
+            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const long o = (widx * 64 + r) * DK + cc;
+            *reinterpret_cast<float4*>(&sm.Kh[r * PK + cc]) = *reinterpret_cast<const float4*>(p.khat + o);
+            *reinterpret_cast<float4*>(&sm.Qh[r * PK + cc]) = *reinterpret_cast<const float4*>(p.qhat + o);
+            *reinterpret_cast<float4*>(&sm.Kd[r * PK + cc]) = *reinterpret_cast<const float4*>(p.kdec + o);
+        }
+        for (int i = tid; i < 64 * 16; i += NT) {
+            const int r = i / 16, cc = 4 * (i % 16);
+            *reinterpret_cast<float4*>(&sm.M[r * PC + cc]) = *reinterpret_cast<const float4*>(mp + widx * 4096 + r * 64 + cc);
+            *reinterpret_cast<float4*>(&sm.P[r * PC + cc]) = *reinterpret_cast<const float4*>(pp + widx * 4096 + r * 64 + cc);
+        }
+        for (int i = tid; i < 64 * DVT / 4; i += NT) {
+            const int r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < len) x = load4_in(vp + ((bos + r) * H + h) * DV + dv0 + cc);
+            *reinterpret_cast<float4*>(&sm.V[r * PV + cc]) = x;
+        }
+        for (int i = tid; i < DK; i += NT) sm.lam[i] = p.lam[widx * DK + i];
+        __syncthreads();
+
+        // X = Kh S^T and Y = Qh S^T (k relabelled to the accumulator rows: step (j, s) takes
+        // d_k column 16j + 4lq + s)
+        f32x4_t X[4], Y[4], D[4], O[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            X[t] = Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKB; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int a = (16 * t + l16) * PK + 16 * j + 4 * lq + s;
+                    X[t] = mfma4(sm.Kh[a], ST[j][s], X[t]);
+                    Y[t] = mfma4(sm.Qh[a], ST[j][s], Y[t]);
+                }
+        }
+        // R = V - X (in place), Delta = Mmat R, O = Y + P Delta
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) X[t][m] = sm.V[(16 * t + 4 * lq + m) * PV + 16 * wave + l16] - X[t][m];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) D[t] = mfma4(sm.M[(16 * t + l16) * PC + 16 * t2 + 4 * lq + s], X[t2][s], D[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            O[t] = Y[t];
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) O[t] = mfma4(sm.P[(16 * t + l16) * PC + 16 * t2 + 4 * lq + s], D[t2][s], O[t]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * t + 4 * lq + m;
+                if (r < len) static_cast<TO*>(p.o)[((bos + r) * H + h) * DV + dvw + l16] = from_f32<TO>(O[t][m]);
+            }
+        }
+        // S^T <- Diag(lam) S^T + Kd^T Delta
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            f32x4_t acc;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = ST[j][m] * sm.lam[16 * j + 4 * lq + m];
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma4(sm.Kd[(16 * t2 + 4 * lq + s) * PK + 16 * j + l16], D[t2][s], acc);
+            ST[j] = acc;
+        }
+    }
+    if (p.hT) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    }
+}
+
+// -------------------------------------------------------------------- launchers
+KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    KdaLayout w{};
+    w.nc_bound = varlen ? ((long)T + (long)N * 63) / 64 : (long)B * (((long)T + 63) / 64);
+    const size_t units = (size_t)w.nc_bound * H;
+    w.off_base = 0;
+    w.off_m = al(varlen ? (size_t)(N + 1) * 4 : 0);
+    w.off_p = al(w.off_m + units * 4096 * 4);
+    w.off_kh = al(w.off_p + units * 4096 * 4);
+    w.off_qh = al(w.off_kh + units * 64 * dk * 4);
+    w.off_kd = al(w.off_qh + units * 64 * dk * 4);
+    w.off_lam = al(w.off_kd + units * 64 * dk * 4);
+    w.total = w.off_lam + units * dk * 4;
+    if (w.nc_bound == 0) w.total = al(varlen ? (size_t)(N + 1) * 4 : 0);
+    return w;
+}
+
+template <typename TIn, typename TO, int DK, int DV>
+static void kda_launch(const ChunkProblem& p, hipStream_t s) {
+    constexpr int DVT = 32;
+    const long units = p.nc_bound * p.H;
+    if (units > 0) hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK>), dim3((unsigned)units), dim3(256), 0, s, p);
+    const long pairs = (long)p.N * p.H;
+    if (pairs > 0)
+        hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                           dim3(DVT / 16 * 64), 0, s, p);
+}
+
+template <typename TIn, typename TO>
+static void kda_dispatch(const ChunkProblem& p, hipStream_t s) {
+    if (p.dk == 64) {
+        if (p.dv == 64) kda_launch<TIn, TO, 64, 64>(p, s); else kda_launch<TIn, TO, 64, 128>(p, s);
+    } else {
+        if (p.dv == 64) kda_launch<TIn, TO, 128, 64>(p, s); else kda_launch<TIn, TO, 128, 128>(p, s);
+    }
+}
+
+hipError_t launch_kda_chunk_fwd(const ChunkProblem& p, hipStream_t s) {
+    launch_chunk_base(p, s);
+    if (!p.bf16) kda_dispatch<float, float>(p, s);
+    else if (p.o_bf16) kda_dispatch<uint16_t, uint16_t>(p, s);
+    else kda_dispatch<uint16_t, float>(p, s);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -170,3 +170,17 @@ def make_cotangents(x: dict, seed: int, *, dhT: bool = True) -> dict:
     dh = (torch.from_numpy(rng.standard_normal((m["N"], m["H"], m["dv"], m["dk"]), dtype=np.float32))
           if dhT else None)
     return dict(do=do, dhT=dh)
+
+
+def channel_gates(x: dict, seed: int, *, gate_scale: float = 1.0) -> dict:
+    """Replace the scalar gates of an input set (forward or decode) by one gate per key
+    channel, with the same distribution: g = -gate_scale * softplus(N(0,1)) of shape
+    g.shape + (d_k,), drawn from its own seeded generator (the other tensors are unchanged)."""
+    rng = np.random.default_rng(seed)
+    dk = x["meta"]["dk"]
+    shape = tuple(x["g"].shape) + (dk,)
+    g = -np.float32(gate_scale) * _softplus(rng.standard_normal(shape, dtype=np.float32))
+    y = dict(x)
+    y["g"] = torch.from_numpy(g.astype(np.float32))
+    y["meta"] = dict(x["meta"], channel_gate=True)
+    return y

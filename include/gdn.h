@@ -219,6 +219,40 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
                     const float *beta, float *state, void *o, int N, int H, int dk, int dv,
                     int dtype, int o_dtype, void *stream);
 
+/*
+ * Channel-wise decay (one decay per key channel): the pages extend the gated delta rule
+ * "with a channel-wise forgetting gate" (record "LIT-137", "Standing in the anthology";
+ * practice "SOTA-135", "Sequence") without a formula. The operator read from them:
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t,
+ * alpha_t = exp(g_t) in (0,1]^{dk} scaling the state's key channels (its columns). With
+ * the same g in every channel it is the operator of gdn_chunk_fwd.
+ *
+ * gdn_kda_chunk_fwd: chunkwise forward pass, arguments as in gdn_chunk_fwd except
+ *   g_log_alpha [B, T, H, dk] fp32 (16-byte aligned), log of the per-channel decay, <= 0
+ *   workspace   at least gdn_kda_chunk_fwd_workspace_bytes(...) bytes: chunk_base (packed
+ *               only), then fp32 [nc, H, 64, 64] Mmat and P, fp32 [nc, H, 64, dk]
+ *               K * e^gamma, Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk]
+ *               e^{gamma_last} (gamma: per-channel in-chunk cumulative sum of g).
+ * All arithmetic is fp32 (bf16 inputs are widened on load); a bf16 o is the fp32 result
+ * rounded to nearest even.
+ */
+size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
+                                         int chunk, int dtype);
+int gdn_kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                      const float *beta, const float *h0, void *o, float *hT,
+                      const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                      int N, int dtype, int o_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * One decode step of the channel-wise-decay operator, arguments as in gdn_decode_step except
+ * g_log_alpha [N, H, dk] fp32 (16-byte aligned). Per state row s_i: s~ = s_i * alpha,
+ * c_i = beta (v_i - s~ . k), s_i <- s~ + c_i k, o_i = s~ . q + c_i (k . q).
+ */
+int gdn_kda_decode_step(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                        const float *beta, float *state, void *o, int N, int H, int dk, int dv,
+                        int dtype, int o_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
