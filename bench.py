@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["all", "fwd", "decode", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "fwd", "decode", "bwd", "kda"], default="all")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run plain device copies of this many MiB (counter calibration)")
@@ -173,6 +173,58 @@ def bench_backward(args, torch, gb, SY):
     t1 = time.perf_counter()
     return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=t1 - t0,
                 step_ms=[e[0].elapsed_time(e[1]) for e in evs])
+
+
+def bench_kda(args, torch, gb, SY):
+    """gdn_kda_chunk_fwd on the training-shape workload with one decay per key channel (bf16
+    q/k/v/o, fp32 gates and state), two rotating input sets; then 16 chained
+    gdn_kda_decode_step calls on the decode workload with per-channel gates."""
+    w = SY.WORKLOADS[1]
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        x = SY.channel_gates(SY.make_forward_inputs(1, seed=1 + 100 * s), 55 + s)
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+        t["o"] = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        t["hT"] = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        sets.append(t)
+    need = gb.gdn_kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, B, False)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step(t):
+        gb.gdn_kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], o=t["o"], hT=t["hT"], workspace=ws)
+
+    for i in range(2):
+        step(sets[i % 2])
+    n = max(args.bwd_steps, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        evs[i][0].record()
+        step(sets[i % 2])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) / n * 1e3
+
+    wd = SY.WORKLOADS[4]
+    steps = 16
+    d = SY.channel_gates(SY.make_decode_inputs(4, steps=steps), 57)
+    toks = [{n_: d[n_][s].to(dev) for n_ in ("q", "k", "v", "g", "beta")} for s in range(steps)]
+    state = d["state"].to(dev)
+    o = torch.empty((wd.decode_seqs, wd.H, wd.dv), dtype=torch.float32, device=dev)
+    gb.gdn_kda_decode_step(*(toks[0][n_] for n_ in ("q", "k", "v", "g", "beta")), state.clone(), o)
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        devs[s][0].record()
+        gb.gdn_kda_decode_step(*(toks[s][n_] for n_ in ("q", "k", "v", "g", "beta")), state, o)
+        devs[s][1].record()
+    torch.cuda.synchronize()
+    dec_ms = [e[0].elapsed_time(e[1]) for e in devs]
+    return dict(B=B, T=T, H=H, dk=dk, dv=dv, fwd_ms=fwd_ms, fwd_step_ms=[e[0].elapsed_time(e[1]) for e in evs],
+                dec_ms=dec_ms, N=wd.decode_seqs, Hd=wd.H)
 
 
 def bench_decode(args, torch, gb, SY):
@@ -326,7 +378,24 @@ def main():
         if args.only == "bwd":
             out["value"] = b["B"] * b["T"] / (ms / 1e3)
             out["ms_per_step"] = ms
-    if args.cpu_seconds > 0 and args.only not in ("decode", "bwd"):
+    if args.only in ("all", "kda"):
+        k = bench_kda(args, torch, gb, SY)
+        th = k["B"] * k["T"] * k["H"]
+        c = fwd_counts(k["dk"], k["dv"])
+        dmean = sum(k["dec_ms"]) / len(k["dec_ms"])
+        per = (decode_bytes(k["dk"], k["dv"]) + 4 * (k["dk"] - 1)) * k["N"] * k["Hd"]
+        out["kda"] = {"workload": "channel-wise decay: chunkwise forward B4 H16 T2048 d128 bf16 q/k/v/o "
+                                  "(fp32 arithmetic), and decode 256 seq x H32 d128 (16 chained steps)",
+                      "fwd_ms_per_step": k["fwd_ms"], "fwd_ms_median": median(k["fwd_step_ms"]),
+                      "fwd_tokens_per_s": k["B"] * k["T"] / (k["fwd_ms"] / 1e3),
+                      "fwd_tflops_algorithmic": c["flops"] * th / (k["fwd_ms"] / 1e3) / 1e12,
+                      "decode_ms_per_step_mean": dmean,
+                      "decode_hbm_GBps": per / (dmean / 1e3) / 1e9,
+                      "decode_hbm_frac": per / (dmean / 1e3) / PEAK_HBM_BPS}
+        if args.only == "kda":
+            out["value"] = k["B"] * k["T"] / (k["fwd_ms"] / 1e3)
+            out["ms_per_step"] = k["fwd_ms"]
+    if args.cpu_seconds > 0 and args.only not in ("decode", "bwd", "kda"):
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
