@@ -33,6 +33,8 @@ _SIGNATURES = [
     ("gdn_kda_chunk_fwd_workspace_bytes", _SZ, [_I] * 9),
     ("gdn_kda_chunk_fwd", _I, [_P] * 9 + [_I] * 9 + [_P, _SZ, _P]),
     ("gdn_kda_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
+    ("gdn_decoupled_chunk_fwd", _I, [_P] * 10 + [_I] * 9 + [_P, _SZ, _P]),
+    ("gdn_decoupled_decode_step", _I, [_P] * 8 + [_I] * 6 + [_P]),
 ]
 
 _lib = None
@@ -248,4 +250,41 @@ def gdn_kda_decode_step(q, k, v, g, beta, state, o=None, *, o_dtype=torch.float3
                                    N, H, dk, dv, _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1),
                                    _stream(q.device, stream))
     _check(st, "gdn_kda_decode_step")
+    return o
+
+
+def gdn_decoupled_chunk_fwd(q, k, v, g, erase, write, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None,
+                            hT=None, o_dtype=None, output_final_state=True, workspace=None, stream=None):
+    """Chunkwise forward pass with a channel-wise decay g [B,T,H,dk] and decoupled erase
+    [B,T,H,dk] and write [B,T,H,dv] gates (fp32) in place of beta."""
+    _need_gpu(q, k, v, g, erase, write, h0, cu_seqlens, o, hT, workspace)
+    B, T, H, dk, dv, N = _shapes(q, v, cu_seqlens)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = gdn_kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, cu_seqlens is not None, chunk, q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().gdn_decoupled_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase), _ptr(write), _ptr(h0),
+                                       _ptr(o), _ptr(hT), _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
+                                       _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1), _ptr(workspace),
+                                       workspace.numel() if workspace is not None else 0,
+                                       _stream(q.device, stream))
+    _check(st, "gdn_decoupled_chunk_fwd")
+    return o, hT
+
+
+def gdn_decoupled_decode_step(q, k, v, g, erase, write, state, o=None, *, o_dtype=torch.float32, stream=None):
+    """One decode step with a channel-wise decay g [N,H,dk] and decoupled erase [N,H,dk] and
+    write [N,H,dv] gates; the state is updated in place."""
+    _need_gpu(q, k, v, g, erase, write, state, o)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype, device=q.device)
+    st = lib().gdn_decoupled_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase), _ptr(write),
+                                         _ptr(state), _ptr(o), N, H, dk, dv, _DTYPE.get(q.dtype, -1),
+                                         _DTYPE.get(o.dtype, -1), _stream(q.device, stream))
+    _check(st, "gdn_decoupled_decode_step")
     return o

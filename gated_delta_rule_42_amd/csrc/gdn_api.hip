@@ -238,11 +238,12 @@ GDN_EXPORT size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk,
     return gdn::kda_workspace_layout(B, T, H, dk, N, varlen != 0).total;
 }
 
-GDN_EXPORT int gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
-                                 const float* beta, const float* h0, void* o, float* hT,
-                                 const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
-                                 int dv, int N, int dtype, int o_dtype, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+namespace {
+// Shared by the channel-wise-decay entry points: beta, or the erase and write gates.
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                  const float* beta, const float* erase, const float* write, const float* h0, void* o,
+                  float* hT, const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                  int N, int dtype, int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
@@ -256,8 +257,9 @@ GDN_EXPORT int gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, co
     const long long tokens = (long long)B * T;
     if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
         return GDN_ERR_SHAPE;
-    if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !beta || !o)) return GDN_ERR_NULL;
-    const void* al16[] = {q, k, v, o, h0, hT, g_log_alpha};
+    if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !o || (!erase && !beta) || (erase && !write)))
+        return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, o, h0, hT, g_log_alpha, erase, write};
     for (const void* x : al16)
         if (x && !aligned(x, 16)) return GDN_ERR_ALIGN;
     const void* al4[] = {beta, cu_seqlens};
@@ -284,8 +286,30 @@ GDN_EXPORT int gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, co
     P.qhat = any ? reinterpret_cast<float*>(base + w.off_qh) : nullptr;
     P.kdec = any ? reinterpret_cast<float*>(base + w.off_kd) : nullptr;
     P.lam = any ? reinterpret_cast<float*>(base + w.off_lam) : nullptr;
+    P.erase = erase;
+    P.write = erase ? write : nullptr;
     return gdn::launch_kda_chunk_fwd(P, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                        : GDN_ERR_HIP;
+}
+}  // namespace
+
+GDN_EXPORT int gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                                 const float* beta, const float* h0, void* o, float* hT,
+                                 const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
+                                 int dv, int N, int dtype, int o_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return kda_chunk_fwd(q, k, v, g_log_alpha, beta, nullptr, nullptr, h0, o, hT, cu_seqlens, chunk, B, T,
+                         H, dk, dv, N, dtype, o_dtype, workspace, workspace_bytes, stream);
+}
+
+GDN_EXPORT int gdn_decoupled_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                                       const float* erase, const float* write, const float* h0, void* o,
+                                       float* hT, const int32_t* cu_seqlens, int chunk, int B, int T, int H,
+                                       int dk, int dv, int N, int dtype, int o_dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (B * (long long)T > 0 && (!erase || !write)) return GDN_ERR_NULL;
+    return kda_chunk_fwd(q, k, v, g_log_alpha, nullptr, erase, write, h0, o, hT, cu_seqlens, chunk, B, T,
+                         H, dk, dv, N, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 GDN_EXPORT int gdn_kda_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
@@ -303,6 +327,26 @@ GDN_EXPORT int gdn_kda_decode_step(const void* q, const void* k, const void* v, 
     gdn::DecodeProblem p{q,  k, v,  g_log_alpha, beta,           state,
                          o,  N, H,  dk,          dv,   dtype == GDN_BF16, o_dtype == GDN_BF16};
     p.channel_gate = 1;
+    return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
+                                                                                : GDN_ERR_HIP;
+}
+
+GDN_EXPORT int gdn_decoupled_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
+                                         const float* erase, const float* write, float* state, void* o, int N,
+                                         int H, int dk, int dv, int dtype, int o_dtype, void* stream) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1 || (long long)N * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
+    if (!q || !k || !v || !g_log_alpha || !erase || !write || !state || !o) return GDN_ERR_NULL;
+    const void* al16[] = {q, k, v, o, state, g_log_alpha, erase, write};
+    for (const void* x : al16)
+        if (!aligned(x, 16)) return GDN_ERR_ALIGN;
+    gdn::DecodeProblem p{q,  k, v,  g_log_alpha, nullptr,        state,
+                         o,  N, H,  dk,          dv,   dtype == GDN_BF16, o_dtype == GDN_BF16};
+    p.channel_gate = 1;
+    p.erase = erase;
+    p.write = write;
     return gdn::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                 : GDN_ERR_HIP;
 }

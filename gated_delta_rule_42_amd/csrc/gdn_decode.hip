@@ -13,6 +13,9 @@
 // "Standing in the anthology") the decay scales the state's columns instead:
 //   s~_i = s_i * alpha,  a_i = s~_i . k,  b_i = s~_i . q,  c_i = beta (v_i - a_i),
 //   s_i <- s~_i + c_i k,  o_i = b_i + c_i (k . q).
+// With decoupled erase and write gates e [N, H, d_k], w [N, H, d_v] (record "LIT-137",
+// "Standing in the anthology") the erased read runs along e * k and the value is w_i v_i:
+//   a_i = s~_i . (e * k),  c_i = w_i v_i - a_i.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -43,7 +46,7 @@ __device__ __forceinline__ void load_vec(const TS* p, float (&x)[EPL]) {
 // One work-group per (sequence, head). Its 256 lanes form 16 groups of 16; group g owns
 // rows g, g+16, ...; within a group, lane l16 owns columns [l16*EPL, l16*EPL + EPL) so that
 // one group reads a whole row contiguously.
-template <typename TS, typename TO, int DK, int DV, bool CW>
+template <typename TS, typename TO, int DK, int DV, bool CW, bool DEC>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     constexpr int EPL = DK / 16;   // state columns per lane
     constexpr int RPG = DV / 16;   // rows per lane group
@@ -53,12 +56,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     float kf[EPL], qf[EPL];
     load_vec<TS, EPL>(static_cast<const TS*>(p.k) + pr * DK + l16 * EPL, kf);
     load_vec<TS, EPL>(static_cast<const TS*>(p.q) + pr * DK + l16 * EPL, qf);
+    float ke[EPL];   // the key the erased read runs along
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ke[e] = DEC ? p.erase[pr * DK + l16 * EPL + e] * kf[e] : kf[e];
     float kq = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) kq += kf[e] * qf[e];
     kq = row16_sum(kq);
     const float alpha = CW ? 1.f : __expf(p.g[pr]);
-    const float beta = p.beta[pr];
+    const float beta = DEC ? 1.f : p.beta[pr];
     float af[EPL];   // channel-wise decay of this lane's columns
 #pragma unroll
     for (int e = 0; e < EPL; ++e) af[e] = CW ? __expf(p.g[pr * DK + l16 * EPL + e]) : 1.f;
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
             for (int e = 0; e < EPL; ++e) s[it][e] *= af[e];
         }
         vr[it] = to_f32(vp[row]);
+        if constexpr (DEC) vr[it] *= p.write[pr * DV + row];
     }
 #pragma unroll
     for (int it = 0; it < RPG; ++it) {
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
         float sk = 0.f, sq = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            sk += s[it][e] * kf[e];
+            sk += s[it][e] * ke[e];
             sq += s[it][e] * qf[e];
         }
         sk = row16_sum(sk);
@@ -110,12 +117,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
 
 template <typename TS, typename TO, int DK, int DV>
 static void decode_launch(const DecodeProblem& p, hipStream_t s) {
-    if (p.channel_gate)
-        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
-                           0, s, p);
+    const dim3 grid((unsigned)((long)p.N * p.H));
+    if (p.erase)
+        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true, true>), grid, dim3(256), 0, s, p);
+    else if (p.channel_gate)
+        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true, false>), grid, dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, false>), dim3((unsigned)((long)p.N * p.H)), dim3(256),
-                           0, s, p);
+        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, false, false>), grid, dim3(256), 0, s, p);
 }
 
 template <typename TS, typename TO>

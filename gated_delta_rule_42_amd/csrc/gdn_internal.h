@@ -38,6 +38,9 @@ struct ChunkProblem {
     float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma
     float* kdec;                 // [nc_bound, H, 64, dk] K * e^{gamma_last - gamma}
     float* lam;                  // [nc_bound, H, dk] e^{gamma_last}
+    // decoupled gates (replace beta when set): erase [B,T,H,dk], write [B,T,H,dv]
+    const float* erase;
+    const float* write;
 };
 
 // Token range of sequence n, clamped to [0, T] (see chunk_base_kernel).
@@ -143,6 +146,8 @@ struct DecodeProblem {
     int bf16;     // q, k, v are bf16 (else fp32)
     int o_bf16;   // o is bf16 (else fp32)
     int channel_gate;   // g is [N, H, dk] (one decay per key channel), else [N, H]
+    const float* erase;  // decoupled gates (channel_gate only): [N, H, dk] and [N, H, dv];
+    const float* write;  // NULL: beta
 };
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);

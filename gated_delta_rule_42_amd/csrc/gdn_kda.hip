@@ -14,6 +14,11 @@
 //     T     = (I + A)^{-1},   Mmat = T diag(beta)
 //     P     = lower_incl([sum_c q_r k_i e^{gamma_r - gamma_i}])
 //     Delta = Mmat (V - Kh S^T),   O = Qh S^T + P Delta,   S' = S Diag(lam) + Delta^T Kd.
+// With decoupled erase and write gates (record "LIT-137", "Standing in the anthology": beta
+// split into a channel-wise erase gate on the key and a channel-wise write gate on the value;
+// practice "SOTA-135": the erased read runs along a reweighted key) the erased read runs along
+// E * k and the written value is W * v: the same chunk form with A's left factor E * K instead
+// of diag(beta) K, Kh = E * K * e^gamma, V replaced by W * V and Mmat = T.
 // Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head); stage 2
 // (kda_propagate_kernel) carries the state through the chunks. All arithmetic is fp32 (fp32
 // 16x16x4 matrix core); bf16 inputs are widened on load.
@@ -49,14 +54,62 @@ struct alignas(16) KdaPrepSmem {
     float beta[64];
 };
 
-// One work-group (4 waves) per (chunk, head); wave w owns row block w of A and P.
-template <typename TIn, int DK>
+// Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}] for one or
+// two left operands L1, L2 (sharing the right operand K and the exponentials), into O1 (times
+// rs1[r] when rs1 is set; strictly lower when strict1) and O2 (lower including the diagonal).
+// Blocks below the diagonal: fp32 matrix core with the reference gamma of row 16 I (both
+// factors <= 1); the diagonal block: exact sums over the channels.
+template <int DK, bool TWO>
+__device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
+                                          float* O1, float* O2, const float* rs1, bool strict1,
+                                          int wave, int lane) {
+    constexpr int PK = KdaPrepSmem<DK>::PK, PF = KdaPrepSmem<DK>::PF;
+    const int l16 = lane & 15, lq = lane >> 4, I = wave;
+    for (int J = 0; J < I; ++J) {
+        f32x4_t a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const int ch = k0 + lq;
+            const float gref = sm.G[16 * I * PK + ch];
+            const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
+            const float er = __expf(gref - sm.G[(16 * J + l16) * PK + ch]);
+            const float b = sm.K[(16 * J + l16) * PK + ch] * er;
+            a1 = mfma4(L1[(16 * I + l16) * PK + ch] * el, b, a1);
+            if constexpr (TWO) a2 = mfma4(L2[(16 * I + l16) * PK + ch] * el, b, a2);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
+            O1[r * PF + i] = (rs1 ? rs1[r] : 1.f) * a1[m];
+            if constexpr (TWO) O2[r * PF + i] = a2[m];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r = 16 * I + 4 * lq + m, i = 16 * I + l16;
+        float s1 = 0.f, s2 = 0.f;
+        if (i <= r) {
+            for (int ch = 0; ch < DK; ++ch) {
+                const float e = __expf(fminf(sm.G[r * PK + ch] - sm.G[i * PK + ch], 0.f)) * sm.K[i * PK + ch];
+                s1 += L1[r * PK + ch] * e;
+                if constexpr (TWO) s2 += L2[r * PK + ch] * e;
+            }
+        }
+        O1[r * PF + i] = (strict1 ? i < r : i <= r) ? (rs1 ? rs1[r] : 1.f) * s1 : 0.f;
+        if constexpr (TWO) O2[r * PF + i] = s2;
+    }
+}
+
+// One work-group (4 waves) per (chunk, head); wave w owns row block w of A and P. With
+// decoupled gates (DEC) the erased read runs along E * K, so A's left operand is E * K (held
+// in the Q buffer until A is formed, then Q is loaded), Kh is E * K * e^gamma, V is scaled by
+// the write gate in stage 2 and Mmat is T itself.
+template <typename TIn, int DK, bool DEC>
 __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     using SM = KdaPrepSmem<DK>;
     constexpr int PK = SM::PK, PF = SM::PF;
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
     const long c = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -67,20 +120,26 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     const TIn* kp = static_cast<const TIn*>(p.k);
     const TIn* qp = static_cast<const TIn*>(p.q);
 
+    // K, g and (Q, or E * K with decoupled gates) into LDS
     for (int i = tid; i < 64 * DK / 4; i += 256) {
         const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
         float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
         if (r < len) {
             const long o = ((bos + r) * H + h) * DK + cc;
             kv = load4_in(kp + o);
-            qv = load4_in(qp + o);
             gv = *reinterpret_cast<const float4*>(p.g + o);
+            if constexpr (DEC) {
+                const float4 e = *reinterpret_cast<const float4*>(p.erase + o);
+                qv = make_float4(e.x * kv.x, e.y * kv.y, e.z * kv.z, e.w * kv.w);
+            } else {
+                qv = load4_in(qp + o);
+            }
         }
         *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
         *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
         *reinterpret_cast<float4*>(&sm.G[r * PK + cc]) = gv;
     }
-    if (tid < 64) sm.beta[tid] = tid < len ? p.beta[(bos + tid) * H + h] : 0.f;
+    if (tid < 64) sm.beta[tid] = (!DEC && tid < len) ? p.beta[(bos + tid) * H + h] : 0.f;
     __syncthreads();
     if (tid < DK) {   // gamma, one channel per thread (rows past the chunk's end add 0)
         float run = 0.f;
@@ -91,70 +150,59 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     }
     __syncthreads();
 
-    // -- Kh, Qh, Kd and lam to the workspace
-    for (int i = tid; i < 64 * DK / 4; i += 256) {
-        const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
-        const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
-        const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
-        const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
-        const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
-        const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
-        const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
-        const long o = (widx * 64 + r) * DK + cc;
-        *reinterpret_cast<float4*>(p.khat + o) = make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w);
-        *reinterpret_cast<float4*>(p.qhat + o) = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
-        *reinterpret_cast<float4*>(p.kdec + o) = make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w);
-    }
+    // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
+    auto write_scaled = [&](bool kside) {
+        for (int i = tid; i < 64 * DK / 4; i += 256) {
+            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
+            const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
+            const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
+            const long o = (widx * 64 + r) * DK + cc;
+            const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
+            if (!kside) {
+                *reinterpret_cast<float4*>(p.qhat + o) = x;
+                continue;
+            }
+            const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
+            const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
+            const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
+            *reinterpret_cast<float4*>(p.khat + o) =
+                DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w);
+            *reinterpret_cast<float4*>(p.kdec + o) = make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w);
+            if constexpr (!DEC) *reinterpret_cast<float4*>(p.qhat + o) = x;
+        }
+    };
+    write_scaled(true);
     if (tid < DK) p.lam[widx * DK + tid] = __expf(sm.G[63 * PK + tid]);
 
-    // -- A and P, row block I = wave
-    const int I = wave;
-    for (int J = 0; J < I; ++J) {   // below the diagonal: reference gamma at row 16 I
-        f32x4_t ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
-#pragma unroll 4
-        for (int k0 = 0; k0 < DK; k0 += 4) {
-            const int ch = k0 + lq;
-            const float gref = sm.G[16 * I * PK + ch];
-            const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
-            const float er = __expf(gref - sm.G[(16 * J + l16) * PK + ch]);
-            const float b = sm.K[(16 * J + l16) * PK + ch] * er;
-            ak = mfma4(sm.K[(16 * I + l16) * PK + ch] * el, b, ak);
-            aq = mfma4(sm.Q[(16 * I + l16) * PK + ch] * el, b, aq);
+    // -- A and P
+    if constexpr (DEC) {
+        gram_rows<DK, false>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, wave, lane);
+        __syncthreads();  // E * K is dead: load Q in its place
+        for (int i = tid; i < 64 * DK / 4; i += 256) {
+            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < len) qv = load4_in(qp + ((bos + r) * H + h) * DK + cc);
+            *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
         }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
-            sm.A[r * PF + i] = sm.beta[r] * ak[m];
-            sm.P[r * PF + i] = aq[m];
-        }
-    }
-    // the diagonal block: exact sums over the channels
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = 16 * I + 4 * lq + m, i = 16 * I + l16;
-        float sk = 0.f, sq = 0.f;
-        if (i <= r) {
-            for (int ch = 0; ch < DK; ++ch) {
-                const float e = __expf(fminf(sm.G[r * PK + ch] - sm.G[i * PK + ch], 0.f)) * sm.K[i * PK + ch];
-                sk += sm.K[r * PK + ch] * e;
-                sq += sm.Q[r * PK + ch] * e;
-            }
-        }
-        sm.A[r * PF + i] = i < r ? sm.beta[r] * sk : 0.f;
-        sm.P[r * PF + i] = sq;
+        __syncthreads();
+        write_scaled(false);
+        gram_rows<DK, false>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, wave, lane);
+    } else {
+        gram_rows<DK, true>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, wave, lane);
     }
     __syncthreads();
 
     ut_inverse64<PF>(sm.A, sm.T, wave, lane);
 
-    // -- Mmat = T diag(beta) and P (lower incl. diagonal), fp32 row-major
+    // -- Mmat = T diag(beta) (T with decoupled gates) and P (lower incl. diagonal), fp32 row-major
     {
         const int r = tid >> 2, c0 = (tid & 3) * 16;
         float mv[16], pv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int ci = c0 + e;
-            mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * sm.beta[ci] : 0.f;
+            mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
             pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
         }
         store16<float>(static_cast<float*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
@@ -231,7 +279,14 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate_kernel(ChunkProbl
         for (int i = tid; i < 64 * DVT / 4; i += NT) {
             const int r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < len) x = load4_in(vp + ((bos + r) * H + h) * DV + dv0 + cc);
+            if (r < len) {
+                const long o = ((bos + r) * H + h) * DV + dv0 + cc;
+                x = load4_in(vp + o);
+                if (p.write) {   // decoupled gates: the written value is w * v
+                    const float4 w = *reinterpret_cast<const float4*>(p.write + o);
+                    x = make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
+                }
+            }
             *reinterpret_cast<float4*>(&sm.V[r * PV + cc]) = x;
         }
         for (int i = tid; i < DK; i += NT) sm.lam[i] = p.lam[widx * DK + i];
@@ -320,7 +375,12 @@ template <typename TIn, typename TO, int DK, int DV>
 static void kda_launch(const ChunkProblem& p, hipStream_t s) {
     constexpr int DVT = 32;
     const long units = p.nc_bound * p.H;
-    if (units > 0) hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK>), dim3((unsigned)units), dim3(256), 0, s, p);
+    if (units > 0) {
+        if (p.erase)
+            hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK, true>), dim3((unsigned)units), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK, false>), dim3((unsigned)units), dim3(256), 0, s, p);
+    }
     const long pairs = (long)p.N * p.H;
     if (pairs > 0)
         hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),

@@ -184,3 +184,17 @@ def channel_gates(x: dict, seed: int, *, gate_scale: float = 1.0) -> dict:
     y["g"] = torch.from_numpy(g.astype(np.float32))
     y["meta"] = dict(x["meta"], channel_gate=True)
     return y
+
+
+def decoupled_gates(x: dict, seed: int) -> dict:
+    """Replace beta of a channel-gate input set (forward or decode) by an erase gate
+    g.shape (one per key channel) and a write gate of shape beta.shape + (d_v,), both
+    sigmoid(N(0,1)), drawn from their own seeded generator."""
+    rng = np.random.default_rng(seed)
+    m = x["meta"]
+    y = dict(x)
+    y["erase"] = torch.from_numpy(_sigmoid(rng.standard_normal(tuple(x["g"].shape), dtype=np.float32)))
+    y["write"] = torch.from_numpy(_sigmoid(rng.standard_normal(tuple(x["beta"].shape) + (m["dv"],),
+                                                               dtype=np.float32)))
+    y["meta"] = dict(m, decoupled=True)
+    return y

@@ -253,6 +253,31 @@ int gdn_kda_decode_step(const void *q, const void *k, const void *v, const float
                         const float *beta, float *state, void *o, int N, int H, int dk, int dv,
                         int dtype, int o_dtype, void *stream);
 
+/*
+ * Decoupled channel-wise erase and write gates on top of the channel-wise decay: the pages
+ * split beta "into a channel-wise erase gate and a channel-wise write gate on top of KDA's
+ * channel-wise decay" (record "LIT-137", "Standing in the anthology"), the erase gate "on
+ * the key", the write gate "on the value", with "the erased read" running "along a
+ * reweighted key" (practice "SOTA-135", "Where it is incomplete"). The operator read from
+ * them (tied scalar gates give the gated delta rule):
+ *     Sa = S_{t-1} Diag(alpha_t),   S_t = Sa - (Sa (e_t * k_t)) k_t^T + (w_t * v_t) k_t^T,
+ *     o_t = S_t q_t.
+ * gdn_decoupled_chunk_fwd: as gdn_kda_chunk_fwd with beta replaced by
+ *   erase [B, T, H, dk] fp32 and write [B, T, H, dv] fp32 (both required, 16-byte aligned);
+ *   the workspace is the one of gdn_kda_chunk_fwd_workspace_bytes (Mmat holds T itself and
+ *   the K * e^gamma region holds erase * K * e^gamma).
+ * gdn_decoupled_decode_step: as gdn_kda_decode_step with erase [N, H, dk] and write
+ *   [N, H, dv] in place of beta: c_i = w_i v_i - s~_i . (e * k), s_i <- s~_i + c_i k.
+ */
+int gdn_decoupled_chunk_fwd(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                            const float *erase, const float *write, const float *h0, void *o,
+                            float *hT, const int32_t *cu_seqlens, int chunk, int B, int T, int H,
+                            int dk, int dv, int N, int dtype, int o_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
+int gdn_decoupled_decode_step(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                              const float *erase, const float *write, float *state, void *o, int N,
+                              int H, int dk, int dv, int dtype, int o_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
