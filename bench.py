@@ -223,8 +223,25 @@ def bench_kda(args, torch, gb, SY):
         devs[s][1].record()
     torch.cuda.synchronize()
     dec_ms = [e[0].elapsed_time(e[1]) for e in devs]
+
+    # decoupled erase / write gates on the same workload
+    for i, t in enumerate(sets):
+        x = SY.decoupled_gates(dict(meta=dict(dv=dv), g=t["g"].cpu(), beta=t["beta"].cpu()), 58 + i)
+        t["erase"], t["write"] = x["erase"].to(dev), x["write"].to(dev)
+
+    def dstep(t):
+        gb.gdn_decoupled_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["erase"], t["write"], o=t["o"], hT=t["hT"],
+                                   workspace=ws)
+
+    dstep(sets[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        dstep(sets[i % 2])
+    torch.cuda.synchronize()
+    dc_ms = (time.perf_counter() - t0) / n * 1e3
     return dict(B=B, T=T, H=H, dk=dk, dv=dv, fwd_ms=fwd_ms, fwd_step_ms=[e[0].elapsed_time(e[1]) for e in evs],
-                dec_ms=dec_ms, N=wd.decode_seqs, Hd=wd.H)
+                dec_ms=dec_ms, N=wd.decode_seqs, Hd=wd.H, dc_ms=dc_ms)
 
 
 def bench_decode(args, torch, gb, SY):
@@ -391,7 +408,9 @@ def main():
                       "fwd_tflops_algorithmic": c["flops"] * th / (k["fwd_ms"] / 1e3) / 1e12,
                       "decode_ms_per_step_mean": dmean,
                       "decode_hbm_GBps": per / (dmean / 1e3) / 1e9,
-                      "decode_hbm_frac": per / (dmean / 1e3) / PEAK_HBM_BPS}
+                      "decode_hbm_frac": per / (dmean / 1e3) / PEAK_HBM_BPS,
+                      "decoupled_gates_fwd_ms_per_step": k["dc_ms"],
+                      "decoupled_gates_fwd_tokens_per_s": k["B"] * k["T"] / (k["dc_ms"] / 1e3)}
         if args.only == "kda":
             out["value"] = k["B"] * k["T"] / (k["fwd_ms"] / 1e3)
             out["ms_per_step"] = k["fwd_ms"]
