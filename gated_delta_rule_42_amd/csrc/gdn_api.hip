@@ -235,7 +235,7 @@ GDN_EXPORT size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk,
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
     if (B < 1 || H < 1 || T < 0) return 0;
     if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
-    return gdn::kda_workspace_layout(B, T, H, dk, N, varlen != 0).total;
+    return gdn::kda_workspace_layout(B, T, H, dk, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
 }
 
 namespace {
@@ -265,7 +265,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_lo
     const void* al4[] = {beta, cu_seqlens};
     for (const void* x : al4)
         if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
-    const gdn::KdaLayout w = gdn::kda_workspace_layout(B, T, H, dk, N, cu_seqlens != nullptr);
+    const gdn::KdaLayout w = gdn::kda_workspace_layout(B, T, H, dk, N, cu_seqlens != nullptr, dtype == GDN_BF16 ? 2 : 4);
     if (w.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
     if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return GDN_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 256)) return GDN_ERR_ALIGN;

@@ -34,9 +34,9 @@ struct ChunkProblem {
     float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
     float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
     // channel-wise decay (g is [B,T,H,dk]): chunk operators of the fp32 kernels
-    float* khat;                 // [nc_bound, H, 64, dk] K * e^gamma
-    float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma
-    float* kdec;                 // [nc_bound, H, 64, dk] K * e^{gamma_last - gamma}
+    float* khat;                 // [nc_bound, H, 64, dk] K * e^gamma          (fp16 for bf16 inputs)
+    float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma          (fp16 for bf16 inputs)
+    float* kdec;                 // [nc_bound, H, 64, dk] K * e^{gamma_last - gamma} (same)
     float* lam;                  // [nc_bound, H, dk] e^{gamma_last}
     // decoupled gates (replace beta when set): erase [B,T,H,dk], write [B,T,H,dv]
     const float* erase;
@@ -131,7 +131,7 @@ struct KdaLayout {
     size_t off_base, off_m, off_p, off_kh, off_qh, off_kd, off_lam, total;
     long nc_bound;
 };
-KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen);
+KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem);
 hipError_t launch_kda_chunk_fwd(const ChunkProblem& p, hipStream_t s);
 
 struct DecodeProblem {

@@ -29,6 +29,7 @@
 // over the channels with the exponent of each difference directly.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_stage2.h"
 #include "gdn_ut.h"
 
 namespace gdn {
@@ -39,6 +40,12 @@ __device__ __forceinline__ float4 load4_in(const uint16_t* p) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
     return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// Four fp32 values stored as the operand type (fp32, or fp16 for bf16 inputs).
+__device__ __forceinline__ void put4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+__device__ __forceinline__ void put4(_Float16* p, float4 x) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_f16x2(x.x, x.y), pack_f16x2(x.z, x.w));
 }
 
 // ------------------------------------------------------------------- stage 1
@@ -119,6 +126,10 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     const long widx = c * H + h;
     const TIn* kp = static_cast<const TIn*>(p.k);
     const TIn* qp = static_cast<const TIn*>(p.q);
+    using TM = typename Operand<TIn>::type;   // operators are written as fp16 for bf16 inputs
+    TM* khat = reinterpret_cast<TM*>(p.khat);
+    TM* qhat = reinterpret_cast<TM*>(p.qhat);
+    TM* kdec = reinterpret_cast<TM*>(p.kdec);
 
     // K, g and (Q, or E * K with decoupled gates) into LDS
     for (int i = tid; i < 64 * DK / 4; i += 256) {
@@ -160,16 +171,15 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
             const long o = (widx * 64 + r) * DK + cc;
             const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
             if (!kside) {
-                *reinterpret_cast<float4*>(p.qhat + o) = x;
+                put4(qhat + o, x);
                 continue;
             }
             const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
             const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
             const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
-            *reinterpret_cast<float4*>(p.khat + o) =
-                DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w);
-            *reinterpret_cast<float4*>(p.kdec + o) = make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w);
-            if constexpr (!DEC) *reinterpret_cast<float4*>(p.qhat + o) = x;
+            put4(khat + o, DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w));
+            put4(kdec + o, make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w));
+            if constexpr (!DEC) put4(qhat + o, x);
         }
     };
     write_scaled(true);
@@ -205,8 +215,8 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
             mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
             pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
         }
-        store16<float>(static_cast<float*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
-        store16<float>(static_cast<float*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+        store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+        store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
     }
 }
 
@@ -353,19 +363,167 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate_kernel(ChunkProbl
     }
 }
 
+// --------------------------------------------------- stage 2, bf16 inputs (fp16 operands)
+template <int DK, int DVT>
+struct alignas(16) KdaProp16Smem {
+    using KL = KQLayout<_Float16, DK>;
+    static constexpr int PK = KL::kPitch, PC = 72, PV = DVT + 4;
+    _Float16 Kh[64 * PK];
+    _Float16 Qh[64 * PK];
+    _Float16 Kd[64 * PK];
+    _Float16 M[64 * PC];
+    _Float16 P[64 * PC];
+    float V[64 * PV];
+    float lam[DK];
+};
+
+// The stage-2 products of kda_propagate_kernel on the fp16 matrix core (16x16x32, fp32
+// accumulation), as the scalar-gate path multiplies bf16 inputs: stage 1 left Kh, Qh, Kd, Mmat
+// and P in fp16, the state is packed to fp16 as an operand and kept in fp32.
+template <typename TO, int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkProblem p) {
+    using SM = KdaProp16Smem<DK, DVT>;
+    using KL = typename SM::KL;
+    constexpr int PC = SM::PC, PV = SM::PV, NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
+    constexpr int NT = DVT / 16 * 64;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long pair = blockIdx.x / NTILE;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + 63) / 64;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+
+    f32x4_t ST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        if (p.h0) {
+            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
+            ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const uint16_t* vp = static_cast<const uint16_t*>(p.v);
+    const _Float16* kh = reinterpret_cast<const _Float16*>(p.khat);
+    const _Float16* qh = reinterpret_cast<const _Float16*>(p.qhat);
+    const _Float16* kd = reinterpret_cast<const _Float16*>(p.kdec);
+    const _Float16* mp = static_cast<const _Float16*>(p.mmat);
+    const _Float16* pp = static_cast<const _Float16*>(p.pmat);
+
+    for (long jc = 0; jc < nchunks; ++jc) {
+        const long bos = sbos + jc * 64, widx = (cbase + jc) * H + h;
+        const int len = (int)min(64L, seos - bos);
+        __syncthreads();  // the previous chunk's LDS data is dead
+        for (int i = tid; i < 64 * DK / 8; i += NT) {
+            const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const long o = (widx * 64 + r) * DK + cc;
+            *reinterpret_cast<uint4*>(&sm.Kh[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(kh + o);
+            *reinterpret_cast<uint4*>(&sm.Qh[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(qh + o);
+            *reinterpret_cast<uint4*>(&sm.Kd[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(kd + o);
+        }
+        for (int i = tid; i < 64 * 8; i += NT) {
+            const int r = i / 8, cc = 8 * (i % 8);
+            *reinterpret_cast<uint4*>(&sm.M[r * PC + cc]) = *reinterpret_cast<const uint4*>(mp + widx * 4096 + r * 64 + cc);
+            *reinterpret_cast<uint4*>(&sm.P[r * PC + cc]) = *reinterpret_cast<const uint4*>(pp + widx * 4096 + r * 64 + cc);
+        }
+        for (int i = tid; i < 64 * DVT / 4; i += NT) {
+            const int r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < len) {
+                const long o = ((bos + r) * H + h) * DV + dv0 + cc;
+                x = load4_in(vp + o);
+                if (p.write) {   // decoupled gates: the written value is w * v
+                    const float4 w = *reinterpret_cast<const float4*>(p.write + o);
+                    x = make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
+                }
+            }
+            *reinterpret_cast<float4*>(&sm.V[r * PV + cc]) = x;
+        }
+        for (int i = tid; i < DK; i += NT) sm.lam[i] = p.lam[widx * DK + i];
+        __syncthreads();
+
+        // X = Kh S^T, Y = Qh S^T (rows: tokens)
+        Frag<_Float16> BS[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_frag<_Float16>(ST[2 * s], ST[2 * s + 1]);
+        f32x4_t X[4], Y[4], D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            X[t] = Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * t + l16;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int c0 = 32 * s + 4 * lq, c1 = c0 + 16;
+                mma_k32(X[t], load_frag2<_Float16>(&sm.Kh[KL::off(row, c0)], &sm.Kh[KL::off(row, c1)]), BS[s]);
+                mma_k32(Y[t], load_frag2<_Float16>(&sm.Qh[KL::off(row, c0)], &sm.Qh[KL::off(row, c1)]), BS[s]);
+            }
+        }
+        // R = V - X, Delta = Mmat R, O = Y + P Delta
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) X[t][m] = sm.V[(16 * t + 4 * lq + m) * PV + 16 * wave + l16] - X[t][m];
+        const Frag<_Float16> BR0 = pack_frag<_Float16>(X[0], X[1]), BR1 = pack_frag<_Float16>(X[2], X[3]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const _Float16* mrow = &sm.M[(16 * t + l16) * PC + 4 * lq];
+            mma_k32(D[t], load_frag2<_Float16>(mrow, mrow + 16), BR0);
+            mma_k32(D[t], load_frag2<_Float16>(mrow + 32, mrow + 48), BR1);
+        }
+        const Frag<_Float16> BD0 = pack_frag<_Float16>(D[0], D[1]), BD1 = pack_frag<_Float16>(D[2], D[3]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4_t O = Y[t];
+            const _Float16* prow = &sm.P[(16 * t + l16) * PC + 4 * lq];
+            mma_k32(O, load_frag2<_Float16>(prow, prow + 16), BD0);
+            mma_k32(O, load_frag2<_Float16>(prow + 32, prow + 48), BD1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * t + 4 * lq + m;
+                if (r < len) static_cast<TO*>(p.o)[((bos + r) * H + h) * DV + dvw + l16] = from_f32<TO>(O[m]);
+            }
+        }
+        // S^T <- Diag(lam) S^T + Kd^T Delta
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            f32x4_t acc;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = ST[j][m] * sm.lam[16 * j + 4 * lq + m];
+            mma_k32(acc, load_kt<_Float16, DK>(sm.Kd, 4 * lq, 16 + 4 * lq, j), BD0);
+            mma_k32(acc, load_kt<_Float16, DK>(sm.Kd, 32 + 4 * lq, 48 + 4 * lq, j), BD1);
+            ST[j] = acc;
+        }
+    }
+    if (p.hT) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    }
+}
+
 // -------------------------------------------------------------------- launchers
-KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen) {
+KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     KdaLayout w{};
     w.nc_bound = varlen ? ((long)T + (long)N * 63) / 64 : (long)B * (((long)T + 63) / 64);
     const size_t units = (size_t)w.nc_bound * H;
     w.off_base = 0;
     w.off_m = al(varlen ? (size_t)(N + 1) * 4 : 0);
-    w.off_p = al(w.off_m + units * 4096 * 4);
-    w.off_kh = al(w.off_p + units * 4096 * 4);
-    w.off_qh = al(w.off_kh + units * 64 * dk * 4);
-    w.off_kd = al(w.off_qh + units * 64 * dk * 4);
-    w.off_lam = al(w.off_kd + units * 64 * dk * 4);
+    w.off_p = al(w.off_m + units * 4096 * elem);
+    w.off_kh = al(w.off_p + units * 4096 * elem);
+    w.off_qh = al(w.off_kh + units * 64 * dk * elem);
+    w.off_kd = al(w.off_qh + units * 64 * dk * elem);
+    w.off_lam = al(w.off_kd + units * 64 * dk * elem);
     w.total = w.off_lam + units * dk * 4;
     if (w.nc_bound == 0) w.total = al(varlen ? (size_t)(N + 1) * 4 : 0);
     return w;
@@ -382,9 +540,14 @@ static void kda_launch(const ChunkProblem& p, hipStream_t s) {
             hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK, false>), dim3((unsigned)units), dim3(256), 0, s, p);
     }
     const long pairs = (long)p.N * p.H;
-    if (pairs > 0)
-        hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                           dim3(DVT / 16 * 64), 0, s, p);
+    if (pairs > 0) {
+        if constexpr (sizeof(TIn) == 2)
+            hipLaunchKernelGGL((kda_propagate16_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                               dim3(DVT / 16 * 64), 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                               dim3(DVT / 16 * 64), 0, s, p);
+    }
 }
 
 template <typename TIn, typename TO>

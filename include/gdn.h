@@ -230,11 +230,14 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
  * gdn_kda_chunk_fwd: chunkwise forward pass, arguments as in gdn_chunk_fwd except
  *   g_log_alpha [B, T, H, dk] fp32 (16-byte aligned), log of the per-channel decay, <= 0
  *   workspace   at least gdn_kda_chunk_fwd_workspace_bytes(...) bytes: chunk_base (packed
- *               only), then fp32 [nc, H, 64, 64] Mmat and P, fp32 [nc, H, 64, dk]
- *               K * e^gamma, Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk]
- *               e^{gamma_last} (gamma: per-channel in-chunk cumulative sum of g).
- * All arithmetic is fp32 (bf16 inputs are widened on load); a bf16 o is the fp32 result
- * rounded to nearest even.
+ *               only), then op [nc, H, 64, 64] Mmat and P, op [nc, H, 64, dk] K * e^gamma,
+ *               Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk] e^{gamma_last}
+ *               (gamma: per-channel in-chunk cumulative sum of g), all row-major, with
+ *               op = fp32 for fp32 inputs and fp16 for bf16 inputs.
+ * Stage 1 computes in fp32 (bf16 inputs widened on load). Stage 2 multiplies fp32 operators
+ * on the fp32 matrix core, and for bf16 inputs fp16 operators (the state packed to fp16 as
+ * an operand, fp32 accumulation), as gdn_chunk_fwd does; a bf16 o is the fp32 result rounded
+ * to nearest even.
  */
 size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
                                          int chunk, int dtype);
