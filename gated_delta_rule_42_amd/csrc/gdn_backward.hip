@@ -26,13 +26,17 @@
 // (":" is the sum of an elementwise product over the d_v columns; Gamma[r,i] = e^{gamma_r -
 // gamma_i} for i <= r.)
 //
-// Passes, all in fp32: (0) bf16 q, k, v, dO are widened into the workspace; (1) stage 1 of
-// the forward pass (gate tables, Mmat, P) also keeping T; (2) stage 2 of the forward pass
-// keeping the state entering every chunk instead of writing o; (3) chunk_bwd_state_kernel,
-// the reverse walk, keeping dS' of every chunk and writing dh0; (4) chunk_bwd_grad_kernel,
-// every (chunk, head) on its own. The products run on the fp32 matrix core (16x16x4).
+// Passes: (0) bf16 q, k, v, dO are widened into the workspace; (1) stage 1 of the forward
+// pass in fp32 (gate tables, Mmat, P) also keeping T (and, for bf16 inputs, fp16 copies of
+// Mmat and P); (2) stage 2 of the forward pass keeping the state entering every chunk
+// instead of writing o; (3) the reverse walk, keeping dS' of every chunk and writing dh0;
+// (4) chunk_bwd_grad_kernel, every (chunk, head) on its own, fp32 on the 16x16x4 matrix core.
+// For fp32 inputs (2) and (3) run on the fp32 matrix core too; for bf16 inputs they run on
+// fp16 operands with fp32 accumulation and fp32 states (chunk_propagate_kernel<bf16>,
+// chunk_bwd_state16_kernel), the numerics of the forward pass.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_stage2.h"
 
 namespace gdn {
 
@@ -184,6 +188,204 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state_kernel(ChunkPro
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc = mfma4(sm.K[(16 * t + 4 * lq + s) * PK + 16 * j + l16], EdR[t][s], acc);
+            dST[j] = acc;
+        }
+    }
+    if (dh0) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(dh0 + srow + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+    }
+}
+
+// ------------------------------------------- reverse walk, bf16 inputs (fp16 operands)
+template <int DK, int DVT>
+struct alignas(16) BwdState16Smem {
+    using KL = KQLayout<_Float16, DK>;
+    static constexpr int PK = KL::kPitch, PC = 72, PV = DVT + 8;
+    _Float16 K[64 * PK];
+    _Float16 Q[64 * PK];
+    _Float16 M[64 * PC];
+    _Float16 P[64 * PC];
+    _Float16 dO[64 * PV];   // the work-group's d_v columns
+    float gt[128];          // e^gamma, then e^{gamma_last - gamma}
+};
+
+// Register staging of one chunk's raw bf16 K, Q, dO, fp16 Mmat, P and the gate tables, so
+// that chunk c-1's loads are in flight while chunk c is computed.
+template <int DK, int DV, int DVT>
+struct BwdState16Stage {
+    static constexpr int NT = DVT / 16 * 64;
+    static constexpr int NK = 64 * DK / 8 / NT, NM = 64 * 64 / 8 / NT, NO = 64 * DVT / 8 / NT;
+    uint4 rk[NK], rq[NK], rm[NM], rp[NM], ro[NO];
+    float4 rg;
+
+    __device__ __forceinline__ void load(const ChunkProblem& p, const uint16_t* dop, long bos, int len,
+                                         long widx, int h, int dv0, int tid) {
+        const int H = p.H;
+        const uint16_t* kp = static_cast<const uint16_t*>(p.k);
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8);
+            rk[it] = rq[it] = zero16();
+            if (r < len) {
+                const long o = ((bos + r) * H + h) * DK + 8 * cv;
+                rk[it] = *reinterpret_cast<const uint4*>(kp + o);
+                rq[it] = *reinterpret_cast<const uint4*>(qp + o);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NM; ++it) {
+            rm[it] = reinterpret_cast<const uint4*>(p.mmat16 + widx * 4096)[tid + NT * it];
+            rp[it] = reinterpret_cast<const uint4*>(p.pmat16 + widx * 4096)[tid + NT * it];
+        }
+#pragma unroll
+        for (int it = 0; it < NO; ++it) {
+            const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
+            ro[it] = r < len ? *reinterpret_cast<const uint4*>(dop + ((bos + r) * H + h) * p.dv + dv0 + 8 * cv)
+                             : zero16();
+        }
+        if (tid < 32) rg = reinterpret_cast<const float4*>(p.gates + widx * 128)[tid];
+    }
+
+    __device__ __forceinline__ void store(BwdState16Smem<DK, DVT>& sm, int tid) const {
+        using SM = BwdState16Smem<DK, DVT>;
+        using KL = typename SM::KL;
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8);
+            *reinterpret_cast<uint4*>(&sm.K[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(rk[it]);
+            *reinterpret_cast<uint4*>(&sm.Q[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(rq[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NM; ++it) {
+            const int vi = tid + NT * it, r = vi / 8, cv = vi % 8;
+            *reinterpret_cast<uint4*>(&sm.M[r * SM::PC + 8 * cv]) = rm[it];
+            *reinterpret_cast<uint4*>(&sm.P[r * SM::PC + 8 * cv]) = rp[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NO; ++it) {
+            const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
+            *reinterpret_cast<uint4*>(&sm.dO[r * SM::PV + 8 * cv]) = to_operand16<uint16_t>(ro[it]);
+        }
+        if (tid < 32) reinterpret_cast<float4*>(sm.gt)[tid] = rg;
+    }
+};
+
+// The reverse walk of chunk_bwd_state_kernel on the fp16 matrix core (16x16x32, fp32
+// accumulation, the state gradient kept in fp32 and packed to fp16 as an operand), reading the
+// raw bf16 inputs and fp16 Mmat, P. The transposed operands (P^T, Mmat^T, Q^T, K^T and dO as a
+// right operand) use the transposing LDS read; k is the chunk's token index throughout, in the
+// slot order of fragments packed from two accumulator tiles.
+template <int DK, int DV, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state16_kernel(ChunkProblem p, const uint16_t* dop,
+                                                                           const float* dhT, float* dstates,
+                                                                           float* dh0) {
+    using SM = BwdState16Smem<DK, DVT>;
+    using KL = typename SM::KL;
+    constexpr int PC = SM::PC, PV = SM::PV, NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long pair = blockIdx.x / NTILE;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + 63) / 64;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+    auto chunk_len = [&](long jc) { return (int)min(64L, seos - (sbos + jc * 64)); };
+
+    f32x4_t dST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        if (dhT) {
+            const float4 x = *reinterpret_cast<const float4*>(dhT + srow + 16 * j);
+            dST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+        } else {
+            dST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    BwdState16Stage<DK, DV, DVT> stage;
+    if (nchunks > 0)
+        stage.load(p, dop, sbos + (nchunks - 1) * 64, chunk_len(nchunks - 1), (cbase + nchunks - 1) * H + h, h, dv0, tid);
+
+    for (long jc = nchunks - 1; jc >= 0; --jc) {
+        const long widx = (cbase + jc) * H + h;
+        __syncthreads();  // the previous chunk's LDS data is dead
+        stage.store(sm, tid);
+        __syncthreads();
+        if (jc > 0) stage.load(p, dop, sbos + (jc - 1) * 64, chunk_len(jc - 1), widx - H, h, dv0, tid);
+
+        float* ds = dstates + (widx * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(ds + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+
+        // Z = K dS'^T
+        Frag<_Float16> BS[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_frag<_Float16>(dST[2 * s], dST[2 * s + 1]);
+        f32x4_t Z[4], dD[4], dR[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            Z[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * t + l16;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int c0 = 32 * s + 4 * lq;
+                mma_k32(Z[t], load_frag2<_Float16>(&sm.K[KL::off(row, c0)], &sm.K[KL::off(row, c0 + 16)]), BS[s]);
+            }
+        }
+        // dO as a right operand (k = token), plain and scaled by e^gamma
+        Frag<_Float16> DF[2], EDF[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            DF[hf] = load_frag_t<_Float16>(&sm.dO[(32 * hf + 4 * lq) * PV + 16 * wave],
+                                           &sm.dO[(32 * hf + 16 + 4 * lq) * PV + 16 * wave], PV);
+            const f16x8_t x = __builtin_bit_cast(f16x8_t, DF[hf].v);
+            const float4 e0 = *reinterpret_cast<const float4*>(&sm.gt[32 * hf + 4 * lq]);
+            const float4 e1 = *reinterpret_cast<const float4*>(&sm.gt[32 * hf + 16 + 4 * lq]);
+            EDF[hf] = pack_frag<_Float16>(
+                f32x4_t{e0.x * (float)x[0], e0.y * (float)x[1], e0.z * (float)x[2], e0.w * (float)x[3]},
+                f32x4_t{e1.x * (float)x[4], e1.y * (float)x[5], e1.z * (float)x[6], e1.w * (float)x[7]});
+        }
+        // dDelta = P^T dO + Ed Z;  dR = Mmat^T dDelta
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dD[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                mma_k32(dD[t], load_frag_t<_Float16>(&sm.P[(32 * hf + 4 * lq) * PC + 16 * t],
+                                                     &sm.P[(32 * hf + 16 + 4 * lq) * PC + 16 * t], PC), DF[hf]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dD[t][m] += sm.gt[64 + 16 * t + 4 * lq + m] * Z[t][m];
+        }
+        const Frag<_Float16> BD0 = pack_frag<_Float16>(dD[0], dD[1]), BD1 = pack_frag<_Float16>(dD[2], dD[3]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            mma_k32(dR[t], load_frag_t<_Float16>(&sm.M[(4 * lq) * PC + 16 * t], &sm.M[(16 + 4 * lq) * PC + 16 * t], PC), BD0);
+            mma_k32(dR[t], load_frag_t<_Float16>(&sm.M[(32 + 4 * lq) * PC + 16 * t], &sm.M[(48 + 4 * lq) * PC + 16 * t], PC), BD1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dR[t][m] *= -sm.gt[16 * t + 4 * lq + m];
+        }
+        // dS'^T <- lam dS'^T + Q^T (E dO) - K^T (E dR)
+        const Frag<_Float16> BR0 = pack_frag<_Float16>(dR[0], dR[1]), BR1 = pack_frag<_Float16>(dR[2], dR[3]);
+        const float lam = sm.gt[63];
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            f32x4_t acc = dST[j] * lam;
+            mma_k32(acc, load_kt<_Float16, DK>(sm.Q, 4 * lq, 16 + 4 * lq, j), EDF[0]);
+            mma_k32(acc, load_kt<_Float16, DK>(sm.Q, 32 + 4 * lq, 48 + 4 * lq, j), EDF[1]);
+            mma_k32(acc, load_kt<_Float16, DK>(sm.K, 4 * lq, 16 + 4 * lq, j), BR0);
+            mma_k32(acc, load_kt<_Float16, DK>(sm.K, 32 + 4 * lq, 48 + 4 * lq, j), BR1);
             dST[j] = acc;
         }
     }
@@ -543,7 +745,9 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
         w.off_k32 = al(w.off_q32 + tok * dk * 4);
         w.off_v32 = al(w.off_k32 + tok * dk * 4);
         w.off_do32 = al(w.off_v32 + tok * dv * 4);
-        end = w.off_do32 + tok * dv * 4;
+        w.off_m16 = al(w.off_do32 + tok * dv * 4);
+        w.off_p16 = al(w.off_m16 + units * 4096 * 2);
+        end = w.off_p16 + units * 4096 * 2;
     }
     w.total = end;
     return w;
@@ -554,9 +758,19 @@ static void bwd_launch(const BwdProblem& b, hipStream_t s) {
     const ChunkProblem& p = b.f;
     constexpr int DVT = 32;
     const long pairs = (long)p.N * p.H;
-    if (pairs > 0)
-        hipLaunchKernelGGL((chunk_bwd_state_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                           dim3(DVT / 16 * 64), 0, s, p, b.do32, b.dhT, b.dstates, b.dh0);
+    if (pairs > 0) {
+        if (p.mmat16) {   // bf16 inputs: raw inputs, fp16 operands
+            ChunkProblem r = p;
+            r.q = b.q_in;
+            r.k = b.k_in;
+            hipLaunchKernelGGL((chunk_bwd_state16_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                               dim3(DVT / 16 * 64), 0, s, r, static_cast<const uint16_t*>(b.do_in), b.dhT,
+                               b.dstates, b.dh0);
+        } else {
+            hipLaunchKernelGGL((chunk_bwd_state_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                               dim3(DVT / 16 * 64), 0, s, p, b.do32, b.dhT, b.dstates, b.dh0);
+        }
+    }
     const long units = p.nc_bound * p.H;
     if (units > 0)
         hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
@@ -588,7 +802,15 @@ hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
     }
     hipError_t e = launch_chunk_prepare(p, s);
     if (e != hipSuccess) return e;
-    e = launch_chunk_propagate(p, s);
+    if (p.mmat16) {   // bf16 inputs: the state recompute on fp16 operands from the raw inputs
+        ChunkProblem r = p;
+        r.q = b.q_in;
+        r.k = b.k_in;
+        r.v = b.v_in;
+        e = launch_chunk_propagate_f16(r, s);
+    } else {
+        e = launch_chunk_propagate(p, s);
+    }
     if (e != hipSuccess) return e;
     if (b.grad_bf16) bwd_dispatch<uint16_t>(b, s); else bwd_dispatch<float>(b, s);
     return hipGetLastError();

@@ -284,6 +284,10 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
                 if (p.tmat) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
+                if (p.mmat16) {  // fp16 copies for the fp16-operand kernels of the backward pass
+                    store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
+                    store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
+                }
             } else {
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
@@ -1013,6 +1017,29 @@ static void prop_dispatch(const ChunkProblem& p, hipStream_t s) {
     } else {
         if (p.dv == 64) prop_launch<TIn, TO, 128, 64>(p, s); else prop_launch<TIn, TO, 128, 128>(p, s);
     }
+}
+
+// Stage 2 on fp16 operands from raw bf16 q, k, v and fp16 row-major Mmat, P (p.mmat16,
+// p.pmat16), register-staged: the state recompute of the backward pass for bf16 inputs.
+hipError_t launch_chunk_propagate_f16(const ChunkProblem& p, hipStream_t s) {
+    ChunkProblem q = p;
+    q.mmat = p.mmat16;
+    q.pmat = p.pmat16;
+    constexpr int DVT = 32;
+    const long pairs = (long)p.N * p.H;
+    if (pairs > 0) {
+        auto go = [&](auto kern, int dv) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)(pairs * (dv / DVT))), dim3(DVT / 16 * 64), 0, s, q);
+        };
+        if (p.dk == 64) {
+            if (p.dv == 64) go(chunk_propagate_kernel<uint16_t, float, 64, 64, DVT>, 64);
+            else go(chunk_propagate_kernel<uint16_t, float, 64, 128, DVT>, 128);
+        } else {
+            if (p.dv == 64) go(chunk_propagate_kernel<uint16_t, float, 128, 64, DVT>, 64);
+            else go(chunk_propagate_kernel<uint16_t, float, 128, 128, DVT>, 128);
+        }
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s) {
