@@ -729,6 +729,350 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdProblem bp) {
     }
 }
 
+// ------------------------------------------- per-chunk gradients, bf16 inputs (fp16 operands)
+// The products of chunk_bwd_grad_kernel on the fp16 matrix core (16x16x32, fp32 accumulation):
+// every operand tile is staged in LDS as fp16 (the raw bf16 inputs, the fp32 operators, state
+// and state gradient rounded once), results accumulate in fp32. k runs in the slot order of
+// fragments packed from two accumulator tiles (4lq + 0..3, then 16 + 4lq + 0..3 of each
+// 32-wide k slice): an operand stored along k is read as two 8-byte runs (load_frag2), one
+// stored across k with the transposing read (load_frag_t). d_v is processed in 32-column
+// slices so that the d_v contractions fill whole 32-wide k slices.
+template <int DK>
+struct alignas(16) Grad16Smem {
+    static constexpr int PK = DK + 8, PT = 72, PS = DK + 8, PV = 40;
+    _Float16 K[64 * PK];
+    _Float16 Q[64 * PK];
+    _Float16 T[64 * PT];
+    _Float16 P[64 * PT];
+    union {
+        struct {                 // one 32-column d_v slice
+            _Float16 S[32 * PS];   // rows of the entering state
+            _Float16 dS[32 * PS];  // the same rows of dS'
+            _Float16 V[64 * PV], dO[64 * PV], EdO[64 * PV], R[64 * PV], BR[64 * PV];
+            _Float16 D[64 * PV], EdD[64 * PV], dD[64 * PV], EdR[64 * PV];
+        } sl;
+        struct {
+            _Float16 X1[64 * PT];  // dT, then dG
+            _Float16 X2[64 * PT];  // dT T^T
+            _Float16 X3[64 * PT];  // dPg
+        } cc;
+    } u;
+    float gam[64], eg[64], ed[64], beta[64];
+    float colg[4][64], colb[4][64];
+    float rowg[64], rowb[64];
+    float tailw[4];
+};
+
+template <typename TO, int DK, int DV>
+__global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
+    using SM = Grad16Smem<DK>;
+    constexpr int PK = SM::PK, PT = SM::PT, PS = SM::PS, PV = SM::PV, NKB = DK / 16, NKS = DK / 32;
+    __shared__ SM sm;
+    const ChunkProblem& p = bp.f;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const long unit = blockIdx.x, c = unit / H;
+    const int h = (int)(unit % H);
+    long bos;
+    int len;
+    if (!locate_chunk(p, c, bos, len)) return;   // uniform over the work-group
+    const long widx = c * H + h;
+    const uint16_t* kp = static_cast<const uint16_t*>(bp.k_in);
+    const uint16_t* qp = static_cast<const uint16_t*>(bp.q_in);
+    const uint16_t* vp = static_cast<const uint16_t*>(bp.v_in);
+    const uint16_t* dop = static_cast<const uint16_t*>(bp.do_in);
+    auto pack8 = [](float4 a, float4 b) {
+        return make_uint4(pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w));
+    };
+
+    for (int i = tid; i < 64 * DK / 8; i += 256) {
+        const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+        uint4 kv = zero16(), qv = kv;
+        if (r < len) {
+            kv = to_operand16<uint16_t>(*reinterpret_cast<const uint4*>(kp + ((bos + r) * H + h) * DK + cc));
+            qv = to_operand16<uint16_t>(*reinterpret_cast<const uint4*>(qp + ((bos + r) * H + h) * DK + cc));
+        }
+        *reinterpret_cast<uint4*>(&sm.K[r * PK + cc]) = kv;
+        *reinterpret_cast<uint4*>(&sm.Q[r * PK + cc]) = qv;
+    }
+    for (int i = tid; i < 64 * 8; i += 256) {
+        const int r = i / 8, cc = 8 * (i % 8);
+        const float* tp = p.tmat + widx * 4096 + r * 64 + cc;
+        const float* pq = static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc;
+        *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) =
+            pack8(*reinterpret_cast<const float4*>(tp), *reinterpret_cast<const float4*>(tp + 4));
+        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) =
+            pack8(*reinterpret_cast<const float4*>(pq), *reinterpret_cast<const float4*>(pq + 4));
+    }
+    if (wave == 0) {
+        const long o = (bos + lane) * H + h;
+        const float gr = lane < len ? p.g[o] : 0.f;
+        sm.beta[lane] = lane < len ? p.beta[o] : 0.f;
+        sm.gam[lane] = wave_inclusive_sum(gr);
+        sm.eg[lane] = p.gates[widx * 128 + lane];
+        sm.ed[lane] = p.gates[widx * 128 + 64 + lane];
+    }
+
+    const int row = 16 * wave + l16;   // this lane's row as a left operand
+    // left operand read along k (row `r` of a row-major tile) and right operand read across k
+    auto rowf = [&](const _Float16* t, int pitch, int r, int k0) {
+        return load_frag2<_Float16>(&t[r * pitch + k0 + 4 * lq], &t[r * pitch + k0 + 16 + 4 * lq]);
+    };
+    auto colf = [&](const _Float16* t, int pitch, int k0, int c0) {
+        return load_frag_t<_Float16>(&t[(k0 + 4 * lq) * pitch + c0], &t[(k0 + 16 + 4 * lq) * pitch + c0], pitch);
+    };
+    f32x4_t dP[4], dM[4], dQ1[NKB], dK1[NKB];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dP[t] = dM[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) dQ1[j] = dK1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float gacc[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma of rows 16 wave + 4 lq + m
+    float tail = 0.f;                       // lam (dS' : S) + sum z, this thread's share
+    auto& sl = sm.u.sl;
+
+    for (int js = 0; js < DV / 32; ++js) {
+        const int dv0 = 32 * js;
+        __syncthreads();  // the previous slice is dead (first slice: the loads above are done)
+        const float lam = sm.eg[63];
+        for (int i = tid; i < 32 * DK / 8; i += 256) {
+            const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const float* sp = p.states + (widx * DV + dv0 + r) * DK + cc;
+            const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
+            const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
+            const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+            *reinterpret_cast<uint4*>(&sl.S[r * PS + cc]) = pack8(s0, s1);
+            *reinterpret_cast<uint4*>(&sl.dS[r * PS + cc]) = pack8(d0, d1);
+            tail += lam * (s0.x * d0.x + s0.y * d0.y + s0.z * d0.z + s0.w * d0.w +
+                           s1.x * d1.x + s1.y * d1.y + s1.z * d1.z + s1.w * d1.w);
+        }
+        {
+            const int r = tid >> 2, cc = 8 * (tid & 3);
+            uint4 v = zero16(), d = v;
+            if (r < len) {
+                v = *reinterpret_cast<const uint4*>(vp + ((bos + r) * H + h) * DV + dv0 + cc);
+                d = *reinterpret_cast<const uint4*>(dop + ((bos + r) * H + h) * DV + dv0 + cc);
+            }
+            const uint4 d16 = to_operand16<uint16_t>(d);
+            *reinterpret_cast<uint4*>(&sl.V[r * PV + cc]) = to_operand16<uint16_t>(v);
+            *reinterpret_cast<uint4*>(&sl.dO[r * PV + cc]) = d16;
+            const f16x8_t dh = __builtin_bit_cast(f16x8_t, d16);
+            const float e = sm.eg[r];
+            *reinterpret_cast<uint4*>(&sl.EdO[r * PV + cc]) =
+                pack8(make_float4(e * (float)dh[0], e * (float)dh[1], e * (float)dh[2], e * (float)dh[3]),
+                      make_float4(e * (float)dh[4], e * (float)dh[5], e * (float)dh[6], e * (float)dh[7]));
+        }
+        __syncthreads();
+
+        // X = K S^T, Y = Q S^T, Z = K dS'^T for this wave's rows and the slice's two column tiles
+        f32x4_t X[2], Y[2], Z[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) X[nt] = Y[nt] = Z[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const Frag<_Float16> ak = rowf(sm.K, PK, row, 32 * s), aq = rowf(sm.Q, PK, row, 32 * s);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const Frag<_Float16> bs = rowf(sl.S, PS, 16 * nt + l16, 32 * s), bd = rowf(sl.dS, PS, 16 * nt + l16, 32 * s);
+                mma_k32(X[nt], ak, bs);
+                mma_k32(Y[nt], aq, bs);
+                mma_k32(Z[nt], ak, bd);
+            }
+        }
+        float EX[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
+                EX[nt][m] = sm.eg[r] * X[nt][m];
+                const float rv = (float)sl.V[r * PV + v] - EX[nt][m];
+                sl.R[r * PV + v] = (_Float16)rv;
+                sl.BR[r * PV + v] = (_Float16)(sm.beta[r] * rv);
+                gacc[m] += (float)sl.EdO[r * PV + v] * Y[nt][m];
+            }
+        __syncthreads();
+
+        // Delta = T (beta R), dDelta = P^T dO + Ed Z
+        f32x4_t Dl[2], dDl[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            Dl[nt] = dDl[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < 64; k0 += 32) {
+                mma_k32(Dl[nt], rowf(sm.T, PT, row, k0), colf(sl.BR, PV, k0, 16 * nt));
+                mma_k32(dDl[nt], colf(sm.P, PT, k0, 16 * wave), colf(sl.dO, PV, k0, 16 * nt));
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
+                const float z = sm.ed[r] * Dl[nt][m] * Z[nt][m];
+                dDl[nt][m] += sm.ed[r] * Z[nt][m];
+                gacc[m] -= z;
+                tail += z;
+                sl.D[r * PV + v] = (_Float16)Dl[nt][m];
+                sl.EdD[r * PV + v] = (_Float16)(sm.ed[r] * Dl[nt][m]);
+                sl.dD[r * PV + v] = (_Float16)dDl[nt][m];
+            }
+        __syncthreads();
+
+        // dR = diag(beta) T^T dDelta (= dV)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x4_t dRl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(dRl, colf(sm.T, PT, k0, 16 * wave), colf(sl.dD, PV, k0, 16 * nt));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
+                const float d = sm.beta[r] * dRl[m];
+                gacc[m] -= d * EX[nt][m];
+                sl.EdR[r * PV + v] = (_Float16)(-sm.eg[r] * d);
+                if (r < len) store_elem<TO>(static_cast<TO*>(bp.dv) + ((bos + r) * H + h) * DV + dv0 + v, d);
+            }
+        }
+        __syncthreads();
+
+        // dP += dO Delta^T, dMmat += dDelta R^T, dQ1 += E dO S, dK1 += -E dR S + Ed Delta dS'
+        {
+            const Frag<_Float16> ao = rowf(sl.dO, PV, row, 0), ad = rowf(sl.dD, PV, row, 0);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                mma_k32(dP[ct], ao, rowf(sl.D, PV, 16 * ct + l16, 0));
+                mma_k32(dM[ct], ad, rowf(sl.R, PV, 16 * ct + l16, 0));
+            }
+            const Frag<_Float16> a1 = rowf(sl.EdO, PV, row, 0), a2 = rowf(sl.EdR, PV, row, 0),
+                                 a3 = rowf(sl.EdD, PV, row, 0);
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) {
+                const Frag<_Float16> bS = colf(sl.S, PS, 0, 16 * j), bdS = colf(sl.dS, PS, 0, 16 * j);
+                mma_k32(dQ1[j], a1, bS);
+                mma_k32(dK1[j], a2, bS);
+                mma_k32(dK1[j], a3, bdS);
+            }
+        }
+    }
+    __syncthreads();  // slice buffers are dead; their space becomes X1, X2, X3
+
+    // -- dPg (X3) and the P terms of dgamma; dT (X1) and the Mmat term of dbeta
+    float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, dbrow[4] = {0.f, 0.f, 0.f, 0.f};
+    float colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};   // column 16 ct + l16
+    auto& cc = sm.u.cc;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const int col = 16 * ct + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            float dpg = 0.f;
+            if (col <= r) {
+                const float x = dP[ct][m] * (float)sm.P[r * PT + col];
+                rowacc[m] += x;
+                colg[ct] -= x;
+                dpg = dP[ct][m] * __expf(sm.gam[r] - sm.gam[col]);
+            }
+            cc.X3[r * PT + col] = (_Float16)dpg;
+            colb[ct] += dM[ct][m] * (float)sm.T[r * PT + col];
+            cc.X1[r * PT + col] = (_Float16)(dM[ct][m] * sm.beta[col]);
+        }
+    }
+    __syncthreads();
+    // -- X2 = dT T^T
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(acc, rowf(cc.X1, PT, row, k0), rowf(sm.T, PT, 16 * ct + l16, k0));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cc.X2[(16 * wave + 4 * lq + m) * PT + 16 * ct + l16] = (_Float16)acc[m];
+    }
+    __syncthreads();
+    // -- dA = strict_lower(-T^T X2); with G = K K^T: the A terms of dbeta and dgamma, dG into X1
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4_t ta = {0.f, 0.f, 0.f, 0.f}, G = ta;
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(ta, colf(sm.T, PT, k0, 16 * wave), colf(cc.X2, PT, k0, 16 * ct));
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) mma_k32(G, rowf(sm.K, PK, row, 32 * s), rowf(sm.K, PK, 16 * ct + l16, 32 * s));
+        const int col = 16 * ct + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            float dg = 0.f;
+            if (col < r) {
+                const float da = -ta[m], gm = __expf(sm.gam[r] - sm.gam[col]);
+                const float ag = G[m] * gm;
+                dbrow[m] += da * ag;
+                const float aa = da * sm.beta[r] * ag;
+                rowacc[m] += aa;
+                colg[ct] -= aa;
+                dg = da * sm.beta[r] * gm;
+            }
+            cc.X1[r * PT + col] = (_Float16)dg;
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const float g = sum_lq(colg[ct]), b = sum_lq(colb[ct]);
+        if (lq == 0) {
+            sm.colg[wave][16 * ct + l16] = g;
+            sm.colb[wave][16 * ct + l16] = b;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float g = sum_l16(gacc[m] + rowacc[m]), b = sum_l16(dbrow[m]);
+        if (l16 == 0) {
+            sm.rowg[16 * wave + 4 * lq + m] = g;
+            sm.rowb[16 * wave + 4 * lq + m] = b;
+        }
+    }
+    {
+        const float t = sum_l16(sum_lq(tail));
+        if (lane == 0) sm.tailw[wave] = t;
+    }
+    __syncthreads();
+
+    // -- dQ = dQ1 + dPg K, dK = dK1 + dPg^T Q + dG K + dG^T K
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        f32x4_t aq = dQ1[j], ak = dK1[j];
+#pragma unroll
+        for (int k0 = 0; k0 < 64; k0 += 32) {
+            const Frag<_Float16> bK = colf(sm.K, PK, k0, 16 * j), bQ = colf(sm.Q, PK, k0, 16 * j);
+            mma_k32(aq, rowf(cc.X3, PT, row, k0), bK);
+            mma_k32(ak, colf(cc.X3, PT, k0, 16 * wave), bQ);
+            mma_k32(ak, rowf(cc.X1, PT, row, k0), bK);
+            mma_k32(ak, colf(cc.X1, PT, k0, 16 * wave), bK);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * wave + 4 * lq + m;
+            if (r < len) {
+                const long o = ((bos + r) * H + h) * DK + 16 * j + l16;
+                store_elem<TO>(static_cast<TO*>(bp.dq) + o, aq[m]);
+                store_elem<TO>(static_cast<TO*>(bp.dk) + o, ak[m]);
+            }
+        }
+    }
+    // -- dg = reverse cumulative sum of dgamma; dbeta
+    if (wave == 0) {
+        const int r = 63 - lane;
+        float dgam = sm.rowg[r] + ((sm.colg[0][r] + sm.colg[1][r]) + (sm.colg[2][r] + sm.colg[3][r]));
+        if (r == 63) dgam += (sm.tailw[0] + sm.tailw[1]) + (sm.tailw[2] + sm.tailw[3]);
+        const float x = wave_inclusive_sum(dgam);
+        if (r < len) {
+            bp.dg[(bos + r) * H + h] = x;
+            bp.dbeta[(bos + r) * H + h] =
+                sm.rowb[r] + ((sm.colb[0][r] + sm.colb[1][r]) + (sm.colb[2][r] + sm.colb[3][r]));
+        }
+    }
+}
+
 // -------------------------------------------------------------------- launchers
 BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -772,8 +1116,12 @@ static void bwd_launch(const BwdProblem& b, hipStream_t s) {
         }
     }
     const long units = p.nc_bound * p.H;
-    if (units > 0)
-        hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+    if (units > 0) {
+        if (p.mmat16)
+            hipLaunchKernelGGL((chunk_bwd_grad16_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+        else
+            hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+    }
 }
 
 template <typename TO>
