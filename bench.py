@@ -24,9 +24,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GDN chunk-fwd tokens/s + %MFMA peak (B4 H16 T2048 d128); decode %HBM BW"
-PEAK_BF16_FLOPS = 2516.6e12   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (MI355X, ~2.5 PF)
+PEAK_BF16_FLOPS = 2516.6e12   # 256 CU x 2.4 GHz x 4096 dense bf16/fp16 FLOP/clk/CU (MI355X, ~2.5 PF)
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
-PEAK_FP32_MFMA = 157.3e12     # dense fp32 matrix (MI355X)
 CHUNK = 64
 
 
@@ -45,8 +44,8 @@ def fwd_counts(dk, dv, C=CHUNK, elem=2):
 
 
 def bwd_counts(dk, dv, C=CHUNK):
-    """FLOP per token-head of the two backward kernels of this implementation (fp32 matrix
-    core): the reverse walk (K dS'^T, P^T dO, Mmat^T dDelta, the two rank-C state-gradient
+    """Algorithmic FLOP per token-head of the two backward kernels of this implementation
+    (the second fp16 MFMA of operands carried as hi + lo pairs is not counted): the reverse walk (K dS'^T, P^T dO, Mmat^T dDelta, the two rank-C state-gradient
     updates) and the per-chunk gradients (K S^T, Q S^T, K dS'^T, Mmat R, P^T dO, Mmat^T dDelta,
     dO Delta^T, dDelta R^T, E dO S, E dR S, Ed Delta dS', dT T^T, T^T X, K K^T, dPg K,
     dPg^T Q, dG K, dG^T K)."""
@@ -384,14 +383,17 @@ def main():
         th = b["B"] * b["T"] * b["H"]
         ms = b["wall_s"] / args.bwd_steps * 1e3
         c = bwd_counts(b["dk"], b["dv"])
+        fl = (c["state_flops"] + c["grad_flops"]) * th
         out["bwd"] = {"workload": "chunkwise backward B4 H16 T2048 d_k=d_v=128 chunk 64, bf16 "
-                                  "q/k/v/dO and gradients, fp32 arithmetic, no h0 / dhT",
+                                  "q/k/v/dO and gradients, fp16 matrix-core operands with fp32 "
+                                  "accumulation, states and gate gradients, no h0 / dhT",
                       "ms_per_step": ms, "ms_per_step_median": median(b["step_ms"]),
                       "tokens_per_s": b["B"] * b["T"] / (ms / 1e3),
-                      "fp32_mfma_tflops_issued": (c["state_flops"] + c["grad_flops"]) * th / (ms / 1e3) / 1e12,
+                      "tflops": fl / (ms / 1e3) / 1e12,
+                      "mfma_frac": fl / (ms / 1e3) / PEAK_BF16_FLOPS,
                       "grad_kernel_flops_per_launch": c["grad_flops"] * th,
                       "state_kernel_flops_per_launch": c["state_flops"] * th,
-                      "fp32_mfma_peak_tflops": PEAK_FP32_MFMA / 1e12}
+                      "mfma_peak_tflops": PEAK_BF16_FLOPS / 1e12}
         if args.only == "bwd":
             out["value"] = b["B"] * b["T"] / (ms / 1e3)
             out["ms_per_step"] = ms

@@ -198,20 +198,14 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     gdn::BwdProblem b{};
     gdn::ChunkProblem& P = b.f;
     b.q_in = q; b.k_in = k; b.v_in = v; b.do_in = d_o;
-    if (bf16 && tokens > 0) {
-        b.q32 = reinterpret_cast<float*>(base + w.off_q32);
-        b.k32 = reinterpret_cast<float*>(base + w.off_k32);
-        b.v32 = reinterpret_cast<float*>(base + w.off_v32);
-        b.do32w = reinterpret_cast<float*>(base + w.off_do32);
-    }
-    P.q = bf16 ? b.q32 : q;
-    P.k = bf16 ? b.k32 : k;
-    P.v = bf16 ? b.v32 : v;
-    b.do32 = bf16 ? b.do32w : static_cast<const float*>(d_o);
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    b.do32 = bf16 ? nullptr : static_cast<const float*>(d_o);
     P.g = g_log_alpha; P.beta = beta; P.h0 = h0; P.o = nullptr; P.hT = nullptr;
     P.cu_seqlens = cu_seqlens;
     P.B = B; P.T = T; P.H = H; P.dk = dk; P.dv = dv; P.N = N;
-    P.bf16 = 0; P.o_bf16 = 0;
+    P.bf16 = bf16; P.o_bf16 = 0;
     P.nc_bound = w.fwd.nc_bound;
     P.nc_per_seq = (T + 63) / 64;
     const bool any = w.fwd.nc_bound > 0;

@@ -26,31 +26,20 @@
 // (":" is the sum of an elementwise product over the d_v columns; Gamma[r,i] = e^{gamma_r -
 // gamma_i} for i <= r.)
 //
-// Passes: (0) bf16 q, k, v, dO are widened into the workspace; (1) stage 1 of the forward
-// pass in fp32 (gate tables, Mmat, P) also keeping T (and, for bf16 inputs, fp16 copies of
-// Mmat and P); (2) stage 2 of the forward pass keeping the state entering every chunk
-// instead of writing o; (3) the reverse walk, keeping dS' of every chunk and writing dh0;
-// (4) chunk_bwd_grad_kernel, every (chunk, head) on its own, fp32 on the 16x16x4 matrix core.
-// For fp32 inputs (2) and (3) run on the fp32 matrix core too; for bf16 inputs they run on
-// fp16 operands with fp32 accumulation and fp32 states (chunk_propagate_kernel<bf16>,
-// chunk_bwd_state16_kernel), the numerics of the forward pass.
+// Passes: (1) stage 1 of the forward pass (gate tables, Mmat, P; gram products accumulated
+// in fp32) also keeping T in fp32, row-major (for bf16 inputs, read straight from the raw
+// inputs: fp32 P and fp16 copies of Mmat and P, row-major); (2) stage 2 of the forward pass
+// keeping the state entering every chunk instead of writing o; (3) the reverse walk, keeping
+// dS' of every chunk and writing dh0; (4) every (chunk, head) on its own. fp32 inputs run
+// (2)-(4) on the fp32 16x16x4 matrix core (chunk_propagate_kernel<float>,
+// chunk_bwd_state_kernel, chunk_bwd_grad_kernel). bf16 inputs run them on fp16 operands
+// with fp32 accumulation and fp32 states (chunk_propagate_kernel<bf16>,
+// chunk_bwd_state16_kernel, chunk_bwd_grad16_kernel), the numerics of the forward pass.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_stage2.h"
 
 namespace gdn {
-
-// ------------------------------------------------------------------ widening
-__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src,
-                                                         float* __restrict__ dst, long n8) {
-    for (long i = blockIdx.x * 256L + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
-        const uint4 raw = reinterpret_cast<const uint4*>(src)[i];
-        auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
-        auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
-        reinterpret_cast<float4*>(dst)[2 * i] = make_float4(lo(raw.x), hi(raw.x), lo(raw.y), hi(raw.y));
-        reinterpret_cast<float4*>(dst)[2 * i + 1] = make_float4(lo(raw.z), hi(raw.z), lo(raw.w), hi(raw.w));
-    }
-}
 
 // ------------------------------------------------------- reverse walk (pass 3)
 template <int DK, int DVT>
@@ -731,30 +720,35 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdProblem bp) {
 
 // ------------------------------------------- per-chunk gradients, bf16 inputs (fp16 operands)
 // The products of chunk_bwd_grad_kernel on the fp16 matrix core (16x16x32, fp32 accumulation):
-// every operand tile is staged in LDS as fp16 (the raw bf16 inputs, the fp32 operators, state
-// and state gradient rounded once), results accumulate in fp32. k runs in the slot order of
-// fragments packed from two accumulator tiles (4lq + 0..3, then 16 + 4lq + 0..3 of each
-// 32-wide k slice): an operand stored along k is read as two 8-byte runs (load_frag2), one
-// stored across k with the transposing read (load_frag_t). d_v is processed in 32-column
-// slices so that the d_v contractions fill whole 32-wide k slices.
+// every operand tile is staged in LDS as fp16 (the raw bf16 inputs exactly, computed values
+// rounded once), results accumulate in fp32. The operands whose single rounding would dominate
+// the gradients' error (P, the state gradient, beta R, Delta, Ed Delta, dDelta where it forms
+// dV, and dPg) are carried as two fp16 tiles, hi = fp16(x) and lo = fp16(x - hi), and their
+// products take one extra MFMA per rounded factor (the lo x lo term is dropped): about 22 bits
+// of the operand survive instead of 11. k runs in the slot order of fragments packed from two
+// accumulator tiles (4lq + 0..3, then 16 + 4lq + 0..3 of each 32-wide k slice): an operand
+// stored along k is read as two 8-byte runs (load_frag2), one stored across k with the
+// transposing read (load_frag_t). d_v is processed in 32-column slices so that the d_v
+// contractions fill whole 32-wide k slices.
 template <int DK>
 struct alignas(16) Grad16Smem {
     static constexpr int PK = DK + 8, PT = 72, PS = DK + 8, PV = 40;
     _Float16 K[64 * PK];
     _Float16 Q[64 * PK];
     _Float16 T[64 * PT];
-    _Float16 P[64 * PT];
+    _Float16 P[64 * PT], Plo[64 * PT];
     union {
         struct {                 // one 32-column d_v slice
             _Float16 S[32 * PS];   // rows of the entering state
-            _Float16 dS[32 * PS];  // the same rows of dS'
-            _Float16 V[64 * PV], dO[64 * PV], EdO[64 * PV], R[64 * PV], BR[64 * PV];
-            _Float16 D[64 * PV], EdD[64 * PV], dD[64 * PV], EdR[64 * PV];
+            _Float16 dS[32 * PS], dSlo[32 * PS];  // the same rows of dS'
+            _Float16 V[64 * PV], dO[64 * PV], EdO[64 * PV], R[64 * PV], BR[64 * PV], BRlo[64 * PV];
+            _Float16 D[64 * PV], Dlo[64 * PV], EdD[64 * PV], EdDlo[64 * PV], dD[64 * PV], dDlo[64 * PV];
+            _Float16 EdR[64 * PV];
         } sl;
         struct {
             _Float16 X1[64 * PT];  // dT, then dG
             _Float16 X2[64 * PT];  // dT T^T
-            _Float16 X3[64 * PT];  // dPg
+            _Float16 X3[64 * PT], X3lo[64 * PT];  // dPg
         } cc;
     } u;
     float gam[64], eg[64], ed[64], beta[64];
@@ -785,6 +779,17 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     auto pack8 = [](float4 a, float4 b) {
         return make_uint4(pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w));
     };
+    // the fp16 residual x - fp16(x) of eight values whose fp16 rounding is `hi`
+    auto resid8 = [](float4 a, float4 b, uint4 hi) {
+        const f16x8_t h = __builtin_bit_cast(f16x8_t, hi);
+        return make_uint4(pack_f16x2(a.x - (float)h[0], a.y - (float)h[1]), pack_f16x2(a.z - (float)h[2], a.w - (float)h[3]),
+                          pack_f16x2(b.x - (float)h[4], b.y - (float)h[5]), pack_f16x2(b.z - (float)h[6], b.w - (float)h[7]));
+    };
+    auto split = [](float x, _Float16* hi, _Float16* lo, int o) {
+        const _Float16 h = (_Float16)x;
+        hi[o] = h;
+        lo[o] = (_Float16)(x - (float)h);
+    };
 
     for (int i = tid; i < 64 * DK / 8; i += 256) {
         const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
@@ -802,8 +807,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         const float* pq = static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc;
         *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) =
             pack8(*reinterpret_cast<const float4*>(tp), *reinterpret_cast<const float4*>(tp + 4));
-        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) =
-            pack8(*reinterpret_cast<const float4*>(pq), *reinterpret_cast<const float4*>(pq + 4));
+        const float4 p0 = *reinterpret_cast<const float4*>(pq), p1 = *reinterpret_cast<const float4*>(pq + 4);
+        const uint4 ph = pack8(p0, p1);
+        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) = ph;
+        *reinterpret_cast<uint4*>(&sm.Plo[r * PT + cc]) = resid8(p0, p1, ph);
     }
     if (wave == 0) {
         const long o = (bos + lane) * H + h;
@@ -841,8 +848,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
             const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
             const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+            const uint4 dh = pack8(d0, d1);
             *reinterpret_cast<uint4*>(&sl.S[r * PS + cc]) = pack8(s0, s1);
-            *reinterpret_cast<uint4*>(&sl.dS[r * PS + cc]) = pack8(d0, d1);
+            *reinterpret_cast<uint4*>(&sl.dS[r * PS + cc]) = dh;
+            *reinterpret_cast<uint4*>(&sl.dSlo[r * PS + cc]) = resid8(d0, d1, dh);
             tail += lam * (s0.x * d0.x + s0.y * d0.y + s0.z * d0.z + s0.w * d0.w +
                            s1.x * d1.x + s1.y * d1.y + s1.z * d1.z + s1.w * d1.w);
         }
@@ -877,6 +886,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 mma_k32(X[nt], ak, bs);
                 mma_k32(Y[nt], aq, bs);
                 mma_k32(Z[nt], ak, bd);
+                mma_k32(Z[nt], ak, rowf(sl.dSlo, PS, 16 * nt + l16, 32 * s));
             }
         }
         float EX[2][4];
@@ -888,7 +898,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 EX[nt][m] = sm.eg[r] * X[nt][m];
                 const float rv = (float)sl.V[r * PV + v] - EX[nt][m];
                 sl.R[r * PV + v] = (_Float16)rv;
-                sl.BR[r * PV + v] = (_Float16)(sm.beta[r] * rv);
+                split(sm.beta[r] * rv, sl.BR, sl.BRlo, r * PV + v);
                 gacc[m] += (float)sl.EdO[r * PV + v] * Y[nt][m];
             }
         __syncthreads();
@@ -900,8 +910,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             Dl[nt] = dDl[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32) {
-                mma_k32(Dl[nt], rowf(sm.T, PT, row, k0), colf(sl.BR, PV, k0, 16 * nt));
-                mma_k32(dDl[nt], colf(sm.P, PT, k0, 16 * wave), colf(sl.dO, PV, k0, 16 * nt));
+                const Frag<_Float16> at = rowf(sm.T, PT, row, k0), bo = colf(sl.dO, PV, k0, 16 * nt);
+                mma_k32(Dl[nt], at, colf(sl.BR, PV, k0, 16 * nt));
+                mma_k32(Dl[nt], at, colf(sl.BRlo, PV, k0, 16 * nt));
+                mma_k32(dDl[nt], colf(sm.P, PT, k0, 16 * wave), bo);
+                mma_k32(dDl[nt], colf(sm.Plo, PT, k0, 16 * wave), bo);
             }
         }
 #pragma unroll
@@ -913,9 +926,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 dDl[nt][m] += sm.ed[r] * Z[nt][m];
                 gacc[m] -= z;
                 tail += z;
-                sl.D[r * PV + v] = (_Float16)Dl[nt][m];
-                sl.EdD[r * PV + v] = (_Float16)(sm.ed[r] * Dl[nt][m]);
-                sl.dD[r * PV + v] = (_Float16)dDl[nt][m];
+                split(Dl[nt][m], sl.D, sl.Dlo, r * PV + v);
+                split(sm.ed[r] * Dl[nt][m], sl.EdD, sl.EdDlo, r * PV + v);
+                split(dDl[nt][m], sl.dD, sl.dDlo, r * PV + v);
             }
         __syncthreads();
 
@@ -924,7 +937,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         for (int nt = 0; nt < 2; ++nt) {
             f32x4_t dRl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(dRl, colf(sm.T, PT, k0, 16 * wave), colf(sl.dD, PV, k0, 16 * nt));
+            for (int k0 = 0; k0 < 64; k0 += 32) {
+                const Frag<_Float16> at = colf(sm.T, PT, k0, 16 * wave);
+                mma_k32(dRl, at, colf(sl.dD, PV, k0, 16 * nt));
+                mma_k32(dRl, at, colf(sl.dDlo, PV, k0, 16 * nt));
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
@@ -942,16 +959,19 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 mma_k32(dP[ct], ao, rowf(sl.D, PV, 16 * ct + l16, 0));
+                mma_k32(dP[ct], ao, rowf(sl.Dlo, PV, 16 * ct + l16, 0));
                 mma_k32(dM[ct], ad, rowf(sl.R, PV, 16 * ct + l16, 0));
             }
             const Frag<_Float16> a1 = rowf(sl.EdO, PV, row, 0), a2 = rowf(sl.EdR, PV, row, 0),
-                                 a3 = rowf(sl.EdD, PV, row, 0);
+                                 a3 = rowf(sl.EdD, PV, row, 0), a3l = rowf(sl.EdDlo, PV, row, 0);
 #pragma unroll
             for (int j = 0; j < NKB; ++j) {
                 const Frag<_Float16> bS = colf(sl.S, PS, 0, 16 * j), bdS = colf(sl.dS, PS, 0, 16 * j);
                 mma_k32(dQ1[j], a1, bS);
                 mma_k32(dK1[j], a2, bS);
                 mma_k32(dK1[j], a3, bdS);
+                mma_k32(dK1[j], a3l, bdS);
+                mma_k32(dK1[j], a3, colf(sl.dSlo, PS, 0, 16 * j));
             }
         }
     }
@@ -969,12 +989,12 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             const int r = 16 * wave + 4 * lq + m;
             float dpg = 0.f;
             if (col <= r) {
-                const float x = dP[ct][m] * (float)sm.P[r * PT + col];
+                const float x = dP[ct][m] * ((float)sm.P[r * PT + col] + (float)sm.Plo[r * PT + col]);
                 rowacc[m] += x;
                 colg[ct] -= x;
                 dpg = dP[ct][m] * __expf(sm.gam[r] - sm.gam[col]);
             }
-            cc.X3[r * PT + col] = (_Float16)dpg;
+            split(dpg, cc.X3, cc.X3lo, r * PT + col);
             colb[ct] += dM[ct][m] * (float)sm.T[r * PT + col];
             cc.X1[r * PT + col] = (_Float16)(dM[ct][m] * sm.beta[col]);
         }
@@ -1045,7 +1065,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         for (int k0 = 0; k0 < 64; k0 += 32) {
             const Frag<_Float16> bK = colf(sm.K, PK, k0, 16 * j), bQ = colf(sm.Q, PK, k0, 16 * j);
             mma_k32(aq, rowf(cc.X3, PT, row, k0), bK);
+            mma_k32(aq, rowf(cc.X3lo, PT, row, k0), bK);
             mma_k32(ak, colf(cc.X3, PT, k0, 16 * wave), bQ);
+            mma_k32(ak, colf(cc.X3lo, PT, k0, 16 * wave), bQ);
             mma_k32(ak, rowf(cc.X1, PT, row, k0), bK);
             mma_k32(ak, colf(cc.X1, PT, k0, 16 * wave), bK);
         }
@@ -1083,13 +1105,8 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
     w.off_states = al(w.off_t + units * 4096 * 4);
     w.off_dstates = al(w.off_states + units * dv * dk * 4);
     size_t end = w.off_dstates + units * dv * dk * 4;
-    const size_t tok = (size_t)B * T * H;
     if (bf16) {
-        w.off_q32 = al(end);
-        w.off_k32 = al(w.off_q32 + tok * dk * 4);
-        w.off_v32 = al(w.off_k32 + tok * dk * 4);
-        w.off_do32 = al(w.off_v32 + tok * dv * 4);
-        w.off_m16 = al(w.off_do32 + tok * dv * 4);
+        w.off_m16 = al(end);
         w.off_p16 = al(w.off_m16 + units * 4096 * 2);
         end = w.off_p16 + units * 4096 * 2;
     }
@@ -1136,26 +1153,12 @@ static void bwd_dispatch(const BwdProblem& b, hipStream_t s) {
 
 hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
     const ChunkProblem& p = b.f;
-    const long tok = (long)p.B * p.T * p.H;
-    if (b.q32) {   // bf16 inputs: widen q, k, v, dO
-        const void* src[4] = {b.q_in, b.k_in, b.v_in, b.do_in};
-        float* dst[4] = {b.q32, b.k32, b.v32, b.do32w};
-        const long n8[4] = {tok * p.dk / 8, tok * p.dk / 8, tok * p.dv / 8, tok * p.dv / 8};
-        for (int i = 0; i < 4; ++i) {
-            if (n8[i] == 0) continue;
-            const long blocks = min(n8[i] / 256 + 1, 4096L);
-            hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                               static_cast<const uint16_t*>(src[i]), dst[i], n8[i]);
-        }
-    }
+    // stage 1 again (bf16 inputs: straight from the raw inputs, with fp32 T and P and fp16
+    // Mmat and P, all row-major), then the state recompute
     hipError_t e = launch_chunk_prepare(p, s);
     if (e != hipSuccess) return e;
-    if (p.mmat16) {   // bf16 inputs: the state recompute on fp16 operands from the raw inputs
-        ChunkProblem r = p;
-        r.q = b.q_in;
-        r.k = b.k_in;
-        r.v = b.v_in;
-        e = launch_chunk_propagate_f16(r, s);
+    if (p.mmat16) {   // bf16 inputs: fp16 operands
+        e = launch_chunk_propagate_f16(p, s);
     } else {
         e = launch_chunk_propagate(p, s);
     }

@@ -260,6 +260,8 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                         const float pp = (i <= r) ? P0[cb][v] * e : 0.f;
                         sm.u.tri.A[r * PF + i] = a;
                         sm.P[r * PC + i] = from_f32<TM>(pp);
+                        // backward pass, bf16 inputs: P also in fp32, row-major, before its rounding
+                        if (sizeof(TM) == 2 && p.tmat) static_cast<float*>(p.pmat)[widx * 4096 + r * 64 + i] = pp;
                     }
                 }
             }
@@ -288,6 +290,19 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                     store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
                     store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
                 }
+            } else if (p.tmat) {  // backward pass, bf16 inputs: fp32 T, fp16 Mmat and P, row-major
+                const int r = tid >> 2, c0 = (tid & 3) * 16;
+                float mv[16], pv[16], tv[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int ci = c0 + e;
+                    tv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
+                    mv[e] = tv[e] * sm.beta[ci];
+                    pv[e] = to_f32(sm.P[r * PC + ci]);
+                }
+                store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
+                store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
+                store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
             } else {
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {

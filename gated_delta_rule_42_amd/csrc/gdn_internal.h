@@ -96,20 +96,16 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate_f16(const ChunkProblem& p, hipStream_t s);
 
-// Backward pass. `f` describes the forward problem over fp32 q, k, v (the caller's, or
-// widened copies in the workspace) with its stage-1 workspace and the tmat and states
-// regions set; the rest are the backward's own inputs, outputs and regions.
+// Backward pass. `f` describes the forward problem over the caller's q, k, v with its stage-1
+// workspace and the tmat and states regions set (bf16 inputs: also mmat16, pmat16); the rest
+// are the backward's own inputs, outputs and regions.
 struct BwdProblem {
     ChunkProblem f;
     const void* q_in;            // caller's q, k, v, dO in the caller's dtype
     const void* k_in;
     const void* v_in;
     const void* do_in;
-    const float* do32;           // fp32 dO (the caller's, or the widened copy)
-    float* q32;                  // widening targets (bf16 inputs only, else NULL)
-    float* k32;
-    float* v32;
-    float* do32w;
+    const float* do32;           // fp32 dO (fp32 inputs only, else NULL)
     const float* dhT;            // NULL: zero
     void* dq;                    // [B,T,H,dk] caller's dtype
     void* dk;
@@ -123,7 +119,7 @@ struct BwdProblem {
 
 struct BwdLayout {
     WorkspaceLayout fwd;         // stage-1 regions (fp32 operands)
-    size_t off_t, off_states, off_dstates, off_q32, off_k32, off_v32, off_do32, off_m16, off_p16, total;
+    size_t off_t, off_states, off_dstates, off_m16, off_p16, total;
 };
 
 BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16);

@@ -160,11 +160,11 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  * gdn_chunk_fwd_workspace_bytes; 0 for arguments gdn_chunk_bwd would reject or when no
  * chunk exists). Contents, 256-byte aligned regions in this order (nc as above):
  *   the regions of gdn_chunk_fwd_workspace_bytes for fp32 operators (chunk_base, gates,
- *   Mmat, P), then
+ *   Mmat, P; row-major [nc, H, 64, 64], Mmat left unwritten for bf16 inputs), then
  *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major
  *   states   fp32 [nc, H, dv, dk]  the state entering each chunk
  *   dstates  fp32 [nc, H, dv, dk]  the gradient reaching the state after each chunk
- *   q, k, v, dO widened to fp32 ([B, T, H, d] each; bf16 inputs only).
+ *   Mmat, P  fp16 [nc, H, 64, 64] each, row-major (bf16 inputs only).
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
                                      int chunk, int dtype);
@@ -177,8 +177,11 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  * no gradient formulas; these are the adjoint of the chunk equations of gdn_chunk_propagate,
  * computed chunk by chunk: stage 1 and 2 of the forward pass again (keeping T and the state
  * entering every chunk), a reverse walk over the chunks of each sequence carrying the
- * state gradient, then every (chunk, head) independently. All arithmetic is fp32 (bf16
- * inputs are widened exactly); bf16 gradients are the fp32 results rounded to nearest even.
+ * state gradient, then every (chunk, head) independently. fp32 inputs: all arithmetic is
+ * fp32. bf16 inputs: the products run on fp16 operands with fp32 accumulation, fp32 states
+ * and state gradients (the forward pass's numerics); the operands whose rounding would
+ * dominate the per-chunk gradients are carried as fp16 hi + lo pairs. bf16 gradients are the
+ * fp32 results rounded to nearest even.
  *
  *   q, k, v, g_log_alpha, beta, h0, cu_seqlens, chunk, B, T, H, dk, dv, N, dtype:
  *               the forward pass's arguments, as in gdn_chunk_fwd
