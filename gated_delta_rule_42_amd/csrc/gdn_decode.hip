@@ -37,28 +37,30 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-template <typename TS, int EPL>
-__device__ __forceinline__ void load_vec(const TS* p, float (&x)[EPL]) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = to_f32(p[e]);
-}
-
 // One work-group per (sequence, head). Its 256 lanes form 16 groups of 16; group g owns
-// rows g, g+16, ...; within a group, lane l16 owns columns [l16*EPL, l16*EPL + EPL) so that
-// one group reads a whole row contiguously.
+// rows g, g+16, ...; within a group, lane l16 owns the columns 4 l16 + 0..3 of each 64-column
+// half of a row, so that every load and store of the state covers whole 256-byte runs
+// (16 lanes x 16 bytes, full cache lines). The state is streamed with non-temporal loads and
+// stores: each byte is touched once per step.
 template <typename TS, typename TO, int DK, int DV, bool CW, bool DEC>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     constexpr int EPL = DK / 16;   // state columns per lane
+    constexpr int NH = EPL / 4;    // 16-byte pieces per lane and row
+    constexpr int HW = DK / NH;    // columns between a lane's pieces
     constexpr int RPG = DV / 16;   // rows per lane group
     const long pr = blockIdx.x;
     const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+    auto col = [&](int e) { return HW * (e >> 2) + 4 * l16 + (e & 3); };   // column of value e
 
     float kf[EPL], qf[EPL];
-    load_vec<TS, EPL>(static_cast<const TS*>(p.k) + pr * DK + l16 * EPL, kf);
-    load_vec<TS, EPL>(static_cast<const TS*>(p.q) + pr * DK + l16 * EPL, qf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        kf[e] = to_f32(static_cast<const TS*>(p.k)[pr * DK + col(e)]);
+        qf[e] = to_f32(static_cast<const TS*>(p.q)[pr * DK + col(e)]);
+    }
     float ke[EPL];   // the key the erased read runs along
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ke[e] = DEC ? p.erase[pr * DK + l16 * EPL + e] * kf[e] : kf[e];
+    for (int e = 0; e < EPL; ++e) ke[e] = DEC ? p.erase[pr * DK + col(e)] * kf[e] : kf[e];
     float kq = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) kq += kf[e] * qf[e];
@@ -67,9 +69,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
     const float beta = DEC ? 1.f : p.beta[pr];
     float af[EPL];   // channel-wise decay of this lane's columns
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) af[e] = CW ? __expf(p.g[pr * DK + l16 * EPL + e]) : 1.f;
+    for (int e = 0; e < EPL; ++e) af[e] = CW ? __expf(p.g[pr * DK + col(e)]) : 1.f;
 
-    float* st = p.state + pr * (long)DV * DK + l16 * EPL;
+    float* st = p.state + pr * (long)DV * DK + 4 * l16;
     const TS* vp = static_cast<const TS*>(p.v) + pr * DV;
     TO* op = static_cast<TO*>(p.o) + pr * DV;
 
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
         const int row = grp + 16 * it;
 #pragma unroll
         for (int e = 0; e < EPL; e += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(st + (long)row * DK + e);
-            s[it][e] = x.x; s[it][e + 1] = x.y; s[it][e + 2] = x.z; s[it][e + 3] = x.w;
+            const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(st + (long)row * DK + HW * (e >> 2)));
+            s[it][e] = x[0]; s[it][e + 1] = x[1]; s[it][e + 2] = x[2]; s[it][e + 3] = x[3];
         }
         if constexpr (CW) {
 #pragma unroll
@@ -104,12 +106,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
         const float c = beta * (vr[it] - alpha * sk);
 #pragma unroll
         for (int e = 0; e < EPL; e += 4) {
-            float4 x;
-            x.x = alpha * s[it][e] + c * kf[e];
-            x.y = alpha * s[it][e + 1] + c * kf[e + 1];
-            x.z = alpha * s[it][e + 2] + c * kf[e + 2];
-            x.w = alpha * s[it][e + 3] + c * kf[e + 3];
-            *reinterpret_cast<float4*>(st + (long)row * DK + e) = x;
+            const f32x4_t x = {alpha * s[it][e] + c * kf[e], alpha * s[it][e + 1] + c * kf[e + 1],
+                               alpha * s[it][e + 2] + c * kf[e + 2], alpha * s[it][e + 3] + c * kf[e + 3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(st + (long)row * DK + HW * (e >> 2)));
         }
         if (l16 == 0) op[row] = from_f32<TO>(alpha * sq + c * kq);
     }
