@@ -23,10 +23,11 @@
 // (kda_propagate_kernel) carries the state through the chunks. All arithmetic is fp32 (fp32
 // 16x16x4 matrix core); bf16 inputs are widened on load.
 //
-// A and P never form e^{-gamma} (it overflows under strong decay): blocks below the 16x16
-// diagonal use a reference at the first row of the row block, so both factors
-// e^{gamma_r - gamma_ref} and e^{gamma_ref - gamma_i} are <= 1; diagonal blocks are summed
-// over the channels with the exponent of each difference directly.
+// A and P never form e^{-gamma} (it overflows under strong decay): every 16-row block uses a
+// reference at its first row, so the factor e^{gamma_r - gamma_ref} of a row is <= 1 and
+// e^{gamma_ref - gamma_i} of a column is <= 1 below the diagonal block and at most
+// e^kMaxRange within it; channels that decay more than that over a block are summed exactly
+// there, term by term.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_stage2.h"
@@ -61,49 +62,73 @@ struct alignas(16) KdaPrepSmem {
     float beta[64];
 };
 
-// Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}] for one or
-// two left operands L1, L2 (sharing the right operand K and the exponentials), into O1 (times
-// rs1[r] when rs1 is set; strictly lower when strict1) and O2 (lower including the diagonal).
-// Blocks below the diagonal: fp32 matrix core with the reference gamma of row 16 I (both
-// factors <= 1); the diagonal block: exact sums over the channels.
+// Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}], i < 16 (I + 1),
+// for one or two left operands L1, L2 (sharing the right operand K and the exponentials), into
+// O1 (times rs1[r] when rs1 is set; strictly lower when strict1) and O2 (lower including the
+// diagonal). All column blocks on the fp32 matrix core with the reference gamma of row 16 I:
+// left factor L[r] e^{gamma_r - gamma_ref} (<= |L|: r >= ref), right factor
+// K[i] e^{gamma_ref - gamma_i}, which is <= |K| below the diagonal block (i < ref) and, in the
+// diagonal block, grows with the channel's decay over the block's rows. A channel whose decay
+// over the block exceeds e^kMaxRange is left out of the diagonal block's product and summed
+// there exactly instead (one exponent per term), so no factor exceeds e^kMaxRange.
+constexpr float kMaxRange = 60.f;
 template <int DK, bool TWO>
 __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
                                           float* O1, float* O2, const float* rs1, bool strict1,
                                           int wave, int lane) {
     constexpr int PK = KdaPrepSmem<DK>::PK, PF = KdaPrepSmem<DK>::PF;
     const int l16 = lane & 15, lq = lane >> 4, I = wave;
-    for (int J = 0; J < I; ++J) {
-        f32x4_t a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-#pragma unroll 4
-        for (int k0 = 0; k0 < DK; k0 += 4) {
-            const int ch = k0 + lq;
-            const float gref = sm.G[16 * I * PK + ch];
-            const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
-            const float er = __expf(gref - sm.G[(16 * J + l16) * PK + ch]);
-            const float b = sm.K[(16 * J + l16) * PK + ch] * er;
-            a1 = mfma4(L1[(16 * I + l16) * PK + ch] * el, b, a1);
-            if constexpr (TWO) a2 = mfma4(L2[(16 * I + l16) * PK + ch] * el, b, a2);
-        }
+    f32x4_t a1[4], a2[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
-            O1[r * PF + i] = (rs1 ? rs1[r] : 1.f) * a1[m];
-            if constexpr (TWO) O2[r * PF + i] = a2[m];
+    for (int J = 0; J < 4; ++J) a1[J] = a2[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+        const int ch = k0 + lq;
+        const float gref = sm.G[16 * I * PK + ch];
+        const bool fits = gref - sm.G[(16 * I + 15) * PK + ch] <= kMaxRange;
+        const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
+        const float x1 = L1[(16 * I + l16) * PK + ch] * el;
+        const float x2 = TWO ? L2[(16 * I + l16) * PK + ch] * el : 0.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J > I) break;   // uniform over the wave
+            const int i = 16 * J + l16;
+            const float b = sm.K[i * PK + ch] * __expf(gref - sm.G[i * PK + ch]);
+            const float bb = (J < I || fits) ? b : 0.f;
+            a1[J] = mfma4(x1, bb, a1[J]);
+            if constexpr (TWO) a2[J] = mfma4(x2, bb, a2[J]);
         }
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = 16 * I + 4 * lq + m, i = 16 * I + l16;
-        float s1 = 0.f, s2 = 0.f;
-        if (i <= r) {
-            for (int ch = 0; ch < DK; ++ch) {
-                const float e = __expf(fminf(sm.G[r * PK + ch] - sm.G[i * PK + ch], 0.f)) * sm.K[i * PK + ch];
-                s1 += L1[r * PK + ch] * e;
-                if constexpr (TWO) s2 += L2[r * PK + ch] * e;
+    for (int J = 0; J < 4; ++J) {
+        if (J > I) break;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
+            const bool k1 = J < I || (strict1 ? i < r : i <= r), k2 = J < I || i <= r;
+            O1[r * PF + i] = k1 ? (rs1 ? rs1[r] : 1.f) * a1[J][m] : 0.f;
+            if constexpr (TWO) O2[r * PF + i] = k2 ? a2[J][m] : 0.f;
+        }
+    }
+    // channels left out of the diagonal block's product: exact sums over them (each lane adds to
+    // the entries it wrote above)
+    for (int c0 = 0; c0 < DK; c0 += 64) {
+        const int ch = c0 + lane;
+        const bool out = ch < DK && sm.G[16 * I * PK + ch] - sm.G[(16 * I + 15) * PK + ch] > kMaxRange;
+        unsigned long long bits = __ballot(out);
+        while (bits) {
+            const int c = c0 + __builtin_ctzll(bits);
+            bits &= bits - 1;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * I + 4 * lq + m, i = 16 * I + l16;
+                if (i <= r) {
+                    const float e = __expf(sm.G[r * PK + c] - sm.G[i * PK + c]) * sm.K[i * PK + c];
+                    if (strict1 ? i < r : true) O1[r * PF + i] += (rs1 ? rs1[r] : 1.f) * L1[r * PK + c] * e;
+                    if constexpr (TWO) O2[r * PF + i] += L2[r * PK + c] * e;
+                }
             }
         }
-        O1[r * PF + i] = (strict1 ? i < r : i <= r) ? (rs1 ? rs1[r] : 1.f) * s1 : 0.f;
-        if constexpr (TWO) O2[r * PF + i] = s2;
     }
 }
 
@@ -152,13 +177,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     }
     if (tid < 64) sm.beta[tid] = (!DEC && tid < len) ? p.beta[(bos + tid) * H + h] : 0.f;
     __syncthreads();
-    if (tid < DK) {   // gamma, one channel per thread (rows past the chunk's end add 0)
-        float run = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            run += sm.G[r * PK + tid];
-            sm.G[r * PK + tid] = run;
-        }
-    }
+    // gamma: inclusive scans down the 64 rows, one channel at a time per wave (lane = row;
+    // rows past the chunk's end add 0)
+    for (int ch = wave; ch < DK; ch += 4) sm.G[lane * PK + ch] = wave_inclusive_sum(sm.G[lane * PK + ch]);
     __syncthreads();
 
     // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
