@@ -398,9 +398,85 @@ struct alignas(16) KdaProp16Smem {
     float lam[DK];
 };
 
+// One chunk's stage-2 inputs, staged in registers: the fp16 Kh, Qh, Kd, Mmat and P of the
+// workspace, the raw bf16 V columns of the work-group (and the write gate with decoupled
+// gates) and lam. Every load is issued unconditionally, rows past the chunk's end through
+// buffer resources that read them as zeros.
+template <int DK, int DVT, int NT>
+struct KdaStage16 {
+    using KL = typename KdaProp16Smem<DK, DVT>::KL;
+    static constexpr int PC = KdaProp16Smem<DK, DVT>::PC, PV = KdaProp16Smem<DK, DVT>::PV;
+    static constexpr int NKQ = 64 * DK / 8 / NT;   // 16-byte pieces per thread of Kh, Qh, Kd
+    static constexpr int NMP = 64 * 8 / NT;        // of Mmat and P
+    static constexpr int NV = 64 * DVT / 4 / NT;   // groups of 4 values of V
+    // native vector types: a struct-typed element copy would go through memory
+    u32x4_t kh[NKQ], qh[NKQ], kd[NKQ], m[NMP], pm[NMP];
+    u32x2_t v[NV];
+    f32x4_t w[NV];
+    float lam;
+
+    __device__ __forceinline__ void load(const ChunkProblem& p, long bos, int len, long widx, int h, int dv0,
+                                         int tid) {
+        const int H = p.H, DV = p.dv;
+        const _Float16* kh_ = reinterpret_cast<const _Float16*>(p.khat) + widx * 64 * DK;
+        const _Float16* qh_ = reinterpret_cast<const _Float16*>(p.qhat) + widx * 64 * DK;
+        const _Float16* kd_ = reinterpret_cast<const _Float16*>(p.kdec) + widx * 64 * DK;
+#pragma unroll
+        for (int it = 0; it < NKQ; ++it) {
+            const int i = tid + NT * it;
+            kh[it] = reinterpret_cast<const u32x4_t*>(kh_)[i];
+            qh[it] = reinterpret_cast<const u32x4_t*>(qh_)[i];
+            kd[it] = reinterpret_cast<const u32x4_t*>(kd_)[i];
+        }
+#pragma unroll
+        for (int it = 0; it < NMP; ++it) {
+            const int i = tid + NT * it;
+            m[it] = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.mmat) + widx * 4096)[i];
+            pm[it] = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.pmat) + widx * 4096)[i];
+        }
+        const long vo = (bos * H + h) * DV + dv0;
+        const unsigned vrows = (unsigned)((len - 1) * H * DV + DVT);
+        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + vo, vrows * 2);
+        const auto wr = make_rsrc(p.write ? p.write + vo : nullptr, p.write ? vrows * 4 : 0u);
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int i = tid + NT * it, r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
+            v[it] = __builtin_amdgcn_raw_buffer_load_b64(vr, (r * H * DV + cc) * 2, 0, 0);
+            w[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, (r * H * DV + cc) * 4, 0, 0));
+        }
+        lam = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lam + widx * DK, DK * 4), tid * 4, 0, 0));
+    }
+
+    __device__ __forceinline__ void store(KdaProp16Smem<DK, DVT>& sm, bool write_gate, int tid) const {
+#pragma unroll
+        for (int it = 0; it < NKQ; ++it) {
+            const int i = tid + NT * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            *reinterpret_cast<u32x4_t*>(&sm.Kh[KL::off(r, cc)]) = kh[it];
+            *reinterpret_cast<u32x4_t*>(&sm.Qh[KL::off(r, cc)]) = qh[it];
+            *reinterpret_cast<u32x4_t*>(&sm.Kd[KL::off(r, cc)]) = kd[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NMP; ++it) {
+            const int i = tid + NT * it, r = i / 8, cc = 8 * (i % 8);
+            *reinterpret_cast<u32x4_t*>(&sm.M[r * PC + cc]) = m[it];
+            *reinterpret_cast<u32x4_t*>(&sm.P[r * PC + cc]) = pm[it];
+        }
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int i = tid + NT * it, r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
+            f32x4_t x = {__uint_as_float(v[it][0] << 16), __uint_as_float(v[it][0] & 0xffff0000u),
+                         __uint_as_float(v[it][1] << 16), __uint_as_float(v[it][1] & 0xffff0000u)};
+            if (write_gate) x = {x[0] * w[it][0], x[1] * w[it][1], x[2] * w[it][2], x[3] * w[it][3]};  // w * v
+            *reinterpret_cast<f32x4_t*>(&sm.V[r * PV + cc]) = x;
+        }
+        if (tid < DK) sm.lam[tid] = lam;
+    }
+};
+
 // The stage-2 products of kda_propagate_kernel on the fp16 matrix core (16x16x32, fp32
 // accumulation), as the scalar-gate path multiplies bf16 inputs: stage 1 left Kh, Qh, Kd, Mmat
-// and P in fp16, the state is packed to fp16 as an operand and kept in fp32.
+// and P in fp16, the state is packed to fp16 as an operand and kept in fp32. The next chunk's
+// inputs are loaded into registers while the current one is computed.
 template <typename TO, int DK, int DV, int DVT>
 __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkProblem p) {
     using SM = KdaProp16Smem<DK, DVT>;
@@ -433,44 +509,34 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkPro
             ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
-    const uint16_t* vp = static_cast<const uint16_t*>(p.v);
-    const _Float16* kh = reinterpret_cast<const _Float16*>(p.khat);
-    const _Float16* qh = reinterpret_cast<const _Float16*>(p.qhat);
-    const _Float16* kd = reinterpret_cast<const _Float16*>(p.kdec);
-    const _Float16* mp = static_cast<const _Float16*>(p.mmat);
-    const _Float16* pp = static_cast<const _Float16*>(p.pmat);
-
+    auto chunk_at = [&](long jc, long& bos, int& len, long& widx) {
+        bos = sbos + jc * 64;
+        len = (int)min(64L, seos - bos);
+        widx = (cbase + jc) * H + h;
+    };
+    KdaStage16<DK, DVT, NT> stage;
+    if (nchunks > 0) {
+        long b0, w0;
+        int l0;
+        chunk_at(0, b0, l0, w0);
+        stage.load(p, b0, l0, w0, h, dv0, tid);
+    }
+    const bool write_gate = p.write != nullptr;
     for (long jc = 0; jc < nchunks; ++jc) {
-        const long bos = sbos + jc * 64, widx = (cbase + jc) * H + h;
-        const int len = (int)min(64L, seos - bos);
+        long bos, widx;
+        int len;
+        chunk_at(jc, bos, len, widx);
         __syncthreads();  // the previous chunk's LDS data is dead
-        for (int i = tid; i < 64 * DK / 8; i += NT) {
-            const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-            const long o = (widx * 64 + r) * DK + cc;
-            *reinterpret_cast<uint4*>(&sm.Kh[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(kh + o);
-            *reinterpret_cast<uint4*>(&sm.Qh[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(qh + o);
-            *reinterpret_cast<uint4*>(&sm.Kd[KL::off(r, cc)]) = *reinterpret_cast<const uint4*>(kd + o);
-        }
-        for (int i = tid; i < 64 * 8; i += NT) {
-            const int r = i / 8, cc = 8 * (i % 8);
-            *reinterpret_cast<uint4*>(&sm.M[r * PC + cc]) = *reinterpret_cast<const uint4*>(mp + widx * 4096 + r * 64 + cc);
-            *reinterpret_cast<uint4*>(&sm.P[r * PC + cc]) = *reinterpret_cast<const uint4*>(pp + widx * 4096 + r * 64 + cc);
-        }
-        for (int i = tid; i < 64 * DVT / 4; i += NT) {
-            const int r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < len) {
-                const long o = ((bos + r) * H + h) * DV + dv0 + cc;
-                x = load4_in(vp + o);
-                if (p.write) {   // decoupled gates: the written value is w * v
-                    const float4 w = *reinterpret_cast<const float4*>(p.write + o);
-                    x = make_float4(x.x * w.x, x.y * w.y, x.z * w.z, x.w * w.w);
-                }
-            }
-            *reinterpret_cast<float4*>(&sm.V[r * PV + cc]) = x;
-        }
-        for (int i = tid; i < DK; i += NT) sm.lam[i] = p.lam[widx * DK + i];
+        stage.store(sm, write_gate, tid);
         __syncthreads();
+        {   // the next chunk's inputs (the last chunk's again past the end: every pass loads)
+            long nb, nw;
+            int nl;
+            chunk_at(jc + 1 < nchunks ? jc + 1 : jc, nb, nl, nw);
+            stage.load(p, nb, nl, nw, h, dv0, tid);
+        }
+        const auto orr = make_rsrc(static_cast<TO*>(p.o) + (bos * H + h) * DV,
+                                   (unsigned)(((len - 1) * H * DV + DV) * (int)sizeof(TO)));
 
         // X = Kh S^T, Y = Qh S^T (rows: tokens)
         Frag<_Float16> BS[NKS];
@@ -509,9 +575,12 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkPro
             mma_k32(O, load_frag2<_Float16>(prow, prow + 16), BD0);
             mma_k32(O, load_frag2<_Float16>(prow + 32, prow + 48), BD1);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = 16 * t + 4 * lq + m;
-                if (r < len) static_cast<TO*>(p.o)[((bos + r) * H + h) * DV + dvw + l16] = from_f32<TO>(O[m]);
+            for (int m = 0; m < 4; ++m) {   // rows past the chunk's end fall outside orr
+                const int off = ((16 * t + 4 * lq + m) * H * DV + dvw + l16) * (int)sizeof(TO);
+                if constexpr (sizeof(TO) == 2)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(O[m]), orr, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m]), orr, off, 0, 0);
             }
         }
         // S^T <- Diag(lam) S^T + Kd^T Delta
