@@ -72,16 +72,15 @@ struct alignas(16) KdaPrepSmem {
 // over the block exceeds e^kMaxRange is left out of the diagonal block's product and summed
 // there exactly instead (one exponent per term), so no factor exceeds e^kMaxRange.
 constexpr float kMaxRange = 60.f;
-template <int DK, bool TWO>
-__device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
-                                          float* O1, float* O2, const float* rs1, bool strict1,
-                                          int wave, int lane) {
+template <int DK, bool TWO, int I>
+__device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
+                                             float* O1, float* O2, const float* rs1, bool strict1, int lane) {
     constexpr int PK = KdaPrepSmem<DK>::PK, PF = KdaPrepSmem<DK>::PF;
-    const int l16 = lane & 15, lq = lane >> 4, I = wave;
+    const int l16 = lane & 15, lq = lane >> 4;
     f32x4_t a1[4], a2[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) a1[J] = a2[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll 8
     for (int k0 = 0; k0 < DK; k0 += 4) {
         const int ch = k0 + lq;
         const float gref = sm.G[16 * I * PK + ch];
@@ -90,8 +89,7 @@ __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float
         const float x1 = L1[(16 * I + l16) * PK + ch] * el;
         const float x2 = TWO ? L2[(16 * I + l16) * PK + ch] * el : 0.f;
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            if (J > I) break;   // uniform over the wave
+        for (int J = 0; J <= I; ++J) {
             const int i = 16 * J + l16;
             const float b = sm.K[i * PK + ch] * __expf(gref - sm.G[i * PK + ch]);
             const float bb = (J < I || fits) ? b : 0.f;
@@ -100,8 +98,7 @@ __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float
         }
     }
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        if (J > I) break;
+    for (int J = 0; J <= I; ++J) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
@@ -132,7 +129,89 @@ __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float
     }
 }
 
-// One work-group (4 waves) per (chunk, head); wave w owns row block w of A and P. With
+// gram_rows_of for the row block of this wave (the row block is a compile-time constant of each
+// wave's code, so its loops are static)
+template <int DK, bool TWO>
+__device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
+                                          float* O1, float* O2, const float* rs1, bool strict1,
+                                          int wave, int lane) {
+    switch (wave) {
+        case 0: gram_rows_of<DK, TWO, 0>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
+        case 1: gram_rows_of<DK, TWO, 1>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
+        case 2: gram_rows_of<DK, TWO, 2>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
+        default: gram_rows_of<DK, TWO, 3>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
+    }
+}
+
+// One (chunk, head) unit's stage-1 inputs, staged in registers: K, g and Q (or, with decoupled
+// gates, the erase gate), 4 values per group, and beta. Every load is issued unconditionally,
+// rows past the chunk's end through buffer resources that read them as zeros; the element
+// arrays use native vector types (a struct-typed copy would go through memory).
+template <typename TIn, int DK, bool DEC>
+struct KdaPrepStage {
+    static constexpr int NP = 64 * DK / 4 / 256;   // groups of 4 values per thread
+    static constexpr int EB = (int)sizeof(TIn);    // bytes of an input element
+    u32x4_t k[NP], q[NP];                         // raw groups (bf16: the low 8 bytes)
+    f32x4_t g[NP], e[NP];
+    float beta;
+
+    __device__ __forceinline__ static u32x4_t raw4(__amdgpu_buffer_rsrc_t r, int off) {
+        if constexpr (EB == 2) {
+            const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            return u32x4_t{x[0], x[1], 0u, 0u};
+        } else {
+            return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        }
+    }
+    __device__ __forceinline__ static float4 widen(u32x4_t x) {
+        if constexpr (EB == 2)
+            return make_float4(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                               __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u));
+        else
+            return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+    }
+
+    __device__ __forceinline__ void load(const ChunkProblem& p, long bos, int len, int h, int tid) {
+        const int H = p.H;
+        const long o = (bos * H + h) * DK;
+        const unsigned rows = (unsigned)((len - 1) * H * DK + DK);
+        const auto kr = make_rsrc(static_cast<const TIn*>(p.k) + o, rows * EB);
+        const auto qr = make_rsrc(static_cast<const TIn*>(p.q) + o, DEC ? 0u : rows * EB);
+        const auto gr = make_rsrc(p.g + o, rows * 4);
+        const auto er = make_rsrc(DEC ? p.erase + o : p.g, DEC ? rows * 4 : 0u);
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + 256 * it, r = i / (DK / 4), cc = 4 * (i % (DK / 4)), x = r * H * DK + cc;
+            k[it] = raw4(kr, x * EB);
+            q[it] = raw4(qr, x * EB);
+            g[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(gr, x * 4, 0, 0));
+            e[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(er, x * 4, 0, 0));
+        }
+        const auto br = make_rsrc(p.beta + bos * H + h, DEC ? 0u : (unsigned)(((len - 1) * H + 1) * 4));
+        beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, tid * H * 4, 0, 0));
+    }
+
+    // K, g and (Q, or E * K with decoupled gates) into LDS as fp32
+    __device__ __forceinline__ void store(KdaPrepSmem<DK>& sm, int tid) const {
+        constexpr int PK = KdaPrepSmem<DK>::PK;
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int i = tid + 256 * it, r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const float4 kv = widen(k[it]);
+            const float4 qv = DEC ? make_float4(e[it][0] * kv.x, e[it][1] * kv.y, e[it][2] * kv.z, e[it][3] * kv.w)
+                                  : widen(q[it]);
+            *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
+            *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+            *reinterpret_cast<f32x4_t*>(&sm.G[r * PK + cc]) = g[it];
+        }
+        if (tid < 64) sm.beta[tid] = beta;
+    }
+};
+
+// Persistent work-groups: each walks (chunk, head) units with a stride of the grid, keeping the
+// next unit's inputs in flight in registers while the current one is computed (the loads are
+// issued on every pass, for the current unit again past the last one, which keeps the
+// compiler's waits for them exact). Wave w owns row block w of A and P. With
 // decoupled gates (DEC) the erased read runs along E * K, so A's left operand is E * K (held
 // in the Q buffer until A is formed, then Q is loaded), Kh is E * K * e^gamma, V is scaled by
 // the write gate in stage 2 and Mmat is T itself.
@@ -143,101 +222,103 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = p.H;
-    const long c = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
-    long bos;
-    int len;
-    if (!locate_chunk(p, c, bos, len)) return;   // uniform over the work-group
-    const long widx = c * H + h;
-    const TIn* kp = static_cast<const TIn*>(p.k);
+    const long nunits = p.nc_bound * H;
     const TIn* qp = static_cast<const TIn*>(p.q);
     using TM = typename Operand<TIn>::type;   // operators are written as fp16 for bf16 inputs
     TM* khat = reinterpret_cast<TM*>(p.khat);
     TM* qhat = reinterpret_cast<TM*>(p.qhat);
     TM* kdec = reinterpret_cast<TM*>(p.kdec);
 
-    // K, g and (Q, or E * K with decoupled gates) into LDS
-    for (int i = tid; i < 64 * DK / 4; i += 256) {
-        const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
-        if (r < len) {
-            const long o = ((bos + r) * H + h) * DK + cc;
-            kv = load4_in(kp + o);
-            gv = *reinterpret_cast<const float4*>(p.g + o);
-            if constexpr (DEC) {
-                const float4 e = *reinterpret_cast<const float4*>(p.erase + o);
-                qv = make_float4(e.x * kv.x, e.y * kv.y, e.z * kv.z, e.w * kv.w);
-            } else {
-                qv = load4_in(qp + o);
-            }
+    KdaPrepStage<TIn, DK, DEC> stage;
+    long unit = blockIdx.x, bos = 0;
+    int len = 0;
+    bool ok = unit < nunits && locate_chunk(p, unit / H, bos, len);
+    if (ok) stage.load(p, bos, len, (int)(unit % H), tid);
+    while (unit < nunits) {
+        const long nxt = unit + gridDim.x;
+        long nbos = 0;
+        int nlen = 0;
+        const bool nok = nxt < nunits && locate_chunk(p, nxt / H, nbos, nlen);
+        if (!ok) {
+            if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
+            unit = nxt; ok = nok; bos = nbos; len = nlen;
+            continue;
         }
-        *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
-        *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
-        *reinterpret_cast<float4*>(&sm.G[r * PK + cc]) = gv;
-    }
-    if (tid < 64) sm.beta[tid] = (!DEC && tid < len) ? p.beta[(bos + tid) * H + h] : 0.f;
-    __syncthreads();
-    // gamma: inclusive scans down the 64 rows, one channel at a time per wave (lane = row;
-    // rows past the chunk's end add 0)
-    for (int ch = wave; ch < DK; ch += 4) sm.G[lane * PK + ch] = wave_inclusive_sum(sm.G[lane * PK + ch]);
-    __syncthreads();
-
-    // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
-    auto write_scaled = [&](bool kside) {
-        for (int i = tid; i < 64 * DK / 4; i += 256) {
-            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
-            const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
-            const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
-            const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
-            const long o = (widx * 64 + r) * DK + cc;
-            const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
-            if (!kside) {
-                put4(qhat + o, x);
-                continue;
-            }
-            const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
-            const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
-            const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
-            put4(khat + o, DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w));
-            put4(kdec + o, make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w));
-            if constexpr (!DEC) put4(qhat + o, x);
-        }
-    };
-    write_scaled(true);
-    if (tid < DK) p.lam[widx * DK + tid] = __expf(sm.G[63 * PK + tid]);
-
-    // -- A and P
-    if constexpr (DEC) {
-        gram_rows<DK, false>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, wave, lane);
-        __syncthreads();  // E * K is dead: load Q in its place
-        for (int i = tid; i < 64 * DK / 4; i += 256) {
-            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
-            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < len) qv = load4_in(qp + ((bos + r) * H + h) * DK + cc);
-            *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+        const int h = (int)(unit % H);
+        const long widx = unit;   // (chunk, head) = (unit / H, unit % H)
+        __syncthreads();  // the previous unit is done with LDS
+        stage.store(sm, tid);
+        __syncthreads();
+        if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
+        else stage.load(p, bos, len, h, tid);
+        // gamma: inclusive scans down the 64 rows (lane = row; rows past the chunk's end add 0),
+        // four channels at a time per wave
+        for (int ch = 4 * wave; ch < DK; ch += 16) {
+            f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.G[lane * PK + ch]);
+            x = f32x4_t{wave_inclusive_sum(x[0]), wave_inclusive_sum(x[1]), wave_inclusive_sum(x[2]),
+                        wave_inclusive_sum(x[3])};
+            *reinterpret_cast<f32x4_t*>(&sm.G[lane * PK + ch]) = x;
         }
         __syncthreads();
-        write_scaled(false);
-        gram_rows<DK, false>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, wave, lane);
-    } else {
-        gram_rows<DK, true>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, wave, lane);
-    }
-    __syncthreads();
 
-    ut_inverse64<PF>(sm.A, sm.T, wave, lane);
+        // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
+        auto write_scaled = [&](bool kside) {
+            for (int i = tid; i < 64 * DK / 4; i += 256) {
+                const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+                const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
+                const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
+                const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
+                const long o = (widx * 64 + r) * DK + cc;
+                const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
+                if (!kside) {
+                    put4(qhat + o, x);
+                    continue;
+                }
+                const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
+                const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
+                const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
+                put4(khat + o, DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w));
+                put4(kdec + o, make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w));
+                if constexpr (!DEC) put4(qhat + o, x);
+            }
+        };
+        write_scaled(true);
+        if (tid < DK) p.lam[widx * DK + tid] = __expf(sm.G[63 * PK + tid]);
 
-    // -- Mmat = T diag(beta) (T with decoupled gates) and P (lower incl. diagonal), fp32 row-major
-    {
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
-        float mv[16], pv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int ci = c0 + e;
-            mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
-            pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
+        // -- A and P
+        if constexpr (DEC) {
+            gram_rows<DK, false>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, wave, lane);
+            __syncthreads();  // E * K is dead: load Q in its place
+            for (int i = tid; i < 64 * DK / 4; i += 256) {
+                const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+                float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (r < len) qv = load4_in(qp + ((bos + r) * H + h) * DK + cc);
+                *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+            }
+            __syncthreads();
+            write_scaled(false);
+            gram_rows<DK, false>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, wave, lane);
+        } else {
+            gram_rows<DK, true>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, wave, lane);
         }
-        store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
-        store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+        __syncthreads();
+
+        ut_inverse64<PF>(sm.A, sm.T, wave, lane);
+
+        // -- Mmat = T diag(beta) (T with decoupled gates) and P (lower incl. diagonal), fp32 row-major
+        {
+            const int r = tid >> 2, c0 = (tid & 3) * 16;
+            float mv[16], pv[16];
+    #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int ci = c0 + e;
+                mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
+                pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
+            }
+            store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+            store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+        }
+        unit = nxt; ok = nok; bos = nbos; len = nlen;
     }
 }
 
@@ -624,10 +705,24 @@ static void kda_launch(const ChunkProblem& p, hipStream_t s) {
     constexpr int DVT = 32;
     const long units = p.nc_bound * p.H;
     if (units > 0) {
-        if (p.erase)
-            hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK, true>), dim3((unsigned)units), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((kda_prepare_kernel<TIn, DK, false>), dim3((unsigned)units), dim3(256), 0, s, p);
+        // persistent grid: as many work-groups as the device holds at once (queried once per
+        // device and kernel)
+        auto go = [&](auto kern) {
+            static int resident[64] = {0};
+            int dev = 0;
+            (void)hipGetDevice(&dev);
+            int& cap = resident[dev & 63];
+            if (cap == 0) {
+                int per_cu = 0, cus = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                    per_cu < 1 || cus < 1)
+                    per_cu = 1, cus = 256;
+                cap = per_cu * cus;
+            }
+            hipLaunchKernelGGL(kern, dim3((unsigned)(units < cap ? units : cap)), dim3(256), 0, s, p);
+        };
+        if (p.erase) go(kda_prepare_kernel<TIn, DK, true>); else go(kda_prepare_kernel<TIn, DK, false>);
     }
     const long pairs = (long)p.N * p.H;
     if (pairs > 0) {

@@ -44,23 +44,28 @@ __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wav
     for (int d = 1; d < 4; ++d) {
         if (wave < 4 - d) {
             const int ib = d + wave, jb = ib - d;
-            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            for (int m = jb; m < ib; ++m) {
+            // all operands of this block read before the products (d blocks of 4 k-steps; d is
+            // a constant of the unrolled loop), so the reads overlap instead of each product
+            // waiting for its own
+            float av[12], bv[12], tv[4];   // 4 d <= 12 used
+#pragma unroll
+            for (int mm = 0; mm < d; ++mm)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const float av = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
-                    const float bv = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
-                    z = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, z, 0, 0, 0);
+                    const int m = jb + mm;
+                    av[4 * mm + s] = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
+                    bv[4 * mm + s] = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
                 }
-            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) tv[s] = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
+            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4 * d; ++k) z = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], z, 0, 0, 0);
             // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it as the
             // right operand with k relabelled to 4*lq + s in step s.
             f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float av = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
-                t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, z[s], t, 0, 0, 0);
-            }
+            for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s], z[s], t, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
         }
