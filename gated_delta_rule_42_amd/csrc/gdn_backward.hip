@@ -838,16 +838,41 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     float tail = 0.f;                       // lam (dS' : S) + sum z, this thread's share
     auto& sl = sm.u.sl;
 
+    // One d_v slice's rows of the entering state and of dS', and its V and dO columns, staged in
+    // registers: slice js+1 is loaded while slice js is computed. Native vector types (a
+    // struct-typed copy would go through memory); every load is issued (past the last slice
+    // they reload it), V and dO rows past the chunk's end read as zeros through buffer resources.
+    constexpr int NSI = 32 * DK / 8 / 256;
+    f32x4_t rs[NSI][2], rd[NSI][2];
+    u32x4_t rv, ro;
+    const unsigned vrow_bytes = (unsigned)((len - 1) * H * DV + 32) * 2;
+    auto load_slice = [&](int js) __attribute__((always_inline)) {
+        const int dv0 = 32 * js;
+#pragma unroll
+        for (int it = 0; it < NSI; ++it) {
+            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const float* sp = p.states + (widx * DV + dv0 + r) * DK + cc;
+            const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
+            rs[it][0] = *reinterpret_cast<const f32x4_t*>(sp);
+            rs[it][1] = *reinterpret_cast<const f32x4_t*>(sp + 4);
+            rd[it][0] = *reinterpret_cast<const f32x4_t*>(dp);
+            rd[it][1] = *reinterpret_cast<const f32x4_t*>(dp + 4);
+        }
+        const int r = tid >> 2, cc = 8 * (tid & 3), off = (r * H * DV + cc) * 2;
+        rv = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(vp + (bos * H + h) * DV + dv0, vrow_bytes), off, 0, 0);
+        ro = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(dop + (bos * H + h) * DV + dv0, vrow_bytes), off, 0, 0);
+    };
+    auto f4 = [](f32x4_t x) { return make_float4(x[0], x[1], x[2], x[3]); };
+    load_slice(0);
+
     for (int js = 0; js < DV / 32; ++js) {
         const int dv0 = 32 * js;
         __syncthreads();  // the previous slice is dead (first slice: the loads above are done)
         const float lam = sm.eg[63];
-        for (int i = tid; i < 32 * DK / 8; i += 256) {
-            const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-            const float* sp = p.states + (widx * DV + dv0 + r) * DK + cc;
-            const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
-            const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
-            const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+#pragma unroll
+        for (int it = 0; it < NSI; ++it) {
+            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const float4 s0 = f4(rs[it][0]), s1 = f4(rs[it][1]), d0 = f4(rd[it][0]), d1 = f4(rd[it][1]);
             const uint4 dh = pack8(d0, d1);
             *reinterpret_cast<uint4*>(&sl.S[r * PS + cc]) = pack8(s0, s1);
             *reinterpret_cast<uint4*>(&sl.dS[r * PS + cc]) = dh;
@@ -857,11 +882,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         }
         {
             const int r = tid >> 2, cc = 8 * (tid & 3);
-            uint4 v = zero16(), d = v;
-            if (r < len) {
-                v = *reinterpret_cast<const uint4*>(vp + ((bos + r) * H + h) * DV + dv0 + cc);
-                d = *reinterpret_cast<const uint4*>(dop + ((bos + r) * H + h) * DV + dv0 + cc);
-            }
+            const uint4 v = make_uint4(rv[0], rv[1], rv[2], rv[3]), d = make_uint4(ro[0], ro[1], ro[2], ro[3]);
             const uint4 d16 = to_operand16<uint16_t>(d);
             *reinterpret_cast<uint4*>(&sl.V[r * PV + cc]) = to_operand16<uint16_t>(v);
             *reinterpret_cast<uint4*>(&sl.dO[r * PV + cc]) = d16;
@@ -872,6 +893,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                       make_float4(e * (float)dh[4], e * (float)dh[5], e * (float)dh[6], e * (float)dh[7]));
         }
         __syncthreads();
+        load_slice(js + 1 < DV / 32 ? js + 1 : js);
+        const auto dvr = make_rsrc(static_cast<TO*>(bp.dv) + (bos * H + h) * DV + dv0,
+                                   (unsigned)(((len - 1) * H * DV + 32) * (int)sizeof(TO)));
 
         // X = K S^T, Y = Q S^T, Z = K dS'^T for this wave's rows and the slice's two column tiles
         f32x4_t X[2], Y[2], Z[2];
@@ -948,7 +972,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 const float d = sm.beta[r] * dRl[m];
                 gacc[m] -= d * EX[nt][m];
                 sl.EdR[r * PV + v] = (_Float16)(-sm.eg[r] * d);
-                if (r < len) store_elem<TO>(static_cast<TO*>(bp.dv) + ((bos + r) * H + h) * DV + dv0 + v, d);
+                const int off = (r * H * DV + v) * (int)sizeof(TO);   // rows past the end fall outside dvr
+                if constexpr (sizeof(TO) == 2)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(d), dvr, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d), dvr, off, 0, 0);
             }
         }
         __syncthreads();

@@ -80,7 +80,6 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
     f32x4_t a1[4], a2[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) a1[J] = a2[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
     for (int k0 = 0; k0 < DK; k0 += 4) {
         const int ch = k0 + lq;
         const float gref = sm.G[16 * I * PK + ch];

@@ -6,12 +6,45 @@
 
 namespace gdn {
 
+// The blocks on sub-diagonal D of T (wave w < 4 - D computes block (D + w, w)):
+// T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, fp32 MFMA (16x16x4). All operands of the block are
+// read before the products, so the reads overlap instead of each product waiting for its own.
+template <int PF, int D>
+__device__ __forceinline__ void ut_subdiagonal(const float* At, float* Tt, int wave, int lane) {
+    const int l16 = lane & 15, lq = lane >> 4;
+    if (wave < 4 - D) {
+        const int ib = D + wave, jb = ib - D;
+        float av[4 * D], bv[4 * D], tv[4];
+#pragma unroll
+        for (int mm = 0; mm < D; ++mm)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int m = jb + mm;
+                av[4 * mm + s] = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
+                bv[4 * mm + s] = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
+            }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) tv[s] = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4 * D; ++k) z = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], z, 0, 0, 0);
+        // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it as the
+        // right operand with k relabelled to 4*lq + s in step s.
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s], z[s], t, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
+    }
+    __syncthreads();
+}
+
 // A and T are fp32 [64, PF] in LDS (row pitch PF); A's strictly lower part is read, T's lower
 // blocks are written (blocks above the 16x16 block diagonal are left untouched). Diagonal
 // 16x16 blocks: wave w inverts block w by forward substitution, lane l16 computing column l16
 // with the block's strictly lower entries held in registers. Then the blocks below the
-// diagonal, one sub-diagonal at a time: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj (fp32 MFMA,
-// 16x16x4). Called by all 256 threads; ends with a barrier.
+// diagonal, one sub-diagonal at a time (ut_subdiagonal). Called by all 256 threads; ends with
+// a barrier.
 template <int PF>
 __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wave, int lane) {
     const int l16 = lane & 15, lq = lane >> 4;
@@ -40,37 +73,9 @@ __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wav
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        if (wave < 4 - d) {
-            const int ib = d + wave, jb = ib - d;
-            // all operands of this block read before the products (d blocks of 4 k-steps; d is
-            // a constant of the unrolled loop), so the reads overlap instead of each product
-            // waiting for its own
-            float av[12], bv[12], tv[4];   // 4 d <= 12 used
-#pragma unroll
-            for (int mm = 0; mm < d; ++mm)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int m = jb + mm;
-                    av[4 * mm + s] = At[(16 * ib + l16) * PF + 16 * m + 4 * s + lq];
-                    bv[4 * mm + s] = Tt[(16 * m + 4 * s + lq) * PF + 16 * jb + l16];
-                }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) tv[s] = Tt[(16 * ib + l16) * PF + 16 * ib + 4 * lq + s];
-            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < 4 * d; ++k) z = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], z, 0, 0, 0);
-            // z is in accumulator layout (lane holds rows 4*lq+s of column l16); use it as the
-            // right operand with k relabelled to 4*lq + s in step s.
-            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s], z[s], t, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
-        }
-        __syncthreads();
-    }
+    ut_subdiagonal<PF, 1>(At, Tt, wave, lane);
+    ut_subdiagonal<PF, 2>(At, Tt, wave, lane);
+    ut_subdiagonal<PF, 3>(At, Tt, wave, lane);
 }
 
 }  // namespace gdn
