@@ -182,8 +182,11 @@ __device__ __forceinline__ void write_kq_images(const PrepSmem<TIn, DK>& sm, _Fl
 }
 
 // Persistent work-groups: each walks (chunk, head) units with a stride of the grid, keeping
-// the next unit's inputs in flight in registers while the current one is computed.
-template <typename TIn, int DK>
+// the next unit's inputs in flight in registers while the current one is computed. BWD: the
+// instance run by the backward pass, which also keeps T (fp32, row-major) and writes the
+// operators row-major for its own kernels (fp32 inputs: fp32 Mmat, P and, when set, fp16
+// copies; bf16 inputs: fp32 P and fp16 Mmat and P).
+template <typename TIn, int DK, bool BWD>
 __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
     using SM = PrepSmem<TIn, DK>;
     using TM = typename SM::TM;
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                         sm.u.tri.A[r * PF + i] = a;
                         sm.P[r * PC + i] = from_f32<TM>(pp);
                         // backward pass, bf16 inputs: P also in fp32, row-major, before its rounding
-                        if (sizeof(TM) == 2 && p.tmat) static_cast<float*>(p.pmat)[widx * 4096 + r * 64 + i] = pp;
+                        if (sizeof(TM) == 2 && BWD) static_cast<float*>(p.pmat)[widx * 4096 + r * 64 + i] = pp;
                     }
                 }
             }
@@ -285,12 +288,12 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 }
                 store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
-                if (p.tmat) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
-                if (p.mmat16) {  // fp16 copies for the fp16-operand kernels of the backward pass
+                if (BWD) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
+                if (BWD && p.mmat16) {  // fp16 copies for the fp16-operand kernels of the backward pass
                     store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
                     store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
                 }
-            } else if (p.tmat) {  // backward pass, bf16 inputs: fp32 T, fp16 Mmat and P, row-major
+            } else if (BWD) {  // backward pass, bf16 inputs: fp32 T, fp16 Mmat and P, row-major
                 const int r = tid >> 2, c0 = (tid & 3) * 16;
                 float mv[16], pv[16], tv[16];
 #pragma unroll
@@ -970,7 +973,7 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
     return w;
 }
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, bool BWD>
 static void prep_launch(const ChunkProblem& p, hipStream_t s) {
     // persistent grid: as many work-groups as the device holds at once (queried once per
     // device), so that every (chunk, head) unit is taken by an already running work-group
@@ -980,7 +983,7 @@ static void prep_launch(const ChunkProblem& p, hipStream_t s) {
     int& cap = resident[dev & 63];
     if (cap == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<TIn, DK>, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<TIn, DK, BWD>, 256, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             per_cu < 1 || cus < 1)
             per_cu = 2, cus = 256;
@@ -988,7 +991,7 @@ static void prep_launch(const ChunkProblem& p, hipStream_t s) {
     }
     const long units = p.nc_bound * p.H;
     const long blocks = units < cap ? units : cap;
-    hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, p);
 }
 
 void launch_chunk_base(const ChunkProblem& p, hipStream_t s) {
@@ -997,14 +1000,20 @@ void launch_chunk_base(const ChunkProblem& p, hipStream_t s) {
                            p.chunk_base);
 }
 
+template <bool BWD>
+static void prep_dispatch(const ChunkProblem& p, hipStream_t s) {
+    if (p.bf16) {
+        if (p.dk == 64) prep_launch<uint16_t, 64, BWD>(p, s); else prep_launch<uint16_t, 128, BWD>(p, s);
+    } else {
+        if (p.dk == 64) prep_launch<float, 64, BWD>(p, s); else prep_launch<float, 128, BWD>(p, s);
+    }
+}
+
+// p.tmat set (the backward pass): the BWD instance
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
     launch_chunk_base(p, s);
     if (p.nc_bound > 0) {
-        if (p.bf16) {
-            if (p.dk == 64) prep_launch<uint16_t, 64>(p, s); else prep_launch<uint16_t, 128>(p, s);
-        } else {
-            if (p.dk == 64) prep_launch<float, 64>(p, s); else prep_launch<float, 128>(p, s);
-        }
+        if (p.tmat) prep_dispatch<true>(p, s); else prep_dispatch<false>(p, s);
     }
     return hipGetLastError();
 }
