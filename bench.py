@@ -54,6 +54,18 @@ def bwd_counts(dk, dv, C=CHUNK):
     return dict(state_flops=state, grad_flops=grad)
 
 
+def bwd_bytes(dk, dv, elem=2):
+    """Algorithmic HBM bytes per token-head of one backward call: q, k, v, dO read and dq, dk, dv
+    written (elem bytes each), g and beta read and dg, dbeta written (fp32)."""
+    return (2 * dk + 2 * dv) * elem + (2 * dk + dv) * elem + 16
+
+
+def kda_bytes(dk, dv, elem=2):
+    """Algorithmic HBM bytes per token-head of one channel-wise-decay forward call: q, k, v read
+    and o written (elem bytes each), the per-channel g (fp32, d_k) and beta read."""
+    return (2 * dk + 2 * dv) * elem + 4 * dk + 4
+
+
 def decode_bytes(dk, dv, elem=2, o_elem=4):
     """Bytes one decode step moves per (sequence, head): the fp32 state read and written,
     plus q, k, v (elem bytes), o (o_elem bytes) and the two gates."""
@@ -290,6 +302,43 @@ def cpu_baseline(seconds):
                       f"{el:.1f} s wall, {os.cpu_count()} host CPUs visible)"}
 
 
+def cpu_baseline_slices(kind, seconds):
+    """The fp64 numpy oracle of a path beyond the headline (kind "bwd": the gradient oracle,
+    "kda": the channel-wise-decay forward) on one (sequence, head) slice of the training-shape
+    workload at a time, over successive slices until `seconds` have passed, with one BLAS
+    thread. A slice is T tokens of one head, i.e. T / H tokens of the full workload."""
+    from threadpoolctl import threadpool_limits
+
+    from gated_delta_rule_42_amd import synthetic as SY
+    from oracle import backward as BW
+    from oracle import kda as KD
+
+    x = SY.make_forward_inputs(1)
+    B, T, H = x["q"].shape[0], x["q"].shape[1], x["q"].shape[2]
+    if kind == "bwd":
+        extra = SY.make_cotangents(x, 7, dhT=False)["do"]
+    else:
+        x = SY.channel_gates(x, 55)
+        extra = None
+    n, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            b, h = n % B, (n // B) % H
+            sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()  # noqa: E731
+            if kind == "bwd":
+                BW.backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), sl(extra))
+            else:
+                KD.forward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": n * T / H / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} (sequence, head) slices of T {T} of the B{B} H{H} T{T} d128 workload "
+                      f"({'gradient oracle' if kind == 'bwd' else 'channel-wise-decay oracle'}, "
+                      f"numpy fp64, one BLAS thread, {el:.1f} s wall), scaled to tokens of all {H} heads"}
+
+
 def calib_copy(torch, mb):
     n = mb * 1024 * 1024 // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -384,6 +433,7 @@ def main():
         ms = b["wall_s"] / args.bwd_steps * 1e3
         c = bwd_counts(b["dk"], b["dv"])
         fl = (c["state_flops"] + c["grad_flops"]) * th
+        bb = bwd_bytes(b["dk"], b["dv"]) * th
         out["bwd"] = {"workload": "chunkwise backward B4 H16 T2048 d_k=d_v=128 chunk 64, bf16 "
                                   "q/k/v/dO and gradients, fp16 matrix-core operands with fp32 "
                                   "accumulation, states and gate gradients, no h0 / dhT",
@@ -393,7 +443,15 @@ def main():
                       "mfma_frac": fl / (ms / 1e3) / PEAK_BF16_FLOPS,
                       "grad_kernel_flops_per_launch": c["grad_flops"] * th,
                       "state_kernel_flops_per_launch": c["state_flops"] * th,
-                      "mfma_peak_tflops": PEAK_BF16_FLOPS / 1e12}
+                      "mfma_peak_tflops": PEAK_BF16_FLOPS / 1e12,
+                      # whole call (four launches in one entry point): HBM is the nearer bound
+                      # (algorithmic bytes at peak take longer than algorithmic FLOP at peak)
+                      "roofline": {"kernel": "gdn_chunk_bwd (whole call)", "bound": "hbm",
+                                   "achieved": bb / (ms / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                                   "unit": "GB/s", "frac": bb / (ms / 1e3) / PEAK_HBM_BPS, "traffic": None,
+                                   "algorithmic_bytes_per_call": bb}}
+        if args.cpu_seconds > 0:
+            out["bwd"]["cpu_baseline"] = cpu_baseline_slices("bwd", args.cpu_seconds / 2)
         if args.only == "bwd":
             out["value"] = b["B"] * b["T"] / (ms / 1e3)
             out["ms_per_step"] = ms
@@ -414,6 +472,15 @@ def main():
                       "decode_hbm_frac": per / (dmean / 1e3) / PEAK_HBM_BPS,
                       "decoupled_gates_fwd_ms_per_step": k["dc_ms"],
                       "decoupled_gates_fwd_tokens_per_s": k["B"] * k["T"] / (k["dc_ms"] / 1e3)}
+        kb = kda_bytes(k["dk"], k["dv"]) * th
+        # the channel-wise-decay forward, whole call (two launches in one entry point): HBM is the
+        # nearer bound
+        out["kda"]["roofline"] = {"kernel": "gdn_kda_chunk_fwd (whole call)", "bound": "hbm",
+                                  "achieved": kb / (k["fwd_ms"] / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                                  "unit": "GB/s", "frac": kb / (k["fwd_ms"] / 1e3) / PEAK_HBM_BPS,
+                                  "traffic": None, "algorithmic_bytes_per_call": kb}
+        if args.cpu_seconds > 0:
+            out["kda"]["cpu_baseline"] = cpu_baseline_slices("kda", args.cpu_seconds / 2)
         if args.only == "kda":
             out["value"] = k["B"] * k["T"] / (k["fwd_ms"] / 1e3)
             out["ms_per_step"] = k["fwd_ms"]
