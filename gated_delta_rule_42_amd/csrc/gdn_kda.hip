@@ -19,9 +19,10 @@
 // practice "SOTA-135": the erased read runs along a reweighted key) the erased read runs along
 // E * k and the written value is W * v: the same chunk form with A's left factor E * K instead
 // of diag(beta) K, Kh = E * K * e^gamma, V replaced by W * V and Mmat = T.
-// Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head); stage 2
-// (kda_propagate_kernel) carries the state through the chunks. All arithmetic is fp32 (fp32
-// 16x16x4 matrix core); bf16 inputs are widened on load.
+// Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head) in fp32 (bf16
+// inputs widened on load; the operators are stored as fp16 for bf16 inputs); stage 2 carries the
+// fp32 state through the chunks: kda_propagate_kernel for fp32 inputs (fp32 16x16x4 matrix core),
+// kda_propagate16_kernel for bf16 inputs (fp16 16x16x32 matrix core, fp32 accumulation).
 //
 // A and P never form e^{-gamma} (it overflows under strong decay): every 16-row block uses a
 // reference at its first row, so the factor e^{gamma_r - gamma_ref} of a row is <= 1 and
