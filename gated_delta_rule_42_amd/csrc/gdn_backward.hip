@@ -201,64 +201,65 @@ struct alignas(16) BwdState16Smem {
 };
 
 // Register staging of one chunk's raw bf16 K, Q, dO, fp16 Mmat, P and the gate tables, so
-// that chunk c-1's loads are in flight while chunk c is computed.
+// that chunk c-1's loads are in flight while chunk c is computed. Every load is issued
+// unconditionally (rows past the chunk's end and lanes past the gate table read zeros through
+// buffer resources), with native vector types, so that the compiler's waits for the staged
+// registers count exactly and do not also wait for the state-gradient stores issued after them.
 template <int DK, int DV, int DVT>
 struct BwdState16Stage {
     static constexpr int NT = DVT / 16 * 64;
     static constexpr int NK = 64 * DK / 8 / NT, NM = 64 * 64 / 8 / NT, NO = 64 * DVT / 8 / NT;
-    uint4 rk[NK], rq[NK], rm[NM], rp[NM], ro[NO];
-    float4 rg;
+    u32x4_t rk[NK], rq[NK], rm[NM], rp[NM], ro[NO], rg;
 
     __device__ __forceinline__ void load(const ChunkProblem& p, const uint16_t* dop, long bos, int len,
                                          long widx, int h, int dv0, int tid) {
-        const int H = p.H;
-        const uint16_t* kp = static_cast<const uint16_t*>(p.k);
-        const uint16_t* qp = static_cast<const uint16_t*>(p.q);
+        const int H = p.H, DVF = p.dv;
+        const long o = (bos * H + h) * DK;
+        const unsigned kbytes = (unsigned)((len - 1) * H * DK + DK) * 2;
+        const auto kr = make_rsrc(static_cast<const uint16_t*>(p.k) + o, kbytes);
+        const auto qr = make_rsrc(static_cast<const uint16_t*>(p.q) + o, kbytes);
 #pragma unroll
         for (int it = 0; it < NK; ++it) {
-            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8);
-            rk[it] = rq[it] = zero16();
-            if (r < len) {
-                const long o = ((bos + r) * H + h) * DK + 8 * cv;
-                rk[it] = *reinterpret_cast<const uint4*>(kp + o);
-                rq[it] = *reinterpret_cast<const uint4*>(qp + o);
-            }
+            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8), off = (r * H * DK + 8 * cv) * 2;
+            rk[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+            rq[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
         }
 #pragma unroll
         for (int it = 0; it < NM; ++it) {
-            rm[it] = reinterpret_cast<const uint4*>(p.mmat16 + widx * 4096)[tid + NT * it];
-            rp[it] = reinterpret_cast<const uint4*>(p.pmat16 + widx * 4096)[tid + NT * it];
+            rm[it] = reinterpret_cast<const u32x4_t*>(p.mmat16 + widx * 4096)[tid + NT * it];
+            rp[it] = reinterpret_cast<const u32x4_t*>(p.pmat16 + widx * 4096)[tid + NT * it];
         }
+        const auto orr = make_rsrc(dop + (bos * H + h) * DVF + dv0, (unsigned)((len - 1) * H * DVF + DVT) * 2);
 #pragma unroll
         for (int it = 0; it < NO; ++it) {
             const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
-            ro[it] = r < len ? *reinterpret_cast<const uint4*>(dop + ((bos + r) * H + h) * p.dv + dv0 + 8 * cv)
-                             : zero16();
+            ro[it] = __builtin_amdgcn_raw_buffer_load_b128(orr, (r * H * DVF + 8 * cv) * 2, 0, 0);
         }
-        if (tid < 32) rg = reinterpret_cast<const float4*>(p.gates + widx * 128)[tid];
+        rg = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.gates + widx * 128, 512u), tid * 16, 0, 0);
     }
 
     __device__ __forceinline__ void store(BwdState16Smem<DK, DVT>& sm, int tid) const {
         using SM = BwdState16Smem<DK, DVT>;
         using KL = typename SM::KL;
+        auto u4 = [](u32x4_t x) { return make_uint4(x[0], x[1], x[2], x[3]); };
 #pragma unroll
         for (int it = 0; it < NK; ++it) {
             const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8);
-            *reinterpret_cast<uint4*>(&sm.K[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(rk[it]);
-            *reinterpret_cast<uint4*>(&sm.Q[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(rq[it]);
+            *reinterpret_cast<uint4*>(&sm.K[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(u4(rk[it]));
+            *reinterpret_cast<uint4*>(&sm.Q[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(u4(rq[it]));
         }
 #pragma unroll
         for (int it = 0; it < NM; ++it) {
             const int vi = tid + NT * it, r = vi / 8, cv = vi % 8;
-            *reinterpret_cast<uint4*>(&sm.M[r * SM::PC + 8 * cv]) = rm[it];
-            *reinterpret_cast<uint4*>(&sm.P[r * SM::PC + 8 * cv]) = rp[it];
+            *reinterpret_cast<u32x4_t*>(&sm.M[r * SM::PC + 8 * cv]) = rm[it];
+            *reinterpret_cast<u32x4_t*>(&sm.P[r * SM::PC + 8 * cv]) = rp[it];
         }
 #pragma unroll
         for (int it = 0; it < NO; ++it) {
             const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
-            *reinterpret_cast<uint4*>(&sm.dO[r * SM::PV + 8 * cv]) = to_operand16<uint16_t>(ro[it]);
+            *reinterpret_cast<uint4*>(&sm.dO[r * SM::PV + 8 * cv]) = to_operand16<uint16_t>(u4(ro[it]));
         }
-        if (tid < 32) reinterpret_cast<float4*>(sm.gt)[tid] = rg;
+        if (tid < 32) reinterpret_cast<u32x4_t*>(sm.gt)[tid] = rg;
     }
 };
 
@@ -310,7 +311,10 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state16_kernel(ChunkP
         __syncthreads();  // the previous chunk's LDS data is dead
         stage.store(sm, tid);
         __syncthreads();
-        if (jc > 0) stage.load(p, dop, sbos + (jc - 1) * 64, chunk_len(jc - 1), widx - H, h, dv0, tid);
+        {   // the chunk before (chunk 0 again at the end: every pass loads)
+            const long jn = jc > 0 ? jc - 1 : 0;
+            stage.load(p, dop, sbos + jn * 64, chunk_len(jn), (cbase + jn) * H + h, h, dv0, tid);
+        }
 
         float* ds = dstates + (widx * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
