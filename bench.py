@@ -462,7 +462,8 @@ def main():
         dmean = sum(k["dec_ms"]) / len(k["dec_ms"])
         per = (decode_bytes(k["dk"], k["dv"]) + 4 * (k["dk"] - 1)) * k["N"] * k["Hd"]
         out["kda"] = {"workload": "channel-wise decay: chunkwise forward B4 H16 T2048 d128 bf16 q/k/v/o "
-                                  "(fp32 stage 1; stage 2 on fp16 matrix-core operands with fp32 "
+                                  "(stage 1 fp32, its Gram blocks below the diagonal on fp16 operands; stage 2 on fp16 "
+                                  "matrix-core operands with fp32 "
                                   "accumulation and state), and decode 256 seq x H32 d128 (16 chained steps)",
                       "fwd_ms_per_step": k["fwd_ms"], "fwd_ms_median": median(k["fwd_step_ms"]),
                       "fwd_tokens_per_s": k["B"] * k["T"] / (k["fwd_ms"] / 1e3),

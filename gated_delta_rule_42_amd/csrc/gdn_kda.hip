@@ -20,7 +20,8 @@
 // E * k and the written value is W * v: the same chunk form with A's left factor E * K instead
 // of diag(beta) K, Kh = E * K * e^gamma, V replaced by W * V and Mmat = T.
 // Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head) in fp32 (bf16
-// inputs widened on load; the operators are stored as fp16 for bf16 inputs); stage 2 carries the
+// inputs widened on load; the operators are stored as fp16 for bf16 inputs; for bf16 inputs the
+// Gram blocks below the diagonal blocks take fp16 operands, see gram_rows_of); stage 2 carries the
 // fp32 state through the chunks: kda_propagate_kernel for fp32 inputs (fp32 16x16x4 matrix core),
 // kda_propagate16_kernel for bf16 inputs (fp16 16x16x32 matrix core, fp32 accumulation).
 //
@@ -66,35 +67,146 @@ struct alignas(16) KdaPrepSmem {
 // Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}], i < 16 (I + 1),
 // for one or two left operands L1, L2 (sharing the right operand K and the exponentials), into
 // O1 (times rs1[r] when rs1 is set; strictly lower when strict1) and O2 (lower including the
-// diagonal). All column blocks on the fp32 matrix core with the reference gamma of row 16 I:
+// diagonal). Column blocks on the fp32 matrix core with the reference gamma of row 16 I:
 // left factor L[r] e^{gamma_r - gamma_ref} (<= |L|: r >= ref), right factor
 // K[i] e^{gamma_ref - gamma_i}, which is <= |K| below the diagonal block (i < ref) and, in the
 // diagonal block, grows with the channel's decay over the block's rows. A channel whose decay
 // over the block exceeds e^kMaxRange is left out of the diagonal block's product and summed
 // there exactly instead (one exponent per term), so no factor exceeds e^kMaxRange.
+//
+// F16 (bf16 inputs): the blocks below the diagonal block (J < I) go to the fp16 matrix core
+// instead, factored through the last row of column block J: the left factor
+// L[r] e^{gamma_r - gamma_last(J)} = (L[r] e^{gamma_r - gamma_ref}) e^{gamma_ref - gamma_last(J)}
+// and the right factor K[i] e^{gamma_last(J) - gamma_i} are both <= |L|, |K| (rows r > last(J)
+// >= i, and gamma does not increase down the chunk), so nothing overflows fp16; a factor that
+// underflows belongs to a term below fp16's resolution of the entry. The right factors depend
+// on J alone: wave J forms them once as fp16 fragments (zf) for the waves below it, and wave I
+// forms its channel scalars e^{gamma_ref - gamma_last(J)} (ss); see gram_offdiag_prep.
 constexpr float kMaxRange = 60.f;
-template <int DK, bool TWO, int I>
+
+// Scratch of the fp16 off-diagonal products (in the T buffer, which the UT transform fills
+// only after the Gram products): zf[J][s][lane] = the right-operand fragment of column block J
+// (J < 3) for d_k slice s, ss[pair][c] = e^{gamma_ref(I) - gamma_last(J)} for pair
+// I (I - 1) / 2 + J.
+template <int DK>
+struct KdaOffdiag {
+    static constexpr int NS = DK / 32;
+    static constexpr int BYTES = 3 * NS * 64 * 16 + 6 * DK * 4;
+    uint4* zf;
+    float* ss;
+    __device__ __forceinline__ explicit KdaOffdiag(float* base)
+        : zf(reinterpret_cast<uint4*>(base)), ss(base + 3 * NS * 64 * 4) {}
+};
+
+// Wave I's share of the scratch: the right-operand fragments of column block I (I < 3; lane
+// (l16, lq) holds row 16 I + l16, channels 32 s + 4 lq + 0..3 and 32 s + 16 + 4 lq + 0..3, the
+// k-slot order of the products) and the channel scalars of its pairs (I > 0).
+template <int DK, int I>
+__device__ __forceinline__ void gram_offdiag_prep(const KdaPrepSmem<DK>& sm, KdaOffdiag<DK> od, int lane) {
+    constexpr int PK = KdaPrepSmem<DK>::PK, NS = KdaOffdiag<DK>::NS;
+    const int l16 = lane & 15, lq = lane >> 4;
+    if constexpr (I < 3) {
+        const int i = 16 * I + l16, last = 16 * I + 15;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int c0 = 32 * s + 4 * lq;
+            uint32_t w[4];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4_t k = *reinterpret_cast<const f32x4_t*>(&sm.K[i * PK + c0 + 16 * hf]);
+                const f32x4_t g = *reinterpret_cast<const f32x4_t*>(&sm.G[i * PK + c0 + 16 * hf]);
+                const f32x4_t gl = *reinterpret_cast<const f32x4_t*>(&sm.G[last * PK + c0 + 16 * hf]);
+                w[2 * hf] = pack_f16x2(k[0] * __expf(gl[0] - g[0]), k[1] * __expf(gl[1] - g[1]));
+                w[2 * hf + 1] = pack_f16x2(k[2] * __expf(gl[2] - g[2]), k[3] * __expf(gl[3] - g[3]));
+            }
+            od.zf[(I * NS + s) * 64 + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+#pragma unroll
+    for (int J = 0; J < I; ++J)
+#pragma unroll
+        for (int c = lane; c < DK; c += 64)
+            od.ss[(I * (I - 1) / 2 + J) * DK + c] = __expf(sm.G[16 * I * PK + c] - sm.G[(16 * J + 15) * PK + c]);
+}
+
+template <int DK, bool TWO, int I, bool F16>
 __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
-                                             float* O1, float* O2, const float* rs1, bool strict1, int lane) {
+                                             float* O1, float* O2, const float* rs1, bool strict1,
+                                             KdaOffdiag<DK> od, int lane) {
     constexpr int PK = KdaPrepSmem<DK>::PK, PF = KdaPrepSmem<DK>::PF;
     const int l16 = lane & 15, lq = lane >> 4;
     f32x4_t a1[4], a2[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) a1[J] = a2[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < DK; k0 += 4) {
-        const int ch = k0 + lq;
-        const float gref = sm.G[16 * I * PK + ch];
-        const bool fits = gref - sm.G[(16 * I + 15) * PK + ch] <= kMaxRange;
-        const float el = __expf(sm.G[(16 * I + l16) * PK + ch] - gref);
-        const float x1 = L1[(16 * I + l16) * PK + ch] * el;
-        const float x2 = TWO ? L2[(16 * I + l16) * PK + ch] * el : 0.f;
+    if constexpr (F16 && I > 0) {
+        constexpr int NS = KdaOffdiag<DK>::NS;
+        const int r = 16 * I + l16;
+#pragma unroll 1
+        for (int s = 0; s < NS; ++s) {
+            const int c0 = 32 * s + 4 * lq;
+            float x1[8], x2[8];
 #pragma unroll
-        for (int J = 0; J <= I; ++J) {
-            const int i = 16 * J + l16;
-            const float b = sm.K[i * PK + ch] * __expf(gref - sm.G[i * PK + ch]);
-            const float bb = (J < I || fits) ? b : 0.f;
-            a1[J] = mfma4(x1, bb, a1[J]);
-            if constexpr (TWO) a2[J] = mfma4(x2, bb, a2[J]);
+            for (int hf = 0; hf < 2; ++hf) {
+                const int c = c0 + 16 * hf;
+                const f32x4_t g = *reinterpret_cast<const f32x4_t*>(&sm.G[r * PK + c]);
+                const f32x4_t gf = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
+                const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[r * PK + c]);
+                f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[r * PK + c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float el = __expf(g[e] - gf[e]);
+                    x1[4 * hf + e] = l1[e] * el;
+                    x2[4 * hf + e] = l2[e] * el;
+                }
+            }
+#pragma unroll
+            for (int J = 0; J < I; ++J) {
+                const float* sc = od.ss + (I * (I - 1) / 2 + J) * DK;
+                const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(&sc[c0]);
+                const f32x4_t sb = *reinterpret_cast<const f32x4_t*>(&sc[c0 + 16]);
+                const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+                const uint4 bz = od.zf[(J * NS + s) * 64 + lane];
+                const uint4 f1 = make_uint4(pack_f16x2(x1[0] * sv[0], x1[1] * sv[1]), pack_f16x2(x1[2] * sv[2], x1[3] * sv[3]),
+                                            pack_f16x2(x1[4] * sv[4], x1[5] * sv[5]), pack_f16x2(x1[6] * sv[6], x1[7] * sv[7]));
+                a1[J] = mfma_f16(f1, bz, a1[J]);
+                if constexpr (TWO) {
+                    const uint4 f2 = make_uint4(pack_f16x2(x2[0] * sv[0], x2[1] * sv[1]), pack_f16x2(x2[2] * sv[2], x2[3] * sv[3]),
+                                                pack_f16x2(x2[4] * sv[4], x2[5] * sv[5]), pack_f16x2(x2[6] * sv[6], x2[7] * sv[7]));
+                    a2[J] = mfma_f16(f2, bz, a2[J]);
+                }
+            }
+        }
+    }
+    // fp32 products: lane (l16, lq) takes channels 16 u + 4 lq + e, e = 0..3, in product (u, e),
+    // so its operands arrive as 16-byte reads
+    constexpr int J0 = F16 ? I : 0;  // first column block on the fp32 matrix core
+    for (int u = 0; u < DK / 16; ++u) {
+        const int c = 16 * u + 4 * lq;
+        const f32x4_t gref = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
+        const f32x4_t glast = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + 15) * PK + c]);
+        const f32x4_t grow = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + l16) * PK + c]);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[(16 * I + l16) * PK + c]);
+        f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[(16 * I + l16) * PK + c]);
+        f32x4_t kj[I + 1], gj[I + 1];
+#pragma unroll
+        for (int J = J0; J <= I; ++J) {
+            kj[J] = *reinterpret_cast<const f32x4_t*>(&sm.K[(16 * J + l16) * PK + c]);
+            gj[J] = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * J + l16) * PK + c]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool fits = gref[e] - glast[e] <= kMaxRange;
+            const float el = __expf(grow[e] - gref[e]);
+            const float x1 = l1[e] * el, x2 = l2[e] * el;
+#pragma unroll
+            for (int J = J0; J <= I; ++J) {
+                const float b = kj[J][e] * __expf(gref[e] - gj[J][e]);
+                const float bb = (J < I || fits) ? b : 0.f;
+                a1[J] = mfma4(x1, bb, a1[J]);
+                if constexpr (TWO) a2[J] = mfma4(x2, bb, a2[J]);
+            }
         }
     }
 #pragma unroll
@@ -131,15 +243,26 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
 
 // gram_rows_of for the row block of this wave (the row block is a compile-time constant of each
 // wave's code, so its loops are static)
-template <int DK, bool TWO>
+// (F16: the scratch is filled first, then a barrier.) Called by all 256 threads.
+template <int DK, bool TWO, bool F16>
 __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
                                           float* O1, float* O2, const float* rs1, bool strict1,
-                                          int wave, int lane) {
+                                          float* scratch, int wave, int lane) {
+    const KdaOffdiag<DK> od(scratch);
+    if constexpr (F16) {
+        switch (wave) {
+            case 0: gram_offdiag_prep<DK, 0>(sm, od, lane); break;
+            case 1: gram_offdiag_prep<DK, 1>(sm, od, lane); break;
+            case 2: gram_offdiag_prep<DK, 2>(sm, od, lane); break;
+            default: gram_offdiag_prep<DK, 3>(sm, od, lane); break;
+        }
+        __syncthreads();
+    }
     switch (wave) {
-        case 0: gram_rows_of<DK, TWO, 0>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
-        case 1: gram_rows_of<DK, TWO, 1>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
-        case 2: gram_rows_of<DK, TWO, 2>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
-        default: gram_rows_of<DK, TWO, 3>(sm, L1, L2, O1, O2, rs1, strict1, lane); break;
+        case 0: gram_rows_of<DK, TWO, 0, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
+        case 1: gram_rows_of<DK, TWO, 1, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
+        case 2: gram_rows_of<DK, TWO, 2, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
+        default: gram_rows_of<DK, TWO, 3, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
     }
 }
 
@@ -219,6 +342,8 @@ template <typename TIn, int DK, bool DEC>
 __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     using SM = KdaPrepSmem<DK>;
     constexpr int PK = SM::PK, PF = SM::PF;
+    constexpr bool F16 = sizeof(TIn) == 2;  // off-diagonal Gram blocks on the fp16 matrix core
+    static_assert(KdaOffdiag<DK>::BYTES <= (int)sizeof(SM::T), "off-diagonal scratch fits in T");
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = p.H;
@@ -287,7 +412,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
 
         // -- A and P
         if constexpr (DEC) {
-            gram_rows<DK, false>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, wave, lane);
+            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, sm.T, wave, lane);
             __syncthreads();  // E * K is dead: load Q in its place
             for (int i = tid; i < 64 * DK / 4; i += 256) {
                 const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
@@ -297,9 +422,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
             }
             __syncthreads();
             write_scaled(false);
-            gram_rows<DK, false>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, wave, lane);
+            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, sm.T, wave, lane);
         } else {
-            gram_rows<DK, true>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, wave, lane);
+            gram_rows<DK, true, F16>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, sm.T, wave, lane);
         }
         __syncthreads();
 

@@ -237,7 +237,9 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
  *               Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk] e^{gamma_last}
  *               (gamma: per-channel in-chunk cumulative sum of g), all row-major, with
  *               op = fp32 for fp32 inputs and fp16 for bf16 inputs.
- * Stage 1 computes in fp32 (bf16 inputs widened on load). Stage 2 multiplies fp32 operators
+ * Stage 1 computes in fp32 (bf16 inputs widened on load), except that for bf16 inputs the
+ * products below the 16x16 diagonal blocks of A and P take fp16 operands (every gate factor
+ * there is at most 1) with fp32 accumulation. Stage 2 multiplies fp32 operators
  * on the fp32 matrix core, and for bf16 inputs fp16 operators (the state packed to fp16 as
  * an operand, fp32 accumulation), as gdn_chunk_fwd does; a bf16 o is the fp32 result rounded
  * to nearest even.
