@@ -795,34 +795,40 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         lo[o] = (_Float16)(x - (float)h);
     };
 
-    for (int i = tid; i < 64 * DK / 8; i += 256) {
-        const int r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-        uint4 kv = zero16(), qv = kv;
-        if (r < len) {
-            kv = to_operand16<uint16_t>(*reinterpret_cast<const uint4*>(kp + ((bos + r) * H + h) * DK + cc));
-            qv = to_operand16<uint16_t>(*reinterpret_cast<const uint4*>(qp + ((bos + r) * H + h) * DK + cc));
+    // The unit's first loads are all issued before any is used (one memory latency instead of
+    // one per group): K, Q (rows past the chunk's end read as zeros through resources sized to
+    // the valid rows), T and P, the gates and, further below, the first d_v slice.
+    constexpr int NKQ = 64 * DK / 8 / 256;
+    u32x4_t kin[NKQ], qin[NKQ];
+    {
+        const unsigned kbytes = (unsigned)((len - 1) * H * DK + DK) * 2;
+        const auto kr = make_rsrc(kp + (bos * H + h) * DK, kbytes);
+        const auto qr = make_rsrc(qp + (bos * H + h) * DK, kbytes);
+#pragma unroll
+        for (int it = 0; it < NKQ; ++it) {
+            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8)), off = (r * H * DK + cc) * 2;
+            kin[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+            qin[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
         }
-        *reinterpret_cast<uint4*>(&sm.K[r * PK + cc]) = kv;
-        *reinterpret_cast<uint4*>(&sm.Q[r * PK + cc]) = qv;
     }
-    for (int i = tid; i < 64 * 8; i += 256) {
-        const int r = i / 8, cc = 8 * (i % 8);
-        const float* tp = p.tmat + widx * 4096 + r * 64 + cc;
-        const float* pq = static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc;
-        *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) =
-            pack8(*reinterpret_cast<const float4*>(tp), *reinterpret_cast<const float4*>(tp + 4));
-        const float4 p0 = *reinterpret_cast<const float4*>(pq), p1 = *reinterpret_cast<const float4*>(pq + 4);
-        const uint4 ph = pack8(p0, p1);
-        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) = ph;
-        *reinterpret_cast<uint4*>(&sm.Plo[r * PT + cc]) = resid8(p0, p1, ph);
+    f32x4_t tin[2][2], pin[2][2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
+        const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(p.tmat + widx * 4096 + r * 64 + cc);
+        const f32x4_t* pq = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc);
+        tin[it][0] = tp[0];
+        tin[it][1] = tp[1];
+        pin[it][0] = pq[0];
+        pin[it][1] = pq[1];
     }
+    float gin = 0.f, bin = 0.f, egin = 0.f, edin = 0.f;
     if (wave == 0) {
-        const long o = (bos + lane) * H + h;
-        const float gr = lane < len ? p.g[o] : 0.f;
-        sm.beta[lane] = lane < len ? p.beta[o] : 0.f;
-        sm.gam[lane] = wave_inclusive_sum(gr);
-        sm.eg[lane] = p.gates[widx * 128 + lane];
-        sm.ed[lane] = p.gates[widx * 128 + 64 + lane];
+        const unsigned gbytes = (unsigned)(((len - 1) * H + 1) * 4);
+        gin = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.g + bos * H + h, gbytes), lane * H * 4, 0, 0));
+        bin = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.beta + bos * H + h, gbytes), lane * H * 4, 0, 0));
+        egin = p.gates[widx * 128 + lane];
+        edin = p.gates[widx * 128 + 64 + lane];
     }
 
     const int row = 16 * wave + l16;   // this lane's row as a left operand
@@ -868,6 +874,29 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     };
     auto f4 = [](f32x4_t x) { return make_float4(x[0], x[1], x[2], x[3]); };
     load_slice(0);
+#pragma unroll
+    for (int it = 0; it < NKQ; ++it) {
+        const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+        *reinterpret_cast<uint4*>(&sm.K[r * PK + cc]) =
+            to_operand16<uint16_t>(make_uint4(kin[it][0], kin[it][1], kin[it][2], kin[it][3]));
+        *reinterpret_cast<uint4*>(&sm.Q[r * PK + cc]) =
+            to_operand16<uint16_t>(make_uint4(qin[it][0], qin[it][1], qin[it][2], qin[it][3]));
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
+        *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) = pack8(f4(tin[it][0]), f4(tin[it][1]));
+        const float4 p0 = f4(pin[it][0]), p1 = f4(pin[it][1]);
+        const uint4 ph = pack8(p0, p1);
+        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) = ph;
+        *reinterpret_cast<uint4*>(&sm.Plo[r * PT + cc]) = resid8(p0, p1, ph);
+    }
+    if (wave == 0) {
+        sm.beta[lane] = bin;
+        sm.gam[lane] = wave_inclusive_sum(gin);
+        sm.eg[lane] = egin;
+        sm.ed[lane] = edin;
+    }
 
     for (int js = 0; js < DV / 32; ++js) {
         const int dv0 = 32 * js;
