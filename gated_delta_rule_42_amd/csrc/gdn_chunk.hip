@@ -59,35 +59,6 @@ __global__ __launch_bounds__(1024) void chunk_base_kernel(const int32_t* __restr
     if (tid == 1023) base[N] = part[1023];
 }
 
-// ------------------------------------------------------- LDS images (bf16 inputs)
-// For bf16 inputs stage 1 stores the fp16 operands of stage 2 (K, diag(e^gamma) Q: W = d_k
-// columns; Mmat, P: W = 64) as byte images of the LDS tiles stage 2 reads, so that stage 2
-// copies them with plain 1 KB DMA blocks. A row is cut into 16-byte pieces; piece pc holds
-// the 8 contraction indices one lane feeds to a 16x16x32 product, columns
-// 32(pc>>2) + 4(pc&3) + 0..3 then the same + 16, and sits at position pc ^ img_swz<W>(r)
-// of row r. With that permutation the row-fragment reads (16 rows x 16 bytes per quarter
-// wave) and the transposing reads of K (4 rows x 32 bytes per quarter wave) touch distinct
-// banks.
-template <int W>
-__device__ __forceinline__ int img_swz(int r) {
-    if constexpr (W == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-    else return (r >> 1) & 7;  // W = 64: two rows per 256-byte bank line
-}
-// element offset, in a [64, W] image, of the 4-element run at column c (c % 4 == 0) of row r
-template <int W>
-__device__ __forceinline__ int img_off(int r, int c) {
-    const int s = c >> 5, a = (c >> 4) & 1, m = (c >> 2) & 3;
-    return r * W + 8 * ((4 * s + m) ^ img_swz<W>(r)) + 4 * a;
-}
-// source columns of image piece i (pieces numbered in storage order): c0 .. c0+3, c0+16 .. c0+19
-template <int W>
-__device__ __forceinline__ void img_piece(int i, int& r, int& c0) {
-    constexpr int NP = W / 8;
-    r = i / NP;
-    const int pc = (i % NP) ^ img_swz<W>(r);
-    c0 = 32 * (pc >> 2) + 4 * (pc & 3);
-}
-
 // ------------------------------------------------------------------- stage 1
 template <typename TIn, int DK>
 struct alignas(16) PrepSmem {
@@ -632,16 +603,6 @@ struct alignas(16) MPVChunk {
     float ed[64];          // e^{gamma_last - gamma_r}
 };
 
-// Output staging for one chunk: the compute waves leave o^T tiles here and the store wave
-// writes them out as whole rows of the work-group's columns. Rows are padded by 16 bytes so
-// that the compute waves' 4-column writes of 16 consecutive tokens fall in distinct banks.
-template <typename TO, int DVT>
-struct alignas(16) OStage {
-    static constexpr int ROWB = DVT * (int)sizeof(TO);  // bytes of one token's columns
-    static constexpr int PITCH = ROWB + 16;
-    char b[64 * PITCH];
-};
-
 // The DMA wave's copies for one chunk, as 1 KB DMA blocks: the Q image (copy_kq), and the K
 // image, Mmat, P, the gate tables and V (copy_mpv; V rows gathered from the input, rows past the
 // chunk's end read as zeros). copy_mpv issues kMpvCopies instructions.
@@ -679,18 +640,6 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
         dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
         dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
     }
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Work-group barrier that orders LDS accesses only: the waves' global stores and copies are
-// not waited for (the DMA wave waits for its own copies explicitly).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // One work-group per (sequence, head, DVT-column tile) with DVT/16 compute waves, one DMA wave

@@ -23,7 +23,10 @@
 // inputs widened on load; the operators are stored as fp16 for bf16 inputs; for bf16 inputs the
 // Gram blocks below the diagonal blocks take fp16 operands, see gram_rows_of); stage 2 carries the
 // fp32 state through the chunks: kda_propagate_kernel for fp32 inputs (fp32 16x16x4 matrix core),
-// kda_propagate16_kernel for bf16 inputs (fp16 16x16x32 matrix core, fp32 accumulation).
+// for bf16 inputs kda_propagate_dma_kernel (operators copied into LDS by a DMA wave from the
+// images stage 1 writes) or, with decoupled gates, kda_propagate16_kernel (register-staged, the
+// write gate applied to V on the way), both on the fp16 16x16x32 matrix core with fp32
+// accumulation.
 //
 // A and P never form e^{-gamma} (it overflows under strong decay): every 16-row block uses a
 // reference at its first row, so the factor e^{gamma_r - gamma_ref} of a row is <= 1 and
@@ -343,6 +346,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     using SM = KdaPrepSmem<DK>;
     constexpr int PK = SM::PK, PF = SM::PF;
     constexpr bool F16 = sizeof(TIn) == 2;  // off-diagonal Gram blocks on the fp16 matrix core
+    // bf16 without decoupled gates: the operators go out as the LDS images the DMA-fed stage 2
+    // copies (kda_propagate_dma_kernel); otherwise row-major
+    constexpr bool IMG = sizeof(TIn) == 2 && !DEC;
     static_assert(KdaOffdiag<DK>::BYTES <= (int)sizeof(SM::T), "off-diagonal scratch fits in T");
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
                 const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
                 const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
                 const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
-                const long o = (widx * 64 + r) * DK + cc;
+                const long o = widx * 64 * DK + (IMG ? img_off<DK>(r, cc) : r * DK + cc);
                 const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
                 if (!kside) {
                     put4(qhat + o, x);
@@ -440,8 +446,19 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
                 mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
                 pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
             }
-            store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
-            store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+            if constexpr (IMG) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int o = img_off<64>(r, c0 + 4 * q4);
+                    put4(static_cast<TM*>(p.mmat) + widx * 4096 + o,
+                         make_float4(mv[4 * q4], mv[4 * q4 + 1], mv[4 * q4 + 2], mv[4 * q4 + 3]));
+                    put4(static_cast<TM*>(p.pmat) + widx * 4096 + o,
+                         make_float4(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]));
+                }
+            } else {
+                store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
+                store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+            }
         }
         unit = nxt; ok = nok; bos = nbos; len = nlen;
     }
@@ -807,6 +824,278 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkPro
     }
 }
 
+// ------------------------------------- stage 2, bf16 inputs without decoupled gates (DMA)
+// The products of kda_propagate16_kernel with the operands copied global -> LDS by the DMA
+// path of the buffer loads (no registers, no conversion), as the scalar-gate stage 2 for bf16
+// inputs does: stage 1 leaves Kh, Qh, Kd, Mmat and P as LDS images (img_off), V stays bf16 and
+// enters only the fp32 residual. Per work-group: DVT/16 compute waves (16 columns each), a DMA
+// wave and a store wave. A chunk's operands take 68.5 KB of LDS (Kd beside Kh), so both rings
+// are two deep: the DMA wave copies chunk c+1 while chunk c is computed and, before the next
+// barrier, waits for all of it. The compute waves differ from the scalar-gate ones in three
+// places: the residual is V - Kh S^T (Kh carries the decay), the state's columns decay by lam
+// one channel each, and K^T of the state update is read from Kd.
+template <int DK, int DVT>
+struct alignas(16) KdaDmaChunk {
+    _Float16 Q[64 * DK];    // Qh
+    _Float16 K[64 * DK];    // Kh
+    _Float16 Kd[64 * DK];
+    _Float16 M[64 * 64];    // Mmat
+    _Float16 P[64 * 64];
+    uint16_t V[64 * DVT];   // bf16, the work-group's d_v columns
+    float lam[DK];          // e^{gamma_last} per channel
+};
+// The DMA wave's copies of one chunk: 1 KB blocks of the images, V rows gathered from the
+// input (rows past the chunk's end read as zeros), lam.
+template <int DK, int DV, int DVT>
+__device__ __forceinline__ void kda_copy(KdaDmaChunk<DK, DVT>& dst, const ChunkProblem& p, long bos, int len,
+                                         long widx, int h, int dv0, int lane) {
+    constexpr int NB_K = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
+    const int H = p.H;
+    const unsigned lo = 16u * lane;
+    auto img = [&](const float* base, long elems) {
+        return reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(base) + elems);
+    };
+    const char* qimg = img(p.qhat, widx * 64 * DK);
+    const char* kimg = img(p.khat, widx * 64 * DK);
+    const char* dimg = img(p.kdec, widx * 64 * DK);
+    const char* mimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.mmat) + widx * 4096);
+    const char* pimg = reinterpret_cast<const char*>(static_cast<const _Float16*>(p.pmat) + widx * 4096);
+    const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
+    const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
+    if (lane < DK / 4) dma16g(reinterpret_cast<const char*>(p.lam + widx * DK), lo, dst.lam);
+#pragma unroll
+    for (int b = 0; b < NB_V; ++b) {
+        const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
+        dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
+    }
+#pragma unroll
+    for (int b = 0; b < NB_K; ++b) {
+        dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
+        dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
+        dma16g(dimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Kd) + 1024 * b);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
+        dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+    }
+}
+
+template <typename TO, int DK, int DV, int DVT>
+__global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(ChunkProblem p) {
+    using CH = KdaDmaChunk<DK, DVT>;
+    using OS = OStage<TO, DVT>;
+    constexpr int NW = DVT / 16;   // compute waves
+    constexpr int NKB = DK / 16;   // d_k tiles of the state
+    constexpr int NKS = DK / 32;   // 32-wide d_k slices
+    constexpr int NTILE = DV / DVT;
+    __shared__ CH ch[2];
+    __shared__ OS ost[2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+
+    // (sequence, head) pair and column tile; with a pair count divisible by 8 the tiles of one
+    // pair get block ids equal modulo 8 (same XCD, shared L2 for the pair's operators)
+    const long NP = (long)p.N * H;
+    const long bid = blockIdx.x;
+    long pair;
+    int tile;
+    if (NP % 8 == 0) {
+        const long x = bid % 8, i = bid / 8;
+        tile = (int)(i % NTILE);
+        pair = (i / NTILE) * 8 + x;
+    } else {
+        pair = bid / NTILE;
+        tile = (int)(bid % NTILE);
+    }
+    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int dv0 = tile * DVT;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + 63) / 64;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+    auto chunk_len = [&](long jc) {
+        const long l = seos - (sbos + jc * 64);
+        return (int)(l < 64 ? l : 64);
+    };
+
+    if (wave == NW) {
+        // ------------------------------------------------------------------- DMA wave
+        auto copy = [&](long jc) {
+            kda_copy<DK, DV, DVT>(ch[jc & 1], p, sbos + jc * 64, chunk_len(jc), (cbase + jc) * H + h, h, dv0, lane);
+        };
+        if (nchunks > 0) copy(0);
+        for (long jc = 0; jc < nchunks; ++jc) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            lds_barrier();  // chunk jc's operands are in LDS; chunk jc-1's buffers are free
+            if (jc + 1 < nchunks) copy(jc + 1);
+        }
+        lds_barrier();
+        return;
+    }
+    if (wave == NW + 1) {
+        // ----------------------------------------------------------------- store wave
+        // outputs of chunk jc through a resource sized to the valid rows; NV adjacent lanes
+        // write one token row's columns (16 bytes each), so an instruction covers 64/NV rows
+        auto store_out = [&](const OS& os, long jc) {
+            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16, RPI = 64 / NV;
+            const long obos = sbos + jc * 64;
+            const int olen = chunk_len(jc);
+            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
+                                       (unsigned)((olen - 1) * H * DV + DVT) * E);
+            const int rr = lane / NV, pc = lane % NV;
+            u32x4_t piece[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                piece[i] = *reinterpret_cast<const u32x4_t*>(&os.b[(RPI * i + rr) * OS::PITCH + 16 * pc]);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(piece[i], orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
+        };
+        for (long jc = 0; jc < nchunks; ++jc) {
+            lds_barrier();
+            if (jc > 0) store_out(ost[(jc - 1) & 1], jc - 1);
+        }
+        lds_barrier();  // the last chunk's outputs are staged
+        if (nchunks > 0) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
+        return;
+    }
+
+    // ------------------------------------------------------------------- compute waves
+    // wave w: columns dv0 + 16w .. +15; lane holds S[dv0 + 16w + l16][16j + 4lq + 0..3] in ST[j]
+    const int dvw = dv0 + 16 * wave;
+    f32x4_t ST[NKB];
+    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+    {
+        // the initial state through a resource of zero size when there is none (loads read 0)
+        const auto hr = make_rsrc(p.h0 ? p.h0 + (pair * DV + dvw) * DK : nullptr, p.h0 ? (unsigned)(16 * DK * 4) : 0u);
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            ST[j] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, (l16 * DK + 4 * lq + 16 * j) * 4, 0, 0));
+    }
+
+    auto step = [&](const CH& cm, OS& os) {
+        lds_barrier();  // chunk data in cm; os free
+        uint4 MF[4][2], PF[4][2];
+        float4 V4[4];
+        auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    f[t][hf] = *reinterpret_cast<const uint4*>(&src[img_off<64>(16 * t + l16, 32 * hf + 4 * lq)]);
+        };
+
+        // X = Kh S^T [64 tokens x 16 columns] and Y^T = S Qh^T [16 columns x 64 tokens]
+        uint4 BS[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_f16_frag(ST[2 * s], ST[2 * s + 1]);
+        uint4 KF[2][4], QF[2][4];  // fragments of slice s in [s % 2]
+        auto load_xy = [&](int s, uint4 (&kf)[4], uint4 (&qf)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int row = 16 * t + l16, c0 = 32 * s + 4 * lq;
+                kf[t] = *reinterpret_cast<const uint4*>(&cm.K[img_off<DK>(row, c0)]);
+                qf[t] = *reinterpret_cast<const uint4*>(&cm.Q[img_off<DK>(row, c0)]);
+            }
+        };
+        load_xy(0, KF[0], QF[0]);
+        f32x4_t X[4], Y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            X[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int b = s & 1;
+            if (s + 1 < NKS) {
+                load_xy(s + 1, KF[b ^ 1], QF[b ^ 1]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) V4[t] = load4_t<uint16_t>(&cm.V[(16 * t + 4 * lq) * DVT + 16 * wave], DVT);
+                load_mp(cm.M, MF);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                X[t] = mfma_f16(KF[b][t], BS[s], X[t]);
+                Y[t] = mfma_f16(BS[s], QF[b][t], Y[t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // R = V - X;  Delta = Mmat R
+        load_mp(cm.P, PF);
+        f32x4_t R[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            R[t] = f32x4_t{V4[t].x - X[t][0], V4[t].y - X[t][1], V4[t].z - X[t][2], V4[t].w - X[t][3]};
+        const uint4 BR[2] = {pack_f16_frag(R[0], R[1]), pack_f16_frag(R[2], R[3])};
+        f32x4_t D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) D[t] = mfma_f16(MF[t][hf], BR[hf], D[t]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Kd^T fragments for the state update, read while the output product runs
+        const int tr = l16 >> 2, tc = 4 * (l16 & 3);
+        uint4 KT[NKB][2];
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+            const int c = 16 * j + tc;
+            KT[j][0] = lds_frag2_t(&cm.Kd[img_off<DK>(4 * lq + tr, c)], &cm.Kd[img_off<DK>(16 + 4 * lq + tr, c)]);
+            KT[j][1] = lds_frag2_t(&cm.Kd[img_off<DK>(32 + 4 * lq + tr, c)], &cm.Kd[img_off<DK>(48 + 4 * lq + tr, c)]);
+        }
+
+        // O^T = S Qh^T + Delta^T P^T, staged in LDS for the store wave (lane: token 16t + l16,
+        // columns 16 wave + 4 lq .. +3)
+        const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
+        f32x4_t O[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) O[t] = Y[t];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            char* dst = &os.b[(16 * t + l16) * OS::PITCH + (16 * wave + 4 * lq) * (int)sizeof(TO)];
+            if constexpr (sizeof(TO) == 2)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(O[t][0], O[t][1]), pack_bf16x2(O[t][2], O[t][3]));
+            else
+                *reinterpret_cast<float4*>(dst) = make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+        }
+
+        // S^T <- Diag(lam) S^T + Kd^T Delta
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) ST[j] *= *reinterpret_cast<const f32x4_t*>(&cm.lam[16 * j + 4 * lq]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BD[hf], ST[j]);
+    };
+
+    for (long jc = 0; jc < nchunks; ++jc) step(ch[jc & 1], ost[jc & 1]);
+    lds_barrier();  // hand the last chunk's outputs to the store wave
+
+    if (p.hT) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    }
+}
+
 // -------------------------------------------------------------------- launchers
 KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -851,9 +1140,14 @@ static void kda_launch(const ChunkProblem& p, hipStream_t s) {
     }
     const long pairs = (long)p.N * p.H;
     if (pairs > 0) {
-        if constexpr (sizeof(TIn) == 2)
-            hipLaunchKernelGGL((kda_propagate16_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                               dim3(DVT / 16 * 64), 0, s, p);
+        if constexpr (sizeof(TIn) == 2) {
+            if (p.erase == nullptr)   // the images of kda_prepare_kernel<..., false>
+                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                                   dim3((DVT / 16 + 2) * 64), 0, s, p);
+            else
+                hipLaunchKernelGGL((kda_propagate16_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
+                                   dim3(DVT / 16 * 64), 0, s, p);
+        }
         else
             hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
                                dim3(DVT / 16 * 64), 0, s, p);

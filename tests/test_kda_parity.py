@@ -50,6 +50,9 @@ KDA_SMALL = [
     (1, 257, 2, 128, 64, "bf16", True, 0.05),
     (1, 1, 2, 128, 128, "bf16", True, 1.0),
     (1, 190, 2, 128, 128, "f32", True, 5.0),     # strong decay: up to e^-30 per token
+    (1, 200, 2, 64, 64, "bf16", False, 1.0),
+    (1, 100, 2, 64, 128, "bf16", True, 1.0),
+    (1, 190, 2, 128, 128, "bf16", True, 5.0),
 ]
 
 
