@@ -24,9 +24,8 @@
 // Gram blocks below the diagonal blocks take fp16 operands, see gram_rows_of); stage 2 carries the
 // fp32 state through the chunks: kda_propagate_kernel for fp32 inputs (fp32 16x16x4 matrix core),
 // for bf16 inputs kda_propagate_dma_kernel (operators copied into LDS by a DMA wave from the
-// images stage 1 writes) or, with decoupled gates, kda_propagate16_kernel (register-staged, the
-// write gate applied to V on the way), both on the fp16 16x16x32 matrix core with fp32
-// accumulation.
+// images stage 1 writes; with decoupled gates the write gate is copied beside V), on the fp16
+// 16x16x32 matrix core with fp32 accumulation.
 //
 // A and P never form e^{-gamma} (it overflows under strong decay): every 16-row block uses a
 // reference at its first row, so the factor e^{gamma_r - gamma_ref} of a row is <= 1 and
@@ -346,9 +345,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
     using SM = KdaPrepSmem<DK>;
     constexpr int PK = SM::PK, PF = SM::PF;
     constexpr bool F16 = sizeof(TIn) == 2;  // off-diagonal Gram blocks on the fp16 matrix core
-    // bf16 without decoupled gates: the operators go out as the LDS images the DMA-fed stage 2
-    // copies (kda_propagate_dma_kernel); otherwise row-major
-    constexpr bool IMG = sizeof(TIn) == 2 && !DEC;
+    // bf16: the operators go out as the LDS images the DMA-fed stage 2 copies
+    // (kda_propagate_dma_kernel); fp32: row-major
+    constexpr bool IMG = sizeof(TIn) == 2;
     static_assert(KdaOffdiag<DK>::BYTES <= (int)sizeof(SM::T), "off-diagonal scratch fits in T");
     __shared__ SM sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -607,234 +606,21 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate_kernel(ChunkProbl
     }
 }
 
-// --------------------------------------------------- stage 2, bf16 inputs (fp16 operands)
-template <int DK, int DVT>
-struct alignas(16) KdaProp16Smem {
-    using KL = KQLayout<_Float16, DK>;
-    static constexpr int PK = KL::kPitch, PC = 72, PV = DVT + 4;
-    _Float16 Kh[64 * PK];
-    _Float16 Qh[64 * PK];
-    _Float16 Kd[64 * PK];
-    _Float16 M[64 * PC];
-    _Float16 P[64 * PC];
-    float V[64 * PV];
-    float lam[DK];
-};
-
-// One chunk's stage-2 inputs, staged in registers: the fp16 Kh, Qh, Kd, Mmat and P of the
-// workspace, the raw bf16 V columns of the work-group (and the write gate with decoupled
-// gates) and lam. Every load is issued unconditionally, rows past the chunk's end through
-// buffer resources that read them as zeros.
-template <int DK, int DVT, int NT>
-struct KdaStage16 {
-    using KL = typename KdaProp16Smem<DK, DVT>::KL;
-    static constexpr int PC = KdaProp16Smem<DK, DVT>::PC, PV = KdaProp16Smem<DK, DVT>::PV;
-    static constexpr int NKQ = 64 * DK / 8 / NT;   // 16-byte pieces per thread of Kh, Qh, Kd
-    static constexpr int NMP = 64 * 8 / NT;        // of Mmat and P
-    static constexpr int NV = 64 * DVT / 4 / NT;   // groups of 4 values of V
-    // native vector types: a struct-typed element copy would go through memory
-    u32x4_t kh[NKQ], qh[NKQ], kd[NKQ], m[NMP], pm[NMP];
-    u32x2_t v[NV];
-    f32x4_t w[NV];
-    float lam;
-
-    __device__ __forceinline__ void load(const ChunkProblem& p, long bos, int len, long widx, int h, int dv0,
-                                         int tid) {
-        const int H = p.H, DV = p.dv;
-        const _Float16* kh_ = reinterpret_cast<const _Float16*>(p.khat) + widx * 64 * DK;
-        const _Float16* qh_ = reinterpret_cast<const _Float16*>(p.qhat) + widx * 64 * DK;
-        const _Float16* kd_ = reinterpret_cast<const _Float16*>(p.kdec) + widx * 64 * DK;
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-            const int i = tid + NT * it;
-            kh[it] = reinterpret_cast<const u32x4_t*>(kh_)[i];
-            qh[it] = reinterpret_cast<const u32x4_t*>(qh_)[i];
-            kd[it] = reinterpret_cast<const u32x4_t*>(kd_)[i];
-        }
-#pragma unroll
-        for (int it = 0; it < NMP; ++it) {
-            const int i = tid + NT * it;
-            m[it] = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.mmat) + widx * 4096)[i];
-            pm[it] = reinterpret_cast<const u32x4_t*>(static_cast<const _Float16*>(p.pmat) + widx * 4096)[i];
-        }
-        const long vo = (bos * H + h) * DV + dv0;
-        const unsigned vrows = (unsigned)((len - 1) * H * DV + DVT);
-        const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + vo, vrows * 2);
-        const auto wr = make_rsrc(p.write ? p.write + vo : nullptr, p.write ? vrows * 4 : 0u);
-#pragma unroll
-        for (int it = 0; it < NV; ++it) {
-            const int i = tid + NT * it, r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
-            v[it] = __builtin_amdgcn_raw_buffer_load_b64(vr, (r * H * DV + cc) * 2, 0, 0);
-            w[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, (r * H * DV + cc) * 4, 0, 0));
-        }
-        lam = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.lam + widx * DK, DK * 4), tid * 4, 0, 0));
-    }
-
-    __device__ __forceinline__ void store(KdaProp16Smem<DK, DVT>& sm, bool write_gate, int tid) const {
-#pragma unroll
-        for (int it = 0; it < NKQ; ++it) {
-            const int i = tid + NT * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-            *reinterpret_cast<u32x4_t*>(&sm.Kh[KL::off(r, cc)]) = kh[it];
-            *reinterpret_cast<u32x4_t*>(&sm.Qh[KL::off(r, cc)]) = qh[it];
-            *reinterpret_cast<u32x4_t*>(&sm.Kd[KL::off(r, cc)]) = kd[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NMP; ++it) {
-            const int i = tid + NT * it, r = i / 8, cc = 8 * (i % 8);
-            *reinterpret_cast<u32x4_t*>(&sm.M[r * PC + cc]) = m[it];
-            *reinterpret_cast<u32x4_t*>(&sm.P[r * PC + cc]) = pm[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NV; ++it) {
-            const int i = tid + NT * it, r = i / (DVT / 4), cc = 4 * (i % (DVT / 4));
-            f32x4_t x = {__uint_as_float(v[it][0] << 16), __uint_as_float(v[it][0] & 0xffff0000u),
-                         __uint_as_float(v[it][1] << 16), __uint_as_float(v[it][1] & 0xffff0000u)};
-            if (write_gate) x = {x[0] * w[it][0], x[1] * w[it][1], x[2] * w[it][2], x[3] * w[it][3]};  // w * v
-            *reinterpret_cast<f32x4_t*>(&sm.V[r * PV + cc]) = x;
-        }
-        if (tid < DK) sm.lam[tid] = lam;
-    }
-};
-
-// The stage-2 products of kda_propagate_kernel on the fp16 matrix core (16x16x32, fp32
-// accumulation), as the scalar-gate path multiplies bf16 inputs: stage 1 left Kh, Qh, Kd, Mmat
-// and P in fp16, the state is packed to fp16 as an operand and kept in fp32. The next chunk's
-// inputs are loaded into registers while the current one is computed.
-template <typename TO, int DK, int DV, int DVT>
-__global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate16_kernel(ChunkProblem p) {
-    using SM = KdaProp16Smem<DK, DVT>;
-    using KL = typename SM::KL;
-    constexpr int PC = SM::PC, PV = SM::PV, NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
-    constexpr int NT = DVT / 16 * 64;
-    __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
-    const int H = p.H;
-    const long pair = blockIdx.x / NTILE;
-    const int tile = (int)(blockIdx.x % NTILE);
-    const int n = (int)(pair / H), h = (int)(pair % H);
-    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
-
-    long sbos, seos;
-    seq_range(p, n, sbos, seos);
-    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
-    long nchunks = (seos - sbos + 63) / 64;
-    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
-
-    f32x4_t ST[NKB];
-    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
-#pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        if (p.h0) {
-            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
-            ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
-        } else {
-            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    auto chunk_at = [&](long jc, long& bos, int& len, long& widx) {
-        bos = sbos + jc * 64;
-        len = (int)min(64L, seos - bos);
-        widx = (cbase + jc) * H + h;
-    };
-    KdaStage16<DK, DVT, NT> stage;
-    if (nchunks > 0) {
-        long b0, w0;
-        int l0;
-        chunk_at(0, b0, l0, w0);
-        stage.load(p, b0, l0, w0, h, dv0, tid);
-    }
-    const bool write_gate = p.write != nullptr;
-    for (long jc = 0; jc < nchunks; ++jc) {
-        long bos, widx;
-        int len;
-        chunk_at(jc, bos, len, widx);
-        __syncthreads();  // the previous chunk's LDS data is dead
-        stage.store(sm, write_gate, tid);
-        __syncthreads();
-        {   // the next chunk's inputs (the last chunk's again past the end: every pass loads)
-            long nb, nw;
-            int nl;
-            chunk_at(jc + 1 < nchunks ? jc + 1 : jc, nb, nl, nw);
-            stage.load(p, nb, nl, nw, h, dv0, tid);
-        }
-        const auto orr = make_rsrc(static_cast<TO*>(p.o) + (bos * H + h) * DV,
-                                   (unsigned)(((len - 1) * H * DV + DV) * (int)sizeof(TO)));
-
-        // X = Kh S^T, Y = Qh S^T (rows: tokens)
-        Frag<_Float16> BS[NKS];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) BS[s] = pack_frag<_Float16>(ST[2 * s], ST[2 * s + 1]);
-        f32x4_t X[4], Y[4], D[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            X[t] = Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const int row = 16 * t + l16;
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const int c0 = 32 * s + 4 * lq, c1 = c0 + 16;
-                mma_k32(X[t], load_frag2<_Float16>(&sm.Kh[KL::off(row, c0)], &sm.Kh[KL::off(row, c1)]), BS[s]);
-                mma_k32(Y[t], load_frag2<_Float16>(&sm.Qh[KL::off(row, c0)], &sm.Qh[KL::off(row, c1)]), BS[s]);
-            }
-        }
-        // R = V - X, Delta = Mmat R, O = Y + P Delta
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) X[t][m] = sm.V[(16 * t + 4 * lq + m) * PV + 16 * wave + l16] - X[t][m];
-        const Frag<_Float16> BR0 = pack_frag<_Float16>(X[0], X[1]), BR1 = pack_frag<_Float16>(X[2], X[3]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const _Float16* mrow = &sm.M[(16 * t + l16) * PC + 4 * lq];
-            mma_k32(D[t], load_frag2<_Float16>(mrow, mrow + 16), BR0);
-            mma_k32(D[t], load_frag2<_Float16>(mrow + 32, mrow + 48), BR1);
-        }
-        const Frag<_Float16> BD0 = pack_frag<_Float16>(D[0], D[1]), BD1 = pack_frag<_Float16>(D[2], D[3]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4_t O = Y[t];
-            const _Float16* prow = &sm.P[(16 * t + l16) * PC + 4 * lq];
-            mma_k32(O, load_frag2<_Float16>(prow, prow + 16), BD0);
-            mma_k32(O, load_frag2<_Float16>(prow + 32, prow + 48), BD1);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {   // rows past the chunk's end fall outside orr
-                const int off = ((16 * t + 4 * lq + m) * H * DV + dvw + l16) * (int)sizeof(TO);
-                if constexpr (sizeof(TO) == 2)
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(O[m]), orr, off, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m]), orr, off, 0, 0);
-            }
-        }
-        // S^T <- Diag(lam) S^T + Kd^T Delta
-#pragma unroll
-        for (int j = 0; j < NKB; ++j) {
-            f32x4_t acc;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = ST[j][m] * sm.lam[16 * j + 4 * lq + m];
-            mma_k32(acc, load_kt<_Float16, DK>(sm.Kd, 4 * lq, 16 + 4 * lq, j), BD0);
-            mma_k32(acc, load_kt<_Float16, DK>(sm.Kd, 32 + 4 * lq, 48 + 4 * lq, j), BD1);
-            ST[j] = acc;
-        }
-    }
-    if (p.hT) {
-#pragma unroll
-        for (int j = 0; j < NKB; ++j)
-            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
-    }
-}
-
-// ------------------------------------- stage 2, bf16 inputs without decoupled gates (DMA)
-// The products of kda_propagate16_kernel with the operands copied global -> LDS by the DMA
-// path of the buffer loads (no registers, no conversion), as the scalar-gate stage 2 for bf16
-// inputs does: stage 1 leaves Kh, Qh, Kd, Mmat and P as LDS images (img_off), V stays bf16 and
-// enters only the fp32 residual. Per work-group: DVT/16 compute waves (16 columns each), a DMA
-// wave and a store wave. A chunk's operands take 68.5 KB of LDS (Kd beside Kh), so both rings
-// are two deep: the DMA wave copies chunk c+1 while chunk c is computed and, before the next
-// barrier, waits for all of it. The compute waves differ from the scalar-gate ones in three
-// places: the residual is V - Kh S^T (Kh carries the decay), the state's columns decay by lam
-// one channel each, and K^T of the state update is read from Kd.
-template <int DK, int DVT>
+// ------------------------------------------------------------- stage 2, bf16 inputs (DMA)
+// The products of kda_propagate_kernel on the fp16 matrix core (16x16x32, fp32 accumulation),
+// with the operands copied global -> LDS by the DMA path of the buffer loads (no registers, no
+// conversion), as the scalar-gate stage 2 for bf16 inputs does: stage 1 leaves Kh, Qh, Kd,
+// Mmat and P as LDS images (img_off), V stays bf16 and enters only the fp32 residual (times
+// the write gate W with decoupled gates: WG). Per work-group: DVT/16 compute waves (16 columns
+// each), a DMA wave and, without W, a store wave that writes o from an LDS staging buffer as in
+// the scalar-gate kernel; with W (8 KB more per chunk, no room for the staging buffer) the
+// compute waves write o themselves, four adjacent lanes covering 16 consecutive columns of a
+// token. A chunk's operands take 68.5 KB of LDS (Kd beside Kh; 76.5 KB with W), so the ring is
+// two deep: the DMA wave copies chunk c+1 while chunk c is computed and, before the next
+// barrier, waits for all of it. The compute waves differ from the
+// scalar-gate ones in three places: the residual is V - Kh S^T (Kh carries the decay), the
+// state's columns decay by lam one channel each, and K^T of the state update is read from Kd.
+template <int DK, int DVT, bool WG>
 struct alignas(16) KdaDmaChunk {
     _Float16 Q[64 * DK];    // Qh
     _Float16 K[64 * DK];    // Kh
@@ -843,11 +629,12 @@ struct alignas(16) KdaDmaChunk {
     _Float16 P[64 * 64];
     uint16_t V[64 * DVT];   // bf16, the work-group's d_v columns
     float lam[DK];          // e^{gamma_last} per channel
+    float W[WG ? 64 * DVT : 4];  // the write gate of those columns (decoupled gates)
 };
-// The DMA wave's copies of one chunk: 1 KB blocks of the images, V rows gathered from the
-// input (rows past the chunk's end read as zeros), lam.
-template <int DK, int DV, int DVT>
-__device__ __forceinline__ void kda_copy(KdaDmaChunk<DK, DVT>& dst, const ChunkProblem& p, long bos, int len,
+// The DMA wave's copies of one chunk: 1 KB blocks of the images, V (and W) rows gathered from
+// the inputs (rows past the chunk's end read as zeros), lam.
+template <int DK, int DV, int DVT, bool WG>
+__device__ __forceinline__ void kda_copy(KdaDmaChunk<DK, DVT, WG>& dst, const ChunkProblem& p, long bos, int len,
                                          long widx, int h, int dv0, int lane) {
     constexpr int NB_K = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
     const int H = p.H;
@@ -868,6 +655,15 @@ __device__ __forceinline__ void kda_copy(KdaDmaChunk<DK, DVT>& dst, const ChunkP
         const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
         dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
     }
+    if constexpr (WG) {
+        constexpr int NB_W = 64 * DVT * 4 / 1024, ROW_W = DVT * 4;
+        const auto wr = make_rsrc(p.write + (bos * H + h) * DV + dv0, (unsigned)((len - 1) * H * DV + DVT) * 4);
+#pragma unroll
+        for (int b = 0; b < NB_W; ++b) {
+            const int byte = 1024 * b + 16 * lane, r = byte / ROW_W;
+            dma16(wr, reinterpret_cast<const char*>(dst.W) + 1024 * b, r * H * DV * 4 + 16 * ((byte % ROW_W) >> 4));
+        }
+    }
 #pragma unroll
     for (int b = 0; b < NB_K; ++b) {
         dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
@@ -881,16 +677,17 @@ __device__ __forceinline__ void kda_copy(KdaDmaChunk<DK, DVT>& dst, const ChunkP
     }
 }
 
-template <typename TO, int DK, int DV, int DVT>
-__global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(ChunkProblem p) {
-    using CH = KdaDmaChunk<DK, DVT>;
+template <typename TO, int DK, int DV, int DVT, bool WG>
+__global__ __launch_bounds__((DVT / 16 + (WG ? 1 : 2)) * 64) void kda_propagate_dma_kernel(ChunkProblem p) {
+    using CH = KdaDmaChunk<DK, DVT, WG>;
     using OS = OStage<TO, DVT>;
     constexpr int NW = DVT / 16;   // compute waves
     constexpr int NKB = DK / 16;   // d_k tiles of the state
     constexpr int NKS = DK / 32;   // 32-wide d_k slices
     constexpr int NTILE = DV / DVT;
+    constexpr int NOS = WG ? 1 : 2;  // output staging (unused with W)
     __shared__ CH ch[2];
-    __shared__ OS ost[2];
+    __shared__ OS ost[NOS];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -927,7 +724,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
     if (wave == NW) {
         // ------------------------------------------------------------------- DMA wave
         auto copy = [&](long jc) {
-            kda_copy<DK, DV, DVT>(ch[jc & 1], p, sbos + jc * 64, chunk_len(jc), (cbase + jc) * H + h, h, dv0, lane);
+            kda_copy<DK, DV, DVT, WG>(ch[jc & 1], p, sbos + jc * 64, chunk_len(jc), (cbase + jc) * H + h, h, dv0, lane);
         };
         if (nchunks > 0) copy(0);
         for (long jc = 0; jc < nchunks; ++jc) {
@@ -935,35 +732,38 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
             lds_barrier();  // chunk jc's operands are in LDS; chunk jc-1's buffers are free
             if (jc + 1 < nchunks) copy(jc + 1);
         }
-        lds_barrier();
+        if constexpr (!WG) lds_barrier();
         return;
     }
-    if (wave == NW + 1) {
-        // ----------------------------------------------------------------- store wave
-        // outputs of chunk jc through a resource sized to the valid rows; NV adjacent lanes
-        // write one token row's columns (16 bytes each), so an instruction covers 64/NV rows
-        auto store_out = [&](const OS& os, long jc) {
-            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16, RPI = 64 / NV;
-            const long obos = sbos + jc * 64;
-            const int olen = chunk_len(jc);
-            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
-                                       (unsigned)((olen - 1) * H * DV + DVT) * E);
-            const int rr = lane / NV, pc = lane % NV;
-            u32x4_t piece[NV];
+    if constexpr (!WG) {
+        if (wave == NW + 1) {
+            // ------------------------------------------------------------- store wave
+            // outputs of chunk jc through a resource sized to the valid rows; NV adjacent
+            // lanes write one token row's columns (16 bytes each), so an instruction covers
+            // 64/NV rows
+            auto store_out = [&](const OS& os, long jc) {
+                constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16, RPI = 64 / NV;
+                const long obos = sbos + jc * 64;
+                const int olen = chunk_len(jc);
+                const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
+                                           (unsigned)((olen - 1) * H * DV + DVT) * E);
+                const int rr = lane / NV, pc = lane % NV;
+                u32x4_t piece[NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                piece[i] = *reinterpret_cast<const u32x4_t*>(&os.b[(RPI * i + rr) * OS::PITCH + 16 * pc]);
+                for (int i = 0; i < NV; ++i)
+                    piece[i] = *reinterpret_cast<const u32x4_t*>(&os.b[(RPI * i + rr) * OS::PITCH + 16 * pc]);
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(piece[i], orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
-        };
-        for (long jc = 0; jc < nchunks; ++jc) {
-            lds_barrier();
-            if (jc > 0) store_out(ost[(jc - 1) & 1], jc - 1);
+                for (int i = 0; i < NV; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b128(piece[i], orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
+            };
+            for (long jc = 0; jc < nchunks; ++jc) {
+                lds_barrier();
+                if (jc > 0) store_out(ost[(jc - 1) & 1], jc - 1);
+            }
+            lds_barrier();  // the last chunk's outputs are staged
+            if (nchunks > 0) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
+            return;
         }
-        lds_barrier();  // the last chunk's outputs are staged
-        if (nchunks > 0) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
-        return;
     }
 
     // ------------------------------------------------------------------- compute waves
@@ -980,8 +780,9 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
                 f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, (l16 * DK + 4 * lq + 16 * j) * 4, 0, 0));
     }
 
-    auto step = [&](const CH& cm, OS& os) {
-        lds_barrier();  // chunk data in cm; os free
+    constexpr int E = (int)sizeof(TO);
+    auto step = [&](const CH& cm, long jc) {
+        lds_barrier();  // chunk data in cm
         uint4 MF[4][2], PF[4][2];
         float4 V4[4];
         auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
@@ -1031,8 +832,15 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // R = V - X;  Delta = Mmat R
+        // R = V - X (W * V - X with decoupled gates);  Delta = Mmat R
         load_mp(cm.P, PF);
+        if constexpr (WG) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float* wc = &cm.W[(16 * t + 4 * lq) * DVT + 16 * wave + l16];
+                V4[t] = make_float4(V4[t].x * wc[0], V4[t].y * wc[DVT], V4[t].z * wc[2 * DVT], V4[t].w * wc[3 * DVT]);
+            }
+        }
         f32x4_t R[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -1057,8 +865,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
             KT[j][1] = lds_frag2_t(&cm.Kd[img_off<DK>(32 + 4 * lq + tr, c)], &cm.Kd[img_off<DK>(48 + 4 * lq + tr, c)]);
         }
 
-        // O^T = S Qh^T + Delta^T P^T, staged in LDS for the store wave (lane: token 16t + l16,
-        // columns 16 wave + 4 lq .. +3)
+        // O^T = S Qh^T + Delta^T P^T (lane: token 16t + l16, columns 16 wave + 4 lq .. +3): staged
+        // for the store wave, or with W out through a resource sized to the chunk's valid rows
         const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
         f32x4_t O[4];
 #pragma unroll
@@ -1067,13 +875,21 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+        if constexpr (WG) {
+            const auto orr = make_rsrc(static_cast<TO*>(p.o) + ((sbos + jc * 64) * H + h) * DV + dv0,
+                                       (unsigned)((chunk_len(jc) - 1) * H * DV + DVT) * E);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            char* dst = &os.b[(16 * t + l16) * OS::PITCH + (16 * wave + 4 * lq) * (int)sizeof(TO)];
-            if constexpr (sizeof(TO) == 2)
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(O[t][0], O[t][1]), pack_bf16x2(O[t][2], O[t][3]));
-            else
-                *reinterpret_cast<float4*>(dst) = make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+            for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + 16 * wave + 4 * lq) * E, O[t]);
+        } else {
+            OS& os = ost[jc & 1];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                char* dst = &os.b[(16 * t + l16) * OS::PITCH + (16 * wave + 4 * lq) * E];
+                if constexpr (E == 2)
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(O[t][0], O[t][1]), pack_bf16x2(O[t][2], O[t][3]));
+                else
+                    *reinterpret_cast<float4*>(dst) = make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+            }
         }
 
         // S^T <- Diag(lam) S^T + Kd^T Delta
@@ -1086,8 +902,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void kda_propagate_dma_kernel(
             for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BD[hf], ST[j]);
     };
 
-    for (long jc = 0; jc < nchunks; ++jc) step(ch[jc & 1], ost[jc & 1]);
-    lds_barrier();  // hand the last chunk's outputs to the store wave
+    for (long jc = 0; jc < nchunks; ++jc) step(ch[jc & 1], jc);
+    if constexpr (!WG) lds_barrier();  // hand the last chunk's outputs to the store wave
 
     if (p.hT) {
 #pragma unroll
@@ -1141,12 +957,12 @@ static void kda_launch(const ChunkProblem& p, hipStream_t s) {
     const long pairs = (long)p.N * p.H;
     if (pairs > 0) {
         if constexpr (sizeof(TIn) == 2) {
-            if (p.erase == nullptr)   // the images of kda_prepare_kernel<..., false>
-                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                                   dim3((DVT / 16 + 2) * 64), 0, s, p);
+            if (p.write == nullptr)
+                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT, false>),
+                                   dim3((unsigned)(pairs * (DV / DVT))), dim3((DVT / 16 + 2) * 64), 0, s, p);
             else
-                hipLaunchKernelGGL((kda_propagate16_kernel<TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                                   dim3(DVT / 16 * 64), 0, s, p);
+                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT, true>),
+                                   dim3((unsigned)(pairs * (DV / DVT))), dim3((DVT / 16 + 1) * 64), 0, s, p);
         }
         else
             hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),

@@ -237,8 +237,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
  *               Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk] e^{gamma_last}
  *               (gamma: per-channel in-chunk cumulative sum of g), with op = fp32 for fp32
  *               inputs and fp16 for bf16 inputs; row-major, except that for bf16 inputs the
- *               op arrays are stored as the LDS images of gdn_chunk_fwd's workspace (the
- *               decoupled-gate entry point below keeps them row-major).
+ *               op arrays are stored as the LDS images of gdn_chunk_fwd's workspace.
  * Stage 1 computes in fp32 (bf16 inputs widened on load), except that for bf16 inputs the
  * products below the 16x16 diagonal blocks of A and P take fp16 operands (every gate factor
  * there is at most 1) with fp32 accumulation. Stage 2 multiplies fp32 operators
