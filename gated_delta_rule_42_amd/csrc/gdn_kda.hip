@@ -64,6 +64,7 @@ struct alignas(16) KdaPrepSmem {
     float T[64 * PF];
     float P[64 * PF];
     float beta[64];
+    float tot[1024];    // per row block of the gamma scan: the block's sum of g, per channel
 };
 
 // Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}], i < 16 (I + 1),
@@ -275,6 +276,8 @@ __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float
 template <typename TIn, int DK, bool DEC>
 struct KdaPrepStage {
     static constexpr int NP = 64 * DK / 4 / 256;   // groups of 4 values per thread
+    // thread tid holds channels 4 (tid % NG) .. +3 of the NP consecutive rows NP (tid / NG) + it
+    static constexpr int NG = DK / 4, RB = 256 / NG;
     static constexpr int EB = (int)sizeof(TIn);    // bytes of an input element
     u32x4_t k[NP], q[NP];                         // raw groups (bf16: the low 8 bytes)
     f32x4_t g[NP], e[NP];
@@ -306,7 +309,7 @@ struct KdaPrepStage {
         const auto er = make_rsrc(DEC ? p.erase + o : p.g, DEC ? rows * 4 : 0u);
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
-            const int i = tid + 256 * it, r = i / (DK / 4), cc = 4 * (i % (DK / 4)), x = r * H * DK + cc;
+            const int r = NP * (tid / NG) + it, cc = 4 * (tid % NG), x = r * H * DK + cc;
             k[it] = raw4(kr, x * EB);
             q[it] = raw4(qr, x * EB);
             g[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(gr, x * 4, 0, 0));
@@ -316,20 +319,33 @@ struct KdaPrepStage {
         beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, tid * H * 4, 0, 0));
     }
 
-    // K, g and (Q, or E * K with decoupled gates) into LDS as fp32
-    __device__ __forceinline__ void store(KdaPrepSmem<DK>& sm, int tid) const {
+    // K and (Q, or E * K with decoupled gates) into LDS as fp32; g scanned down the thread's
+    // rows in registers, the row block's sum into tot
+    __device__ __forceinline__ void store(KdaPrepSmem<DK>& sm, int tid) {
         constexpr int PK = KdaPrepSmem<DK>::PK;
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
-            const int i = tid + 256 * it, r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const int r = NP * (tid / NG) + it, cc = 4 * (tid % NG);
             const float4 kv = widen(k[it]);
             const float4 qv = DEC ? make_float4(e[it][0] * kv.x, e[it][1] * kv.y, e[it][2] * kv.z, e[it][3] * kv.w)
                                   : widen(q[it]);
             *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
             *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
-            *reinterpret_cast<f32x4_t*>(&sm.G[r * PK + cc]) = g[it];
+            if (it > 0) g[it] += g[it - 1];
         }
+        *reinterpret_cast<f32x4_t*>(&sm.tot[(tid / NG) * DK + 4 * (tid % NG)]) = g[NP - 1];
         if (tid < 64) sm.beta[tid] = beta;
+    }
+    // gamma (the in-chunk inclusive cumulative sum of g, per channel) into LDS: the thread's
+    // rows plus the sums of the row blocks above them. Between a barrier after store and one
+    // before gamma is read.
+    __device__ __forceinline__ void finish_scan(KdaPrepSmem<DK>& sm, int tid) const {
+        constexpr int PK = KdaPrepSmem<DK>::PK;
+        const int rb = tid / NG, cc = 4 * (tid % NG);
+        f32x4_t pre = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < rb; ++b) pre += *reinterpret_cast<const f32x4_t*>(&sm.tot[b * DK + cc]);
+#pragma unroll
+        for (int it = 0; it < NP; ++it) *reinterpret_cast<f32x4_t*>(&sm.G[(NP * rb + it) * PK + cc]) = g[it] + pre;
     }
 };
 
@@ -379,16 +395,10 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
         __syncthreads();  // the previous unit is done with LDS
         stage.store(sm, tid);
         __syncthreads();
+        // gamma: rows past the chunk's end add 0
+        stage.finish_scan(sm, tid);
         if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
         else stage.load(p, bos, len, h, tid);
-        // gamma: inclusive scans down the 64 rows (lane = row; rows past the chunk's end add 0),
-        // four channels at a time per wave
-        for (int ch = 4 * wave; ch < DK; ch += 16) {
-            f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.G[lane * PK + ch]);
-            x = f32x4_t{wave_inclusive_sum(x[0]), wave_inclusive_sum(x[1]), wave_inclusive_sum(x[2]),
-                        wave_inclusive_sum(x[3])};
-            *reinterpret_cast<f32x4_t*>(&sm.G[lane * PK + ch]) = x;
-        }
         __syncthreads();
 
         // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
