@@ -337,15 +337,41 @@ struct KdaPrepStage {
         if (tid < 64) sm.beta[tid] = beta;
     }
     // gamma (the in-chunk inclusive cumulative sum of g, per channel) into LDS: the thread's
-    // rows plus the sums of the row blocks above them. Between a barrier after store and one
-    // before gamma is read.
-    __device__ __forceinline__ void finish_scan(KdaPrepSmem<DK>& sm, int tid) const {
+    // rows plus the sums of the row blocks above them; and the scaled operators of those rows
+    // straight from registers: Kh (E * K * e^gamma with decoupled gates), Qh (not with
+    // decoupled gates, whose Q is loaded later), Kd and lam, at element offset widx * 64 * DK +
+    // (IMG ? the image offset : row-major). Between a barrier after store and one before gamma
+    // is read.
+    template <bool IMG, typename TM>
+    __device__ __forceinline__ void finish_scan(KdaPrepSmem<DK>& sm, int tid, TM* khat, TM* qhat, TM* kdec,
+                                                float* lam, long widx) const {
         constexpr int PK = KdaPrepSmem<DK>::PK;
         const int rb = tid / NG, cc = 4 * (tid % NG);
-        f32x4_t pre = {0.f, 0.f, 0.f, 0.f};
-        for (int b = 0; b < rb; ++b) pre += *reinterpret_cast<const f32x4_t*>(&sm.tot[b * DK + cc]);
+        f32x4_t pre = {0.f, 0.f, 0.f, 0.f}, last = pre;   // rows above the block; gamma_last
+        for (int b = 0; b < RB; ++b) {
+            if (b == rb) pre = last;
+            last += *reinterpret_cast<const f32x4_t*>(&sm.tot[b * DK + cc]);
+        }
 #pragma unroll
-        for (int it = 0; it < NP; ++it) *reinterpret_cast<f32x4_t*>(&sm.G[(NP * rb + it) * PK + cc]) = g[it] + pre;
+        for (int it = 0; it < NP; ++it) {
+            const int r = NP * rb + it;
+            const f32x4_t gm = g[it] + pre;
+            *reinterpret_cast<f32x4_t*>(&sm.G[r * PK + cc]) = gm;
+            const float4 kv = widen(k[it]);
+            const float4 x = DEC ? make_float4(e[it][0] * kv.x, e[it][1] * kv.y, e[it][2] * kv.z, e[it][3] * kv.w)
+                                 : widen(q[it]);
+            const float4 eg = make_float4(__expf(gm[0]), __expf(gm[1]), __expf(gm[2]), __expf(gm[3]));
+            const float4 ed = make_float4(__expf(last[0] - gm[0]), __expf(last[1] - gm[1]), __expf(last[2] - gm[2]),
+                                          __expf(last[3] - gm[3]));
+            const long o = widx * 64 * DK + (IMG ? img_off<DK>(r, cc) : r * DK + cc);
+            const float4 xs = make_float4(x.x * eg.x, x.y * eg.y, x.z * eg.z, x.w * eg.w);
+            put4(khat + o, DEC ? xs : make_float4(kv.x * eg.x, kv.y * eg.y, kv.z * eg.z, kv.w * eg.w));
+            put4(kdec + o, make_float4(kv.x * ed.x, kv.y * ed.y, kv.z * ed.z, kv.w * ed.w));
+            if constexpr (!DEC) put4(qhat + o, xs);
+        }
+        if (rb == 0)
+            *reinterpret_cast<float4*>(lam + widx * DK + cc) =
+                make_float4(__expf(last[0]), __expf(last[1]), __expf(last[2]), __expf(last[3]));
     }
 };
 
@@ -395,35 +421,22 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
         __syncthreads();  // the previous unit is done with LDS
         stage.store(sm, tid);
         __syncthreads();
-        // gamma: rows past the chunk's end add 0
-        stage.finish_scan(sm, tid);
+        // gamma (rows past the chunk's end add 0) and Kh, Qh, Kd, lam to the workspace
+        stage.template finish_scan<IMG>(sm, tid, khat, qhat, kdec, p.lam, widx);
         if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
         else stage.load(p, bos, len, h, tid);
         __syncthreads();
 
-        // -- Kh (E * K * e^gamma with decoupled gates), Qh, Kd and lam to the workspace
-        auto write_scaled = [&](bool kside) {
+        // -- Qh with decoupled gates (Q is loaded after A is formed)
+        auto write_qhat = [&]() {
             for (int i = tid; i < 64 * DK / 4; i += 256) {
                 const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
                 const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
-                const float4 e = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
                 const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
                 const long o = widx * 64 * DK + (IMG ? img_off<DK>(r, cc) : r * DK + cc);
-                const float4 x = make_float4(q.x * e.x, q.y * e.y, q.z * e.z, q.w * e.w);
-                if (!kside) {
-                    put4(qhat + o, x);
-                    continue;
-                }
-                const float4 gl = *reinterpret_cast<const float4*>(&sm.G[63 * PK + cc]);
-                const float4 k = *reinterpret_cast<const float4*>(&sm.K[r * PK + cc]);
-                const float4 ed = make_float4(__expf(gl.x - g.x), __expf(gl.y - g.y), __expf(gl.z - g.z), __expf(gl.w - g.w));
-                put4(khat + o, DEC ? x : make_float4(k.x * e.x, k.y * e.y, k.z * e.z, k.w * e.w));
-                put4(kdec + o, make_float4(k.x * ed.x, k.y * ed.y, k.z * ed.z, k.w * ed.w));
-                if constexpr (!DEC) put4(qhat + o, x);
+                put4(qhat + o, make_float4(q.x * __expf(g.x), q.y * __expf(g.y), q.z * __expf(g.z), q.w * __expf(g.w)));
             }
         };
-        write_scaled(true);
-        if (tid < DK) p.lam[widx * DK + tid] = __expf(sm.G[63 * PK + tid]);
 
         // -- A and P
         if constexpr (DEC) {
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
                 *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
             }
             __syncthreads();
-            write_scaled(false);
+            write_qhat();
             gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, sm.T, wave, lane);
         } else {
             gram_rows<DK, true, F16>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, sm.T, wave, lane);
