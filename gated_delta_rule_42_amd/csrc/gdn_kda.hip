@@ -21,7 +21,8 @@
 // of diag(beta) K, Kh = E * K * e^gamma, V replaced by W * V and Mmat = T.
 // Stage 1 (kda_prepare_kernel) forms Kh, Qh, Kd, lam, Mmat and P per (chunk, head) in fp32 (bf16
 // inputs widened on load; the operators are stored as fp16 for bf16 inputs; for bf16 inputs the
-// Gram blocks below the diagonal blocks take fp16 operands, see gram_rows_of); stage 2 carries the
+// Gram blocks below the diagonal blocks take fp16 operands and the diagonal blocks bf16 hi + lo
+// pairs, see gram_rows_of); stage 2 carries the
 // fp32 state through the chunks: kda_propagate_kernel for fp32 inputs (fp32 16x16x4 matrix core),
 // for bf16 inputs kda_propagate_dma_kernel (operators copied into LDS by a DMA wave from the
 // images stage 1 writes; with decoupled gates the write gate is copied beside V), on the fp16
@@ -84,7 +85,8 @@ struct alignas(16) KdaPrepSmem {
 // >= i, and gamma does not increase down the chunk), so nothing overflows fp16; a factor that
 // underflows belongs to a term below fp16's resolution of the entry. The right factors depend
 // on J alone: wave J forms them once as fp16 fragments (zf) for the waves below it, and wave I
-// forms its channel scalars e^{gamma_ref - gamma_last(J)} (ss); see gram_offdiag_prep.
+// forms its channel scalars e^{gamma_ref - gamma_last(J)} (ss); see gram_offdiag_prep. The
+// diagonal block (F16) runs on the bf16 matrix core with each factor as a bf16 hi + lo pair.
 constexpr float kMaxRange = 60.f;
 
 // Scratch of the fp16 off-diagonal products (in the T buffer, which the UT transform fills
@@ -181,34 +183,79 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
             }
         }
     }
-    // fp32 products: lane (l16, lq) takes channels 16 u + 4 lq + e, e = 0..3, in product (u, e),
-    // so its operands arrive as 16-byte reads
-    constexpr int J0 = F16 ? I : 0;  // first column block on the fp32 matrix core
-    for (int u = 0; u < DK / 16; ++u) {
-        const int c = 16 * u + 4 * lq;
-        const f32x4_t gref = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
-        const f32x4_t glast = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + 15) * PK + c]);
-        const f32x4_t grow = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + l16) * PK + c]);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[(16 * I + l16) * PK + c]);
-        f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[(16 * I + l16) * PK + c]);
-        f32x4_t kj[I + 1], gj[I + 1];
+    if constexpr (F16) {
+        // the diagonal block on the bf16 matrix core (16x16x32): bf16 keeps fp32's exponent
+        // range, so the factors up to e^kMaxRange fit; each factor is a bf16 hi + lo pair and
+        // a slice takes three products (hi hi, hi lo, lo hi), about 16 significant bits per
+        // factor. Lane (l16, lq) gives row 16 I + l16 both as the left operand and as the right
+        // one, channels 32 s + 4 lq + 0..3 and the same + 16.
+        constexpr int NS = DK / 32;
+        const int r = 16 * I + l16;
+#pragma unroll 1
+        for (int s = 0; s < NS; ++s) {
+            const int c0 = 32 * s + 4 * lq;
+            f32x4_t x1[2], x2[2], y[2];
 #pragma unroll
-        for (int J = J0; J <= I; ++J) {
-            kj[J] = *reinterpret_cast<const f32x4_t*>(&sm.K[(16 * J + l16) * PK + c]);
-            gj[J] = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * J + l16) * PK + c]);
+            for (int hf = 0; hf < 2; ++hf) {
+                const int c = c0 + 16 * hf;
+                const f32x4_t g = *reinterpret_cast<const f32x4_t*>(&sm.G[r * PK + c]);
+                const f32x4_t gf = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
+                const f32x4_t gl = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + 15) * PK + c]);
+                const f32x4_t k = *reinterpret_cast<const f32x4_t*>(&sm.K[r * PK + c]);
+                const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[r * PK + c]);
+                f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[r * PK + c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float el = __expf(g[e] - gf[e]);
+                    x1[hf][e] = l1[e] * el;
+                    x2[hf][e] = l2[e] * el;
+                    y[hf][e] = gf[e] - gl[e] <= kMaxRange ? k[e] * __expf(gf[e] - g[e]) : 0.f;
+                }
+            }
+            uint4 yh, yl, xh, xl;
+            split_bf16_frag(y[0], y[1], yh, yl);
+            split_bf16_frag(x1[0], x1[1], xh, xl);
+            a1[I] = mfma_bf16(xh, yh, a1[I]);
+            a1[I] = mfma_bf16(xh, yl, a1[I]);
+            a1[I] = mfma_bf16(xl, yh, a1[I]);
+            if constexpr (TWO) {
+                split_bf16_frag(x2[0], x2[1], xh, xl);
+                a2[I] = mfma_bf16(xh, yh, a2[I]);
+                a2[I] = mfma_bf16(xh, yl, a2[I]);
+                a2[I] = mfma_bf16(xl, yh, a2[I]);
+            }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool fits = gref[e] - glast[e] <= kMaxRange;
-            const float el = __expf(grow[e] - gref[e]);
-            const float x1 = l1[e] * el, x2 = l2[e] * el;
-#pragma unroll
+    } else {
+        // fp32 products: lane (l16, lq) takes channels 16 u + 4 lq + e, e = 0..3, in product (u, e),
+        // so its operands arrive as 16-byte reads
+        constexpr int J0 = 0;
+        for (int u = 0; u < DK / 16; ++u) {
+            const int c = 16 * u + 4 * lq;
+            const f32x4_t gref = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
+            const f32x4_t glast = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + 15) * PK + c]);
+            const f32x4_t grow = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + l16) * PK + c]);
+            const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[(16 * I + l16) * PK + c]);
+            f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[(16 * I + l16) * PK + c]);
+            f32x4_t kj[I + 1], gj[I + 1];
+    #pragma unroll
             for (int J = J0; J <= I; ++J) {
-                const float b = kj[J][e] * __expf(gref[e] - gj[J][e]);
-                const float bb = (J < I || fits) ? b : 0.f;
-                a1[J] = mfma4(x1, bb, a1[J]);
-                if constexpr (TWO) a2[J] = mfma4(x2, bb, a2[J]);
+                kj[J] = *reinterpret_cast<const f32x4_t*>(&sm.K[(16 * J + l16) * PK + c]);
+                gj[J] = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * J + l16) * PK + c]);
+            }
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool fits = gref[e] - glast[e] <= kMaxRange;
+                const float el = __expf(grow[e] - gref[e]);
+                const float x1 = l1[e] * el, x2 = l2[e] * el;
+    #pragma unroll
+                for (int J = J0; J <= I; ++J) {
+                    const float b = kj[J][e] * __expf(gref[e] - gj[J][e]);
+                    const float bb = (J < I || fits) ? b : 0.f;
+                    a1[J] = mfma4(x1, bb, a1[J]);
+                    if constexpr (TWO) a2[J] = mfma4(x2, bb, a2[J]);
+                }
             }
         }
     }

@@ -240,7 +240,8 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
  *               op arrays are stored as the LDS images of gdn_chunk_fwd's workspace.
  * Stage 1 computes in fp32 (bf16 inputs widened on load), except that for bf16 inputs the
  * products below the 16x16 diagonal blocks of A and P take fp16 operands (every gate factor
- * there is at most 1) with fp32 accumulation. Stage 2 multiplies fp32 operators
+ * there is at most 1) and those of the diagonal blocks bf16 hi + lo operand pairs (three
+ * products, about 16 significant bits per factor), with fp32 accumulation. Stage 2 multiplies fp32 operators
  * on the fp32 matrix core, and for bf16 inputs fp16 operators (the state packed to fp16 as
  * an operand, fp32 accumulation), as gdn_chunk_fwd does; a bf16 o is the fp32 result rounded
  * to nearest even.
