@@ -215,8 +215,11 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     P.pmat = any ? base + w.fwd.off_p : nullptr;
     P.tmat = any ? reinterpret_cast<float*>(base + w.off_t) : nullptr;
     P.states = any ? reinterpret_cast<float*>(base + w.off_states) : nullptr;
-    P.mmat16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_m16) : nullptr;
-    P.pmat16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_p16) : nullptr;
+    // bf16: the fp32 Mmat region (not written) holds the fp16 images of Mmat, then of P
+    P.mimg16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.fwd.off_m) : nullptr;
+    P.pimg16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.fwd.off_m) + w.fwd.nc_bound * H * 4096 : nullptr;
+    P.k16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_k16) : nullptr;
+    P.q16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_q16) : nullptr;
     b.dstates = any ? reinterpret_cast<float*>(base + w.off_dstates) : nullptr;
     b.dhT = dhT;
     b.dq = dq; b.dk = dk_out; b.dv = dv_out; b.dg = dg; b.dbeta = dbeta; b.dh0 = dh0;

@@ -28,13 +28,14 @@
 //
 // Passes: (1) stage 1 of the forward pass (gate tables, Mmat, P; gram products accumulated
 // in fp32) also keeping T in fp32, row-major (for bf16 inputs, read straight from the raw
-// inputs: fp32 P and fp16 copies of Mmat and P, row-major); (2) stage 2 of the forward pass
-// keeping the state entering every chunk instead of writing o; (3) the reverse walk, keeping
-// dS' of every chunk and writing dh0; (4) every (chunk, head) on its own. fp32 inputs run
-// (2)-(4) on the fp32 16x16x4 matrix core (chunk_propagate_kernel<float>,
-// chunk_bwd_state_kernel, chunk_bwd_grad_kernel). bf16 inputs run them on fp16 operands
-// with fp32 accumulation and fp32 states (chunk_propagate_kernel<bf16>,
-// chunk_bwd_state16_kernel, chunk_bwd_grad16_kernel), the numerics of the forward pass.
+// inputs: fp32 P row-major and the fp16 LDS images of K, diag(e^gamma) Q, Mmat and P);
+// (2) stage 2 of the forward pass keeping the state entering every chunk instead of writing
+// o; (3) the reverse walk, keeping dS' of every chunk and writing dh0; (4) every (chunk, head)
+// on its own. fp32 inputs run (2)-(4) on the fp32 16x16x4 matrix core
+// (chunk_propagate_kernel<float>, chunk_bwd_state_kernel, chunk_bwd_grad_kernel). bf16 inputs
+// run them on fp16 operands with fp32 accumulation and fp32 states: (2) and (3) DMA-fed from
+// the images (chunk_propagate_bf16_kernel, chunk_bwd_state16_kernel), (4)
+// chunk_bwd_grad16_kernel; the numerics of the forward pass.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_stage2.h"
@@ -187,102 +188,94 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state_kernel(ChunkPro
     }
 }
 
-// ------------------------------------------- reverse walk, bf16 inputs (fp16 operands)
+// ------------------------------------------------- reverse walk, bf16 inputs (DMA-fed)
+// The reverse walk of chunk_bwd_state_kernel on the fp16 matrix core (16x16x32, fp32
+// accumulation, the state gradient kept in fp32 and packed to fp16 as an operand). One
+// work-group per (sequence, head, DVT-column tile): DVT/16 compute waves (16 columns of dS'
+// each) and a DMA wave that copies each chunk's operands into LDS, walking the chunks
+// backwards three deep: the fp16 images stage 1 wrote (K, diag(e^gamma) Q, Mmat, P; img_off),
+// the gate tables and the raw bf16 dO columns of the work-group (rows past the chunk's end
+// read as zeros). The transposed operands (P^T, Mmat^T, Q^T, K^T and dO across tokens) use the
+// transposing LDS read at image addresses; k is the chunk's token index throughout. The Q
+// image carries diag(e^gamma), so Q^T diag(e^gamma) dO is its transpose times plain dO.
 template <int DK, int DVT>
-struct alignas(16) BwdState16Smem {
-    using KL = KQLayout<_Float16, DK>;
-    static constexpr int PK = KL::kPitch, PC = 72, PV = DVT + 8;
-    _Float16 K[64 * PK];
-    _Float16 Q[64 * PK];
-    _Float16 M[64 * PC];
-    _Float16 P[64 * PC];
-    _Float16 dO[64 * PV];   // the work-group's d_v columns
+struct alignas(16) BwdWalkChunk {
+    _Float16 K[64 * DK];
+    _Float16 Q[64 * DK];    // diag(e^gamma) Q
+    _Float16 M[64 * 64];    // Mmat
+    _Float16 P[64 * 64];
+    uint16_t dO[64 * DVT];  // bf16, the work-group's d_v columns
     float gt[128];          // e^gamma, then e^{gamma_last - gamma}
 };
+template <int DK, int DVT>
+constexpr int kWalkCopies = 2 * (64 * DK * 2 / 1024) + 16 + 64 * DVT * 2 / 1024 + 1;
 
-// Register staging of one chunk's raw bf16 K, Q, dO, fp16 Mmat, P and the gate tables, so
-// that chunk c-1's loads are in flight while chunk c is computed. Every load is issued
-// unconditionally (rows past the chunk's end and lanes past the gate table read zeros through
-// buffer resources), with native vector types, so that the compiler's waits for the staged
-// registers count exactly and do not also wait for the state-gradient stores issued after them.
+// The DMA wave's copies of one chunk (kWalkCopies instructions, 1 KB blocks).
 template <int DK, int DV, int DVT>
-struct BwdState16Stage {
-    static constexpr int NT = DVT / 16 * 64;
-    static constexpr int NK = 64 * DK / 8 / NT, NM = 64 * 64 / 8 / NT, NO = 64 * DVT / 8 / NT;
-    u32x4_t rk[NK], rq[NK], rm[NM], rp[NM], ro[NO], rg;
-
-    __device__ __forceinline__ void load(const ChunkProblem& p, const uint16_t* dop, long bos, int len,
-                                         long widx, int h, int dv0, int tid) {
-        const int H = p.H, DVF = p.dv;
-        const long o = (bos * H + h) * DK;
-        const unsigned kbytes = (unsigned)((len - 1) * H * DK + DK) * 2;
-        const auto kr = make_rsrc(static_cast<const uint16_t*>(p.k) + o, kbytes);
-        const auto qr = make_rsrc(static_cast<const uint16_t*>(p.q) + o, kbytes);
+__device__ __forceinline__ void walk_copy(BwdWalkChunk<DK, DVT>& dst, const ChunkProblem& p, const uint16_t* dop,
+                                          long bos, int len, long widx, int h, int dv0, int lane) {
+    constexpr int NB_K = 64 * DK * 2 / 1024, NB_O = 64 * DVT * 2 / 1024, ROW_O = DVT * 2;
+    const int H = p.H;
+    const unsigned lo = 16u * lane;
+    const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
+    const char* qimg = reinterpret_cast<const char*>(p.q16 + widx * 64 * DK);
+    const char* mimg = reinterpret_cast<const char*>(p.mimg16 + widx * 4096);
+    const char* pimg = reinterpret_cast<const char*>(p.pimg16 + widx * 4096);
+    const auto orr = make_rsrc(dop + (bos * H + h) * DV + dv0, (unsigned)((len - 1) * H * DV + DVT) * 2);
+    if (lane < 32) dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.gt);
 #pragma unroll
-        for (int it = 0; it < NK; ++it) {
-            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8), off = (r * H * DK + 8 * cv) * 2;
-            rk[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
-            rq[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
-        }
-#pragma unroll
-        for (int it = 0; it < NM; ++it) {
-            rm[it] = reinterpret_cast<const u32x4_t*>(p.mmat16 + widx * 4096)[tid + NT * it];
-            rp[it] = reinterpret_cast<const u32x4_t*>(p.pmat16 + widx * 4096)[tid + NT * it];
-        }
-        const auto orr = make_rsrc(dop + (bos * H + h) * DVF + dv0, (unsigned)((len - 1) * H * DVF + DVT) * 2);
-#pragma unroll
-        for (int it = 0; it < NO; ++it) {
-            const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
-            ro[it] = __builtin_amdgcn_raw_buffer_load_b128(orr, (r * H * DVF + 8 * cv) * 2, 0, 0);
-        }
-        rg = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.gates + widx * 128, 512u), tid * 16, 0, 0);
+    for (int b = 0; b < NB_O; ++b) {
+        const int byte = 1024 * b + 16 * lane, r = byte / ROW_O;
+        dma16(orr, reinterpret_cast<const char*>(dst.dO) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_O) >> 4));
     }
-
-    __device__ __forceinline__ void store(BwdState16Smem<DK, DVT>& sm, int tid) const {
-        using SM = BwdState16Smem<DK, DVT>;
-        using KL = typename SM::KL;
-        auto u4 = [](u32x4_t x) { return make_uint4(x[0], x[1], x[2], x[3]); };
 #pragma unroll
-        for (int it = 0; it < NK; ++it) {
-            const int vi = tid + NT * it, r = vi / (DK / 8), cv = vi % (DK / 8);
-            *reinterpret_cast<uint4*>(&sm.K[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(u4(rk[it]));
-            *reinterpret_cast<uint4*>(&sm.Q[KL::off(r, 8 * cv)]) = to_operand16<uint16_t>(u4(rq[it]));
-        }
-#pragma unroll
-        for (int it = 0; it < NM; ++it) {
-            const int vi = tid + NT * it, r = vi / 8, cv = vi % 8;
-            *reinterpret_cast<u32x4_t*>(&sm.M[r * SM::PC + 8 * cv]) = rm[it];
-            *reinterpret_cast<u32x4_t*>(&sm.P[r * SM::PC + 8 * cv]) = rp[it];
-        }
-#pragma unroll
-        for (int it = 0; it < NO; ++it) {
-            const int vi = tid + NT * it, r = vi / (DVT / 8), cv = vi % (DVT / 8);
-            *reinterpret_cast<uint4*>(&sm.dO[r * SM::PV + 8 * cv]) = to_operand16<uint16_t>(u4(ro[it]));
-        }
-        if (tid < 32) reinterpret_cast<u32x4_t*>(sm.gt)[tid] = rg;
+    for (int b = 0; b < NB_K; ++b) {
+        dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
+        dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
     }
-};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
+        dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+    }
+}
 
-// The reverse walk of chunk_bwd_state_kernel on the fp16 matrix core (16x16x32, fp32
-// accumulation, the state gradient kept in fp32 and packed to fp16 as an operand), reading the
-// raw bf16 inputs and fp16 Mmat, P. The transposed operands (P^T, Mmat^T, Q^T, K^T and dO as a
-// right operand) use the transposing LDS read; k is the chunk's token index throughout, in the
-// slot order of fragments packed from two accumulator tiles.
+// Transposed operand fragment from a [64, W] image: slots 0-3 are column c0 + l16 of rows
+// r0 .. r0+3, slots 4-7 of rows r1 .. r1+3 (each lane addresses its own 4-element run).
+template <int W>
+__device__ __forceinline__ uint4 img_frag_t(const _Float16* img, int r0, int r1, int c0) {
+    const int l16 = threadIdx.x & 15, tr = l16 >> 2, tc = 4 * (l16 & 3);
+    return lds_frag2_t(&img[img_off<W>(r0 + tr, c0 + tc)], &img[img_off<W>(r1 + tr, c0 + tc)]);
+}
+
 template <int DK, int DV, int DVT>
-__global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state16_kernel(ChunkProblem p, const uint16_t* dop,
-                                                                           const float* dhT, float* dstates,
-                                                                           float* dh0) {
-    using SM = BwdState16Smem<DK, DVT>;
-    using KL = typename SM::KL;
-    constexpr int PC = SM::PC, PV = SM::PV, NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
-    __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_bwd_state16_kernel(ChunkProblem p, const uint16_t* dop,
+                                                                                 const float* dhT, float* dstates,
+                                                                                 float* dh0) {
+    using CH = BwdWalkChunk<DK, DVT>;
+    constexpr int NW = DVT / 16, NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
+    __shared__ CH ch[3];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
-    const long pair = blockIdx.x / NTILE;
-    const int tile = (int)(blockIdx.x % NTILE);
+
+    // (sequence, head) pair and column tile; with a pair count divisible by 8 the tiles of one
+    // pair get block ids equal modulo 8 (same XCD, shared L2 for the pair's operands)
+    const long NP = (long)p.N * H;
+    const long bid = blockIdx.x;
+    long pair;
+    int tile;
+    if (NP % 8 == 0) {
+        const long x = bid % 8, i = bid / 8;
+        tile = (int)(i % NTILE);
+        pair = (i / NTILE) * 8 + x;
+    } else {
+        pair = bid / NTILE;
+        tile = (int)(bid % NTILE);
+    }
     const int n = (int)(pair / H), h = (int)(pair % H);
-    const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
+    const int dv0 = tile * DVT;
 
     long sbos, seos;
     seq_range(p, n, sbos, seos);
@@ -291,101 +284,105 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state16_kernel(ChunkP
     if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
     auto chunk_len = [&](long jc) { return (int)min(64L, seos - (sbos + jc * 64)); };
 
+    if (wave == NW) {
+        // ------------------------------------------------------------------- DMA wave
+        // pass i handles chunk nchunks-1-i; issue order: pass 0, pass 1, then per pass i: pass
+        // i+2. Loads complete in issue order, so at the top of pass i only pass i+1 may still be
+        // in flight.
+        auto copy = [&](long i) {
+            const long jc = nchunks - 1 - i;
+            walk_copy<DK, DV, DVT>(ch[i % 3], p, dop, sbos + jc * 64, chunk_len(jc), (cbase + jc) * H + h, h, dv0, lane);
+        };
+        if (nchunks > 0) copy(0);
+        if (nchunks > 1) copy(1);
+        for (long i = 0; i < nchunks; ++i) {
+            if (i + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWalkCopies<DK, DVT>));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            lds_barrier();  // pass i's operands are in LDS; pass i-1's buffers are free
+            if (i + 2 < nchunks) copy(i + 2);
+        }
+        return;
+    }
+
+    // ------------------------------------------------------------------- compute waves
+    // wave w: columns dv0 + 16w .. +15; lane holds dS'[dv0 + 16w + l16][16j + 4lq + 0..3] in dST[j]
+    const int dvw = dv0 + 16 * wave;
     f32x4_t dST[NKB];
     const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+    {
+        // dhT through a resource of zero size when there is none (loads read 0)
+        const auto hr = make_rsrc(dhT ? dhT + (pair * DV + dvw) * DK : nullptr, dhT ? (unsigned)(16 * DK * 4) : 0u);
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        if (dhT) {
-            const float4 x = *reinterpret_cast<const float4*>(dhT + srow + 16 * j);
-            dST[j] = f32x4_t{x.x, x.y, x.z, x.w};
-        } else {
-            dST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < NKB; ++j)
+            dST[j] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, (l16 * DK + 4 * lq + 16 * j) * 4, 0, 0));
     }
-    BwdState16Stage<DK, DV, DVT> stage;
-    if (nchunks > 0)
-        stage.load(p, dop, sbos + (nchunks - 1) * 64, chunk_len(nchunks - 1), (cbase + nchunks - 1) * H + h, h, dv0, tid);
 
-    for (long jc = nchunks - 1; jc >= 0; --jc) {
-        const long widx = (cbase + jc) * H + h;
-        __syncthreads();  // the previous chunk's LDS data is dead
-        stage.store(sm, tid);
-        __syncthreads();
-        {   // the chunk before (chunk 0 again at the end: every pass loads)
-            const long jn = jc > 0 ? jc - 1 : 0;
-            stage.load(p, dop, sbos + jn * 64, chunk_len(jn), (cbase + jn) * H + h, h, dv0, tid);
-        }
+    for (long i = 0, m3 = 0; i < nchunks; ++i, m3 = (m3 == 2 ? 0 : m3 + 1)) {
+        const long jc = nchunks - 1 - i, widx = (cbase + jc) * H + h;
+        const CH& cm = ch[m3];
+        lds_barrier();  // this pass's operands are in LDS
 
         float* ds = dstates + (widx * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
-        for (int j = 0; j < NKB; ++j)
-            *reinterpret_cast<float4*>(ds + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+        for (int j = 0; j < NKB; ++j) *reinterpret_cast<f32x4_t*>(ds + 16 * j) = dST[j];
 
         // Z = K dS'^T
-        Frag<_Float16> BS[NKS];
+        uint4 BS[NKS];
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) BS[s] = pack_frag<_Float16>(dST[2 * s], dST[2 * s + 1]);
+        for (int s = 0; s < NKS; ++s) BS[s] = pack_f16_frag(dST[2 * s], dST[2 * s + 1]);
         f32x4_t Z[4], dD[4], dR[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             Z[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const int row = 16 * t + l16;
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const int c0 = 32 * s + 4 * lq;
-                mma_k32(Z[t], load_frag2<_Float16>(&sm.K[KL::off(row, c0)], &sm.K[KL::off(row, c0 + 16)]), BS[s]);
-            }
+            for (int s = 0; s < NKS; ++s)
+                Z[t] = mfma_f16(*reinterpret_cast<const uint4*>(&cm.K[img_off<DK>(16 * t + l16, 32 * s + 4 * lq)]),
+                                BS[s], Z[t]);
         }
-        // dO as a right operand (k = token), plain and scaled by e^gamma
-        Frag<_Float16> DF[2], EDF[2];
+        // dO as a right operand (k = token), bf16 -> fp16
+        uint4 DF[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            DF[hf] = load_frag_t<_Float16>(&sm.dO[(32 * hf + 4 * lq) * PV + 16 * wave],
-                                           &sm.dO[(32 * hf + 16 + 4 * lq) * PV + 16 * wave], PV);
-            const f16x8_t x = __builtin_bit_cast(f16x8_t, DF[hf].v);
-            const float4 e0 = *reinterpret_cast<const float4*>(&sm.gt[32 * hf + 4 * lq]);
-            const float4 e1 = *reinterpret_cast<const float4*>(&sm.gt[32 * hf + 16 + 4 * lq]);
-            EDF[hf] = pack_frag<_Float16>(
-                f32x4_t{e0.x * (float)x[0], e0.y * (float)x[1], e0.z * (float)x[2], e0.w * (float)x[3]},
-                f32x4_t{e1.x * (float)x[4], e1.y * (float)x[5], e1.z * (float)x[6], e1.w * (float)x[7]});
+            const uint2 a = lds_read_t16(&cm.dO[(32 * hf + 4 * lq) * DVT + 16 * wave], DVT);
+            const uint2 b = lds_read_t16(&cm.dO[(32 * hf + 16 + 4 * lq) * DVT + 16 * wave], DVT);
+            DF[hf] = to_operand16<uint16_t>(make_uint4(a.x, a.y, b.x, b.y));
         }
-        // dDelta = P^T dO + Ed Z;  dR = Mmat^T dDelta
+        // dDelta = P^T dO + Ed Z;  dR = -E Mmat^T dDelta
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             dD[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
-                mma_k32(dD[t], load_frag_t<_Float16>(&sm.P[(32 * hf + 4 * lq) * PC + 16 * t],
-                                                     &sm.P[(32 * hf + 16 + 4 * lq) * PC + 16 * t], PC), DF[hf]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) dD[t][m] += sm.gt[64 + 16 * t + 4 * lq + m] * Z[t][m];
+                dD[t] = mfma_f16(img_frag_t<64>(cm.P, 32 * hf + 4 * lq, 32 * hf + 16 + 4 * lq, 16 * t), DF[hf], dD[t]);
+            const f32x4_t ed = *reinterpret_cast<const f32x4_t*>(&cm.gt[64 + 16 * t + 4 * lq]);
+            dD[t] += ed * Z[t];
         }
-        const Frag<_Float16> BD0 = pack_frag<_Float16>(dD[0], dD[1]), BD1 = pack_frag<_Float16>(dD[2], dD[3]);
+        const uint4 BD0 = pack_f16_frag(dD[0], dD[1]), BD1 = pack_f16_frag(dD[2], dD[3]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             dR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            mma_k32(dR[t], load_frag_t<_Float16>(&sm.M[(4 * lq) * PC + 16 * t], &sm.M[(16 + 4 * lq) * PC + 16 * t], PC), BD0);
-            mma_k32(dR[t], load_frag_t<_Float16>(&sm.M[(32 + 4 * lq) * PC + 16 * t], &sm.M[(48 + 4 * lq) * PC + 16 * t], PC), BD1);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) dR[t][m] *= -sm.gt[16 * t + 4 * lq + m];
+            dR[t] = mfma_f16(img_frag_t<64>(cm.M, 4 * lq, 16 + 4 * lq, 16 * t), BD0, dR[t]);
+            dR[t] = mfma_f16(img_frag_t<64>(cm.M, 32 + 4 * lq, 48 + 4 * lq, 16 * t), BD1, dR[t]);
+            const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(&cm.gt[16 * t + 4 * lq]);
+            dR[t] *= -eg;
         }
-        // dS'^T <- lam dS'^T + Q^T (E dO) - K^T (E dR)
-        const Frag<_Float16> BR0 = pack_frag<_Float16>(dR[0], dR[1]), BR1 = pack_frag<_Float16>(dR[2], dR[3]);
-        const float lam = sm.gt[63];
+        // dS'^T <- lam dS'^T + (diag(e^gamma) Q)^T dO - K^T (E dR)
+        const uint4 BR0 = pack_f16_frag(dR[0], dR[1]), BR1 = pack_f16_frag(dR[2], dR[3]);
+        const float lam = cm.gt[63];
 #pragma unroll
         for (int j = 0; j < NKB; ++j) {
             f32x4_t acc = dST[j] * lam;
-            mma_k32(acc, load_kt<_Float16, DK>(sm.Q, 4 * lq, 16 + 4 * lq, j), EDF[0]);
-            mma_k32(acc, load_kt<_Float16, DK>(sm.Q, 32 + 4 * lq, 48 + 4 * lq, j), EDF[1]);
-            mma_k32(acc, load_kt<_Float16, DK>(sm.K, 4 * lq, 16 + 4 * lq, j), BR0);
-            mma_k32(acc, load_kt<_Float16, DK>(sm.K, 32 + 4 * lq, 48 + 4 * lq, j), BR1);
+            acc = mfma_f16(img_frag_t<DK>(cm.Q, 4 * lq, 16 + 4 * lq, 16 * j), DF[0], acc);
+            acc = mfma_f16(img_frag_t<DK>(cm.Q, 32 + 4 * lq, 48 + 4 * lq, 16 * j), DF[1], acc);
+            acc = mfma_f16(img_frag_t<DK>(cm.K, 4 * lq, 16 + 4 * lq, 16 * j), BR0, acc);
+            acc = mfma_f16(img_frag_t<DK>(cm.K, 32 + 4 * lq, 48 + 4 * lq, 16 * j), BR1, acc);
             dST[j] = acc;
         }
     }
     if (dh0) {
 #pragma unroll
-        for (int j = 0; j < NKB; ++j)
-            *reinterpret_cast<float4*>(dh0 + srow + 16 * j) = make_float4(dST[j][0], dST[j][1], dST[j][2], dST[j][3]);
+        for (int j = 0; j < NKB; ++j) *reinterpret_cast<f32x4_t*>(dh0 + srow + 16 * j) = dST[j];
     }
 }
 
@@ -1167,9 +1164,9 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
     w.off_dstates = al(w.off_states + units * dv * dk * 4);
     size_t end = w.off_dstates + units * dv * dk * 4;
     if (bf16) {
-        w.off_m16 = al(end);
-        w.off_p16 = al(w.off_m16 + units * 4096 * 2);
-        end = w.off_p16 + units * 4096 * 2;
+        w.off_k16 = al(end);
+        w.off_q16 = al(w.off_k16 + units * 64 * dk * 2);
+        end = w.off_q16 + units * 64 * dk * 2;
     }
     w.total = end;
     return w;
@@ -1181,12 +1178,9 @@ static void bwd_launch(const BwdProblem& b, hipStream_t s) {
     constexpr int DVT = 32;
     const long pairs = (long)p.N * p.H;
     if (pairs > 0) {
-        if (p.mmat16) {   // bf16 inputs: raw inputs, fp16 operands
-            ChunkProblem r = p;
-            r.q = b.q_in;
-            r.k = b.k_in;
+        if (p.mimg16) {   // bf16 inputs: stage 1's fp16 images, the raw dO
             hipLaunchKernelGGL((chunk_bwd_state16_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                               dim3(DVT / 16 * 64), 0, s, r, static_cast<const uint16_t*>(b.do_in), b.dhT,
+                               dim3((DVT / 16 + 1) * 64), 0, s, p, static_cast<const uint16_t*>(b.do_in), b.dhT,
                                b.dstates, b.dh0);
         } else {
             hipLaunchKernelGGL((chunk_bwd_state_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
@@ -1195,7 +1189,7 @@ static void bwd_launch(const BwdProblem& b, hipStream_t s) {
     }
     const long units = p.nc_bound * p.H;
     if (units > 0) {
-        if (p.mmat16)
+        if (p.mimg16)
             hipLaunchKernelGGL((chunk_bwd_grad16_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
         else
             hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
@@ -1214,12 +1208,12 @@ static void bwd_dispatch(const BwdProblem& b, hipStream_t s) {
 
 hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
     const ChunkProblem& p = b.f;
-    // stage 1 again (bf16 inputs: straight from the raw inputs, with fp32 T and P and fp16
-    // Mmat and P, all row-major), then the state recompute
+    // stage 1 again (bf16 inputs: straight from the raw inputs, with fp32 T and P row-major
+    // and the fp16 images of K, diag(e^gamma) Q, Mmat and P), then the state recompute
     hipError_t e = launch_chunk_prepare(p, s);
     if (e != hipSuccess) return e;
-    if (p.mmat16) {   // bf16 inputs: fp16 operands
-        e = launch_chunk_propagate_f16(p, s);
+    if (p.mimg16) {   // bf16 inputs: fp16 operands
+        e = launch_chunk_propagate_states16(p, s);
     } else {
         e = launch_chunk_propagate(p, s);
     }

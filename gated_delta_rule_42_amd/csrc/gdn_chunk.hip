@@ -260,24 +260,20 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
                 if (BWD) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
-                if (BWD && p.mmat16) {  // fp16 copies for the fp16-operand kernels of the backward pass
-                    store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
-                    store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
-                }
-            } else if (BWD) {  // backward pass, bf16 inputs: fp32 T, fp16 Mmat and P, row-major
-                const int r = tid >> 2, c0 = (tid & 3) * 16;
-                float mv[16], pv[16], tv[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int ci = c0 + e;
-                    tv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
-                    mv[e] = tv[e] * sm.beta[ci];
-                    pv[e] = to_f32(sm.P[r * PC + ci]);
-                }
-                store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
-                store16<_Float16>(p.mmat16 + widx * 4096 + r * 64 + c0, mv);
-                store16<_Float16>(p.pmat16 + widx * 4096 + r * 64 + c0, pv);
             } else {
+                if constexpr (BWD) {  // backward pass, bf16 inputs: also fp32 T, row-major
+                    const int r = tid >> 2, c0 = (tid & 3) * 16;
+                    float tv[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ci = c0 + e;
+                        tv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
+                    }
+                    store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
+                }
+                // the backward pass keeps the fp32 P in p.pmat and takes the images from mimg16, pimg16
+                _Float16* mimg = BWD ? p.mimg16 : static_cast<TM*>(p.mmat);
+                _Float16* pimg = BWD ? p.pimg16 : static_cast<TM*>(p.pmat);
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
                     const int i = tid + 256 * it;
@@ -290,10 +286,10 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                         mv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] * sm.beta[ci] : 0.f;
                         pv[e] = to_f32(sm.P[r * PC + ci]);
                     }
-                    reinterpret_cast<uint4*>(static_cast<TM*>(p.mmat) + widx * 4096)[i] =
+                    reinterpret_cast<uint4*>(mimg + widx * 4096)[i] =
                         make_uint4(pack_f16x2(mv[0], mv[1]), pack_f16x2(mv[2], mv[3]),
                                    pack_f16x2(mv[4], mv[5]), pack_f16x2(mv[6], mv[7]));
-                    reinterpret_cast<uint4*>(static_cast<TM*>(p.pmat) + widx * 4096)[i] =
+                    reinterpret_cast<uint4*>(pimg + widx * 4096)[i] =
                         make_uint4(pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
                                    pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7]));
                 }
@@ -645,8 +641,10 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 // One work-group per (sequence, head, DVT-column tile) with DVT/16 compute waves, one DMA wave
 // and one store wave, each on its own SIMD. Compute wave w owns columns dv0 + 16w .. +15 for
 // all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
-// S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it only reads and writes LDS and runs the matrix and
-// vector units. While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
+// S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it reads and writes LDS and runs the matrix and
+// vector units, and writes global memory only for the backward pass's state recompute (the
+// state entering each chunk, p.states; there p.o is NULL and the store wave writes nothing).
+// While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
 // chunk c+2 into ring buffers (2 and 3 deep: memory latency is about one chunk's
 // compute time), and before the next barrier waits for exactly the copies chunk c+1 needs; the
 // store wave writes chunk c-1's outputs from the LDS staging buffer and never waits for its
@@ -743,10 +741,10 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         };
         for (long jc = 0; jc < nchunks; ++jc) {
             lds_barrier();
-            if (jc > 0) store_out(ost[(jc - 1) & 1], jc - 1);
+            if (jc > 0 && p.o) store_out(ost[(jc - 1) & 1], jc - 1);
         }
         lds_barrier();  // the last chunk's outputs are staged
-        if (nchunks > 0) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
+        if (nchunks > 0 && p.o) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
         return;
     }
 
@@ -890,7 +888,14 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
             for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
     };
 
-    for (long jc = 0, m3 = 0; jc < nchunks; ++jc, m3 = (m3 == 2 ? 0 : m3 + 1)) step(kq[jc & 1], mpv[m3], ost[jc & 1]);
+    for (long jc = 0, m3 = 0; jc < nchunks; ++jc, m3 = (m3 == 2 ? 0 : m3 + 1)) {
+        if (p.states) {   // the state entering the chunk (the backward pass keeps it)
+            float* sp = p.states + (((cbase + jc) * H + h) * DV + dvw + l16) * DK + 4 * lq;
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) *reinterpret_cast<f32x4_t*>(sp + 16 * j) = ST[j];
+        }
+        step(kq[jc & 1], mpv[m3], ost[jc & 1]);
+    }
     lds_barrier();  // hand the last chunk's outputs to the store wave
 
     if (p.hT) {
@@ -992,26 +997,16 @@ static void prop_dispatch(const ChunkProblem& p, hipStream_t s) {
     }
 }
 
-// Stage 2 on fp16 operands from raw bf16 q, k, v and fp16 row-major Mmat, P (p.mmat16,
-// p.pmat16), register-staged: the state recompute of the backward pass for bf16 inputs.
-hipError_t launch_chunk_propagate_f16(const ChunkProblem& p, hipStream_t s) {
+// The state recompute of the backward pass for bf16 inputs: the DMA-fed stage 2 on the fp16
+// images its stage 1 wrote (p.k16, p.q16, p.mimg16, p.pimg16), keeping the state entering every
+// chunk (p.states) and writing no output.
+hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s) {
     ChunkProblem q = p;
-    q.mmat = p.mmat16;
-    q.pmat = p.pmat16;
-    constexpr int DVT = 32;
-    const long pairs = (long)p.N * p.H;
-    if (pairs > 0) {
-        auto go = [&](auto kern, int dv) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)(pairs * (dv / DVT))), dim3(DVT / 16 * 64), 0, s, q);
-        };
-        if (p.dk == 64) {
-            if (p.dv == 64) go(chunk_propagate_kernel<uint16_t, float, 64, 64, DVT>, 64);
-            else go(chunk_propagate_kernel<uint16_t, float, 64, 128, DVT>, 128);
-        } else {
-            if (p.dv == 64) go(chunk_propagate_kernel<uint16_t, float, 128, 64, DVT>, 64);
-            else go(chunk_propagate_kernel<uint16_t, float, 128, 128, DVT>, 128);
-        }
-    }
+    q.mmat = p.mimg16;
+    q.pmat = p.pimg16;
+    q.o = nullptr;
+    q.hT = nullptr;
+    if ((long)p.N * p.H > 0) prop_dispatch<uint16_t, float>(q, s);
     return hipGetLastError();
 }
 

@@ -33,8 +33,8 @@ struct ChunkProblem {
     // optional outputs of the fp32 kernels, used by the backward pass (NULL: not written)
     float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
     float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
-    _Float16* mmat16;            // [nc_bound, H, 64, 64] fp16 row-major copies of Mmat and P
-    _Float16* pmat16;            //   (fp32 stage 1 of the backward pass, bf16 inputs)
+    _Float16* mimg16;            // [nc_bound, H, 64, 64] fp16 LDS images of Mmat and P (stage 1
+    _Float16* pimg16;            //   of the backward pass, bf16 inputs; with k16, q16)
     // channel-wise decay (g is [B,T,H,dk]): chunk operators of the fp32 kernels
     float* khat;                 // [nc_bound, H, 64, dk] K * e^gamma          (fp16 for bf16 inputs)
     float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma          (fp16 for bf16 inputs)
@@ -94,10 +94,10 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
 void launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
-hipError_t launch_chunk_propagate_f16(const ChunkProblem& p, hipStream_t s);
+hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s);
 
 // Backward pass. `f` describes the forward problem over the caller's q, k, v with its stage-1
-// workspace and the tmat and states regions set (bf16 inputs: also mmat16, pmat16); the rest
+// workspace and the tmat and states regions set (bf16 inputs: also mimg16, pimg16, k16, q16); the rest
 // are the backward's own inputs, outputs and regions.
 struct BwdProblem {
     ChunkProblem f;
@@ -119,7 +119,7 @@ struct BwdProblem {
 
 struct BwdLayout {
     WorkspaceLayout fwd;         // stage-1 regions (fp32 operands)
-    size_t off_t, off_states, off_dstates, off_m16, off_p16, total;
+    size_t off_t, off_states, off_dstates, off_k16, off_q16, total;
 };
 
 BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16);

@@ -160,11 +160,13 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  * gdn_chunk_fwd_workspace_bytes; 0 for arguments gdn_chunk_bwd would reject or when no
  * chunk exists). Contents, 256-byte aligned regions in this order (nc as above):
  *   the regions of gdn_chunk_fwd_workspace_bytes for fp32 operators (chunk_base, gates,
- *   Mmat, P; row-major [nc, H, 64, 64], Mmat left unwritten for bf16 inputs), then
+ *   Mmat, P; row-major [nc, H, 64, 64]; for bf16 inputs the Mmat region holds instead the
+ *   fp16 LDS images of Mmat [nc, H, 64, 64] and then of P, as gdn_chunk_fwd's workspace
+ *   stores them), then
  *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major
  *   states   fp32 [nc, H, dv, dk]  the state entering each chunk
  *   dstates  fp32 [nc, H, dv, dk]  the gradient reaching the state after each chunk
- *   Mmat, P  fp16 [nc, H, 64, 64] each, row-major (bf16 inputs only).
+ *   K, Q     fp16 [nc, H, 64, dk] each, the LDS images of K and diag(e^gamma) Q (bf16 only).
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
                                      int chunk, int dtype);
