@@ -68,6 +68,8 @@ BW_SMALL = [
     (1, 257, 2, 128, 128, "bf16", True, True, 0.01),
     (1, 64, 3, 64, 64, "bf16", False, True, 1.0),
     (1, 1, 2, 128, 128, "bf16", True, True, 1.0),
+    (1, 190, 2, 128, 64, "bf16", True, True, 0.05),
+    (2, 100, 2, 64, 128, "bf16", False, False, 1.0),
 ]
 
 
