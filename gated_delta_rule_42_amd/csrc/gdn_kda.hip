@@ -143,53 +143,17 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
     f32x4_t a1[4], a2[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) a1[J] = a2[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (F16 && I > 0) {
-        constexpr int NS = KdaOffdiag<DK>::NS;
-        const int r = 16 * I + l16;
-#pragma unroll 1
-        for (int s = 0; s < NS; ++s) {
-            const int c0 = 32 * s + 4 * lq;
-            float x1[8], x2[8];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int c = c0 + 16 * hf;
-                const f32x4_t g = *reinterpret_cast<const f32x4_t*>(&sm.G[r * PK + c]);
-                const f32x4_t gf = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
-                const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&L1[r * PK + c]);
-                f32x4_t l2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if constexpr (TWO) l2 = *reinterpret_cast<const f32x4_t*>(&L2[r * PK + c]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float el = __expf(g[e] - gf[e]);
-                    x1[4 * hf + e] = l1[e] * el;
-                    x2[4 * hf + e] = l2[e] * el;
-                }
-            }
-#pragma unroll
-            for (int J = 0; J < I; ++J) {
-                const float* sc = od.ss + (I * (I - 1) / 2 + J) * DK;
-                const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(&sc[c0]);
-                const f32x4_t sb = *reinterpret_cast<const f32x4_t*>(&sc[c0 + 16]);
-                const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-                const uint4 bz = od.zf[(J * NS + s) * 64 + lane];
-                const uint4 f1 = make_uint4(pack_f16x2(x1[0] * sv[0], x1[1] * sv[1]), pack_f16x2(x1[2] * sv[2], x1[3] * sv[3]),
-                                            pack_f16x2(x1[4] * sv[4], x1[5] * sv[5]), pack_f16x2(x1[6] * sv[6], x1[7] * sv[7]));
-                a1[J] = mfma_f16(f1, bz, a1[J]);
-                if constexpr (TWO) {
-                    const uint4 f2 = make_uint4(pack_f16x2(x2[0] * sv[0], x2[1] * sv[1]), pack_f16x2(x2[2] * sv[2], x2[3] * sv[3]),
-                                                pack_f16x2(x2[4] * sv[4], x2[5] * sv[5]), pack_f16x2(x2[6] * sv[6], x2[7] * sv[7]));
-                    a2[J] = mfma_f16(f2, bz, a2[J]);
-                }
-            }
-        }
-    }
     if constexpr (F16) {
-        // the diagonal block on the bf16 matrix core (16x16x32): bf16 keeps fp32's exponent
-        // range, so the factors up to e^kMaxRange fit; each factor is a bf16 hi + lo pair and
-        // a slice takes three products (hi hi, hi lo, lo hi), about 16 significant bits per
-        // factor. Lane (l16, lq) gives row 16 I + l16 both as the left operand and as the right
-        // one, channels 32 s + 4 lq + 0..3 and the same + 16.
-        constexpr int NS = DK / 32;
+        // One pass per 32-channel slice over the lane's row r = 16 I + l16 (channels
+        // 32 s + 4 lq + 0..3 and the same + 16): the left factors L e^{gamma_r - gamma_ref}
+        // serve both products.
+        // Below the diagonal block (J < I): fp16 operands, the left factor times the channel
+        // scalars e^{gamma_ref - gamma_last(J)} against wave J's right-factor fragments.
+        // The diagonal block on the bf16 matrix core (16x16x32): bf16 keeps fp32's exponent
+        // range, so the factors up to e^kMaxRange fit; each factor is a bf16 hi + lo pair and a
+        // slice takes three products (hi hi, hi lo, lo hi), about 16 significant bits per
+        // factor; the lane gives row r both as the left operand and as the right one.
+        constexpr int NS = KdaOffdiag<DK>::NS;
         const int r = 16 * I + l16;
 #pragma unroll 1
         for (int s = 0; s < NS; ++s) {
@@ -211,6 +175,21 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
                     x1[hf][e] = l1[e] * el;
                     x2[hf][e] = l2[e] * el;
                     y[hf][e] = gf[e] - gl[e] <= kMaxRange ? k[e] * __expf(gf[e] - g[e]) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int J = 0; J < I; ++J) {
+                const float* sc = od.ss + (I * (I - 1) / 2 + J) * DK;
+                const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(&sc[c0]);
+                const f32x4_t sb = *reinterpret_cast<const f32x4_t*>(&sc[c0 + 16]);
+                const uint4 bz = od.zf[(J * NS + s) * 64 + lane];
+                const uint4 f1 = make_uint4(pack_f16x2(x1[0][0] * sa[0], x1[0][1] * sa[1]), pack_f16x2(x1[0][2] * sa[2], x1[0][3] * sa[3]),
+                                            pack_f16x2(x1[1][0] * sb[0], x1[1][1] * sb[1]), pack_f16x2(x1[1][2] * sb[2], x1[1][3] * sb[3]));
+                a1[J] = mfma_f16(f1, bz, a1[J]);
+                if constexpr (TWO) {
+                    const uint4 f2 = make_uint4(pack_f16x2(x2[0][0] * sa[0], x2[0][1] * sa[1]), pack_f16x2(x2[0][2] * sa[2], x2[0][3] * sa[3]),
+                                                pack_f16x2(x2[1][0] * sb[0], x2[1][1] * sb[1]), pack_f16x2(x2[1][2] * sb[2], x2[1][3] * sb[3]));
+                    a2[J] = mfma_f16(f2, bz, a2[J]);
                 }
             }
             uint4 yh, yl, xh, xl;
