@@ -6,14 +6,16 @@
 
 namespace gdn {
 
-// The blocks on sub-diagonal D of T (wave w < 4 - D computes block (D + w, w)):
-// T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, fp32 MFMA (16x16x4). All operands of the block are
-// read before the products, so the reads overlap instead of each product waiting for its own.
-template <int PF, int D>
-__device__ __forceinline__ void ut_subdiagonal(const float* At, float* Tt, int wave, int lane) {
+// Block (IB, JB) of T below the block diagonal: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj, fp32
+// MFMA (16x16x4). It reads the diagonal block T_ii and the blocks above it in its own column.
+// All operands of the block are read before the products, so the reads overlap instead of
+// each product waiting for its own.
+template <int PF, int IB, int JB>
+__device__ __forceinline__ void ut_block(const float* At, float* Tt, int lane) {
+    constexpr int D = IB - JB;
     const int l16 = lane & 15, lq = lane >> 4;
-    if (wave < 4 - D) {
-        const int ib = D + wave, jb = ib - D;
+    {
+        constexpr int ib = IB, jb = JB;
         float av[4 * D], bv[4 * D], tv[4];
 #pragma unroll
         for (int mm = 0; mm < D; ++mm)
@@ -36,15 +38,15 @@ __device__ __forceinline__ void ut_subdiagonal(const float* At, float* Tt, int w
 #pragma unroll
         for (int v = 0; v < 4; ++v) Tt[(16 * ib + 4 * lq + v) * PF + 16 * jb + l16] = -t[v];
     }
-    __syncthreads();
 }
 
 // A and T are fp32 [64, PF] in LDS (row pitch PF); A's strictly lower part is read, T's lower
 // blocks are written (blocks above the 16x16 block diagonal are left untouched). Diagonal
 // 16x16 blocks: wave w inverts block w by forward substitution, lane l16 computing column l16
-// with the block's strictly lower entries held in registers. Then the blocks below the
-// diagonal, one sub-diagonal at a time (ut_subdiagonal). Called by all 256 threads; ends with
-// a barrier.
+// with the block's strictly lower entries held in registers. Then, after one barrier, wave w
+// walks block column w downwards (ut_block): each block needs only the diagonal blocks and the
+// blocks above it in its column, which the same wave wrote just before, so no further barrier
+// is needed until the end. Called by all 256 threads; ends with a barrier.
 template <int PF>
 __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wave, int lane) {
     const int l16 = lane & 15, lq = lane >> 4;
@@ -73,9 +75,23 @@ __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wav
         }
     }
     __syncthreads();
-    ut_subdiagonal<PF, 1>(At, Tt, wave, lane);
-    ut_subdiagonal<PF, 2>(At, Tt, wave, lane);
-    ut_subdiagonal<PF, 3>(At, Tt, wave, lane);
+    switch (wave) {
+        case 0:
+            ut_block<PF, 1, 0>(At, Tt, lane);
+            ut_block<PF, 2, 0>(At, Tt, lane);
+            ut_block<PF, 3, 0>(At, Tt, lane);
+            break;
+        case 1:
+            ut_block<PF, 2, 1>(At, Tt, lane);
+            ut_block<PF, 3, 1>(At, Tt, lane);
+            break;
+        case 2:
+            ut_block<PF, 3, 2>(At, Tt, lane);
+            break;
+        default:
+            break;
+    }
+    __syncthreads();
 }
 
 }  // namespace gdn
