@@ -836,6 +836,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     auto colf = [&](const _Float16* t, int pitch, int k0, int c0) {
         return load_frag_t<_Float16>(&t[(k0 + 4 * lq) * pitch + c0], &t[(k0 + 16 + 4 * lq) * pitch + c0], pitch);
     };
+    // For a product whose two operands are both rows read along k, k runs in its natural order
+    // instead (8 consecutive k per lane: one 16-byte read per fragment).
+    auto rowc = [&](const _Float16* t, int pitch, int r, int k0) {
+        Frag<_Float16> f;
+        f.v = *reinterpret_cast<const uint4*>(&t[r * pitch + k0 + 8 * lq]);
+        return f;
+    };
     f32x4_t dP[4], dM[4], dQ1[NKB], dK1[NKB];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dP[t] = dM[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -933,14 +940,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         for (int nt = 0; nt < 2; ++nt) X[nt] = Y[nt] = Z[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            const Frag<_Float16> ak = rowf(sm.K, PK, row, 32 * s), aq = rowf(sm.Q, PK, row, 32 * s);
+            const Frag<_Float16> ak = rowc(sm.K, PK, row, 32 * s), aq = rowc(sm.Q, PK, row, 32 * s);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const Frag<_Float16> bs = rowf(sl.S, PS, 16 * nt + l16, 32 * s), bd = rowf(sl.dS, PS, 16 * nt + l16, 32 * s);
+                const Frag<_Float16> bs = rowc(sl.S, PS, 16 * nt + l16, 32 * s), bd = rowc(sl.dS, PS, 16 * nt + l16, 32 * s);
                 mma_k32(X[nt], ak, bs);
                 mma_k32(Y[nt], aq, bs);
                 mma_k32(Z[nt], ak, bd);
-                mma_k32(Z[nt], ak, rowf(sl.dSlo, PS, 16 * nt + l16, 32 * s));
+                mma_k32(Z[nt], ak, rowc(sl.dSlo, PS, 16 * nt + l16, 32 * s));
             }
         }
         float EX[2][4];
@@ -1013,12 +1020,12 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 
         // dP += dO Delta^T, dMmat += dDelta R^T, dQ1 += E dO S, dK1 += -E dR S + Ed Delta dS'
         {
-            const Frag<_Float16> ao = rowf(sl.dO, PV, row, 0), ad = rowf(sl.dD, PV, row, 0);
+            const Frag<_Float16> ao = rowc(sl.dO, PV, row, 0), ad = rowc(sl.dD, PV, row, 0);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                mma_k32(dP[ct], ao, rowf(sl.D, PV, 16 * ct + l16, 0));
-                mma_k32(dP[ct], ao, rowf(sl.Dlo, PV, 16 * ct + l16, 0));
-                mma_k32(dM[ct], ad, rowf(sl.R, PV, 16 * ct + l16, 0));
+                mma_k32(dP[ct], ao, rowc(sl.D, PV, 16 * ct + l16, 0));
+                mma_k32(dP[ct], ao, rowc(sl.Dlo, PV, 16 * ct + l16, 0));
+                mma_k32(dM[ct], ad, rowc(sl.R, PV, 16 * ct + l16, 0));
             }
             const Frag<_Float16> a1 = rowf(sl.EdO, PV, row, 0), a2 = rowf(sl.EdR, PV, row, 0),
                                  a3 = rowf(sl.EdD, PV, row, 0), a3l = rowf(sl.EdDlo, PV, row, 0);
@@ -1063,7 +1070,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     for (int ct = 0; ct < 4; ++ct) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(acc, rowf(cc.X1, PT, row, k0), rowf(sm.T, PT, 16 * ct + l16, k0));
+        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(acc, rowc(cc.X1, PT, row, k0), rowc(sm.T, PT, 16 * ct + l16, k0));
 #pragma unroll
         for (int m = 0; m < 4; ++m) cc.X2[(16 * wave + 4 * lq + m) * PT + 16 * ct + l16] = (_Float16)acc[m];
     }
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(ta, colf(sm.T, PT, k0, 16 * wave), colf(cc.X2, PT, k0, 16 * ct));
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) mma_k32(G, rowf(sm.K, PK, row, 32 * s), rowf(sm.K, PK, 16 * ct + l16, 32 * s));
+        for (int s = 0; s < NKS; ++s) mma_k32(G, rowc(sm.K, PK, row, 32 * s), rowc(sm.K, PK, 16 * ct + l16, 32 * s));
         const int col = 16 * ct + l16;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
