@@ -829,19 +829,16 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     }
 
     const int row = 16 * wave + l16;   // this lane's row as a left operand
-    // left operand read along k (row `r` of a row-major tile) and right operand read across k
-    auto rowf = [&](const _Float16* t, int pitch, int r, int k0) {
-        return load_frag2<_Float16>(&t[r * pitch + k0 + 4 * lq], &t[r * pitch + k0 + 16 + 4 * lq]);
-    };
-    auto colf = [&](const _Float16* t, int pitch, int k0, int c0) {
-        return load_frag_t<_Float16>(&t[(k0 + 4 * lq) * pitch + c0], &t[(k0 + 16 + 4 * lq) * pitch + c0], pitch);
-    };
-    // For a product whose two operands are both rows read along k, k runs in its natural order
-    // instead (8 consecutive k per lane: one 16-byte read per fragment).
+    // Every operand of every product here is read from LDS, so k runs in its natural order
+    // within a fragment (8 consecutive k per lane): a row read along k is one 16-byte read, and a
+    // read across k takes the lane's 8 rows as two transposed 4-row blocks.
     auto rowc = [&](const _Float16* t, int pitch, int r, int k0) {
         Frag<_Float16> f;
         f.v = *reinterpret_cast<const uint4*>(&t[r * pitch + k0 + 8 * lq]);
         return f;
+    };
+    auto colc = [&](const _Float16* t, int pitch, int k0, int c0) {
+        return load_frag_t<_Float16>(&t[(k0 + 8 * lq) * pitch + c0], &t[(k0 + 8 * lq + 4) * pitch + c0], pitch);
     };
     f32x4_t dP[4], dM[4], dQ1[NKB], dK1[NKB];
 #pragma unroll
@@ -971,11 +968,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             Dl[nt] = dDl[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32) {
-                const Frag<_Float16> at = rowf(sm.T, PT, row, k0), bo = colf(sl.dO, PV, k0, 16 * nt);
-                mma_k32(Dl[nt], at, colf(sl.BR, PV, k0, 16 * nt));
-                mma_k32(Dl[nt], at, colf(sl.BRlo, PV, k0, 16 * nt));
-                mma_k32(dDl[nt], colf(sm.P, PT, k0, 16 * wave), bo);
-                mma_k32(dDl[nt], colf(sm.Plo, PT, k0, 16 * wave), bo);
+                const Frag<_Float16> at = rowc(sm.T, PT, row, k0), bo = colc(sl.dO, PV, k0, 16 * nt);
+                mma_k32(Dl[nt], at, colc(sl.BR, PV, k0, 16 * nt));
+                mma_k32(Dl[nt], at, colc(sl.BRlo, PV, k0, 16 * nt));
+                mma_k32(dDl[nt], colc(sm.P, PT, k0, 16 * wave), bo);
+                mma_k32(dDl[nt], colc(sm.Plo, PT, k0, 16 * wave), bo);
             }
         }
 #pragma unroll
@@ -999,9 +996,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             f32x4_t dRl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32) {
-                const Frag<_Float16> at = colf(sm.T, PT, k0, 16 * wave);
-                mma_k32(dRl, at, colf(sl.dD, PV, k0, 16 * nt));
-                mma_k32(dRl, at, colf(sl.dDlo, PV, k0, 16 * nt));
+                const Frag<_Float16> at = colc(sm.T, PT, k0, 16 * wave);
+                mma_k32(dRl, at, colc(sl.dD, PV, k0, 16 * nt));
+                mma_k32(dRl, at, colc(sl.dDlo, PV, k0, 16 * nt));
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -1027,16 +1024,16 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 mma_k32(dP[ct], ao, rowc(sl.Dlo, PV, 16 * ct + l16, 0));
                 mma_k32(dM[ct], ad, rowc(sl.R, PV, 16 * ct + l16, 0));
             }
-            const Frag<_Float16> a1 = rowf(sl.EdO, PV, row, 0), a2 = rowf(sl.EdR, PV, row, 0),
-                                 a3 = rowf(sl.EdD, PV, row, 0), a3l = rowf(sl.EdDlo, PV, row, 0);
+            const Frag<_Float16> a1 = rowc(sl.EdO, PV, row, 0), a2 = rowc(sl.EdR, PV, row, 0),
+                                 a3 = rowc(sl.EdD, PV, row, 0), a3l = rowc(sl.EdDlo, PV, row, 0);
 #pragma unroll
             for (int j = 0; j < NKB; ++j) {
-                const Frag<_Float16> bS = colf(sl.S, PS, 0, 16 * j), bdS = colf(sl.dS, PS, 0, 16 * j);
+                const Frag<_Float16> bS = colc(sl.S, PS, 0, 16 * j), bdS = colc(sl.dS, PS, 0, 16 * j);
                 mma_k32(dQ1[j], a1, bS);
                 mma_k32(dK1[j], a2, bS);
                 mma_k32(dK1[j], a3, bdS);
                 mma_k32(dK1[j], a3l, bdS);
-                mma_k32(dK1[j], a3, colf(sl.dSlo, PS, 0, 16 * j));
+                mma_k32(dK1[j], a3, colc(sl.dSlo, PS, 0, 16 * j));
             }
         }
     }
@@ -1080,7 +1077,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     for (int ct = 0; ct < 4; ++ct) {
         f32x4_t ta = {0.f, 0.f, 0.f, 0.f}, G = ta;
 #pragma unroll
-        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(ta, colf(sm.T, PT, k0, 16 * wave), colf(cc.X2, PT, k0, 16 * ct));
+        for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(ta, colc(sm.T, PT, k0, 16 * wave), colc(cc.X2, PT, k0, 16 * ct));
 #pragma unroll
         for (int s = 0; s < NKS; ++s) mma_k32(G, rowc(sm.K, PK, row, 32 * s), rowc(sm.K, PK, 16 * ct + l16, 32 * s));
         const int col = 16 * ct + l16;
@@ -1128,13 +1125,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         f32x4_t aq = dQ1[j], ak = dK1[j];
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32) {
-            const Frag<_Float16> bK = colf(sm.K, PK, k0, 16 * j), bQ = colf(sm.Q, PK, k0, 16 * j);
-            mma_k32(aq, rowf(cc.X3, PT, row, k0), bK);
-            mma_k32(aq, rowf(cc.X3lo, PT, row, k0), bK);
-            mma_k32(ak, colf(cc.X3, PT, k0, 16 * wave), bQ);
-            mma_k32(ak, colf(cc.X3lo, PT, k0, 16 * wave), bQ);
-            mma_k32(ak, rowf(cc.X1, PT, row, k0), bK);
-            mma_k32(ak, colf(cc.X1, PT, k0, 16 * wave), bK);
+            const Frag<_Float16> bK = colc(sm.K, PK, k0, 16 * j), bQ = colc(sm.Q, PK, k0, 16 * j);
+            mma_k32(aq, rowc(cc.X3, PT, row, k0), bK);
+            mma_k32(aq, rowc(cc.X3lo, PT, row, k0), bK);
+            mma_k32(ak, colc(cc.X3, PT, k0, 16 * wave), bQ);
+            mma_k32(ak, colc(cc.X3lo, PT, k0, 16 * wave), bQ);
+            mma_k32(ak, rowc(cc.X1, PT, row, k0), bK);
+            mma_k32(ak, colc(cc.X1, PT, k0, 16 * wave), bK);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
