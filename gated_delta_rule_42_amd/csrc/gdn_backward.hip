@@ -854,7 +854,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     // struct-typed copy would go through memory); every load is issued (past the last slice
     // they reload it), V and dO rows past the chunk's end read as zeros through buffer resources.
     constexpr int NSI = 32 * DK / 8 / 256;
-    f32x4_t rs[NSI][2], rd[NSI][2];
+    u32x4_t rs[NSI];
+    f32x4_t rd[NSI][2];
     u32x4_t rv, ro;
     const unsigned vrow_bytes = (unsigned)((len - 1) * H * DV + 32) * 2;
     auto load_slice = [&](int js) __attribute__((always_inline)) {
@@ -862,10 +863,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 #pragma unroll
         for (int it = 0; it < NSI; ++it) {
             const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-            const float* sp = p.states + (widx * DV + dv0 + r) * DK + cc;
+            const _Float16* sp = p.states16 + (widx * DV + dv0 + r) * DK + cc;
             const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
-            rs[it][0] = *reinterpret_cast<const f32x4_t*>(sp);
-            rs[it][1] = *reinterpret_cast<const f32x4_t*>(sp + 4);
+            rs[it] = *reinterpret_cast<const u32x4_t*>(sp);
             rd[it][0] = *reinterpret_cast<const f32x4_t*>(dp);
             rd[it][1] = *reinterpret_cast<const f32x4_t*>(dp + 4);
         }
@@ -906,9 +906,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 #pragma unroll
         for (int it = 0; it < NSI; ++it) {
             const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
-            const float4 s0 = f4(rs[it][0]), s1 = f4(rs[it][1]), d0 = f4(rd[it][0]), d1 = f4(rd[it][1]);
+            const uint4 sh = make_uint4(rs[it][0], rs[it][1], rs[it][2], rs[it][3]);
+            const f16x8_t s8 = __builtin_bit_cast(f16x8_t, sh);
+            const float4 s0 = make_float4((float)s8[0], (float)s8[1], (float)s8[2], (float)s8[3]),
+                         s1 = make_float4((float)s8[4], (float)s8[5], (float)s8[6], (float)s8[7]);
+            const float4 d0 = f4(rd[it][0]), d1 = f4(rd[it][1]);
             const uint4 dh = pack8(d0, d1);
-            *reinterpret_cast<uint4*>(&sl.S[r * PS + cc]) = pack8(s0, s1);
+            *reinterpret_cast<uint4*>(&sl.S[r * PS + cc]) = sh;
             *reinterpret_cast<uint4*>(&sl.dS[r * PS + cc]) = dh;
             *reinterpret_cast<uint4*>(&sl.dSlo[r * PS + cc]) = resid8(d0, d1, dh);
             tail += lam * (s0.x * d0.x + s0.y * d0.y + s0.z * d0.z + s0.w * d0.w +
@@ -1165,7 +1169,7 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
     const size_t units = (size_t)w.fwd.nc_bound * H;
     w.off_t = al(w.fwd.total);
     w.off_states = al(w.off_t + units * 4096 * 4);
-    w.off_dstates = al(w.off_states + units * dv * dk * 4);
+    w.off_dstates = al(w.off_states + units * dv * dk * (bf16 ? 2 : 4));
     size_t end = w.off_dstates + units * dv * dk * 4;
     if (bf16) {
         w.off_k16 = al(end);

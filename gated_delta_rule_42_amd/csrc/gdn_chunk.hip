@@ -643,7 +643,8 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 // all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
 // S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it reads and writes LDS and runs the matrix and
 // vector units, and writes global memory only for the backward pass's state recompute (the
-// state entering each chunk, p.states; there p.o is NULL and the store wave writes nothing).
+// state entering each chunk in fp16, p.states16; there p.o is NULL and the store wave writes
+// nothing).
 // While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
 // chunk c+2 into ring buffers (2 and 3 deep: memory latency is about one chunk's
 // compute time), and before the next barrier waits for exactly the copies chunk c+1 needs; the
@@ -889,10 +890,12 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     };
 
     for (long jc = 0, m3 = 0; jc < nchunks; ++jc, m3 = (m3 == 2 ? 0 : m3 + 1)) {
-        if (p.states) {   // the state entering the chunk (the backward pass keeps it)
-            float* sp = p.states + (((cbase + jc) * H + h) * DV + dvw + l16) * DK + 4 * lq;
+        if (p.states16) {   // the state entering the chunk, in the fp16 its products take later
+            _Float16* sp = p.states16 + (((cbase + jc) * H + h) * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
-            for (int j = 0; j < NKB; ++j) *reinterpret_cast<f32x4_t*>(sp + 16 * j) = ST[j];
+            for (int j = 0; j < NKB; ++j)
+                *reinterpret_cast<uint2*>(sp + 16 * j) =
+                    make_uint2(pack_f16x2(ST[j][0], ST[j][1]), pack_f16x2(ST[j][2], ST[j][3]));
         }
         step(kq[jc & 1], mpv[m3], ost[jc & 1]);
     }
@@ -999,7 +1002,7 @@ static void prop_dispatch(const ChunkProblem& p, hipStream_t s) {
 
 // The state recompute of the backward pass for bf16 inputs: the DMA-fed stage 2 on the fp16
 // images its stage 1 wrote (p.k16, p.q16, p.mimg16, p.pimg16), keeping the state entering every
-// chunk (p.states) and writing no output.
+// chunk in fp16 (p.states16) and writing no output.
 hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s) {
     ChunkProblem q = p;
     q.mmat = p.mimg16;

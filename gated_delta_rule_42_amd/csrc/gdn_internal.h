@@ -33,6 +33,7 @@ struct ChunkProblem {
     // optional outputs of the fp32 kernels, used by the backward pass (NULL: not written)
     float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
     float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
+    _Float16* states16;          // the same in fp16 (backward pass, bf16 inputs; states NULL)
     _Float16* mimg16;            // [nc_bound, H, 64, 64] fp16 LDS images of Mmat and P (stage 1
     _Float16* pimg16;            //   of the backward pass, bf16 inputs; with k16, q16)
     // channel-wise decay (g is [B,T,H,dk]): chunk operators of the fp32 kernels

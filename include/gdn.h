@@ -164,7 +164,8 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  *   fp16 LDS images of Mmat [nc, H, 64, 64] and then of P, as gdn_chunk_fwd's workspace
  *   stores them), then
  *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major
- *   states   fp32 [nc, H, dv, dk]  the state entering each chunk
+ *   states   fp32 [nc, H, dv, dk]  the state entering each chunk (bf16 inputs: fp16, the
+ *                                  precision its products take, and half the size)
  *   dstates  fp32 [nc, H, dv, dk]  the gradient reaching the state after each chunk
  *   K, Q     fp16 [nc, H, 64, dk] each, the LDS images of K and diag(e^gamma) Q (bf16 only).
  */
@@ -181,8 +182,9 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  * entering every chunk), a reverse walk over the chunks of each sequence carrying the
  * state gradient, then every (chunk, head) independently. fp32 inputs: all arithmetic is
  * fp32. bf16 inputs: the products run on fp16 operands with fp32 accumulation, fp32 states
- * and state gradients (the forward pass's numerics); the operands whose rounding would
- * dominate the per-chunk gradients are carried as fp16 hi + lo pairs. bf16 gradients are the
+ * and state gradients (the forward pass's numerics; the state entering each chunk is kept
+ * for the per-chunk gradients in fp16, which is what their products take); the operands whose
+ * rounding would dominate the per-chunk gradients are carried as fp16 hi + lo pairs. bf16 gradients are the
  * fp32 results rounded to nearest even.
  *
  *   q, k, v, g_log_alpha, beta, h0, cu_seqlens, chunk, B, T, H, dk, dv, N, dtype:
