@@ -213,7 +213,8 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     P.gates = any ? reinterpret_cast<float*>(base + w.fwd.off_gates) : nullptr;
     P.mmat = any ? base + w.fwd.off_m : nullptr;
     P.pmat = any ? base + w.fwd.off_p : nullptr;
-    P.tmat = any ? reinterpret_cast<float*>(base + w.off_t) : nullptr;
+    P.tmat = (any && !bf16) ? reinterpret_cast<float*>(base + w.off_t) : nullptr;
+    P.tmat16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_t) : nullptr;
     P.states = (any && !bf16) ? reinterpret_cast<float*>(base + w.off_states) : nullptr;
     P.states16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_states) : nullptr;
     // bf16: the fp32 Mmat region (not written) holds the fp16 images of Mmat, then of P

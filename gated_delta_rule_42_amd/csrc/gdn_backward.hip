@@ -808,14 +808,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             qin[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
         }
     }
-    f32x4_t tin[2][2], pin[2][2];
+    u32x4_t tin[2];
+    f32x4_t pin[2][2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
-        const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(p.tmat + widx * 4096 + r * 64 + cc);
         const f32x4_t* pq = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc);
-        tin[it][0] = tp[0];
-        tin[it][1] = tp[1];
+        tin[it] = *reinterpret_cast<const u32x4_t*>(p.tmat16 + widx * 4096 + r * 64 + cc);
         pin[it][0] = pq[0];
         pin[it][1] = pq[1];
     }
@@ -886,7 +885,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
-        *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) = pack8(f4(tin[it][0]), f4(tin[it][1]));
+        *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) = make_uint4(tin[it][0], tin[it][1], tin[it][2], tin[it][3]);
         const float4 p0 = f4(pin[it][0]), p1 = f4(pin[it][1]);
         const uint4 ph = pack8(p0, p1);
         *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) = ph;
@@ -1168,7 +1167,7 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
     w.fwd = workspace_layout(B, T, H, dk, N, varlen, 4);
     const size_t units = (size_t)w.fwd.nc_bound * H;
     w.off_t = al(w.fwd.total);
-    w.off_states = al(w.off_t + units * 4096 * 4);
+    w.off_states = al(w.off_t + units * 4096 * (bf16 ? 2 : 4));
     w.off_dstates = al(w.off_states + units * dv * dk * (bf16 ? 2 : 4));
     size_t end = w.off_dstates + units * dv * dk * 4;
     if (bf16) {

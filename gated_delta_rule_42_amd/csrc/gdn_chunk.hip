@@ -261,15 +261,18 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                 store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
                 if (BWD) store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
             } else {
-                if constexpr (BWD) {  // backward pass, bf16 inputs: also fp32 T, row-major
+                if constexpr (BWD) {  // backward pass, bf16 inputs: also T, fp16 row-major
                     const int r = tid >> 2, c0 = (tid & 3) * 16;
-                    float tv[16];
+                    uint32_t tv[8];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int ci = c0 + e;
-                        tv[e] = ((ci >> 4) <= (r >> 4)) ? Tt[r * PF + ci] : 0.f;
+                    for (int e = 0; e < 8; ++e) {
+                        const int ci = c0 + 2 * e;
+                        const bool on = (ci >> 4) <= (r >> 4);   // both columns in one 16-block
+                        tv[e] = pack_f16x2(on ? Tt[r * PF + ci] : 0.f, on ? Tt[r * PF + ci + 1] : 0.f);
                     }
-                    store16<float>(p.tmat + widx * 4096 + r * 64 + c0, tv);
+                    uint4* tq = reinterpret_cast<uint4*>(p.tmat16 + widx * 4096 + r * 64 + c0);
+                    tq[0] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+                    tq[1] = make_uint4(tv[4], tv[5], tv[6], tv[7]);
                 }
                 // the backward pass keeps the fp32 P in p.pmat and takes the images from mimg16, pimg16
                 _Float16* mimg = BWD ? p.mimg16 : static_cast<TM*>(p.mmat);
@@ -966,11 +969,11 @@ static void prep_dispatch(const ChunkProblem& p, hipStream_t s) {
     }
 }
 
-// p.tmat set (the backward pass): the BWD instance
+// p.tmat or p.tmat16 set (the backward pass): the BWD instance
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
     launch_chunk_base(p, s);
     if (p.nc_bound > 0) {
-        if (p.tmat) prep_dispatch<true>(p, s); else prep_dispatch<false>(p, s);
+        if (p.tmat || p.tmat16) prep_dispatch<true>(p, s); else prep_dispatch<false>(p, s);
     }
     return hipGetLastError();
 }

@@ -32,6 +32,7 @@ struct ChunkProblem {
     _Float16* q16;               // [nc_bound, H, 64, dk] fp16 diag(e^gamma) Q (bf16 inputs only)
     // optional outputs of the fp32 kernels, used by the backward pass (NULL: not written)
     float* tmat;                 // [nc_bound, H, 64, 64] T = (I + A)^{-1} (stage 1)
+    _Float16* tmat16;            // the same in fp16 (backward pass, bf16 inputs; tmat NULL)
     float* states;               // [nc_bound, H, dv, dk] state entering each chunk (stage 2)
     _Float16* states16;          // the same in fp16 (backward pass, bf16 inputs; states NULL)
     _Float16* mimg16;            // [nc_bound, H, 64, 64] fp16 LDS images of Mmat and P (stage 1
@@ -98,8 +99,8 @@ hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s);
 
 // Backward pass. `f` describes the forward problem over the caller's q, k, v with its stage-1
-// workspace and the tmat and states regions set (bf16 inputs: also mimg16, pimg16, k16, q16); the rest
-// are the backward's own inputs, outputs and regions.
+// workspace and the tmat and states regions set (bf16 inputs: tmat16 and states16 instead, and
+// mimg16, pimg16, k16, q16); the rest are the backward's own inputs, outputs and regions.
 struct BwdProblem {
     ChunkProblem f;
     const void* q_in;            // caller's q, k, v, dO in the caller's dtype

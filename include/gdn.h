@@ -163,7 +163,7 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  *   Mmat, P; row-major [nc, H, 64, 64]; for bf16 inputs the Mmat region holds instead the
  *   fp16 LDS images of Mmat [nc, H, 64, 64] and then of P, as gdn_chunk_fwd's workspace
  *   stores them), then
- *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major
+ *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major (bf16 inputs: fp16)
  *   states   fp32 [nc, H, dv, dk]  the state entering each chunk (bf16 inputs: fp16, the
  *                                  precision its products take, and half the size)
  *   dstates  fp32 [nc, H, dv, dk]  the gradient reaching the state after each chunk
