@@ -220,6 +220,8 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     // bf16: the fp32 Mmat region (not written) holds the fp16 images of Mmat, then of P
     P.mimg16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.fwd.off_m) : nullptr;
     P.pimg16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.fwd.off_m) + w.fwd.nc_bound * H * 4096 : nullptr;
+    // bf16: the fp32 P region (not written) holds the image of P's fp16 rounding remainder
+    P.plo16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.fwd.off_p) : nullptr;
     P.k16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_k16) : nullptr;
     P.q16 = (any && bf16) ? reinterpret_cast<_Float16*>(base + w.off_q16) : nullptr;
     b.dstates = any ? reinterpret_cast<float*>(base + w.off_dstates) : nullptr;

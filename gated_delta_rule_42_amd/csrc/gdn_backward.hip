@@ -808,15 +808,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             qin[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
         }
     }
-    u32x4_t tin[2];
-    f32x4_t pin[2][2];
+    // T fp16 row-major; P as fp16 hi + lo, two images (piece i: row r, columns c0..+3, c0+16..+19)
+    u32x4_t tin[2], phi[2], plo[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
-        const f32x4_t* pq = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.pmat) + widx * 4096 + r * 64 + cc);
         tin[it] = *reinterpret_cast<const u32x4_t*>(p.tmat16 + widx * 4096 + r * 64 + cc);
-        pin[it][0] = pq[0];
-        pin[it][1] = pq[1];
+        phi[it] = reinterpret_cast<const u32x4_t*>(p.pimg16 + widx * 4096)[i];
+        plo[it] = reinterpret_cast<const u32x4_t*>(p.plo16 + widx * 4096)[i];
     }
     float gin = 0.f, bin = 0.f, egin = 0.f, edin = 0.f;
     if (wave == 0) {
@@ -886,10 +885,12 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     for (int it = 0; it < 2; ++it) {
         const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
         *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) = make_uint4(tin[it][0], tin[it][1], tin[it][2], tin[it][3]);
-        const float4 p0 = f4(pin[it][0]), p1 = f4(pin[it][1]);
-        const uint4 ph = pack8(p0, p1);
-        *reinterpret_cast<uint4*>(&sm.P[r * PT + cc]) = ph;
-        *reinterpret_cast<uint4*>(&sm.Plo[r * PT + cc]) = resid8(p0, p1, ph);
+        int pr, pc0;
+        img_piece<64>(i, pr, pc0);
+        *reinterpret_cast<uint2*>(&sm.P[pr * PT + pc0]) = make_uint2(phi[it][0], phi[it][1]);
+        *reinterpret_cast<uint2*>(&sm.P[pr * PT + pc0 + 16]) = make_uint2(phi[it][2], phi[it][3]);
+        *reinterpret_cast<uint2*>(&sm.Plo[pr * PT + pc0]) = make_uint2(plo[it][0], plo[it][1]);
+        *reinterpret_cast<uint2*>(&sm.Plo[pr * PT + pc0 + 16]) = make_uint2(plo[it][2], plo[it][3]);
     }
     if (wave == 0) {
         sm.beta[lane] = bin;

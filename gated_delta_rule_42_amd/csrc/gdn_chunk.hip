@@ -71,6 +71,7 @@ struct alignas(16) PrepSmem {
         struct { float A[64 * PF]; float T[64 * PF]; } tri;
     } u;
     TM P[64 * PC];
+    TM Plo[sizeof(TM) == 2 ? 64 * PC : 8];   // fp16 operands: P - fp16(P) (backward pass)
     float graw[64];   // g as loaded
     float gam[64];    // its in-chunk inclusive cumulative sum
     float beta[64];
@@ -233,9 +234,10 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                         const float a = (i < r) ? brv[v] * G[cb][v] * e : 0.f;
                         const float pp = (i <= r) ? P0[cb][v] * e : 0.f;
                         sm.u.tri.A[r * PF + i] = a;
-                        sm.P[r * PC + i] = from_f32<TM>(pp);
-                        // backward pass, bf16 inputs: P also in fp32, row-major, before its rounding
-                        if (sizeof(TM) == 2 && BWD) static_cast<float*>(p.pmat)[widx * 4096 + r * 64 + i] = pp;
+                        const TM ph = from_f32<TM>(pp);
+                        sm.P[r * PC + i] = ph;
+                        // backward pass, bf16 inputs: also P's fp16 rounding remainder
+                        if constexpr (sizeof(TM) == 2 && BWD) sm.Plo[r * PC + i] = (TM)(pp - (float)ph);
                     }
                 }
             }
@@ -274,7 +276,8 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                     tq[0] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
                     tq[1] = make_uint4(tv[4], tv[5], tv[6], tv[7]);
                 }
-                // the backward pass keeps the fp32 P in p.pmat and takes the images from mimg16, pimg16
+                // the backward pass takes the images from mimg16, pimg16 and adds that of P's
+                // rounding remainder (plo16)
                 _Float16* mimg = BWD ? p.mimg16 : static_cast<TM*>(p.mmat);
                 _Float16* pimg = BWD ? p.pimg16 : static_cast<TM*>(p.pmat);
 #pragma unroll
@@ -295,6 +298,11 @@ __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
                     reinterpret_cast<uint4*>(pimg + widx * 4096)[i] =
                         make_uint4(pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
                                    pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7]));
+                    if constexpr (BWD) {
+                        const uint2 la = *reinterpret_cast<const uint2*>(&sm.Plo[r * PC + c0]);
+                        const uint2 lb = *reinterpret_cast<const uint2*>(&sm.Plo[r * PC + c0 + 16]);
+                        reinterpret_cast<uint4*>(p.plo16 + widx * 4096)[i] = make_uint4(la.x, la.y, lb.x, lb.y);
+                    }
                 }
             }
         } else if (nok) {

@@ -37,6 +37,7 @@ struct ChunkProblem {
     _Float16* states16;          // the same in fp16 (backward pass, bf16 inputs; states NULL)
     _Float16* mimg16;            // [nc_bound, H, 64, 64] fp16 LDS images of Mmat and P (stage 1
     _Float16* pimg16;            //   of the backward pass, bf16 inputs; with k16, q16)
+    _Float16* plo16;             // [nc_bound, H, 64, 64] image of P - fp16(P), fp16 (the same)
     // channel-wise decay (g is [B,T,H,dk]): chunk operators of the fp32 kernels
     float* khat;                 // [nc_bound, H, 64, dk] K * e^gamma          (fp16 for bf16 inputs)
     float* qhat;                 // [nc_bound, H, 64, dk] Q * e^gamma          (fp16 for bf16 inputs)

@@ -162,7 +162,7 @@ int gdn_chunk_propagate(const void *q, const void *k, const void *v, const float
  *   the regions of gdn_chunk_fwd_workspace_bytes for fp32 operators (chunk_base, gates,
  *   Mmat, P; row-major [nc, H, 64, 64]; for bf16 inputs the Mmat region holds instead the
  *   fp16 LDS images of Mmat [nc, H, 64, 64] and then of P, as gdn_chunk_fwd's workspace
- *   stores them), then
+ *   stores them, and the P region the image of P - fp16(P) in fp16), then
  *   T        fp32 [nc, H, 64, 64]  (I + A)^{-1}, row-major (bf16 inputs: fp16)
  *   states   fp32 [nc, H, dv, dk]  the state entering each chunk (bf16 inputs: fp16, the
  *                                  precision its products take, and half the size)
