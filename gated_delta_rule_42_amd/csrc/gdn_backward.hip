@@ -27,13 +27,13 @@
 // gamma_i} for i <= r.)
 //
 // Passes: (1) stage 1 of the forward pass (gate tables, Mmat, P; gram products accumulated
-// in fp32) also keeping T in fp32, row-major (for bf16 inputs, read straight from the raw
-// inputs: fp32 P row-major and the fp16 LDS images of K, diag(e^gamma) Q, Mmat and P);
-// (2) stage 2 of the forward pass keeping the state entering every chunk instead of writing
-// o; (3) the reverse walk, keeping dS' of every chunk and writing dh0; (4) every (chunk, head)
+// in fp32) also keeping T, row-major (fp32; for bf16 inputs, read straight from the raw
+// inputs: T in fp16, the fp16 LDS images of K, diag(e^gamma) Q, Mmat and P, and the image of
+// P's fp16 rounding remainder); (2) stage 2 of the forward pass keeping the state entering
+// every chunk instead of writing o (bf16 inputs: in fp16, the precision (4) takes it in); (3) the reverse walk, keeping dS' of every chunk and writing dh0; (4) every (chunk, head)
 // on its own. fp32 inputs run (2)-(4) on the fp32 16x16x4 matrix core
 // (chunk_propagate_kernel<float>, chunk_bwd_state_kernel, chunk_bwd_grad_kernel). bf16 inputs
-// run them on fp16 operands with fp32 accumulation and fp32 states: (2) and (3) DMA-fed from
+// run them on fp16 operands with fp32 accumulation and fp32 state chains: (2) and (3) DMA-fed from
 // the images (chunk_propagate_bf16_kernel, chunk_bwd_state16_kernel), (4)
 // chunk_bwd_grad16_kernel; the numerics of the forward pass.
 #include "gdn_device.h"
@@ -1216,8 +1216,9 @@ static void bwd_dispatch(const BwdProblem& b, hipStream_t s) {
 
 hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
     const ChunkProblem& p = b.f;
-    // stage 1 again (bf16 inputs: straight from the raw inputs, with fp32 T and P row-major
-    // and the fp16 images of K, diag(e^gamma) Q, Mmat and P), then the state recompute
+    // stage 1 again (bf16 inputs: straight from the raw inputs, with T in fp16 row-major and
+    // the fp16 images of K, diag(e^gamma) Q, Mmat, P and P's rounding remainder), then the
+    // state recompute
     hipError_t e = launch_chunk_prepare(p, s);
     if (e != hipSuccess) return e;
     if (p.mimg16) {   // bf16 inputs: fp16 operands

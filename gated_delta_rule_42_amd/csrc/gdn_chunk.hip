@@ -155,9 +155,9 @@ __device__ __forceinline__ void write_kq_images(const PrepSmem<TIn, DK>& sm, _Fl
 
 // Persistent work-groups: each walks (chunk, head) units with a stride of the grid, keeping
 // the next unit's inputs in flight in registers while the current one is computed. BWD: the
-// instance run by the backward pass, which also keeps T (fp32, row-major) and writes the
-// operators row-major for its own kernels (fp32 inputs: fp32 Mmat, P and, when set, fp16
-// copies; bf16 inputs: fp32 P and fp16 Mmat and P).
+// instance run by the backward pass, which also keeps T row-major and writes the operators
+// for its own kernels (fp32 inputs: fp32 T, Mmat, P row-major and, when set, fp16 copies;
+// bf16 inputs: fp16 T row-major and the fp16 images of Mmat, P and P's rounding remainder).
 template <typename TIn, int DK, bool BWD>
 __global__ __launch_bounds__(256) void chunk_prepare_kernel(ChunkProblem p) {
     using SM = PrepSmem<TIn, DK>;
