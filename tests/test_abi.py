@@ -80,6 +80,36 @@ def test_workspace_bytes(L):
     assert L.gdn_chunk_fwd_workspace_bytes(2, 10, 2, 64, 64, 3, 1, 64, 1) == 0
 
 
+def test_bwd_workspace_bytes(L):
+    """The backward workspace is the region list of its header: the forward's regions with
+    fp32 operators, then T, the state entering each chunk and the state gradient, and for bf16
+    inputs the K and Q images; T and the entering state are fp16 for bf16 inputs."""
+    import torch
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+
+    def expect(nc, H, dk, dv, bf16, varlen_n=None):
+        fwd = (al((varlen_n + 1) * 4) if varlen_n else 0) + al(nc * H * 128 * 4) \
+            + al(nc * H * 4096 * 4) + nc * H * 4096 * 4
+        e16 = 2 if bf16 else 4
+        off = al(al(al(fwd) + nc * H * 4096 * e16) + nc * H * dv * dk * e16)
+        end = off + nc * H * dv * dk * 4
+        if bf16:
+            end = al(al(end) + nc * H * 64 * dk * 2) + nc * H * 64 * dk * 2
+        return end
+
+    # B4 H16 T2048 d128: 128 chunks x 16 heads
+    for dt, bf16 in ((torch.float32, False), (torch.bfloat16, True)):
+        assert gb.gdn_chunk_bwd_workspace_bytes(4, 2048, 16, 128, 128, 4, False, dtype=dt) == \
+            expect(128, 16, 128, 128, bf16)
+    # packed, d_k != d_v: chunk bound floor((T + N*63)/64) and the chunk table
+    T, N, H = 1000, 5, 2
+    ncb = (T + N * 63) // 64
+    for dt, bf16 in ((torch.float32, False), (torch.bfloat16, True)):
+        assert gb.gdn_chunk_bwd_workspace_bytes(1, T, H, 64, 128, N, True, dtype=dt) == \
+            expect(ncb, H, 64, 128, bf16, varlen_n=N)
+    assert gb.gdn_chunk_bwd_workspace_bytes(1, 0, 2, 64, 64, 1, False) == 0
+
+
 FAKE = 1 << 20  # an aligned, never dereferenced address: every call below fails validation
 
 
