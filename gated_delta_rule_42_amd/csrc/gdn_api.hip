@@ -4,12 +4,33 @@
 #include "gdn.h"
 #include "gdn_internal.h"
 
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
 #define GDN_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// GDN_CHECK=1 in the environment: copy cu_seqlens to the host (this synchronises `stream`) and
+// reject offsets that break 0 = cu[0] <= cu[1] <= ... <= cu[N] = T. A debugging aid: without it
+// the offsets are a precondition that the kernels only clamp into [0, T].
+int debug_check_offsets(const int32_t* cu, int N, int T, hipStream_t s) {
+    const char* env = std::getenv("GDN_CHECK");
+    if (!cu || !env || std::strcmp(env, "1") != 0) return GDN_OK;
+    std::vector<int32_t> h((size_t)N + 1);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (h[0] != 0 || h[(size_t)N] != T) return GDN_ERR_SHAPE;
+    for (int i = 0; i < N; ++i)
+        if (h[(size_t)i + 1] < h[(size_t)i]) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
 
 // Shared checks of the chunked forward entry points. `need` flags: 1 = q,k,g,beta;
 // 2 = v,o. Fills the problem description on success.
@@ -101,6 +122,8 @@ GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, c
     int st = check_chunk(q, k, nullptr, g, beta, nullptr, nullptr, nullptr, cu_seqlens, chunk, B, T,
                          H, dk, dv, N, dtype, GDN_F32, workspace, workspace_bytes, 1, &p);
     if (st != GDN_OK) return st;
+    st = debug_check_offsets(cu_seqlens, N, T, static_cast<hipStream_t>(stream));
+    if (st != GDN_OK) return st;
     return gdn::launch_chunk_prepare(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                       : GDN_ERR_HIP;
 }
@@ -113,24 +136,52 @@ GDN_EXPORT int gdn_chunk_propagate(const void* q, const void* k, const void* v, 
     int st = check_chunk(q, k, v, nullptr, nullptr, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
                          N, dtype, o_dtype, workspace, workspace_bytes, 2, &p);
     if (st != GDN_OK) return st;
+    st = debug_check_offsets(cu_seqlens, N, T, static_cast<hipStream_t>(stream));
+    if (st != GDN_OK) return st;
     return gdn::launch_chunk_propagate(p, static_cast<hipStream_t>(stream)) == hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }
+
+namespace gdn {
+// gdn_chunk_fwd's argument checks (host only, no HIP call) for a caller that will supply a
+// workspace of gdn_chunk_fwd_workspace_bytes(...) bytes itself: GDN_OK or the status
+// gdn_chunk_fwd would return for any argument other than the workspace.
+int chunk_fwd_check(const void* q, const void* k, const void* v, const float* g_log_alpha, const float* beta,
+                    const float* h0, const void* o, const float* hT, const int32_t* cu_seqlens, int chunk,
+                    int B, int T, int H, int dk, int dv, int N, int dtype, int o_dtype) {
+    gdn::ChunkProblem p{};
+    const int st = check_chunk(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv, N,
+                               dtype, o_dtype, nullptr, 0, 3, &p);
+    return st == GDN_ERR_WORKSPACE ? GDN_OK : st;
+}
+
+// gdn_chunk_fwd with its arguments as given (also serves entry points that supply their own
+// workspace)
+int chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha, const float* beta,
+              const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int chunk, int B, int T,
+              int H, int dk, int dv, int N, int dtype, int o_dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    gdn::ChunkProblem p{};
+    int st = check_chunk(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
+                         N, dtype, o_dtype, workspace, workspace_bytes, 3, &p);
+    if (st != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = debug_check_offsets(cu_seqlens, N, T, s);
+    if (st != GDN_OK) return st;
+    if (gdn::launch_chunk_prepare(p, s) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_chunk_propagate(p, s) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
+}
+}  // namespace gdn
 
 GDN_EXPORT int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha,
                              const float* beta, const float* h0, void* o, float* hT,
                              const int32_t* cu_seqlens, int chunk, int B, int T, int H, int dk,
                              int dv, int N, int dtype, int o_dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-    gdn::ChunkProblem p{};
-    int st = check_chunk(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv,
-                         N, dtype, o_dtype, workspace, workspace_bytes, 3, &p);
-    if (st != GDN_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (gdn::launch_chunk_prepare(p, s) != hipSuccess) return GDN_ERR_HIP;
-    if (gdn::launch_chunk_propagate(p, s) != hipSuccess) return GDN_ERR_HIP;
-    return GDN_OK;
+    return gdn::chunk_fwd(q, k, v, g_log_alpha, beta, h0, o, hT, cu_seqlens, chunk, B, T, H, dk, dv, N,
+                          dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 GDN_EXPORT int gdn_decode_step(const void* q, const void* k, const void* v, const float* g_log_alpha,
@@ -228,6 +279,8 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     b.dhT = dhT;
     b.dq = dq; b.dk = dk_out; b.dv = dv_out; b.dg = dg; b.dbeta = dbeta; b.dh0 = dh0;
     b.grad_bf16 = grad_dtype == GDN_BF16;
+    const int chk = debug_check_offsets(cu_seqlens, N, T, static_cast<hipStream_t>(stream));
+    if (chk != GDN_OK) return chk;
     return gdn::launch_chunk_backward(b, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                        : GDN_ERR_HIP;
 }
@@ -291,6 +344,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_lo
     P.lam = any ? reinterpret_cast<float*>(base + w.off_lam) : nullptr;
     P.erase = erase;
     P.write = erase ? write : nullptr;
+    const int chk = debug_check_offsets(cu_seqlens, N, T, static_cast<hipStream_t>(stream));
+    if (chk != GDN_OK) return chk;
     return gdn::launch_kda_chunk_fwd(P, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK
                                                                                        : GDN_ERR_HIP;
 }

@@ -1181,37 +1181,36 @@ BwdLayout bwd_workspace_layout(int B, int T, int H, int dk, int dv, int N, int v
 }
 
 template <typename TO, int DK, int DV>
-static void bwd_launch(const BwdProblem& b, hipStream_t s) {
+static hipError_t bwd_launch(const BwdProblem& b, hipStream_t s) {
     const ChunkProblem& p = b.f;
     constexpr int DVT = 32;
     const long pairs = (long)p.N * p.H;
+    hipError_t e = hipSuccess;
     if (pairs > 0) {
-        if (p.mimg16) {   // bf16 inputs: stage 1's fp16 images, the raw dO
-            hipLaunchKernelGGL((chunk_bwd_state16_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                               dim3((DVT / 16 + 1) * 64), 0, s, p, static_cast<const uint16_t*>(b.do_in), b.dhT,
-                               b.dstates, b.dh0);
-        } else {
-            hipLaunchKernelGGL((chunk_bwd_state_kernel<DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                               dim3(DVT / 16 * 64), 0, s, p, b.do32, b.dhT, b.dstates, b.dh0);
-        }
+        if (p.mimg16)   // bf16 inputs: stage 1's fp16 images, the raw dO
+            e = launch(chunk_bwd_state16_kernel<DK, DV, DVT>, dim3((unsigned)(pairs * (DV / DVT))),
+                       dim3((DVT / 16 + 1) * 64), s, p, static_cast<const uint16_t*>(b.do_in), b.dhT,
+                       b.dstates, b.dh0);
+        else
+            e = launch(chunk_bwd_state_kernel<DK, DV, DVT>, dim3((unsigned)(pairs * (DV / DVT))),
+                       dim3(DVT / 16 * 64), s, p, b.do32, b.dhT, b.dstates, b.dh0);
     }
     const long units = p.nc_bound * p.H;
-    if (units > 0) {
+    if (e == hipSuccess && units > 0) {
         if (p.mimg16)
-            hipLaunchKernelGGL((chunk_bwd_grad16_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+            e = launch(chunk_bwd_grad16_kernel<TO, DK, DV>, dim3((unsigned)units), dim3(256), s, b);
         else
-            hipLaunchKernelGGL((chunk_bwd_grad_kernel<TO, DK, DV>), dim3((unsigned)units), dim3(256), 0, s, b);
+            e = launch(chunk_bwd_grad_kernel<TO, DK, DV>, dim3((unsigned)units), dim3(256), s, b);
     }
+    return e;
 }
 
 template <typename TO>
-static void bwd_dispatch(const BwdProblem& b, hipStream_t s) {
+static hipError_t bwd_dispatch(const BwdProblem& b, hipStream_t s) {
     const int dk = b.f.dk, dv = b.f.dv;
-    if (dk == 64) {
-        if (dv == 64) bwd_launch<TO, 64, 64>(b, s); else bwd_launch<TO, 64, 128>(b, s);
-    } else {
-        if (dv == 64) bwd_launch<TO, 128, 64>(b, s); else bwd_launch<TO, 128, 128>(b, s);
-    }
+    if (dk == 64)
+        return dv == 64 ? bwd_launch<TO, 64, 64>(b, s) : bwd_launch<TO, 64, 128>(b, s);
+    return dv == 64 ? bwd_launch<TO, 128, 64>(b, s) : bwd_launch<TO, 128, 128>(b, s);
 }
 
 hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
@@ -1221,14 +1220,10 @@ hipError_t launch_chunk_backward(const BwdProblem& b, hipStream_t s) {
     // state recompute
     hipError_t e = launch_chunk_prepare(p, s);
     if (e != hipSuccess) return e;
-    if (p.mimg16) {   // bf16 inputs: fp16 operands
-        e = launch_chunk_propagate_states16(p, s);
-    } else {
-        e = launch_chunk_propagate(p, s);
-    }
+    e = p.mimg16 ? launch_chunk_propagate_states16(p, s)   // bf16 inputs: fp16 operands
+                 : launch_chunk_propagate(p, s);
     if (e != hipSuccess) return e;
-    if (b.grad_bf16) bwd_dispatch<uint16_t>(b, s); else bwd_dispatch<float>(b, s);
-    return hipGetLastError();
+    return b.grad_bf16 ? bwd_dispatch<uint16_t>(b, s) : bwd_dispatch<float>(b, s);
 }
 
 }  // namespace gdn

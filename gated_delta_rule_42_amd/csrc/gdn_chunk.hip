@@ -942,73 +942,53 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
 }
 
 template <typename TIn, int DK, bool BWD>
-static void prep_launch(const ChunkProblem& p, hipStream_t s) {
-    // persistent grid: as many work-groups as the device holds at once (queried once per
-    // device), so that every (chunk, head) unit is taken by an already running work-group
-    static int resident[64] = {0};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    int& cap = resident[dev & 63];
-    if (cap == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prepare_kernel<TIn, DK, BWD>, 256, 0) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            per_cu < 1 || cus < 1)
-            per_cu = 2, cus = 256;
-        cap = per_cu * cus;
-    }
+static hipError_t prep_launch(const ChunkProblem& p, hipStream_t s) {
+    // persistent grid: as many work-groups as the device holds at once, so that every
+    // (chunk, head) unit is taken by an already running work-group
+    static std::atomic<int> resident[64];
+    const long cap = resident_blocks(chunk_prepare_kernel<TIn, DK, BWD>, 256, resident, 2);
     const long units = p.nc_bound * p.H;
     const long blocks = units < cap ? units : cap;
-    hipLaunchKernelGGL((chunk_prepare_kernel<TIn, DK, BWD>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return launch(chunk_prepare_kernel<TIn, DK, BWD>, dim3((unsigned)blocks), dim3(256), s, p);
 }
 
-void launch_chunk_base(const ChunkProblem& p, hipStream_t s) {
-    if (p.cu_seqlens)
-        hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.N, p.T,
-                           p.chunk_base);
+hipError_t launch_chunk_base(const ChunkProblem& p, hipStream_t s) {
+    if (!p.cu_seqlens) return hipSuccess;
+    return launch(chunk_base_kernel, dim3(1), dim3(1024), s, p.cu_seqlens, p.N, p.T, p.chunk_base);
 }
 
 template <bool BWD>
-static void prep_dispatch(const ChunkProblem& p, hipStream_t s) {
-    if (p.bf16) {
-        if (p.dk == 64) prep_launch<uint16_t, 64, BWD>(p, s); else prep_launch<uint16_t, 128, BWD>(p, s);
-    } else {
-        if (p.dk == 64) prep_launch<float, 64, BWD>(p, s); else prep_launch<float, 128, BWD>(p, s);
-    }
+static hipError_t prep_dispatch(const ChunkProblem& p, hipStream_t s) {
+    if (p.bf16)
+        return p.dk == 64 ? prep_launch<uint16_t, 64, BWD>(p, s) : prep_launch<uint16_t, 128, BWD>(p, s);
+    return p.dk == 64 ? prep_launch<float, 64, BWD>(p, s) : prep_launch<float, 128, BWD>(p, s);
 }
 
 // p.tmat or p.tmat16 set (the backward pass): the BWD instance
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
-    launch_chunk_base(p, s);
-    if (p.nc_bound > 0) {
-        if (p.tmat || p.tmat16) prep_dispatch<true>(p, s); else prep_dispatch<false>(p, s);
-    }
-    return hipGetLastError();
+    hipError_t e = launch_chunk_base(p, s);
+    if (e == hipSuccess && p.nc_bound > 0)
+        e = (p.tmat || p.tmat16) ? prep_dispatch<true>(p, s) : prep_dispatch<false>(p, s);
+    return e;
 }
 
 template <typename TIn, typename TO, int DK, int DV>
-static void prop_launch(const ChunkProblem& p, hipStream_t s) {
-    if constexpr (sizeof(TIn) == 2) {
-        // bf16: two compute waves (32 columns), a DMA wave and a store wave per work-group
-        constexpr int DVT = 32;
-        const long blocks = (long)p.N * p.H * (DV / DVT);
-        hipLaunchKernelGGL((chunk_propagate_bf16_kernel<TO, DK, DV, DVT>), dim3((unsigned)blocks),
-                           dim3((DVT / 16 + 2) * 64), 0, s, p);
-    } else {
-        constexpr int DVT = 32;  // two waves of 16 columns (LDS size)
-        const long blocks = (long)p.N * p.H * (DV / DVT);
-        hipLaunchKernelGGL((chunk_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)blocks),
-                           dim3(DVT / 16 * 64), 0, s, p);
-    }
+static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
+    constexpr int DVT = 32;
+    const long blocks = (long)p.N * p.H * (DV / DVT);
+    if constexpr (sizeof(TIn) == 2)   // two compute waves (32 columns), a DMA wave and a store wave
+        return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT>, dim3((unsigned)blocks),
+                      dim3((DVT / 16 + 2) * 64), s, p);
+    else                              // two waves of 16 columns (LDS size)
+        return launch(chunk_propagate_kernel<TIn, TO, DK, DV, DVT>, dim3((unsigned)blocks),
+                      dim3(DVT / 16 * 64), s, p);
 }
 
 template <typename TIn, typename TO>
-static void prop_dispatch(const ChunkProblem& p, hipStream_t s) {
-    if (p.dk == 64) {
-        if (p.dv == 64) prop_launch<TIn, TO, 64, 64>(p, s); else prop_launch<TIn, TO, 64, 128>(p, s);
-    } else {
-        if (p.dv == 64) prop_launch<TIn, TO, 128, 64>(p, s); else prop_launch<TIn, TO, 128, 128>(p, s);
-    }
+static hipError_t prop_dispatch(const ChunkProblem& p, hipStream_t s) {
+    if (p.dk == 64)
+        return p.dv == 64 ? prop_launch<TIn, TO, 64, 64>(p, s) : prop_launch<TIn, TO, 64, 128>(p, s);
+    return p.dv == 64 ? prop_launch<TIn, TO, 128, 64>(p, s) : prop_launch<TIn, TO, 128, 128>(p, s);
 }
 
 // The state recompute of the backward pass for bf16 inputs: the DMA-fed stage 2 on the fp16
@@ -1020,17 +1000,13 @@ hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s)
     q.pmat = p.pimg16;
     q.o = nullptr;
     q.hT = nullptr;
-    if ((long)p.N * p.H > 0) prop_dispatch<uint16_t, float>(q, s);
-    return hipGetLastError();
+    return (long)p.N * p.H > 0 ? prop_dispatch<uint16_t, float>(q, s) : hipSuccess;
 }
 
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s) {
-    if ((long)p.N * p.H > 0) {
-        if (!p.bf16) prop_dispatch<float, float>(p, s);
-        else if (p.o_bf16) prop_dispatch<uint16_t, uint16_t>(p, s);
-        else prop_dispatch<uint16_t, float>(p, s);
-    }
-    return hipGetLastError();
+    if ((long)p.N * p.H == 0) return hipSuccess;
+    if (!p.bf16) return prop_dispatch<float, float>(p, s);
+    return p.o_bf16 ? prop_dispatch<uint16_t, uint16_t>(p, s) : prop_dispatch<uint16_t, float>(p, s);
 }
 
 }  // namespace gdn

@@ -115,34 +115,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeProblem p) {
 }
 
 template <typename TS, typename TO, int DK, int DV>
-static void decode_launch(const DecodeProblem& p, hipStream_t s) {
+static hipError_t decode_launch(const DecodeProblem& p, hipStream_t s) {
     const dim3 grid((unsigned)((long)p.N * p.H));
-    if (p.erase)
-        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true, true>), grid, dim3(256), 0, s, p);
-    else if (p.channel_gate)
-        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, true, false>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((decode_kernel<TS, TO, DK, DV, false, false>), grid, dim3(256), 0, s, p);
+    if (p.erase) return launch(decode_kernel<TS, TO, DK, DV, true, true>, grid, dim3(256), s, p);
+    if (p.channel_gate) return launch(decode_kernel<TS, TO, DK, DV, true, false>, grid, dim3(256), s, p);
+    return launch(decode_kernel<TS, TO, DK, DV, false, false>, grid, dim3(256), s, p);
 }
 
 template <typename TS, typename TO>
-static void decode_dispatch(const DecodeProblem& p, hipStream_t s) {
-    if (p.dk == 64) {
-        if (p.dv == 64) decode_launch<TS, TO, 64, 64>(p, s); else decode_launch<TS, TO, 64, 128>(p, s);
-    } else {
-        if (p.dv == 64) decode_launch<TS, TO, 128, 64>(p, s); else decode_launch<TS, TO, 128, 128>(p, s);
-    }
+static hipError_t decode_dispatch(const DecodeProblem& p, hipStream_t s) {
+    if (p.dk == 64)
+        return p.dv == 64 ? decode_launch<TS, TO, 64, 64>(p, s) : decode_launch<TS, TO, 64, 128>(p, s);
+    return p.dv == 64 ? decode_launch<TS, TO, 128, 64>(p, s) : decode_launch<TS, TO, 128, 128>(p, s);
 }
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s) {
-    if ((long)p.N * p.H > 0) {
-        if (p.bf16) {
-            if (p.o_bf16) decode_dispatch<uint16_t, uint16_t>(p, s); else decode_dispatch<uint16_t, float>(p, s);
-        } else {
-            if (p.o_bf16) decode_dispatch<float, uint16_t>(p, s); else decode_dispatch<float, float>(p, s);
-        }
-    }
-    return hipGetLastError();
+    if ((long)p.N * p.H == 0) return hipSuccess;
+    if (p.bf16)
+        return p.o_bf16 ? decode_dispatch<uint16_t, uint16_t>(p, s) : decode_dispatch<uint16_t, float>(p, s);
+    return p.o_bf16 ? decode_dispatch<float, uint16_t>(p, s) : decode_dispatch<float, float>(p, s);
 }
 
 }  // namespace gdn

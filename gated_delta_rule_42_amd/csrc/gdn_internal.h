@@ -5,7 +5,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdn {
+
+// Kernel launch that reports its own status (not a sticky error left by an earlier HIP call
+// of the caller, and without clearing one). The trailing arguments are converted to the
+// kernel's parameter types.
+template <typename T> struct NoDeduce { using type = T; };
+template <typename... KArgs>
+inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                         typename NoDeduce<KArgs>::type... args) {
+    void* argv[] = {static_cast<void*>(&args)..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, s);
+}
+
+// Work-groups of `kern` (block threads, no dynamic LDS) that the current device holds at
+// once, cached per device in `cache` (zero = not yet known). Concurrent first calls may
+// both run the query; they store the same value, and the atomics make that race-free.
+template <typename K>
+inline long resident_blocks(K kern, int block, std::atomic<int> (&cache)[64], int fallback_per_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::atomic<int>& slot = cache[dev & 63];
+    int cap = slot.load(std::memory_order_relaxed);
+    if (cap == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            per_cu < 1 || cus < 1)
+            per_cu = fallback_per_cu, cus = 256;
+        cap = per_cu * cus;
+        slot.store(cap, std::memory_order_relaxed);
+    }
+    return cap;
+}
 
 // Resolved problem description for the chunked forward pass.
 struct ChunkProblem {
@@ -94,7 +128,7 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes);
 
-void launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
+hipError_t launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s);
@@ -153,5 +187,17 @@ struct DecodeProblem {
 };
 
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t s);
+
+// gdn_chunk_fwd's host-side argument checks, leaving out the workspace; returns a gdn_status.
+int chunk_fwd_check(const void* q, const void* k, const void* v, const float* g_log_alpha, const float* beta,
+                    const float* h0, const void* o, const float* hT, const int32_t* cu_seqlens, int chunk,
+                    int B, int T, int H, int dk, int dv, int N, int dtype, int o_dtype);
+
+// gdn_chunk_fwd (argument checks, optional GDN_CHECK offsets check, both stages) on the given
+// workspace; returns a gdn_status.
+int chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_alpha, const float* beta,
+              const float* h0, void* o, float* hT, const int32_t* cu_seqlens, int chunk, int B, int T,
+              int H, int dk, int dv, int N, int dtype, int o_dtype, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 }  // namespace gdn

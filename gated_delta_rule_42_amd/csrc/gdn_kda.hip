@@ -980,60 +980,44 @@ KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen, i
 }
 
 template <typename TIn, typename TO, int DK, int DV>
-static void kda_launch(const ChunkProblem& p, hipStream_t s) {
+static hipError_t kda_launch(const ChunkProblem& p, hipStream_t s) {
     constexpr int DVT = 32;
     const long units = p.nc_bound * p.H;
+    hipError_t e = hipSuccess;
     if (units > 0) {
-        // persistent grid: as many work-groups as the device holds at once (queried once per
-        // device and kernel)
-        auto go = [&](auto kern) {
-            static int resident[64] = {0};
-            int dev = 0;
-            (void)hipGetDevice(&dev);
-            int& cap = resident[dev & 63];
-            if (cap == 0) {
-                int per_cu = 0, cus = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
-                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-                    per_cu < 1 || cus < 1)
-                    per_cu = 1, cus = 256;
-                cap = per_cu * cus;
-            }
-            hipLaunchKernelGGL(kern, dim3((unsigned)(units < cap ? units : cap)), dim3(256), 0, s, p);
+        // persistent grid: as many work-groups as the device holds at once
+        auto go = [&](auto kern, std::atomic<int> (&resident)[64]) {
+            const long cap = resident_blocks(kern, 256, resident, 1);
+            return launch(kern, dim3((unsigned)(units < cap ? units : cap)), dim3(256), s, p);
         };
-        if (p.erase) go(kda_prepare_kernel<TIn, DK, true>); else go(kda_prepare_kernel<TIn, DK, false>);
+        static std::atomic<int> resident_erase[64], resident_beta[64];
+        e = p.erase ? go(kda_prepare_kernel<TIn, DK, true>, resident_erase)
+                    : go(kda_prepare_kernel<TIn, DK, false>, resident_beta);
     }
     const long pairs = (long)p.N * p.H;
-    if (pairs > 0) {
-        if constexpr (sizeof(TIn) == 2) {
-            if (p.write == nullptr)
-                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT, false>),
-                                   dim3((unsigned)(pairs * (DV / DVT))), dim3((DVT / 16 + 2) * 64), 0, s, p);
-            else
-                hipLaunchKernelGGL((kda_propagate_dma_kernel<TO, DK, DV, DVT, true>),
-                                   dim3((unsigned)(pairs * (DV / DVT))), dim3((DVT / 16 + 1) * 64), 0, s, p);
-        }
-        else
-            hipLaunchKernelGGL((kda_propagate_kernel<TIn, TO, DK, DV, DVT>), dim3((unsigned)(pairs * (DV / DVT))),
-                               dim3(DVT / 16 * 64), 0, s, p);
+    if (e != hipSuccess || pairs == 0) return e;
+    const dim3 grid((unsigned)(pairs * (DV / DVT)));
+    if constexpr (sizeof(TIn) == 2) {
+        if (p.write == nullptr)
+            return launch(kda_propagate_dma_kernel<TO, DK, DV, DVT, false>, grid, dim3((DVT / 16 + 2) * 64), s, p);
+        return launch(kda_propagate_dma_kernel<TO, DK, DV, DVT, true>, grid, dim3((DVT / 16 + 1) * 64), s, p);
+    } else {
+        return launch(kda_propagate_kernel<TIn, TO, DK, DV, DVT>, grid, dim3(DVT / 16 * 64), s, p);
     }
 }
 
 template <typename TIn, typename TO>
-static void kda_dispatch(const ChunkProblem& p, hipStream_t s) {
-    if (p.dk == 64) {
-        if (p.dv == 64) kda_launch<TIn, TO, 64, 64>(p, s); else kda_launch<TIn, TO, 64, 128>(p, s);
-    } else {
-        if (p.dv == 64) kda_launch<TIn, TO, 128, 64>(p, s); else kda_launch<TIn, TO, 128, 128>(p, s);
-    }
+static hipError_t kda_dispatch(const ChunkProblem& p, hipStream_t s) {
+    if (p.dk == 64)
+        return p.dv == 64 ? kda_launch<TIn, TO, 64, 64>(p, s) : kda_launch<TIn, TO, 64, 128>(p, s);
+    return p.dv == 64 ? kda_launch<TIn, TO, 128, 64>(p, s) : kda_launch<TIn, TO, 128, 128>(p, s);
 }
 
 hipError_t launch_kda_chunk_fwd(const ChunkProblem& p, hipStream_t s) {
-    launch_chunk_base(p, s);
-    if (!p.bf16) kda_dispatch<float, float>(p, s);
-    else if (p.o_bf16) kda_dispatch<uint16_t, uint16_t>(p, s);
-    else kda_dispatch<uint16_t, float>(p, s);
-    return hipGetLastError();
+    hipError_t e = launch_chunk_base(p, s);
+    if (e != hipSuccess) return e;
+    if (!p.bf16) return kda_dispatch<float, float>(p, s);
+    return p.o_bf16 ? kda_dispatch<uint16_t, uint16_t>(p, s) : kda_dispatch<uint16_t, float>(p, s);
 }
 
 }  // namespace gdn

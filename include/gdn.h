@@ -16,8 +16,9 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers allocated and owned by the caller. The
- *    library allocates nothing, keeps no pointer after a call returns and holds no
- *    global state; calls on distinct streams may run concurrently.
+ *    library allocates nothing and keeps no pointer after a call returns. Its only state is
+ *    a per-device cache of occupancy figures (filled on first use, safely under concurrent
+ *    first calls); calls on distinct streams may run concurrently.
  *  - Layouts are dense, row-major, with the feature dimension innermost:
  *      q, k [B, T, H, d_k]     v, o [B, T, H, d_v]     g, beta [B, T, H]
  *      states (h0, hT, decode state) [N, H, d_v, d_k] fp32 (d_k contiguous)
@@ -33,8 +34,12 @@
  *    checked on the device. There is no query scale (o_t = S_t q_t exactly).
  *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and the call
  *    returns at once. The return code reports host-side argument checks, which all run
- *    before any HIP call, and launch errors; faults during execution surface at the
- *    caller's next synchronisation.
+ *    before any HIP call, and the status of the call's own kernel launches (an error left
+ *    pending by an earlier, unrelated HIP call is neither reported nor cleared); faults
+ *    during execution surface at the caller's next synchronisation.
+ *  - GDN_CHECK=1 in the environment (a debugging aid): every entry point that takes
+ *    cu_seqlens first copies it to the host, which synchronises `stream`, and returns
+ *    GDN_ERR_SHAPE unless 0 = cu[0] <= cu[1] <= ... <= cu[N] = T.
  *  - Alignment: q, k, v, o, h0, hT and the decode state 16 bytes; g, beta and cu_seqlens
  *    4 bytes; the workspace 256 bytes. A misaligned pointer gives GDN_ERR_ALIGN.
  */

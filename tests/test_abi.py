@@ -170,3 +170,91 @@ def test_binding_refuses_cpu_tensors(L):
         gb.gdn_chunk_fwd(x, x, x, g, g)
     with pytest.raises(ValueError):
         gb.gdn_decode_step(x[0], x[0], x[0], g[0], g[0], torch.zeros(1, 64, 2, 64, 64))
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The C ABI sees raw pointers only, so the binding checks shapes and dtypes before any call:
+# a mismatched tensor would otherwise be read or written out of bounds on the device. These
+# run on CPU tensors; the shape and dtype checks come before the device check.
+def _fwd_inputs(B=1, T=8, H=2, dk=64, dv=64, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    q = torch.zeros(B, T, H, dk, dtype=dtype)
+    return dict(q=q, k=q.clone(), v=torch.zeros(B, T, H, dv, dtype=dtype),
+                g=torch.zeros(B, T, H), beta=torch.zeros(B, T, H))
+
+
+@pytest.mark.parametrize("bad", ["k_dtype", "k_shape", "v_dtype", "v_rows", "g_dtype", "g_shape",
+                                 "beta_shape", "h0_shape", "h0_dtype", "hT_shape", "o_shape",
+                                 "cu_int64", "cu_2d"])
+def test_binding_rejects_mismatched_forward_arguments(bad):
+    import torch
+    x = _fwd_inputs()
+    kw = {}
+    if bad == "k_dtype":
+        x["k"] = x["k"].float()
+    elif bad == "k_shape":
+        x["k"] = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
+    elif bad == "v_dtype":
+        x["v"] = x["v"].float()
+    elif bad == "v_rows":
+        x["v"] = torch.zeros(1, 7, 2, 64, dtype=torch.bfloat16)
+    elif bad == "g_dtype":
+        x["g"] = x["g"].double()
+    elif bad == "g_shape":
+        x["g"] = torch.zeros(1, 8, 3)
+    elif bad == "beta_shape":
+        x["beta"] = torch.zeros(8, 2)
+    elif bad == "h0_shape":
+        kw["h0"] = torch.zeros(1, 2, 64, 32)
+    elif bad == "h0_dtype":
+        kw["h0"] = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    elif bad == "hT_shape":
+        kw["hT"] = torch.zeros(2, 2, 64, 64)
+    elif bad == "o_shape":
+        kw["o"] = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
+    elif bad == "cu_int64":
+        kw["cu_seqlens"] = torch.tensor([0, 8], dtype=torch.int64)
+    elif bad == "cu_2d":
+        kw["cu_seqlens"] = torch.tensor([[0, 8]], dtype=torch.int32)
+    with pytest.raises(ValueError, match="gdn: "):
+        gb.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], **kw)
+
+
+def test_binding_rejects_cpu_tensors_after_shape_checks():
+    x = _fwd_inputs()
+    with pytest.raises(ValueError, match="on a GPU"):
+        gb.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"])
+
+
+@pytest.mark.parametrize("bad", ["state_bf16", "state_shape", "g_shape", "o_shape", "v_dtype"])
+def test_binding_rejects_mismatched_decode_arguments(bad):
+    import torch
+    N, H, d = 2, 2, 64
+    q = torch.zeros(N, H, d, dtype=torch.bfloat16)
+    a = dict(q=q, k=q.clone(), v=q.clone(), g=torch.zeros(N, H), beta=torch.zeros(N, H),
+             state=torch.zeros(N, H, d, d), o=None)
+    if bad == "state_bf16":
+        a["state"] = a["state"].bfloat16()
+    elif bad == "state_shape":
+        a["state"] = torch.zeros(N, H, d, 32)
+    elif bad == "g_shape":
+        a["g"] = torch.zeros(N, H, d)
+    elif bad == "o_shape":
+        a["o"] = torch.zeros(N, H, 32)
+    elif bad == "v_dtype":
+        a["v"] = a["v"].float()
+    with pytest.raises(ValueError, match="gdn: "):
+        gb.gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"])
+
+
+def test_binding_rejects_mismatched_backward_and_channel_gate_arguments():
+    import torch
+    x = _fwd_inputs()
+    with pytest.raises(ValueError, match="do has"):
+        gb.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["v"].float())
+    with pytest.raises(ValueError, match="g has shape"):   # channel-wise decay needs [B,T,H,dk]
+        gb.gdn_kda_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    gc = torch.zeros(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="write has shape"):
+        gb.gdn_decoupled_chunk_fwd(x["q"], x["k"], x["v"], gc, gc, torch.zeros(1, 8, 2, 32))

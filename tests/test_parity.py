@@ -150,7 +150,8 @@ def test_fwd_empty_sequence_axis():
     assert o.shape == (2, 0, 2, 128) and np.array_equal(hT, x["h0"].double().numpy())
 
 
-@pytest.mark.parametrize("wid,kw", [(1, dict(T=300, B=2, H=3)), (3, dict(lengths=[100, 1, 64, 250], H=2))])
+@pytest.mark.parametrize("wid,kw", [(1, dict(T=300, B=2, H=3)), (3, dict(lengths=[100, 1, 64, 250], H=2)),
+                                    (1, dict()), (2, dict())])
 def test_bf16_output_is_rounded_fp32_output(wid, kw):
     """The bf16-output kernels compute the same fp32 values as the fp32-output kernels and
     round them to nearest even: bit-for-bit equal to torch's rounding of the fp32 output."""
@@ -164,6 +165,23 @@ def test_bf16_output_is_rounded_fp32_output(wid, kw):
     torch.cuda.synchronize()
     assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(h16, h32)
+
+
+@pytest.mark.parametrize("bad", [[0, 5, 3, 8], [1, 4, 8], [0, 4, 7]])
+def test_debug_check_rejects_bad_offsets(monkeypatch, bad):
+    """GDN_CHECK=1: the chunked entry points copy cu_seqlens to the host and reject offsets that
+    are not 0 = cu[0] <= ... <= cu[N] = T; well-formed offsets pass unchanged."""
+    x = SY.make_forward_inputs(3, lengths=[5, 3], H=2)
+    dev = "cuda"
+    t = [x[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    monkeypatch.setenv("GDN_CHECK", "1")
+    o, h = gb.gdn_chunk_fwd(*t, cu_seqlens=x["cu_seqlens"].to(dev))
+    with pytest.raises(gb.GDNError, match="out of range or inconsistent"):
+        gb.gdn_chunk_fwd(*t, cu_seqlens=torch.tensor(bad, dtype=torch.int32, device=dev))
+    monkeypatch.delenv("GDN_CHECK")
+    o2, h2 = gb.gdn_chunk_fwd(*t, cu_seqlens=x["cu_seqlens"].to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(h, h2)
 
 
 def test_h0_none_equals_explicit_zeros():
@@ -335,12 +353,16 @@ def test_decode_beta_to_2(dtype):
     check_decode(SY.make_decode_inputs(w, seed=14, beta_scale=2.0))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_bf16_output_is_rounded_fp32_output(dtype):
-    """o written as bf16 is bit-for-bit the fp32 o rounded to nearest even (torch's rule)."""
-    w = SY.Workload(93, "decode_odtype", H=4, dk=128, dv=128, dtype=dtype, decode_seqs=7,
-                    decode_steps=1)
-    d = SY.make_decode_inputs(w, seed=13)
+@pytest.mark.parametrize("dtype,full", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_decode_bf16_output_is_rounded_fp32_output(dtype, full):
+    """o written as bf16 is bit-for-bit the fp32 o rounded to nearest even (torch's rule); also
+    at the full decode workload's size (256 sequences x H32), the launch the benchmark times."""
+    if full:
+        d = SY.make_decode_inputs(4, steps=1)
+    else:
+        w = SY.Workload(93, "decode_odtype", H=4, dk=128, dv=128, dtype=dtype, decode_seqs=7,
+                        decode_steps=1)
+        d = SY.make_decode_inputs(w, seed=13)
     dev = "cuda"
     tok = [d[n][0].to(dev) for n in ("q", "k", "v", "g", "beta")]
     s1, s2 = d["state"].to(dev), d["state"].to(dev)
