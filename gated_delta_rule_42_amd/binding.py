@@ -25,6 +25,7 @@ _SIGNATURES = [
     ("gdn_status_string", ctypes.c_char_p, [_I]),
     ("gdn_chunk_fwd_workspace_bytes", _SZ, [_I] * 9),
     ("gdn_chunk_fwd", _I, [_P] * 9 + [_I] * 9 + [_P, _SZ, _P]),
+    ("gdn_chunk_fwd_noalloc", _I, [_P] * 9 + [_I] * 9 + [_P]),
     ("gdn_chunk_prepare", _I, [_P] * 5 + [_I] * 8 + [_P, _SZ, _P]),
     ("gdn_chunk_propagate", _I, [_P] * 7 + [_I] * 9 + [_P, _SZ, _P]),
     ("gdn_decode_step", _I, [_P] * 7 + [_I] * 6 + [_P]),
@@ -176,6 +177,24 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=
                              workspace.numel() if workspace is not None else 0,
                              _stream(q.device, stream))
     _check(st, "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0=None, cu_seqlens=None, chunk=CHUNK, *, o=None, hT=None,
+                          o_dtype=None, output_final_state=True, stream=None):
+    """gdn_chunk_fwd on the library's own device scratch array (no workspace argument, no
+    allocation inside the call; outputs are allocated here unless given)."""
+    B, T, H, dk, dv, N = _check_chunk_args(q, k, v, g, beta, h0, cu_seqlens, o, hT)
+    _need_gpu(q, k, v, g, beta, h0, cu_seqlens, o, hT)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    st = lib().gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                     _ptr(hT), _ptr(cu_seqlens), chunk, B, T, H, dk, dv, N,
+                                     _DTYPE.get(q.dtype, -1), _DTYPE.get(o.dtype, -1),
+                                     _stream(q.device, stream))
+    _check(st, "gdn_chunk_fwd_noalloc")
     return o, hT
 
 

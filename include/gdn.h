@@ -18,7 +18,8 @@
  *  - All tensor pointers are DEVICE pointers allocated and owned by the caller. The
  *    library allocates nothing and keeps no pointer after a call returns. Its only state is
  *    a per-device cache of occupancy figures (filled on first use, safely under concurrent
- *    first calls); calls on distinct streams may run concurrently.
+ *    first calls) and the device scratch array of gdn_chunk_fwd_noalloc; calls on distinct
+ *    streams may run concurrently (except overlapping gdn_chunk_fwd_noalloc calls on one GPU).
  *  - Layouts are dense, row-major, with the feature dimension innermost:
  *      q, k [B, T, H, d_k]     v, o [B, T, H, d_v]     g, beta [B, T, H]
  *      states (h0, hT, decode state) [N, H, d_v, d_k] fp32 (d_k contiguous)
@@ -133,6 +134,24 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g_lo
                   const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
                   int N, int dtype, int o_dtype, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, arguments and
+ * checks as gdn_chunk_fwd without the workspace arguments. Its kernels use, as their workspace,
+ * a device array inside the library of GDN_NOALLOC_SCRATCH_BYTES bytes, of which every GPU the
+ * library runs on holds its own copy until the process ends. The call allocates nothing.
+ * A problem whose gdn_chunk_fwd_workspace_bytes(...) exceeds GDN_NOALLOC_SCRATCH_BYTES returns
+ * GDN_ERR_WORKSPACE. Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels write every workspace byte they read, so nothing needs clearing):
+ * calls that overlap in time on one GPU (different streams, or different host threads) race
+ * and must not be issued.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g_log_alpha,
+                          const float *beta, const float *h0, void *o, float *hT,
+                          const int32_t *cu_seqlens, int chunk, int B, int T, int H, int dk, int dv,
+                          int N, int dtype, int o_dtype, void *stream);
 
 /*
  * Stage 1 of gdn_chunk_fwd, independent across chunks (no state dependency): per

@@ -1,0 +1,48 @@
+"""gdn_chunk_fwd_noalloc (the forward pass on the library's own device scratch array) against
+gdn_chunk_fwd on the same inputs, through the C ABI: two calls in a row, the second with a
+smaller input (so it also runs on whatever the first call left in the shared array). The two
+entry points run the same kernels, so their outputs must be bitwise equal."""
+import pytest
+import torch
+
+from gated_delta_rule_42_amd import binding as gb
+from gated_delta_rule_42_amd import synthetic as SY
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, fn):
+    dev = "cuda"
+    t = [x[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    h0 = None if x["h0"] is None else x["h0"].to(dev)
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].to(dev)
+    o, hT = fn(*t, h0, cu)
+    torch.cuda.synchronize()
+    return o, hT
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noalloc_matches_workspace_entry_point(dtype):
+    big = SY.make_forward_inputs(SY.Workload(80, "noalloc_big", H=4, dk=128, dv=128, dtype=dtype, B=2, T=700),
+                                 seed=41, gate_scale=0.05, h0=True)
+    small = SY.make_forward_inputs(SY.Workload(80, "noalloc_small", H=2, dk=128, dv=128, dtype=dtype),
+                                   seed=42, lengths=[130, 1, 64], gate_scale=0.05, h0=True)
+    for x in (big, small):
+        print(f"[gpu] noalloc {x['meta']}", flush=True)
+        o_ref, h_ref = _run(x, gb.gdn_chunk_fwd)
+        o, h = _run(x, gb.gdn_chunk_fwd_noalloc)
+        assert torch.equal(o, o_ref) and torch.equal(h, h_ref)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """A problem whose workspace exceeds the array is refused with GDN_ERR_WORKSPACE before any
+    work is enqueued (the call does not fall back to allocating)."""
+    B, T, H, d = 1, 1 << 20, 64, 128
+    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False, dtype=torch.bfloat16)
+    if need <= (64 << 20):
+        pytest.skip("this problem fits the scratch array")
+    dev = "cuda"
+    q = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
+    g = torch.empty(B, T, H, device=dev)
+    with pytest.raises(gb.GDNError, match="workspace"):
+        gb.gdn_chunk_fwd_noalloc(q, q, q, g, g)
