@@ -37,12 +37,13 @@ def test_noalloc_matches_workspace_entry_point(dtype):
 def test_noalloc_rejects_problems_beyond_its_scratch():
     """A problem whose workspace exceeds the array is refused with GDN_ERR_WORKSPACE before any
     work is enqueued (the call does not fall back to allocating)."""
-    B, T, H, d = 1, 1 << 20, 64, 128
-    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False, dtype=torch.bfloat16)
-    if need <= (64 << 20):
-        pytest.skip("this problem fits the scratch array")
+    # fp32 inputs run the two stages, whose workspace holds fp32 chunk operators (about 33 KB
+    # per chunk and head): 64 chunks x 32 heads need more than the 64 MiB array
+    B, T, H, d = 1, 4096, 32, 128
+    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False, dtype=torch.float32)
+    assert need > (64 << 20)
     dev = "cuda"
-    q = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
-    g = torch.empty(B, T, H, device=dev)
+    q = torch.zeros(B, T, H, d, dtype=torch.float32, device=dev)
+    g = torch.zeros(B, T, H, device=dev)
     with pytest.raises(gb.GDNError, match="workspace"):
         gb.gdn_chunk_fwd_noalloc(q, q, q, g, g)
