@@ -16,6 +16,21 @@ namespace {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
+// The forward workspace: the stage-1 regions, then the state records of the long-chain split
+struct FwdLayout {
+    gdn::WorkspaceLayout w;
+    gdn::SegPlan seg;
+    size_t off_seg, total;
+};
+FwdLayout fwd_layout(int B, int T, int H, int dk, int dv, int N, int varlen, int bf16) {
+    FwdLayout f;
+    f.w = gdn::workspace_layout(B, T, H, dk, N, varlen, bf16 ? 2 : 4);
+    f.seg = gdn::segment_plan(T, H, dk, dv, N, bf16);
+    f.off_seg = (f.w.total + 255) & ~(size_t)255;
+    f.total = f.seg.n > 1 ? f.off_seg + f.seg.bytes : f.w.total;
+    return f;
+}
+
 // GDN_CHECK=1 in the environment: copy cu_seqlens to the host (this synchronises `stream`) and
 // reject offsets that break 0 = cu[0] <= cu[1] <= ... <= cu[N] = T. A debugging aid: without it
 // the offsets are a precondition that the kernels only clamp into [0, T].
@@ -63,10 +78,10 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     const void* al4[] = {g, beta, cu};
     for (const void* x : al4)
         if (x && !aligned(x, 4)) return GDN_ERR_ALIGN;
-    const int elem = dtype == GDN_BF16 ? 2 : 4;
-    const gdn::WorkspaceLayout w = gdn::workspace_layout(B, T, H, dk, N, cu != nullptr, elem);
+    const FwdLayout f = fwd_layout(B, T, H, dk, dv, N, cu != nullptr, dtype == GDN_BF16);
+    const gdn::WorkspaceLayout& w = f.w;
     if (w.nc_bound * H > 0x7fffffffL) return GDN_ERR_SHAPE;
-    if (w.total > 0 && (!ws || ws_bytes < w.total)) return GDN_ERR_WORKSPACE;
+    if (f.total > 0 && (!ws || ws_bytes < f.total)) return GDN_ERR_WORKSPACE;
     if (ws && !aligned(ws, 256)) return GDN_ERR_ALIGN;
 
     gdn::ChunkProblem& P = *p;
@@ -84,6 +99,10 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     P.pmat = w.nc_bound ? base + w.off_p : nullptr;
     P.k16 = (w.nc_bound && P.bf16) ? reinterpret_cast<_Float16*>(base + w.off_k16) : nullptr;
     P.q16 = (w.nc_bound && P.bf16) ? reinterpret_cast<_Float16*>(base + w.off_q16) : nullptr;
+    P.seg_n = f.seg.n;
+    P.seg_len = f.seg.len;
+    P.seg_ncp = f.seg.ncp;
+    P.segst = f.seg.n > 1 ? reinterpret_cast<float*>(base + f.off_seg) : nullptr;
     return GDN_OK;
 }
 
@@ -111,7 +130,7 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
     if (B < 1 || H < 1 || T < 0) return 0;
     if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
-    return gdn::workspace_layout(B, T, H, dk, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
+    return fwd_layout(B, T, H, dk, dv, N, varlen != 0, dtype == GDN_BF16).total;
 }
 
 GDN_EXPORT int gdn_chunk_prepare(const void* q, const void* k, const float* g, const float* beta,

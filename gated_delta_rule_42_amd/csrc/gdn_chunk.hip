@@ -19,6 +19,9 @@
 // e^gamma and e^{gamma_last - gamma}, Mmat and P. Stage 2 (chunk_propagate_kernel) walks the
 // chunks of one (sequence, head, d_v tile) in order with the fp32 state in registers and
 // writes O. Every gate factor is exp of a non-positive difference, masked before the exp.
+#include <algorithm>
+#include <cstdlib>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_stage2.h"
@@ -655,14 +658,29 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 // S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it reads and writes LDS and runs the matrix and
 // vector units, and writes global memory only for the backward pass's state recompute (the
 // state entering each chunk in fp16, p.states16; there p.o is NULL and the store wave writes
-// nothing).
+// nothing) and for the long-chain split below.
 // While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
 // chunk c+2 into ring buffers (2 and 3 deep: memory latency is about one chunk's
 // compute time), and before the next barrier waits for exactly the copies chunk c+1 needs; the
 // store wave writes chunk c-1's outputs from the LDS staging buffer and never waits for its
 // stores. One barrier per chunk.
 // The products are those of the generic stage-2 kernel (chunk_propagate_kernel).
-template <typename TO, int DK, int DV, int DVT>
+//
+// Long chains (few sequence-head pairs, many chunks) leave most of the device idle, so SEG
+// cuts each sequence's chunks into p.seg_n segments of p.seg_len chunks:
+//   SEG = 1: one work-group per (pair, tile, segment); segment 0 starts from h0, the others
+//     from a zero state. Each records its state at segment offsets 1, 2, 4, .. and its final
+//     state in p.segst, and writes o for all its chunks.
+//   SEG = 2: one work-group per (pair, tile) walks segments 1, 2, .. in order from the true
+//     state entering each. After the chunk that ends at a recorded offset it compares its
+//     state with the one SEG = 1 recorded there, bit for bit; once they are equal, every later
+//     chunk of the segment computed in SEG = 1 saw exactly the state this walk would give it
+//     (the chunk step is a fixed function of its inputs), so the walk rewrites o only up to
+//     that point and takes the segment's final state from p.segst. Without a match it runs to
+//     the segment's end. Both ways o and hT equal those of the unsplit kernel bit for bit; the
+//     saving comes from decay: a segment's dependence on its entering state shrinks by the
+//     product of its gates, and once that falls under fp32 rounding the two states agree.
+template <typename TO, int DK, int DV, int DVT, int SEG>
 __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
     using KQ = KQChunk<DK>;
     using MPV = MPVChunk<DK, DVT>;
@@ -674,26 +692,30 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     __shared__ KQ kq[2];
     __shared__ MPV mpv[3];
     __shared__ OS ost[2];
+    __shared__ int match[2][NW];   // SEG = 2: per compute wave, state equal to the record (by chunk parity)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
 
-    // (sequence, head) pair and column tile; with a pair count divisible by 8 the tiles of one
-    // pair get block ids equal modulo 8 (same XCD, shared L2 for K, Q, Mmat and P)
+    // work unit (pair, or pair and segment) and column tile; with a unit count divisible by 8
+    // the tiles of one unit get block ids equal modulo 8 (same XCD, shared L2 for K, Q, Mmat and P)
     const long NP = (long)p.N * H;
+    const long NU = SEG == 1 ? NP * p.seg_n : NP;
     const long bid = blockIdx.x;
-    long pair;
+    long unit;
     int tile;
-    if (NP % 8 == 0) {
+    if (NU % 8 == 0) {
         const long x = bid % 8, i = bid / 8;
         tile = (int)(i % NTILE);
-        pair = (i / NTILE) * 8 + x;
+        unit = (i / NTILE) * 8 + x;
     } else {
-        pair = bid / NTILE;
+        unit = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
+    const long pair = SEG == 1 ? unit / p.seg_n : unit;
+    const int seg = SEG == 1 ? (int)(unit % p.seg_n) : 0;
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int dv0 = tile * DVT;
 
@@ -706,28 +728,71 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         const long l = seos - (sbos + jc * kChunk);
         return (int)(l < kChunk ? l : kChunk);
     };
+    // chunk range [c0, c0 + len) of segment g
+    auto seg_range = [&](int g, long& c0, long& len) {
+        c0 = (long)g * p.seg_len;
+        len = max(0L, min((long)p.seg_len, nchunks - c0));
+    };
+    long c_first = 0, c_count = nchunks;   // SEG 0, 1: the work-group's one range
+    if constexpr (SEG == 1) {
+        seg_range(seg, c_first, c_count);
+        if (seg > 0 && c_count == 0) return;   // the whole work-group leaves
+    }
+    // p.segst slot of (segment g, recorded offset or final state) for this pair
+    const int nslot = p.seg_ncp + 1;
+    auto seg_state = [&](int g, int slot) { return p.segst + ((pair * p.seg_n + g) * nslot + slot) * (long)DV * DK; };
+    // a range ends at the barrier after its last chunk, or (SEG = 2) at the barrier after a chunk
+    // whose end state matched the record; all waves read the same flags after the same barrier
+    auto range_done = [&](int i, long len) {
+        if (i == len) return true;
+        if constexpr (SEG == 2) {
+            if (i > 0) {
+                bool all = true;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) all = all && match[(i - 1) & 1][w] != 0;
+                return all;
+            }
+        }
+        return false;
+    };
+    // offset o (1 <= o < len) has a record when it is a power of two
+    auto recorded = [](int o, long len) { return o < len && (o & (o - 1)) == 0; };
 
     if (wave == NW) {
         // ------------------------------------------------------------------- DMA wave
         // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2). Loads complete
         // in issue order, so at the top of chunk c only MPV(c+1) may still be in flight.
-        auto mpv_copy = [&](long jc) {
-            copy_mpv<DK, DV, DVT>(mpv[jc % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
-                              dv0, lane);
+        auto run = [&](long c0, long len) {
+            auto mpv_copy = [&](int i) {
+                const long jc = c0 + i;
+                copy_mpv<DK, DV, DVT>(mpv[i % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
+                                      dv0, lane);
+            };
+            if (len > 0) {
+                copy_kq<DK>(kq[0], p, (cbase + c0) * H + h, lane);
+                mpv_copy(0);
+            }
+            if (len > 1) mpv_copy(1);
+            for (int i = 0;; ++i) {
+                if (i + 1 < len) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                lds_barrier();  // chunk i's operands are in LDS; chunk i-1's buffers are free
+                if (range_done(i, len)) break;
+                if (i + 1 < len) copy_kq<DK>(kq[(i + 1) & 1], p, (cbase + c0 + i + 1) * H + h, lane);
+                if (i + 2 < len) mpv_copy(i + 2);
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // copies of an abandoned chunk
         };
-        if (nchunks > 0) {
-            copy_kq<DK>(kq[0], p, cbase * H + h, lane);
-            mpv_copy(0);
+        if constexpr (SEG == 2) {
+            for (int g = 1; g < p.seg_n; ++g) {
+                long c0, len;
+                seg_range(g, c0, len);
+                if (len == 0) break;
+                run(c0, len);
+            }
+        } else {
+            run(c_first, c_count);
         }
-        if (nchunks > 1) mpv_copy(1);
-        for (long jc = 0; jc < nchunks; ++jc) {
-            if (jc + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            lds_barrier();  // chunk jc's operands are in LDS; chunk jc-1's buffers are free
-            if (jc + 1 < nchunks) copy_kq<DK>(kq[(jc + 1) & 1], p, (cbase + jc + 1) * H + h, lane);
-            if (jc + 2 < nchunks) mpv_copy(jc + 2);
-        }
-        lds_barrier();
         return;
     }
     if (wave == NW + 1) {
@@ -751,35 +816,56 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
                 __builtin_amdgcn_raw_buffer_store_b128(v, orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
             }
         };
-        for (long jc = 0; jc < nchunks; ++jc) {
-            lds_barrier();
-            if (jc > 0 && p.o) store_out(ost[(jc - 1) & 1], jc - 1);
+        auto run = [&](long c0, long len) {
+            for (int i = 0;; ++i) {
+                lds_barrier();  // chunk i-1's outputs are staged
+                if (i > 0 && p.o) store_out(ost[(i - 1) & 1], c0 + i - 1);
+                if (range_done(i, len)) break;
+            }
+        };
+        if constexpr (SEG == 2) {
+            for (int g = 1; g < p.seg_n; ++g) {
+                long c0, len;
+                seg_range(g, c0, len);
+                if (len == 0) break;
+                run(c0, len);
+            }
+        } else {
+            run(c_first, c_count);
         }
-        lds_barrier();  // the last chunk's outputs are staged
-        if (nchunks > 0 && p.o) store_out(ost[(nchunks - 1) & 1], nchunks - 1);
         return;
     }
 
     // ------------------------------------------------------------------- compute waves
     const int dvw = dv0 + 16 * wave;
     f32x4_t ST[NKB];
-    const long srow = (pair * DV + dvw + l16) * DK + 4 * lq;
+    const long scol = (dvw + l16) * DK + 4 * lq;   // this lane's offset in a [dv, dk] state
+    auto load_state = [&](const float* src) {
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        if (p.h0) {
-            const float4 x = *reinterpret_cast<const float4*>(p.h0 + srow + 16 * j);
+        for (int j = 0; j < NKB; ++j) {
+            const float4 x = *reinterpret_cast<const float4*>(src + scol + 16 * j);
             ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
-        } else {
-            ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+    };
+    auto store_state = [&](float* dst) {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+            *reinterpret_cast<float4*>(dst + scol + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    };
+    if (SEG == 2) {
+        load_state(seg_state(0, p.seg_ncp));
+    } else if (p.h0 && seg == 0) {
+        load_state(p.h0 + pair * DV * DK);
+    } else {
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     // LDS operands are read ahead of the products that use them (the X/Y fragments one
     // 32-wide slice ahead, Mmat and the residual terms in the last slice, P during the
     // residual, K^T during the output product), and each product phase cycles over
     // independent accumulators; the scheduling fences keep that order.
-    auto step = [&](const KQ& ck, const MPV& cm, OS& os) {
-        lds_barrier();  // chunk data in ck, cm; os free
+    auto step = [&](const KQ& ck, const MPV& cm, OS& os) {  // after the chunk's barrier
         uint4 MF[4][2], PF[4][2];
         float4 V4[4], EG4[4];
         auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
@@ -900,22 +986,64 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
             for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
     };
 
-    for (long jc = 0, m3 = 0; jc < nchunks; ++jc, m3 = (m3 == 2 ? 0 : m3 + 1)) {
-        if (p.states16) {   // the state entering the chunk, in the fp16 its products take later
-            _Float16* sp = p.states16 + (((cbase + jc) * H + h) * DV + dvw + l16) * DK + 4 * lq;
+    // runs chunks c0 .. of the range and returns how many it computed (fewer than len: it
+    // stopped at a matching record, SEG = 2)
+    auto run = [&](long c0, long len, int g) {
+        for (int i = 0;; ++i) {
+            lds_barrier();  // chunk i's operands are in LDS; chunk i's staging buffer is free
+            if (range_done(i, len)) return i;
+            if constexpr (SEG == 0) {
+                if (p.states16) {   // the state entering the chunk, in the fp16 its products take later
+                    _Float16* sp = p.states16 + (((cbase + c0 + i) * H + h) * DV + dvw + l16) * DK + 4 * lq;
 #pragma unroll
-            for (int j = 0; j < NKB; ++j)
-                *reinterpret_cast<uint2*>(sp + 16 * j) =
-                    make_uint2(pack_f16x2(ST[j][0], ST[j][1]), pack_f16x2(ST[j][2], ST[j][3]));
+                    for (int j = 0; j < NKB; ++j)
+                        *reinterpret_cast<uint2*>(sp + 16 * j) =
+                            make_uint2(pack_f16x2(ST[j][0], ST[j][1]), pack_f16x2(ST[j][2], ST[j][3]));
+                }
+            }
+            step(kq[i & 1], mpv[i % 3], ost[i & 1]);
+            const int off = i + 1;
+            if constexpr (SEG == 1) {
+                if (recorded(off, len)) store_state(seg_state(g, 31 - __builtin_clz(off)));
+            }
+            if constexpr (SEG == 2) {
+                bool same = false;
+                if (recorded(off, len)) {
+                    const float* rec = seg_state(g, 31 - __builtin_clz(off));
+                    unsigned diff = 0;
+#pragma unroll
+                    for (int j = 0; j < NKB; ++j) {
+                        const uint4 r = *reinterpret_cast<const uint4*>(rec + scol + 16 * j);
+                        diff |= (r.x ^ __float_as_uint(ST[j][0])) | (r.y ^ __float_as_uint(ST[j][1])) |
+                                (r.z ^ __float_as_uint(ST[j][2])) | (r.w ^ __float_as_uint(ST[j][3]));
+                    }
+                    same = __builtin_amdgcn_ballot_w64(diff != 0) == 0;
+                }
+                if (lane == 0) match[i & 1][wave] = same ? 1 : 0;
+            }
         }
-        step(kq[jc & 1], mpv[m3], ost[jc & 1]);
-    }
-    lds_barrier();  // hand the last chunk's outputs to the store wave
+    };
 
-    if (p.hT) {
-#pragma unroll
-        for (int j = 0; j < NKB; ++j)
-            *reinterpret_cast<float4*>(p.hT + srow + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    if constexpr (SEG == 2) {
+        // after the state records: per (pair, tile, segment) the number of chunks this walk
+        // computed, an int32 diagnostic
+        int* reran = reinterpret_cast<int*>(p.segst + NP * p.seg_n * nslot * (long)DV * DK) +
+                     (pair * NTILE + tile) * p.seg_n;
+        for (int g = 1; g < p.seg_n; ++g) {
+            long c0, len;
+            seg_range(g, c0, len);
+            if (len == 0) break;
+            const int m = run(c0, len, g);
+            if (m < len) load_state(seg_state(g, p.seg_ncp));
+            if (wave == 0 && lane == 0) reran[g] = m;
+        }
+    } else {
+        run(c_first, c_count, seg);
+    }
+    if constexpr (SEG == 1) {
+        store_state(seg_state(seg, p.seg_ncp));
+    } else if (p.hT) {
+        store_state(p.hT + pair * DV * DK);
     }
 }
 
@@ -939,6 +1067,34 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
     }
     if (w.nc_bound == 0) w.total = al(base_bytes);
     return w;
+}
+
+// Work-groups the device runs at once for the bf16 state propagation (one per CU: its LDS use
+// admits no second) on a 256-CU gfx950 part, and the shortest segment worth splitting off.
+constexpr int kSegTargetGroups = 256;
+constexpr int kSegMinChunks = 16;
+
+SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16) {
+    SegPlan sp{1, 0, 0, 0};
+    const long nmax = ((long)T + kChunk - 1) / kChunk;   // chunks of the longest possible sequence
+    if (!bf16 || nmax < 2) return sp;
+    long len = 0;
+    if (const char* env = std::getenv("GDN_SEGMENT_CHUNKS")) {
+        len = std::atol(env);
+        if (len <= 0) return sp;
+    } else {
+        const long groups = (long)N * H * (dv / 32);
+        const long g = std::min((long)kSegTargetGroups / groups, nmax / kSegMinChunks);
+        if (g < 2) return sp;
+        len = (nmax + g - 1) / g;
+    }
+    const long n = (nmax + len - 1) / len;
+    if (n < 2 || (long)N * H * (dv / 32) * n > 0x7fffffffL) return sp;   // grid size
+    sp.n = (int)n;
+    sp.len = (int)len;
+    while ((1L << sp.ncp) < len) ++sp.ncp;   // offsets 1, 2, 4, .. below len
+    sp.bytes = (size_t)N * H * n * ((sp.ncp + 1) * dv * dk * sizeof(float) + (dv / 32) * sizeof(int32_t));
+    return sp;
 }
 
 template <typename TIn, int DK, bool BWD>
@@ -976,12 +1132,16 @@ template <typename TIn, typename TO, int DK, int DV>
 static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
     constexpr int DVT = 32;
     const long blocks = (long)p.N * p.H * (DV / DVT);
-    if constexpr (sizeof(TIn) == 2)   // two compute waves (32 columns), a DMA wave and a store wave
-        return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT>, dim3((unsigned)blocks),
-                      dim3((DVT / 16 + 2) * 64), s, p);
-    else                              // two waves of 16 columns (LDS size)
+    if constexpr (sizeof(TIn) == 2) {   // two compute waves (32 columns), a DMA wave and a store wave
+        const dim3 block((DVT / 16 + 2) * 64);
+        if (p.seg_n <= 1) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0>, dim3((unsigned)blocks), block, s, p);
+        const hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>,
+                                    dim3((unsigned)(blocks * p.seg_n)), block, s, p);
+        return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 2>, dim3((unsigned)blocks), block, s, p);
+    } else {                            // two waves of 16 columns (LDS size)
         return launch(chunk_propagate_kernel<TIn, TO, DK, DV, DVT>, dim3((unsigned)blocks),
                       dim3(DVT / 16 * 64), s, p);
+    }
 }
 
 template <typename TIn, typename TO>
@@ -996,6 +1156,7 @@ static hipError_t prop_dispatch(const ChunkProblem& p, hipStream_t s) {
 // chunk in fp16 (p.states16) and writing no output.
 hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s) {
     ChunkProblem q = p;
+    q.seg_n = 1;   // the states of every chunk are wanted: no split
     q.mmat = p.mimg16;
     q.pmat = p.pimg16;
     q.o = nullptr;

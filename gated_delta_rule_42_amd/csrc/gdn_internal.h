@@ -80,6 +80,13 @@ struct ChunkProblem {
     // decoupled gates (replace beta when set): erase [B,T,H,dk], write [B,T,H,dv]
     const float* erase;
     const float* write;
+    // long-chain split of the bf16 state propagation (seg_n > 1): the chunks of a sequence are
+    // cut into segments of seg_len chunks; segst holds, per (sequence, head) and segment, the
+    // states at segment offsets 1, 2, 4, .. < seg_len (seg_ncp of them) and the segment's
+    // final state, each [dv, dk] fp32; then int32 [N*H, dv/32, seg_n], the chunks the
+    // sequential pass recomputed per segment (a diagnostic)
+    int seg_n, seg_len, seg_ncp;
+    float* segst;
 };
 
 // Token range of sequence n, clamped to [0, T] (see chunk_base_kernel).
@@ -127,6 +134,14 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes);
+
+// Segment plan of the long-chain split (SegPlan::n == 1: no split) and the bytes of its state
+// buffer; GDN_SEGMENT_CHUNKS=L in the environment forces segments of L chunks (0: no split).
+struct SegPlan {
+    int n, len, ncp;
+    size_t bytes;
+};
+SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16);
 
 hipError_t launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);

@@ -41,6 +41,10 @@
  *  - GDN_CHECK=1 in the environment (a debugging aid): every entry point that takes
  *    cu_seqlens first copies it to the host, which synchronises `stream`, and returns
  *    GDN_ERR_SHAPE unless 0 = cu[0] <= cu[1] <= ... <= cu[N] = T.
+ *  - GDN_SEGMENT_CHUNKS=L in the environment (for tests and tuning) fixes the segment length
+ *    of the long-chain split of the bf16 forward pass to L chunks; 0 turns the split off.
+ *    Without it the split is chosen from the shape (see gdn_chunk_fwd_workspace_bytes). The
+ *    setting must not change between a workspace size query and the call that uses it.
  *  - Alignment: q, k, v, o, h0, hT and the decode state 16 bytes; g, beta and cu_seqlens
  *    4 bytes; the workspace 256 bytes. A misaligned pointer gives GDN_ERR_ALIGN.
  */
@@ -97,6 +101,21 @@ const char *gdn_status_string(int status);
  * columns 32(pc>>2) + 4(pc&3) + {0..3, 16..19} with pc = pos ^ swz(r), where
  * swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
+ *
+ * Long chains, bf16 inputs: when N*H*(dv/32) is at most 128 and a sequence can span at least
+ * 32 chunks, the state propagation cuts every sequence into `ns` segments of `sl` chunks
+ * (about 256 / (N*H*dv/32) segments, each at least 16 chunks; the longest possible sequence,
+ * ceil(T/64) chunks, sets the count). All segments run at once, segment 0 from h0 and the
+ * others from zero, recording their states at segment offsets 1, 2, 4, .. below sl (`ncp`
+ * of them) and at the end; a second pass walks the segments in order from the true entering
+ * state and stops recomputing a segment at the first recorded offset where its state equals
+ * the record bit for bit. o and hT are bitwise those of the unsplit pass. The workspace then
+ * ends with one more region:
+ *   states      fp32  [N, H, ns, ncp + 1, dv, dk]   the recorded states, then the final one
+ *   reran       int32 [N, H, dv/32, ns]             chunks the second pass computed for each
+ *                                                   segment s >= 1 of each 32-column tile
+ *                                                   (a diagnostic; unset for segments past
+ *                                                   the sequence's end)
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N, int varlen,
                                      int chunk, int dtype);

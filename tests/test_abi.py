@@ -80,6 +80,43 @@ def test_workspace_bytes(L):
     assert L.gdn_chunk_fwd_workspace_bytes(2, 10, 2, 64, 64, 3, 1, 64, 1) == 0
 
 
+def _fwd_base_bytes(B, T, H, d):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nc = B * ((T + 63) // 64)
+    return (al(nc * H * 128 * 4) + al(nc * H * 4096 * 2) + al(nc * H * 4096 * 2)
+            + al(nc * H * 64 * d * 2) + nc * H * 64 * d * 2)
+
+
+def _seg_bytes(N, H, d, ns, sl):
+    ncp = (sl - 1).bit_length()   # offsets 1, 2, 4, .. below sl
+    return N * H * ns * ((ncp + 1) * d * d * 4 + (d // 32) * 4)
+
+
+def test_segment_plan_workspace(L, monkeypatch):
+    """The long-chain split's plan, read from the workspace size: the long-context shape
+    (B1 H16 T32768 d128 bf16: 64 column tiles) gets 4 segments of 128 chunks (7 records each);
+    the training shape (256 tiles) and fp32 inputs get none; GDN_SEGMENT_CHUNKS forces a
+    length or turns the split off."""
+    import torch
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    monkeypatch.delenv("GDN_SEGMENT_CHUNKS", raising=False)
+    base = _fwd_base_bytes(1, 32768, 16, 128)
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == al(base) + _seg_bytes(1, 16, 128, 4, 128)
+    assert gb.gdn_chunk_fwd_workspace_bytes(4, 2048, 16, 128, 128, 4, False) == _fwd_base_bytes(4, 2048, 16, 128)
+    f32 = gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False, dtype=torch.float32)
+    assert f32 == gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 256, 128, 128, 1, False, dtype=torch.float32) // 16
+    # one head of d 64 (2 tiles): 128 segments wanted, but at least 16 chunks each: 32 x 16
+    base = _fwd_base_bytes(1, 32768, 1, 64)
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 1, 64, 64, 1, False) == al(base) + _seg_bytes(1, 1, 64, 32, 16)
+    # fewer than 32 chunks: no split
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 64, 64, 1, False) == _fwd_base_bytes(1, 31 * 64, 1, 64)
+    monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "3")
+    base = _fwd_base_bytes(2, 849, 2, 128)   # 14 chunks per sequence: 5 segments of 3
+    assert gb.gdn_chunk_fwd_workspace_bytes(2, 849, 2, 128, 128, 2, False) == al(base) + _seg_bytes(2, 2, 128, 5, 3)
+    monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "0")
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == _fwd_base_bytes(1, 32768, 16, 128)
+
+
 def test_bwd_workspace_bytes(L):
     """The backward workspace is the region list of its header: the forward's regions with
     fp32 operators, then T, the state entering each chunk and the state gradient, and for bf16
