@@ -652,25 +652,26 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
     }
 }
 
-// One work-group per (sequence, head, DVT-column tile) with DVT/16 compute waves, one DMA wave
-// and one store wave, each on its own SIMD. Compute wave w owns columns dv0 + 16w .. +15 for
-// all tokens, with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
-// S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it reads and writes LDS and runs the matrix and
-// vector units, and writes global memory only for the backward pass's state recompute (the
-// state entering each chunk in fp16, p.states16; there p.o is NULL and the store wave writes
-// nothing) and for the long-chain split below.
-// While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of
-// chunk c+2 into ring buffers (2 and 3 deep: memory latency is about one chunk's
-// compute time), and before the next barrier waits for exactly the copies chunk c+1 needs; the
-// store wave writes chunk c-1's outputs from the LDS staging buffer and never waits for its
-// stores. One barrier per chunk.
+// One work-group per (sequence, head, DVT-column tile) with DVT/16 compute waves (DVT = 64: one
+// on every SIMD) and one DMA wave. Compute wave w owns columns dv0 + 16w .. +15 for all tokens,
+// with the state S^T [d_k, 16] in d_k/16 accumulator tiles (lane holds
+// S[dv0 + 16w + l16][16j + 4*lq + 0..3]); it reads LDS, runs the matrix and vector units and
+// writes its outputs straight to global memory with buffer stores that drop the rows past a
+// chunk's end (it never waits for them; a wave that has no copies of its own in flight can pass
+// the barrier with stores outstanding), the state entering each chunk in fp16 for the backward
+// pass's recompute (p.states16; there p.o is NULL), and the records of the long-chain split
+// below. While chunk c is computed the DMA wave copies Q of chunk c+1 and the rest of chunk c+2
+// into ring buffers (2 and 3 deep: memory latency is about one chunk's compute time), and before
+// the next barrier waits for exactly the copies chunk c+1 needs. One barrier per chunk.
+// LDS bandwidth bounds this loop: every compute wave reads the chunk's K, Q, Mmat, P and K^T
+// from LDS, about 64 KB per chunk.
 // The products are those of the generic stage-2 kernel (chunk_propagate_kernel).
 //
 // Long chains (few sequence-head pairs, many chunks) leave most of the device idle, so SEG
 // cuts each sequence's chunks into p.seg_n segments of p.seg_len chunks:
 //   SEG = 1: one work-group per (pair, tile, segment); segment 0 starts from h0, the others
-//     from a zero state. Each records its state at segment offsets 1, 2, 4, .. and its final
-//     state in p.segst, and writes o for all its chunks.
+//     from a zero state. Each records its final state in p.segst, segments past the first also
+//     their states at segment offsets 1, 2, 4, .., and writes o for all its chunks.
 //   SEG = 2: one work-group per (pair, tile) walks segments 1, 2, .. in order from the true
 //     state entering each. After the chunk that ends at a recorded offset it compares its
 //     state with the one SEG = 1 recorded there, bit for bit; once they are equal, every later
@@ -681,17 +682,15 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 //     saving comes from decay: a segment's dependence on its entering state shrinks by the
 //     product of its gates, and once that falls under fp32 rounding the two states agree.
 template <typename TO, int DK, int DV, int DVT, int SEG>
-__global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
+__global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
     using KQ = KQChunk<DK>;
     using MPV = MPVChunk<DK, DVT>;
-    using OS = OStage<TO, DVT>;
     constexpr int NW = DVT / 16;   // compute waves
     constexpr int NKB = DK / 16;   // d_k tiles of the state
     constexpr int NKS = DK / 32;   // 32-wide d_k slices
     constexpr int NTILE = DV / DVT;
     __shared__ KQ kq[2];
     __shared__ MPV mpv[3];
-    __shared__ OS ost[2];
     __shared__ int match[2][NW];   // SEG = 2: per compute wave, state equal to the record (by chunk parity)
 
     const int lane = threadIdx.x & 63;
@@ -795,47 +794,6 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         }
         return;
     }
-    if (wave == NW + 1) {
-        // ----------------------------------------------------------------- store wave
-        // outputs of chunk jc through a resource sized to the valid rows; NV adjacent lanes
-        // write one token row's columns (16 bytes each), so an instruction covers 64/NV rows
-        auto store_out = [&](const OS& os, long jc) {
-            constexpr int E = (int)sizeof(TO), NV = OS::ROWB / 16, RPI = 64 / NV;
-            const long obos = sbos + jc * kChunk;
-            const int olen = chunk_len(jc);
-            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dv0,
-                                       (unsigned)((olen - 1) * H * DV + DVT) * E);
-            const int rr = lane / NV, pc = lane % NV;
-            uint4 piece[NV];
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                piece[i] = *reinterpret_cast<const uint4*>(&os.b[(RPI * i + rr) * OS::PITCH + 16 * pc]);
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const u32x4_t v = {piece[i].x, piece[i].y, piece[i].z, piece[i].w};
-                __builtin_amdgcn_raw_buffer_store_b128(v, orr, (RPI * i + rr) * H * DV * E + 16 * pc, 0, 0);
-            }
-        };
-        auto run = [&](long c0, long len) {
-            for (int i = 0;; ++i) {
-                lds_barrier();  // chunk i-1's outputs are staged
-                if (i > 0 && p.o) store_out(ost[(i - 1) & 1], c0 + i - 1);
-                if (range_done(i, len)) break;
-            }
-        };
-        if constexpr (SEG == 2) {
-            for (int g = 1; g < p.seg_n; ++g) {
-                long c0, len;
-                seg_range(g, c0, len);
-                if (len == 0) break;
-                run(c0, len);
-            }
-        } else {
-            run(c_first, c_count);
-        }
-        return;
-    }
-
     // ------------------------------------------------------------------- compute waves
     const int dvw = dv0 + 16 * wave;
     f32x4_t ST[NKB];
@@ -865,7 +823,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     // 32-wide slice ahead, Mmat and the residual terms in the last slice, P during the
     // residual, K^T during the output product), and each product phase cycles over
     // independent accumulators; the scheduling fences keep that order.
-    auto step = [&](const KQ& ck, const MPV& cm, OS& os) {  // after the chunk's barrier
+    auto step = [&](const KQ& ck, const MPV& cm, long jc) {  // chunk jc, after its barrier
         uint4 MF[4][2], PF[4][2];
         float4 V4[4], EG4[4];
         auto load_mp = [&](const _Float16* src, uint4 (&f)[4][2]) {
@@ -949,8 +907,8 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
             KT[j][1] = lds_frag2_t(&cm.K[img_off<DK>(32 + 4 * lq + tr, c)], &cm.K[img_off<DK>(48 + 4 * lq + tr, c)]);
         }
 
-        // O^T = e^gamma S Q^T + Delta^T P^T, staged in LDS for the store wave (lane: token
-        // 16t + l16, columns 16 wave + 4 lq .. +3)
+        // O^T = e^gamma S Q^T + Delta^T P^T (lane: token 16t + l16, columns 16 wave + 4 lq .. +3),
+        // stored through a resource that ends at the chunk's last token row
         const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
         f32x4_t O[4];
 #pragma unroll
@@ -959,13 +917,13 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+        if (p.o) {
+            constexpr int E = (int)sizeof(TO);
+            const long obos = sbos + jc * kChunk;
+            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dvw,
+                                       (unsigned)(((chunk_len(jc) - 1) * H * DV + 16) * E));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            char* dst = &os.b[(16 * t + l16) * OS::PITCH + (16 * wave + 4 * lq) * (int)sizeof(TO)];
-            if constexpr (sizeof(TO) == 2)
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(O[t][0], O[t][1]), pack_bf16x2(O[t][2], O[t][3]));
-            else
-                *reinterpret_cast<float4*>(dst) = make_float4(O[t][0], O[t][1], O[t][2], O[t][3]);
+            for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + 4 * lq) * E, O[t]);
         }
 
         // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
@@ -990,7 +948,7 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
     // stopped at a matching record, SEG = 2)
     auto run = [&](long c0, long len, int g) {
         for (int i = 0;; ++i) {
-            lds_barrier();  // chunk i's operands are in LDS; chunk i's staging buffer is free
+            lds_barrier();  // chunk i's operands are in LDS
             if (range_done(i, len)) return i;
             if constexpr (SEG == 0) {
                 if (p.states16) {   // the state entering the chunk, in the fp16 its products take later
@@ -1001,10 +959,10 @@ __global__ __launch_bounds__((DVT / 16 + 2) * 64) void chunk_propagate_bf16_kern
                             make_uint2(pack_f16x2(ST[j][0], ST[j][1]), pack_f16x2(ST[j][2], ST[j][3]));
                 }
             }
-            step(kq[i & 1], mpv[i % 3], ost[i & 1]);
+            step(kq[i & 1], mpv[i % 3], c0 + i);
             const int off = i + 1;
-            if constexpr (SEG == 1) {
-                if (recorded(off, len)) store_state(seg_state(g, 31 - __builtin_clz(off)));
+            if constexpr (SEG == 1) {   // the walk never compares in segment 0
+                if (g > 0 && recorded(off, len)) store_state(seg_state(g, 31 - __builtin_clz(off)));
             }
             if constexpr (SEG == 2) {
                 bool same = false;
@@ -1069,31 +1027,43 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
     return w;
 }
 
-// Work-groups the device runs at once for the bf16 state propagation (one per CU: its LDS use
-// admits no second) on a 256-CU gfx950 part, and the shortest segment worth splitting off.
+// The bf16 state propagation runs one work-group per (sequence, head, tile of 32 or 64 d_v
+// columns), one per CU (its LDS use admits no second). 64-column tiles read the chunk operands
+// from LDS once per 64 columns and keep all four matrix cores busy, so they come first; 32-column
+// tiles serve problems that have too few 64-column tiles to fill the device but enough 32-column
+// ones. Below that the chains are cut into segments (64-column tiles), aiming at kSegTargetGroups
+// work-groups on a 256-CU gfx950 part, with segments of at least kSegMinChunks chunks.
 constexpr int kSegTargetGroups = 256;
 constexpr int kSegMinChunks = 16;
+
+static long tiles_of(int N, int H, int dv, int cols) { return (long)N * H * (dv > cols ? dv / cols : 1); }
+
+// d_v columns per work-group of the bf16 state propagation (without a split)
+static int prop_cols(int N, int H, int dv) {
+    return tiles_of(N, H, dv, 64) < kSegTargetGroups && tiles_of(N, H, dv, 32) >= kSegTargetGroups ? 32 : 64;
+}
 
 SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16) {
     SegPlan sp{1, 0, 0, 0};
     const long nmax = ((long)T + kChunk - 1) / kChunk;   // chunks of the longest possible sequence
     if (!bf16 || nmax < 2) return sp;
+    const long tiles = tiles_of(N, H, dv, 64);
     long len = 0;
     if (const char* env = std::getenv("GDN_SEGMENT_CHUNKS")) {
         len = std::atol(env);
         if (len <= 0) return sp;
     } else {
-        const long groups = (long)N * H * (dv / 32);
-        const long g = std::min((long)kSegTargetGroups / groups, nmax / kSegMinChunks);
+        if (prop_cols(N, H, dv) != 64) return sp;
+        const long g = std::min((long)kSegTargetGroups / tiles, nmax / kSegMinChunks);
         if (g < 2) return sp;
         len = (nmax + g - 1) / g;
     }
     const long n = (nmax + len - 1) / len;
-    if (n < 2 || (long)N * H * (dv / 32) * n > 0x7fffffffL) return sp;   // grid size
+    if (n < 2 || tiles * n > 0x7fffffffL) return sp;   // grid size
     sp.n = (int)n;
     sp.len = (int)len;
     while ((1L << sp.ncp) < len) ++sp.ncp;   // offsets 1, 2, 4, .. below len
-    sp.bytes = (size_t)N * H * n * ((sp.ncp + 1) * dv * dk * sizeof(float) + (dv / 32) * sizeof(int32_t));
+    sp.bytes = (size_t)N * H * n * ((sp.ncp + 1) * dv * dk * sizeof(float)) + (size_t)tiles * n * sizeof(int32_t);
     return sp;
 }
 
@@ -1128,17 +1098,25 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
     return e;
 }
 
+// bf16: DVT/16 compute waves and a DMA wave per work-group
+template <typename TO, int DK, int DV, int DVT>
+static hipError_t prop_launch_bf16(const ChunkProblem& p, hipStream_t s) {
+    const long blocks = (long)p.N * p.H * (DV / DVT);
+    const dim3 block((DVT / 16 + 1) * 64);
+    if (p.seg_n <= 1) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0>, dim3((unsigned)blocks), block, s, p);
+    const hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>,
+                                dim3((unsigned)(blocks * p.seg_n)), block, s, p);
+    return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 2>, dim3((unsigned)blocks), block, s, p);
+}
+
 template <typename TIn, typename TO, int DK, int DV>
 static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
-    constexpr int DVT = 32;
-    const long blocks = (long)p.N * p.H * (DV / DVT);
-    if constexpr (sizeof(TIn) == 2) {   // two compute waves (32 columns), a DMA wave and a store wave
-        const dim3 block((DVT / 16 + 2) * 64);
-        if (p.seg_n <= 1) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0>, dim3((unsigned)blocks), block, s, p);
-        const hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>,
-                                    dim3((unsigned)(blocks * p.seg_n)), block, s, p);
-        return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 2>, dim3((unsigned)blocks), block, s, p);
+    if constexpr (sizeof(TIn) == 2) {
+        if (p.seg_n <= 1 && prop_cols(p.N, p.H, DV) == 32) return prop_launch_bf16<TO, DK, DV, 32>(p, s);
+        return prop_launch_bf16<TO, DK, DV, (DV < 64 ? DV : 64)>(p, s);
     } else {                            // two waves of 16 columns (LDS size)
+        constexpr int DVT = 32;
+        const long blocks = (long)p.N * p.H * (DV / DVT);
         return launch(chunk_propagate_kernel<TIn, TO, DK, DV, DVT>, dim3((unsigned)blocks),
                       dim3(DVT / 16 * 64), s, p);
     }

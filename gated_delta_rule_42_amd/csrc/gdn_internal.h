@@ -83,7 +83,7 @@ struct ChunkProblem {
     // long-chain split of the bf16 state propagation (seg_n > 1): the chunks of a sequence are
     // cut into segments of seg_len chunks; segst holds, per (sequence, head) and segment, the
     // states at segment offsets 1, 2, 4, .. < seg_len (seg_ncp of them) and the segment's
-    // final state, each [dv, dk] fp32; then int32 [N*H, dv/32, seg_n], the chunks the
+    // final state, each [dv, dk] fp32; then int32 [N*H, max(1, dv/64), seg_n], the chunks the
     // sequential pass recomputed per segment (a diagnostic)
     int seg_n, seg_len, seg_ncp;
     float* segst;

@@ -102,18 +102,20 @@ const char *gdn_status_string(int status);
  * swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
  *
- * Long chains, bf16 inputs: when N*H*(dv/32) is at most 128 and a sequence can span at least
- * 32 chunks, the state propagation cuts every sequence into `ns` segments of `sl` chunks
- * (about 256 / (N*H*dv/32) segments, each at least 16 chunks; the longest possible sequence,
- * ceil(T/64) chunks, sets the count). All segments run at once, segment 0 from h0 and the
- * others from zero, recording their states at segment offsets 1, 2, 4, .. below sl (`ncp`
- * of them) and at the end; a second pass walks the segments in order from the true entering
+ * Long chains, bf16 inputs: the state propagation runs one work-group per (sequence, head,
+ * 64-column d_v tile), or per 32-column tile when N*H*(dv/64) < 256 <= N*H*(dv/32). When
+ * neither fills the device (N*H*(dv/64) at most 128) and a sequence can span at least 32
+ * chunks, it cuts every sequence into `ns` segments of `sl` chunks (about 256 / (N*H*dv/64)
+ * segments, each at least 16 chunks; the longest possible sequence, ceil(T/64) chunks, sets the
+ * count). All segments run at once, segment 0 from h0 and the others from zero, recording
+ * their final states and (segments past the first) their states at segment offsets 1, 2, 4, ..
+ * below sl (`ncp` of them); a second pass walks the segments in order from the true entering
  * state and stops recomputing a segment at the first recorded offset where its state equals
  * the record bit for bit. o and hT are bitwise those of the unsplit pass. The workspace then
  * ends with one more region:
  *   states      fp32  [N, H, ns, ncp + 1, dv, dk]   the recorded states, then the final one
- *   reran       int32 [N, H, dv/32, ns]             chunks the second pass computed for each
- *                                                   segment s >= 1 of each 32-column tile
+ *   reran       int32 [N, H, max(1, dv/64), ns]     chunks the second pass computed for each
+ *                                                   segment s >= 1 of each 64-column tile
  *                                                   (a diagnostic; unset for segments past
  *                                                   the sequence's end)
  */

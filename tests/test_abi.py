@@ -59,7 +59,8 @@ def test_version_and_status_strings(L):
     assert gb.gdn_status_string(-99) == "unknown status"
 
 
-def test_workspace_bytes(L):
+def test_workspace_bytes(L, monkeypatch):
+    monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "0")   # the stage-1 regions alone
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # B4 H16 T2048 bf16: 128 chunks x 16 heads
     nc, H = 4 * 32, 16
@@ -89,23 +90,27 @@ def _fwd_base_bytes(B, T, H, d):
 
 def _seg_bytes(N, H, d, ns, sl):
     ncp = (sl - 1).bit_length()   # offsets 1, 2, 4, .. below sl
-    return N * H * ns * ((ncp + 1) * d * d * 4 + (d // 32) * 4)
+    return N * H * ns * (ncp + 1) * d * d * 4 + N * H * max(1, d // 64) * ns * 4
 
 
 def test_segment_plan_workspace(L, monkeypatch):
     """The long-chain split's plan, read from the workspace size: the long-context shape
-    (B1 H16 T32768 d128 bf16: 64 column tiles) gets 4 segments of 128 chunks (7 records each);
-    the training shape (256 tiles) and fp32 inputs get none; GDN_SEGMENT_CHUNKS forces a
-    length or turns the split off."""
+    (B1 H16 T32768 d128 bf16: 32 tiles of 64 columns) gets 8 segments of 64 chunks (6 records
+    each); B2 H16 T2048 (64 tiles of 64 columns, 128 of 32) 2 of 16; the training shape
+    (B4 H16 T2048: 256 tiles of 32 columns), 256 tiles of 64 columns and fp32 inputs get none;
+    GDN_SEGMENT_CHUNKS forces a length or turns the split off."""
     import torch
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     monkeypatch.delenv("GDN_SEGMENT_CHUNKS", raising=False)
     base = _fwd_base_bytes(1, 32768, 16, 128)
-    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == al(base) + _seg_bytes(1, 16, 128, 4, 128)
-    assert gb.gdn_chunk_fwd_workspace_bytes(4, 2048, 16, 128, 128, 4, False) == _fwd_base_bytes(4, 2048, 16, 128)
+    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == al(base) + _seg_bytes(1, 16, 128, 8, 64)
+    base = _fwd_base_bytes(2, 2048, 16, 128)
+    assert gb.gdn_chunk_fwd_workspace_bytes(2, 2048, 16, 128, 128, 2, False) == al(base) + _seg_bytes(2, 16, 128, 2, 16)
+    for B in (4, 8):
+        assert gb.gdn_chunk_fwd_workspace_bytes(B, 2048, 16, 128, 128, B, False) == _fwd_base_bytes(B, 2048, 16, 128)
     f32 = gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False, dtype=torch.float32)
     assert f32 == gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 256, 128, 128, 1, False, dtype=torch.float32) // 16
-    # one head of d 64 (2 tiles): 128 segments wanted, but at least 16 chunks each: 32 x 16
+    # one head of d 64 (one tile): 256 segments wanted, but at least 16 chunks each: 32 x 16
     base = _fwd_base_bytes(1, 32768, 1, 64)
     assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 1, 64, 64, 1, False) == al(base) + _seg_bytes(1, 1, 64, 32, 16)
     # fewer than 32 chunks: no split

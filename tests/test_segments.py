@@ -37,7 +37,7 @@ def rel_rms(x, ref):
 
 def run(x, seg_chunks, monkeypatch, o_dtype=torch.float32):
     """Forward pass with the split forced to `seg_chunks` (0: off); returns o, hT and the
-    per-segment rerun counts [N, H, dv/32, ns] (None without a split)."""
+    per-segment rerun counts [N, H, max(1, dv/64), ns] (None without a split)."""
     monkeypatch.setenv("GDN_SEGMENT_CHUNKS", str(seg_chunks))
     m = x["meta"]
     dev = "cuda"
@@ -54,8 +54,8 @@ def run(x, seg_chunks, monkeypatch, o_dtype=torch.float32):
         nmax = (m["T"] + 63) // 64
         ns = (nmax + seg_chunks - 1) // seg_chunks
         if ns > 1:
-            cnt = N * m["H"] * (m["dv"] // 32) * ns
-            reran = ws[need - 4 * cnt:].cpu().view(torch.int32).numpy().reshape(N, m["H"], m["dv"] // 32, ns)
+            nt = max(1, m["dv"] // 64)
+            reran = ws[need - 4 * N * m["H"] * nt * ns:].cpu().view(torch.int32).numpy().reshape(N, m["H"], nt, ns)
     monkeypatch.delenv("GDN_SEGMENT_CHUNKS")
     return o, hT, reran
 
@@ -138,7 +138,7 @@ def test_split_bf16_output_and_no_final_state(monkeypatch):
 
 
 def test_long_context_split_equals_unsplit(monkeypatch):
-    """B1 H16 T32768 d128: the shape-chosen plan (4 segments of 128 chunks) against the unsplit
+    """B1 H16 T32768 d128: the shape-chosen plan (8 segments of 64 chunks) against the unsplit
     pass, bit for bit; with the workloads' decay the second pass stops at offset 1 or 2."""
     monkeypatch.delenv("GDN_SEGMENT_CHUNKS", raising=False)
     x = SY.make_forward_inputs(2)
@@ -149,7 +149,7 @@ def test_long_context_split_equals_unsplit(monkeypatch):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     o1, h1 = gb.gdn_chunk_fwd(*t, h0, workspace=ws)
     torch.cuda.synchronize()
-    reran = ws[need - 4 * 16 * 4 * 4:].cpu().view(torch.int32).numpy().reshape(16, 4, 4)
+    reran = ws[need - 4 * 16 * 2 * 8:].cpu().view(torch.int32).numpy().reshape(16, 2, 8)
     monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "0")
     o0, h0r = gb.gdn_chunk_fwd(*t, h0)
     torch.cuda.synchronize()
