@@ -2,18 +2,22 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
 A step is one chunkwise forward pass (gate scan, gated Gram, UT transform, chunk operators,
-state propagation and output: gdn_chunk_prepare + gdn_chunk_propagate, exactly the two
-launches gdn_chunk_fwd makes) over the training-shape workload B4 H16 T2048 d_k=d_v=128,
-bf16 q/k/v/o, fp32 gates and state, chunk 64. Inputs are resident in HBM before timing
-and rotate over 4 independent sets (~540 MB) so that no step is served from the 256 MB
-Infinity Cache. The decode step (256 sequences x H32, d128, fp32 state, 64 chained
-steps) is timed in the same run and reported under "decode".
+state propagation and output: gdn_chunk_prepare + gdn_chunk_propagate, exactly the launches
+gdn_chunk_fwd makes) over the training-shape workload B4 H16 T2048 d_k=d_v=128, bf16
+q/k/v/o, fp32 gates and state, chunk 64: the headline line. Inputs are resident in HBM before
+timing and rotate over 4 independent sets (~540 MB) so that no step is served from the 256 MB
+Infinity Cache. The same run times every other workload the same way and reports each under
+"workloads": the tiny fp32 forward, the long-context forward (B1 H16 T32768, h0 != 0), the
+packed variable-length forward (8 sequences, H32) and the decode step (256 sequences x H32,
+d128, fp32 state, bf16 o, 64 chained steps), each with per-call percentiles, algorithmic
+TFLOP/s and HBM rate against the chip's peaks, and the CPU oracle on a bounded sample.
 
 Prints one JSON line (rank 0, one GPU).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -25,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "GDN chunk-fwd tokens/s + %MFMA peak (B4 H16 T2048 d128); decode %HBM BW"
 PEAK_BF16_FLOPS = 2516.6e12   # 256 CU x 2.4 GHz x 4096 dense bf16/fp16 FLOP/clk/CU (MI355X, ~2.5 PF)
+PEAK_F32_FLOPS = 157.3e12     # dense fp32 matrix core
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 CHUNK = 64
 
@@ -119,48 +124,98 @@ def event_steps(n, per, torch):
     return {i: [torch.cuda.Event(enable_timing=True) for _ in range(per)] for i in range(n) if i % EVENT_EVERY == 0}
 
 
-def bench_forward(args, torch, gb, SY):
-    w = SY.WORKLOADS[1]
-    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+def pcts(xs):
+    """p10, median and p90 of a list of samples (nearest rank)."""
+    xs = sorted(xs)
+    if not xs:
+        return {"p10": None, "median": None, "p90": None}
+    q = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]  # noqa: E731
+    return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
+
+
+def bench_forward(wid, steps, warmup, nsets, torch, gb, SY):
+    """gdn_chunk_prepare + gdn_chunk_propagate on forward workload `wid` (o in the input
+    dtype), nsets rotating input sets: `steps` back-to-back calls timed by the wall clock, then
+    as many calls (at least 10) each bracketed by HIP events on the launch stream for the
+    per-call and per-stage distributions."""
+    w = SY.WORKLOADS[wid]
     dev = torch.device("cuda:0")
     sets = []
-    for s in range(4):
-        x = SY.make_forward_inputs(1, seed=1 + 100 * s)
-        t = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
-        t["o"] = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
-        t["hT"] = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    for s in range(nsets):
+        x = SY.make_forward_inputs(wid, seed=w.id + 100 * s)
+        t = {n: (None if x[n] is None else x[n].to(dev)) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+        B, T, H, dk = t["q"].shape
+        dv = t["v"].shape[-1]
+        N = B if t["cu_seqlens"] is None else t["cu_seqlens"].numel() - 1
+        t["o"] = torch.empty((B, T, H, dv), dtype=t["q"].dtype, device=dev)
+        t["hT"] = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
         sets.append(t)
-    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, B, False)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    cu0 = sets[0]["cu_seqlens"]
+    need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, cu0 is not None, dtype=sets[0]["q"].dtype)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def step(t, ev=None):
         if ev is not None:
             ev[0].record()
-        gb.gdn_chunk_prepare(t["q"], t["k"], t["g"], t["beta"], ws, dv=dv)
+        gb.gdn_chunk_prepare(t["q"], t["k"], t["g"], t["beta"], ws, t["cu_seqlens"], dv=dv)
         if ev is not None:
             ev[1].record()
-        gb.gdn_chunk_propagate(t["q"], t["k"], t["v"], ws, o=t["o"], hT=t["hT"])
+        gb.gdn_chunk_propagate(t["q"], t["k"], t["v"], ws, t["h0"], t["cu_seqlens"], o=t["o"], hT=t["hT"])
         if ev is not None:
             ev[2].record()
 
     # the two stage calls are exactly gdn_chunk_fwd
     step(sets[0])
-    o_ref, h_ref = gb.gdn_chunk_fwd(*(sets[0][n] for n in ("q", "k", "v", "g", "beta")))
+    o_ref, h_ref = gb.gdn_chunk_fwd(*(sets[0][n] for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")),
+                                    o_dtype=sets[0]["q"].dtype)
     torch.cuda.synchronize()
     assert torch.equal(o_ref, sets[0]["o"]) and torch.equal(h_ref, sets[0]["hT"])
 
-    for i in range(args.warmup):
-        step(sets[i % 4])
-    evs = event_steps(args.steps, 3, torch)
+    for i in range(warmup):
+        step(sets[i % nsets])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % 4], evs.get(i))
+    for i in range(steps):
+        step(sets[i % nsets])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    prep_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
-    prop_ms = [e[1].elapsed_time(e[2]) for e in evs.values()]
-    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=t1 - t0, prep_ms=prep_ms, prop_ms=prop_ms)
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(10, steps))]
+    for i, e in enumerate(evs):
+        step(sets[i % nsets], e)
+    torch.cuda.synchronize()
+    return dict(wid=wid, name=w.name, B=B, T=T, H=H, dk=dk, dv=dv, N=N, dtype=w.dtype,
+                h0=sets[0]["h0"] is not None, tokens=B * T, ms=wall / steps * 1e3, steps=steps,
+                call_ms=[e[0].elapsed_time(e[2]) for e in evs], prep_ms=[e[0].elapsed_time(e[1]) for e in evs],
+                prop_ms=[e[1].elapsed_time(e[2]) for e in evs])
+
+
+def forward_report(f):
+    """Throughput, algorithmic rates against the chip's peaks and the per-call distribution of
+    one forward workload."""
+    elem = 4 if f["dtype"] == "f32" else 2
+    c = fwd_counts(f["dk"], f["dv"], elem=elem)
+    th = f["tokens"] * f["H"]
+    state_bytes = f["N"] * f["H"] * f["dk"] * f["dv"] * 4 * (2 if f["h0"] else 1)   # h0 read, hT written
+    flops, byts = c["flops"] * th, c["bytes"] * th + state_bytes
+    peak = PEAK_F32_FLOPS if f["dtype"] == "f32" else PEAK_BF16_FLOPS
+    sec = f["ms"] / 1e3
+    # the whole call against its nearer roof: algorithmic bytes at peak HBM vs FLOP at peak MFMA
+    hbm_bound = byts / PEAK_HBM_BPS >= flops / peak
+    return {"workload": f"{f['name']}: B{f['B']} T{f['T']} H{f['H']} d_k={f['dk']} d_v={f['dv']} N={f['N']} "
+                        f"{f['dtype']} q/k/v/o, fp32 gates and state" + (", h0 != 0" if f["h0"] else ""),
+            "tokens": f["tokens"], "ms_per_call": f["ms"], "calls_timed": f["steps"],
+            "ms_per_call_events": pcts(f["call_ms"]),
+            "tokens_per_s": f["tokens"] / sec, "tflops": flops / sec / 1e12,
+            "mfma_frac": flops / sec / peak, "mfma_peak_tflops": peak / 1e12,
+            "hbm_GBps_algorithmic": byts / sec / 1e9, "hbm_frac": byts / sec / PEAK_HBM_BPS,
+            "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": byts,
+            "stages_ms_median": {"chunk_prepare": pcts(f["prep_ms"])["median"],
+                                 "chunk_propagate": pcts(f["prop_ms"])["median"]},
+            "call_roofline": {"bound": "hbm" if hbm_bound else "mfma",
+                              "achieved": byts / sec / 1e9 if hbm_bound else flops / sec / 1e12,
+                              "peak": PEAK_HBM_BPS / 1e9 if hbm_bound else peak / 1e12,
+                              "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                              "frac": byts / sec / PEAK_HBM_BPS if hbm_bound else flops / sec / peak}}
 
 
 def bench_backward(args, torch, gb, SY):
@@ -271,40 +326,46 @@ def bench_kda(args, torch, gb, SY):
 
 
 def bench_decode(args, torch, gb, SY):
+    """gdn_decode_step on the decode workload (fp32 state, bf16 q/k/v and o), args.decode_steps
+    chained steps, each bracketed by HIP events."""
     w = SY.WORKLOADS[4]
     d = SY.make_decode_inputs(4, steps=args.decode_steps)
     dev = torch.device("cuda:0")
     N, H, dk, dv = w.decode_seqs, w.H, w.dk, w.dv
     toks = [{n: d[n][s].to(dev) for n in ("q", "k", "v", "g", "beta")} for s in range(args.decode_steps)]
     state = d["state"].to(dev)
-    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
     warm = state.clone()
     for s in range(min(3, args.decode_steps)):
         gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), warm, o)
     del warm
-    evs = event_steps(args.decode_steps, 2, torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.decode_steps):
-        if s in evs:
-            evs[s][0].record()
         gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), state, o)
-        if s in evs:
-            evs[s][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
-    return dict(N=N, H=H, dk=dk, dv=dv, wall_s=t1 - t0, step_ms=step_ms)
+    wall = time.perf_counter() - t0
+    state = d["state"].to(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    for s, e in enumerate(evs):
+        e[0].record()
+        gb.gdn_decode_step(*(toks[s][n] for n in ("q", "k", "v", "g", "beta")), state, o)
+        e[1].record()
+    torch.cuda.synchronize()
+    return dict(N=N, H=H, dk=dk, dv=dv, ms=wall / args.decode_steps * 1e3,
+                step_ms=[e[0].elapsed_time(e[1]) for e in evs])
 
 
-def cpu_baseline(seconds):
-    """The CPU fp64 oracle (C twin, OpenMP over (sequence, head) pairs) on the same
-    training-shape workload, repeated until `seconds` of wall clock have passed."""
+def cpu_forward(wid, seconds):
+    """The CPU fp64 oracle (C twin: the token recurrence, OpenMP over (sequence, head) pairs)
+    on the whole of forward workload `wid`, repeated until `seconds` of wall clock have passed
+    (at least once)."""
     from gated_delta_rule_42_amd import synthetic as SY
     from oracle import ctwin
 
-    x = SY.make_forward_inputs(1)
-    p = ctwin.prepare_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    w = SY.WORKLOADS[wid]
+    x = SY.make_forward_inputs(wid)
+    p = ctwin.prepare_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], x["cu_seqlens"])
     reps, used = 0, 1
     t0 = time.perf_counter()
     while True:
@@ -315,8 +376,38 @@ def cpu_baseline(seconds):
             break
     tokens = reps * p["B"] * p["T"]
     return {"value": tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"full B4 H16 T2048 d128 workload x{reps} (fp64 token recurrence, "
-                      f"{el:.1f} s wall, {os.cpu_count()} host CPUs visible)"}
+            "sample": f"the full {w.name} workload x{reps} (fp64 token recurrence, {el:.1f} s wall, "
+                      f"{os.cpu_count()} host CPUs visible)"}
+
+
+def cpu_decode(seconds):
+    """The CPU fp64 oracle decode step (C twin, OpenMP over (sequence, head) pairs) on the whole
+    decode workload, chained steps until `seconds` have passed."""
+    import numpy as np
+
+    from gated_delta_rule_42_amd import synthetic as SY
+    from oracle import ctwin
+
+    w = SY.WORKLOADS[4]
+    d = SY.make_decode_inputs(4, steps=8)
+    lib = ctwin.load()
+    f64 = lambda t: np.ascontiguousarray(t.double().numpy())  # noqa: E731
+    S = f64(d["state"])
+    N, H, dv, dk = S.shape
+    toks = [[f64(d[n][s]) for n in ("q", "k", "v", "g", "beta")] for s in range(8)]
+    o = np.zeros((N, H, dv))
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    steps, used = 0, 1
+    t0 = time.perf_counter()
+    while True:
+        q, k, v, g, b = toks[steps % 8]
+        used = lib.gdn_oracle_decode(P(S), P(q), P(k), P(v), P(g), P(b), P(o), N * H, dk, dv)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": steps * N / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{steps} chained steps of the whole {w.name} workload (fp64 step, {el:.1f} s wall)"}
 
 
 def cpu_baseline_slices(kind, seconds):
@@ -393,58 +484,67 @@ def main():
     if args.calib_copy_mb:
         calib_copy(torch, args.calib_copy_mb)
     if args.only in ("all", "fwd"):
-        f = bench_forward(args, torch, gb, SY)
-        c = fwd_counts(f["dk"], f["dv"])
-        th = f["B"] * f["T"] * f["H"]
-        ms_step = f["wall_s"] / args.steps * 1e3
-        tokens = f["B"] * f["T"]
-        prep, prop = sum(f["prep_ms"]) / len(f["prep_ms"]), sum(f["prop_ms"]) / len(f["prop_ms"])
-        out["value"] = tokens / (ms_step / 1e3)
-        out["ms_per_step"] = ms_step
-        out["mfma_frac"] = c["flops"] * th / (ms_step / 1e3) / PEAK_BF16_FLOPS
-        out["tflops"] = c["flops"] * th / (ms_step / 1e3) / 1e12
-        out["hbm_frac_algorithmic"] = c["bytes"] * th / (ms_step / 1e3) / PEAK_HBM_BPS
-        out["stages_ms"] = {"chunk_prepare": prep, "chunk_propagate": prop,
-                            "chunk_prepare_median": median(f["prep_ms"]),
-                            "chunk_propagate_median": median(f["prop_ms"])}
-        if prop >= prep:
-            ach = c["stage2_bytes"] * th / (prop / 1e3)
+        wl = {}
+        # the headline: the training shape over 4 rotating input sets (beyond the Infinity Cache)
+        f1 = bench_forward(1, args.steps, args.warmup, 4, torch, gb, SY)
+        r1 = forward_report(f1)
+        wl["train_1p3b"] = r1
+        out["value"] = r1["tokens_per_s"]
+        out["ms_per_step"] = r1["ms_per_call"]
+        out["mfma_frac"] = r1["mfma_frac"]
+        out["tflops"] = r1["tflops"]
+        out["hbm_frac_algorithmic"] = r1["hbm_frac"]
+        out["ms_per_step_events"] = r1["ms_per_call_events"]
+        out["forward_call_roofline"] = r1["call_roofline"]
+        prep, prop = pcts(f1["prep_ms"])["median"], pcts(f1["prop_ms"])["median"]
+        out["stages_ms"] = {"chunk_prepare_median": prep, "chunk_propagate_median": prop,
+                            "chunk_prepare_mean": sum(f1["prep_ms"]) / len(f1["prep_ms"]),
+                            "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
+        c = fwd_counts(f1["dk"], f1["dv"])
+        th = f1["tokens"] * f1["H"]
+        mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
+        if mean_prop >= mean_prep:
+            ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
             out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
                                "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                                "frac": ach / PEAK_HBM_BPS,
                                "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
                                "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
         else:
-            ach = c["stage1_flops"] * th / (prep / 1e3)
+            ach = c["stage1_flops"] * th / (mean_prep / 1e3)
             out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
                                "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
                                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
                                "traffic": measured_traffic("chunk_prepare_kernel"),
                                "algorithmic_flops_per_launch": c["stage1_flops"] * th}
+        # the other forward workloads, one input set each (each exceeds the Infinity Cache but
+        # the tiny one, which is latency-bound anyway)
+        for wid, steps in ((0, args.steps), (2, max(5, args.steps // 3)), (3, max(5, args.steps // 3))):
+            f = bench_forward(wid, steps, min(args.warmup, 3), 1, torch, gb, SY)
+            wl[SY.WORKLOADS[wid].name] = forward_report(f)
+        t1 = wl["train_1p3b"]["ms_per_call"] / (f1["tokens"] * f1["H"])
+        lw = wl["long_ctx"]
+        t2 = lw["ms_per_call"] / (lw["tokens"] * 16)
+        out["long_vs_train_time_per_token_head"] = t2 / t1
+        out["workloads"] = wl
     if args.only in ("all", "decode"):
         d = bench_decode(args, torch, gb, SY)
-        per = decode_bytes(d["dk"], d["dv"]) * d["N"] * d["H"]
-        med = median(d["step_ms"])
-        mean = sum(d["step_ms"]) / len(d["step_ms"])
-        out["decode"] = {"workload": "decode 256 seq x H32 d128, fp32 state, bf16 q/k/v, fp32 o, "
-                                     f"{args.decode_steps} chained steps ({len(d['step_ms'])} of them timed "
-                                     "with HIP events)",
-                         "ms_per_step_median": med, "ms_per_step_mean": mean,
-                         "tokens_per_s": d["N"] / (mean / 1e3),
-                         "hbm_GBps": per / (mean / 1e3) / 1e9,
-                         "hbm_frac": per / (mean / 1e3) / PEAK_HBM_BPS,
-                         "bytes_per_step": per,
-                         "traffic": measured_traffic("decode_kernel")}
+        per = decode_bytes(d["dk"], d["dv"], o_elem=2) * d["N"] * d["H"]
+        sec = d["ms"] / 1e3
+        rd = {"workload": "decode: 256 sequences x H32 d128, fp32 state, bf16 q/k/v/o, "
+                          f"{args.decode_steps} chained steps",
+              "ms_per_step": d["ms"], "ms_per_step_events": pcts(d["step_ms"]),
+              "tokens_per_s": d["N"] / sec, "hbm_GBps": per / sec / 1e9, "hbm_frac": per / sec / PEAK_HBM_BPS,
+              "bytes_per_step": per, "traffic": measured_traffic("decode_kernel"),
+              "call_roofline": {"bound": "hbm", "achieved": per / sec / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                                "unit": "GB/s", "frac": per / sec / PEAK_HBM_BPS}}
+        out.setdefault("workloads", {})["decode"] = rd
+        out["decode"] = rd
         if args.only == "decode":
-            out["value"] = d["N"] / (mean / 1e3)
-            out["ms_per_step"] = mean
-            out["metric"] = METRIC
-            out["unit"] = "tokens/s"
-            out["roofline"] = {"kernel": "decode_kernel", "bound": "hbm",
-                               "achieved": per / (mean / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
-                               "unit": "GB/s", "frac": per / (mean / 1e3) / PEAK_HBM_BPS,
-                               "traffic": measured_traffic("decode_kernel"),
-                               "algorithmic_bytes_per_launch": per}
+            out["value"] = rd["tokens_per_s"]
+            out["ms_per_step"] = d["ms"]
+            out["roofline"] = dict(rd["call_roofline"], kernel="decode_kernel", traffic=rd["traffic"],
+                                   algorithmic_bytes_per_launch=per)
     if args.only in ("all", "bwd"):
         b = bench_backward(args, torch, gb, SY)
         th = b["B"] * b["T"] * b["H"]
@@ -503,8 +603,14 @@ def main():
         if args.only == "kda":
             out["value"] = k["B"] * k["T"] / (k["fwd_ms"] / 1e3)
             out["ms_per_step"] = k["fwd_ms"]
-    if args.cpu_seconds > 0 and args.only not in ("decode", "bwd", "kda"):
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.cpu_seconds > 0 and args.only in ("all", "fwd"):
+        # the headline's oracle gets the budget, the other workloads a fifth of it each
+        out["cpu_baseline"] = cpu_forward(1, args.cpu_seconds)
+        out["workloads"]["train_1p3b"]["cpu_baseline"] = out["cpu_baseline"]
+        for wid in (0, 2, 3):
+            out["workloads"][SY.WORKLOADS[wid].name]["cpu_baseline"] = cpu_forward(wid, args.cpu_seconds / 5)
+    if args.cpu_seconds > 0 and args.only in ("all", "decode"):
+        out["workloads"]["decode"]["cpu_baseline"] = cpu_decode(args.cpu_seconds / 5)
     print(json.dumps(out), flush=True)
 
 
