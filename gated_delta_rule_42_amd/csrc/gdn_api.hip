@@ -16,6 +16,21 @@ namespace {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
+// Size checks shared by the chunked entry points and their workspace queries (after the dtype,
+// chunk and head-dimension checks): B, H >= 1, T >= 0, H <= 32768 (one chunk of one head spans
+// 64 token rows of H heads, addressed with 32-bit byte offsets inside the kernels), N = B
+// without packed sequences and B = 1, N >= 1 with them, at most 2^40 elements in any token
+// tensor and at most 2^30 (sequence, head) pairs. Each product is formed only once its factors
+// are known to keep it inside 64 bits.
+int shape_check(int B, int T, int H, int dk, int dv, int N, bool varlen) {
+    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
+    if (varlen ? (B != 1 || N < 1) : (N != B)) return GDN_ERR_SHAPE;
+    const long long tokens = (long long)B * T;   // < 2^62
+    if (tokens > (1LL << 40) || tokens * H * (dk > dv ? dk : dv) > (1LL << 40)) return GDN_ERR_SHAPE;
+    if ((long long)N * H > (1LL << 30)) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
 // The forward workspace: the stage-1 regions, then the state records of the long-chain split
 struct FwdLayout {
     gdn::WorkspaceLayout w;
@@ -57,17 +72,9 @@ int check_chunk(const void* q, const void* k, const void* v, const float* g, con
     if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
-    // H bound: one chunk of one head spans 64 token rows of H heads, addressed with 32-bit
-    // byte offsets inside the kernels
-    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
-    if (cu) {
-        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
-    } else if (N != B) {
-        return GDN_ERR_SHAPE;
-    }
+    const int sc = shape_check(B, T, H, dk, dv, N, cu != nullptr);
+    if (sc != GDN_OK) return sc;
     const long long tokens = (long long)B * T;
-    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
-        return GDN_ERR_SHAPE;
     if (tokens > 0) {
         if ((need & 1) && (!q || !k || !g || !beta)) return GDN_ERR_NULL;
         if ((need & 2) && (!q || !k || !v || !o)) return GDN_ERR_NULL;
@@ -128,8 +135,7 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int
                                                 int varlen, int chunk, int dtype) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
-    if (B < 1 || H < 1 || T < 0) return 0;
-    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    if (shape_check(B, T, H, dk, dv, N, varlen != 0) != GDN_OK) return 0;
     return fwd_layout(B, T, H, dk, dv, N, varlen != 0, dtype == GDN_BF16).total;
 }
 
@@ -225,8 +231,7 @@ GDN_EXPORT size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int
                                                 int varlen, int chunk, int dtype) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
-    if (B < 1 || H < 1 || T < 0) return 0;
-    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    if (shape_check(B, T, H, dk, dv, N, varlen != 0) != GDN_OK) return 0;
     return gdn::bwd_workspace_layout(B, T, H, dk, dv, N, varlen != 0, dtype == GDN_BF16).total;
 }
 
@@ -240,15 +245,9 @@ GDN_EXPORT int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
     if (grad_dtype != GDN_F32 && !(grad_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
-    if (cu_seqlens) {
-        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
-    } else if (N != B) {
-        return GDN_ERR_SHAPE;
-    }
+    const int sc = shape_check(B, T, H, dk, dv, N, cu_seqlens != nullptr);
+    if (sc != GDN_OK) return sc;
     const long long tokens = (long long)B * T;
-    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
-        return GDN_ERR_SHAPE;
     if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !beta || !d_o || !dq || !dk_out || !dv_out ||
                        !dg || !dbeta))
         return GDN_ERR_NULL;
@@ -308,8 +307,7 @@ GDN_EXPORT size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk,
                                                     int varlen, int chunk, int dtype) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
     if (chunk != 64 || !head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
-    if (B < 1 || H < 1 || T < 0) return 0;
-    if (varlen ? (B != 1 || N < 1) : (N != B)) return 0;
+    if (shape_check(B, T, H, dk, dv, N, varlen != 0) != GDN_OK) return 0;
     return gdn::kda_workspace_layout(B, T, H, dk, N, varlen != 0, dtype == GDN_BF16 ? 2 : 4).total;
 }
 
@@ -323,15 +321,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g_lo
     if (o_dtype != GDN_F32 && !(o_dtype == GDN_BF16 && dtype == GDN_BF16)) return GDN_ERR_DTYPE;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || H > 32768 || T < 0) return GDN_ERR_SHAPE;
-    if (cu_seqlens) {
-        if (B != 1 || N < 1) return GDN_ERR_SHAPE;
-    } else if (N != B) {
-        return GDN_ERR_SHAPE;
-    }
+    const int sc = shape_check(B, T, H, dk, dv, N, cu_seqlens != nullptr);
+    if (sc != GDN_OK) return sc;
     const long long tokens = (long long)B * T;
-    if (tokens * H * (dk > dv ? dk : dv) > (1LL << 40) || (long long)N * H > (1LL << 30))
-        return GDN_ERR_SHAPE;
     if (tokens > 0 && (!q || !k || !v || !g_log_alpha || !o || (!erase && !beta) || (erase && !write)))
         return GDN_ERR_NULL;
     const void* al16[] = {q, k, v, o, h0, hT, g_log_alpha, erase, write};
