@@ -103,6 +103,9 @@ def parse():
                     help="wall-clock budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--only", choices=["all", "fwd", "decode", "bwd", "kda"], default="all")
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--fwd-workloads", default="all",
+                    help="comma-separated forward workloads to time (train_1p3b, the headline; "
+                         "tiny_fp32, long_ctx, varlen_packed), or 'all'; profiling runs name one")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run plain device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -485,47 +488,52 @@ def main():
         calib_copy(torch, args.calib_copy_mb)
     if args.only in ("all", "fwd"):
         wl = {}
-        # the headline: the training shape over 4 rotating input sets (beyond the Infinity Cache)
-        f1 = bench_forward(1, args.steps, args.warmup, 4, torch, gb, SY)
-        r1 = forward_report(f1)
-        wl["train_1p3b"] = r1
-        out["value"] = r1["tokens_per_s"]
-        out["ms_per_step"] = r1["ms_per_call"]
-        out["mfma_frac"] = r1["mfma_frac"]
-        out["tflops"] = r1["tflops"]
-        out["hbm_frac_algorithmic"] = r1["hbm_frac"]
-        out["ms_per_step_events"] = r1["ms_per_call_events"]
-        out["forward_call_roofline"] = r1["call_roofline"]
-        prep, prop = pcts(f1["prep_ms"])["median"], pcts(f1["prop_ms"])["median"]
-        out["stages_ms"] = {"chunk_prepare_median": prep, "chunk_propagate_median": prop,
-                            "chunk_prepare_mean": sum(f1["prep_ms"]) / len(f1["prep_ms"]),
-                            "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
-        c = fwd_counts(f1["dk"], f1["dv"])
-        th = f1["tokens"] * f1["H"]
-        mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
-        if mean_prop >= mean_prep:
-            ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
-            out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
-                               "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                               "frac": ach / PEAK_HBM_BPS,
-                               "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
-                               "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
-        else:
-            ach = c["stage1_flops"] * th / (mean_prep / 1e3)
-            out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
-                               "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
-                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
-                               "traffic": measured_traffic("chunk_prepare_kernel"),
-                               "algorithmic_flops_per_launch": c["stage1_flops"] * th}
+        names = {w.name: i for i, w in SY.WORKLOADS.items() if i != 4}
+        want = set(names.values()) if args.fwd_workloads == "all" else {names[n] for n in args.fwd_workloads.split(",")}
+        if 1 in want:
+            # the headline: the training shape over 4 rotating input sets (beyond the Infinity Cache)
+            f1 = bench_forward(1, args.steps, args.warmup, 4, torch, gb, SY)
+            r1 = forward_report(f1)
+            wl["train_1p3b"] = r1
+            out["value"] = r1["tokens_per_s"]
+            out["ms_per_step"] = r1["ms_per_call"]
+            out["mfma_frac"] = r1["mfma_frac"]
+            out["tflops"] = r1["tflops"]
+            out["hbm_frac_algorithmic"] = r1["hbm_frac"]
+            out["ms_per_step_events"] = r1["ms_per_call_events"]
+            out["forward_call_roofline"] = r1["call_roofline"]
+            prep, prop = pcts(f1["prep_ms"])["median"], pcts(f1["prop_ms"])["median"]
+            out["stages_ms"] = {"chunk_prepare_median": prep, "chunk_propagate_median": prop,
+                                "chunk_prepare_mean": sum(f1["prep_ms"]) / len(f1["prep_ms"]),
+                                "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
+            c = fwd_counts(f1["dk"], f1["dv"])
+            th = f1["tokens"] * f1["H"]
+            mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
+            if mean_prop >= mean_prep:
+                ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
+                out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
+                                   "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                                   "frac": ach / PEAK_HBM_BPS,
+                                   "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
+                                   "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
+            else:
+                ach = c["stage1_flops"] * th / (mean_prep / 1e3)
+                out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
+                                   "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                                   "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
+                                   "traffic": measured_traffic("chunk_prepare_kernel"),
+                                   "algorithmic_flops_per_launch": c["stage1_flops"] * th}
         # the other forward workloads, one input set each (each exceeds the Infinity Cache but
         # the tiny one, which is latency-bound anyway)
         for wid, steps in ((0, args.steps), (2, max(5, args.steps // 3)), (3, max(5, args.steps // 3))):
-            f = bench_forward(wid, steps, min(args.warmup, 3), 1, torch, gb, SY)
-            wl[SY.WORKLOADS[wid].name] = forward_report(f)
-        t1 = wl["train_1p3b"]["ms_per_call"] / (f1["tokens"] * f1["H"])
-        lw = wl["long_ctx"]
-        t2 = lw["ms_per_call"] / (lw["tokens"] * 16)
-        out["long_vs_train_time_per_token_head"] = t2 / t1
+            if wid in want:
+                f = bench_forward(wid, steps, min(args.warmup, 3), 1, torch, gb, SY)
+                wl[SY.WORKLOADS[wid].name] = forward_report(f)
+        if "long_ctx" in wl and "train_1p3b" in wl:
+            t1 = wl["train_1p3b"]["ms_per_call"] / (wl["train_1p3b"]["tokens"] * 16)
+            lw = wl["long_ctx"]
+            t2 = lw["ms_per_call"] / (lw["tokens"] * 16)
+            out["long_vs_train_time_per_token_head"] = t2 / t1
         out["workloads"] = wl
     if args.only in ("all", "decode"):
         d = bench_decode(args, torch, gb, SY)
@@ -605,10 +613,12 @@ def main():
             out["ms_per_step"] = k["fwd_ms"]
     if args.cpu_seconds > 0 and args.only in ("all", "fwd"):
         # the headline's oracle gets the budget, the other workloads a fifth of it each
-        out["cpu_baseline"] = cpu_forward(1, args.cpu_seconds)
-        out["workloads"]["train_1p3b"]["cpu_baseline"] = out["cpu_baseline"]
+        if "train_1p3b" in out["workloads"]:
+            out["cpu_baseline"] = cpu_forward(1, args.cpu_seconds)
+            out["workloads"]["train_1p3b"]["cpu_baseline"] = out["cpu_baseline"]
         for wid in (0, 2, 3):
-            out["workloads"][SY.WORKLOADS[wid].name]["cpu_baseline"] = cpu_forward(wid, args.cpu_seconds / 5)
+            if SY.WORKLOADS[wid].name in out["workloads"]:
+                out["workloads"][SY.WORKLOADS[wid].name]["cpu_baseline"] = cpu_forward(wid, args.cpu_seconds / 5)
     if args.cpu_seconds > 0 and args.only in ("all", "decode"):
         out["workloads"]["decode"]["cpu_baseline"] = cpu_decode(args.cpu_seconds / 5)
     print(json.dumps(out), flush=True)
