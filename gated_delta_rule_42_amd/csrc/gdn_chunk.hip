@@ -672,15 +672,21 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 //   SEG = 1: one work-group per (pair, tile, segment); segment 0 starts from h0, the others
 //     from a zero state. Each records its final state in p.segst, segments past the first also
 //     their states at segment offsets 1, 2, 4, .., and writes o for all its chunks.
-//   SEG = 2: one work-group per (pair, tile) walks segments 1, 2, .. in order from the true
-//     state entering each. After the chunk that ends at a recorded offset it compares its
-//     state with the one SEG = 1 recorded there, bit for bit; once they are equal, every later
-//     chunk of the segment computed in SEG = 1 saw exactly the state this walk would give it
-//     (the chunk step is a fixed function of its inputs), so the walk rewrites o only up to
-//     that point and takes the segment's final state from p.segst. Without a match it runs to
-//     the segment's end. Both ways o and hT equal those of the unsplit kernel bit for bit; the
-//     saving comes from decay: a segment's dependence on its entering state shrinks by the
-//     product of its gates, and once that falls under fp32 rounding the two states agree.
+//   SEG = 2: one work-group per (pair, tile, segment g >= 1) reruns segment g from the final
+//     state SEG = 1 left for segment g-1. After the chunk that ends at a recorded offset it
+//     compares its state with the one SEG = 1 recorded there, bit for bit; once they are equal,
+//     every later chunk of the segment computed in SEG = 1 saw exactly the state this rerun
+//     would give it (the chunk step is a fixed function of its inputs), so the rerun rewrites o
+//     only up to that point. Without a match it runs to the segment's end and keeps its final
+//     state. It counts the chunks it computed (fewer than the segment's length: it matched).
+//   SEG = 3: one work-group per (pair, tile) walks the segments in order. Segment g's SEG = 2
+//     rerun started from the true state when every segment before it matched (then the final
+//     state of g-1 is the one SEG = 1 left); the walk accepts those, and from the first segment
+//     that did not match it carries the true state itself and reruns the following segments as
+//     SEG = 2 does, until one matches again. It writes hT.
+//   o and hT equal those of the unsplit kernel bit for bit. The saving comes from decay: a
+//   segment's dependence on its entering state shrinks by the product of its gates, and once
+//   that falls under fp32 rounding the two states agree and all segments are fixed at once.
 template <typename TO, int DK, int DV, int DVT, int SEG>
 __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
     using KQ = KQChunk<DK>;
@@ -691,7 +697,8 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
     constexpr int NTILE = DV / DVT;
     __shared__ KQ kq[2];
     __shared__ MPV mpv[3];
-    __shared__ int match[2][NW];   // SEG = 2: per compute wave, state equal to the record (by chunk parity)
+    __shared__ int match[2][NW];   // SEG >= 2: per compute wave, state equal to the record (by chunk parity)
+    constexpr bool CMP = SEG >= 2;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -701,7 +708,7 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
     // work unit (pair, or pair and segment) and column tile; with a unit count divisible by 8
     // the tiles of one unit get block ids equal modulo 8 (same XCD, shared L2 for K, Q, Mmat and P)
     const long NP = (long)p.N * H;
-    const long NU = SEG == 1 ? NP * p.seg_n : NP;
+    const long NU = SEG == 1 ? NP * p.seg_n : SEG == 2 ? NP * (p.seg_n - 1) : NP;
     const long bid = blockIdx.x;
     long unit;
     int tile;
@@ -713,8 +720,8 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         unit = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
-    const long pair = SEG == 1 ? unit / p.seg_n : unit;
-    const int seg = SEG == 1 ? (int)(unit % p.seg_n) : 0;
+    const long pair = SEG == 1 ? unit / p.seg_n : SEG == 2 ? unit / (p.seg_n - 1) : unit;
+    const int seg = SEG == 1 ? (int)(unit % p.seg_n) : SEG == 2 ? 1 + (int)(unit % (p.seg_n - 1)) : 0;
     const int n = (int)(pair / H), h = (int)(pair % H);
     const int dv0 = tile * DVT;
 
@@ -732,19 +739,22 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         c0 = (long)g * p.seg_len;
         len = max(0L, min((long)p.seg_len, nchunks - c0));
     };
-    long c_first = 0, c_count = nchunks;   // SEG 0, 1: the work-group's one range
-    if constexpr (SEG == 1) {
+    long c_first = 0, c_count = nchunks;   // SEG 0, 1, 2: the work-group's one range
+    if constexpr (SEG == 1 || SEG == 2) {
         seg_range(seg, c_first, c_count);
         if (seg > 0 && c_count == 0) return;   // the whole work-group leaves
     }
-    // p.segst slot of (segment g, recorded offset or final state) for this pair
-    const int nslot = p.seg_ncp + 1;
+    // p.segst slot of (segment g, recorded offset, SEG = 1's final state (slot ncp) or SEG = 2's
+    // final state without a match (slot ncp + 1)) for this pair
+    const int nslot = p.seg_ncp + 2;
+    // after the state records: per (pair, tile, segment) the chunks SEG = 2 computed (int32)
+    int* reran = reinterpret_cast<int*>(p.segst + NP * p.seg_n * nslot * (long)DV * DK) + (pair * NTILE + tile) * p.seg_n;
     auto seg_state = [&](int g, int slot) { return p.segst + ((pair * p.seg_n + g) * nslot + slot) * (long)DV * DK; };
-    // a range ends at the barrier after its last chunk, or (SEG = 2) at the barrier after a chunk
+    // a range ends at the barrier after its last chunk, or (SEG >= 2) at the barrier after a chunk
     // whose end state matched the record; all waves read the same flags after the same barrier
     auto range_done = [&](int i, long len) {
         if (i == len) return true;
-        if constexpr (SEG == 2) {
+        if constexpr (CMP) {
             if (i > 0) {
                 bool all = true;
 #pragma unroll
@@ -761,7 +771,7 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         // ------------------------------------------------------------------- DMA wave
         // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2). Loads complete
         // in issue order, so at the top of chunk c only MPV(c+1) may still be in flight.
-        auto run = [&](long c0, long len) {
+        auto run = [&](long c0, long len) -> int {
             auto mpv_copy = [&](int i) {
                 const long jc = c0 + i;
                 copy_mpv<DK, DV, DVT>(mpv[i % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
@@ -776,18 +786,25 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
                 if (i + 1 < len) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 lds_barrier();  // chunk i's operands are in LDS; chunk i-1's buffers are free
-                if (range_done(i, len)) break;
+                if (range_done(i, len)) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // copies of an abandoned chunk
+                    return i;
+                }
                 if (i + 1 < len) copy_kq<DK>(kq[(i + 1) & 1], p, (cbase + c0 + i + 1) * H + h, lane);
                 if (i + 2 < len) mpv_copy(i + 2);
             }
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // copies of an abandoned chunk
         };
-        if constexpr (SEG == 2) {
+        if constexpr (SEG == 3) {   // the same walk as the compute waves'
+            bool ok = true;
             for (int g = 1; g < p.seg_n; ++g) {
                 long c0, len;
                 seg_range(g, c0, len);
                 if (len == 0) break;
-                run(c0, len);
+                if (ok) {
+                    ok = reran[g] < len;
+                    continue;
+                }
+                ok = run(c0, len) < len;
             }
         } else {
             run(c_first, c_count);
@@ -811,8 +828,8 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
             *reinterpret_cast<float4*>(dst + scol + 16 * j) = make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
     };
     if (SEG == 2) {
-        load_state(seg_state(0, p.seg_ncp));
-    } else if (p.h0 && seg == 0) {
+        load_state(seg_state(seg - 1, p.seg_ncp));
+    } else if (p.h0 && seg == 0 && SEG != 3) {   // SEG = 3 loads states where its walk needs them
         load_state(p.h0 + pair * DV * DK);
     } else {
 #pragma unroll
@@ -945,7 +962,7 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
     };
 
     // runs chunks c0 .. of the range and returns how many it computed (fewer than len: it
-    // stopped at a matching record, SEG = 2)
+    // stopped at a matching record, SEG >= 2)
     auto run = [&](long c0, long len, int g) {
         for (int i = 0;; ++i) {
             lds_barrier();  // chunk i's operands are in LDS
@@ -964,7 +981,7 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
             if constexpr (SEG == 1) {   // the walk never compares in segment 0
                 if (g > 0 && recorded(off, len)) store_state(seg_state(g, 31 - __builtin_clz(off)));
             }
-            if constexpr (SEG == 2) {
+            if constexpr (CMP) {
                 bool same = false;
                 if (recorded(off, len)) {
                     const float* rec = seg_state(g, 31 - __builtin_clz(off));
@@ -982,25 +999,34 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         }
     };
 
-    if constexpr (SEG == 2) {
-        // after the state records: per (pair, tile, segment) the number of chunks this walk
-        // computed, an int32 diagnostic
-        int* reran = reinterpret_cast<int*>(p.segst + NP * p.seg_n * nslot * (long)DV * DK) +
-                     (pair * NTILE + tile) * p.seg_n;
+    if constexpr (SEG == 3) {
+        // ok: the state SEG = 2 started segment g from was the true one; otherwise ST holds the
+        // true state entering segment g
+        bool ok = true;
+        int glast = 0;
         for (int g = 1; g < p.seg_n; ++g) {
             long c0, len;
             seg_range(g, c0, len);
             if (len == 0) break;
-            const int m = run(c0, len, g);
-            if (m < len) load_state(seg_state(g, p.seg_ncp));
-            if (wave == 0 && lane == 0) reran[g] = m;
+            glast = g;
+            if (ok) {   // the same test as the DMA wave's: both take the same barriers
+                ok = reran[g] < len;
+                if (!ok) load_state(seg_state(g, p.seg_ncp + 1));   // no match: SEG = 2's final state is the true one
+                continue;
+            }
+            ok = run(c0, len, g) < len;   // matched: the true final state is SEG = 1's
         }
+        if (ok) load_state(seg_state(glast, p.seg_ncp));
     } else {
-        run(c_first, c_count, seg);
+        const int m = run(c_first, c_count, seg);
+        if constexpr (SEG == 2) {
+            if (m == c_count) store_state(seg_state(seg, p.seg_ncp + 1));
+            if (wave == 0 && lane == 0) reran[seg] = m;
+        }
     }
     if constexpr (SEG == 1) {
         store_state(seg_state(seg, p.seg_ncp));
-    } else if (p.hT) {
+    } else if (SEG != 2 && p.hT) {
         store_state(p.hT + pair * DV * DK);
     }
 }
@@ -1063,7 +1089,7 @@ SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16) {
     sp.n = (int)n;
     sp.len = (int)len;
     while ((1L << sp.ncp) < len) ++sp.ncp;   // offsets 1, 2, 4, .. below len
-    sp.bytes = (size_t)N * H * n * ((sp.ncp + 1) * dv * dk * sizeof(float)) + (size_t)tiles * n * sizeof(int32_t);
+    sp.bytes = (size_t)N * H * n * ((sp.ncp + 2) * dv * dk * sizeof(float)) + (size_t)tiles * n * sizeof(int32_t);
     return sp;
 }
 
@@ -1104,9 +1130,10 @@ static hipError_t prop_launch_bf16(const ChunkProblem& p, hipStream_t s) {
     const long blocks = (long)p.N * p.H * (DV / DVT);
     const dim3 block((DVT / 16 + 1) * 64);
     if (p.seg_n <= 1) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0>, dim3((unsigned)blocks), block, s, p);
-    const hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>,
-                                dim3((unsigned)(blocks * p.seg_n)), block, s, p);
-    return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 2>, dim3((unsigned)blocks), block, s, p);
+    hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>, dim3((unsigned)(blocks * p.seg_n)), block, s, p);
+    if (e == hipSuccess)
+        e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 2>, dim3((unsigned)(blocks * (p.seg_n - 1))), block, s, p);
+    return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 3>, dim3((unsigned)blocks), block, s, p);
 }
 
 template <typename TIn, typename TO, int DK, int DV>

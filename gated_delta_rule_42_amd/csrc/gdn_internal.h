@@ -82,9 +82,9 @@ struct ChunkProblem {
     const float* write;
     // long-chain split of the bf16 state propagation (seg_n > 1): the chunks of a sequence are
     // cut into segments of seg_len chunks; segst holds, per (sequence, head) and segment, the
-    // states at segment offsets 1, 2, 4, .. < seg_len (seg_ncp of them) and the segment's
-    // final state, each [dv, dk] fp32; then int32 [N*H, max(1, dv/64), seg_n], the chunks the
-    // sequential pass recomputed per segment (a diagnostic)
+    // states at segment offsets 1, 2, 4, .. < seg_len (seg_ncp of them), the first pass's final
+    // state and the second pass's final state, each [dv, dk] fp32; then int32
+    // [N*H, max(1, dv/64), seg_n], the chunks the second pass recomputed per segment
     int seg_n, seg_len, seg_ncp;
     float* segst;
 };

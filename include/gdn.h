@@ -109,11 +109,15 @@ const char *gdn_status_string(int status);
  * segments, each at least 16 chunks; the longest possible sequence, ceil(T/64) chunks, sets the
  * count). All segments run at once, segment 0 from h0 and the others from zero, recording
  * their final states and (segments past the first) their states at segment offsets 1, 2, 4, ..
- * below sl (`ncp` of them); a second pass walks the segments in order from the true entering
- * state and stops recomputing a segment at the first recorded offset where its state equals
- * the record bit for bit. o and hT are bitwise those of the unsplit pass. The workspace then
- * ends with one more region:
- *   states      fp32  [N, H, ns, ncp + 1, dv, dk]   the recorded states, then the final one
+ * below sl (`ncp` of them). A second pass reruns every segment at once from the final state
+ * the first pass left for the segment before it, and stops at the first recorded offset where
+ * its state equals the record bit for bit; a third walks the segments in order, accepts the
+ * reruns whose starting state was the true one (every earlier segment matched) and recomputes
+ * the rest from the true state. o and hT are bitwise those of the unsplit pass. The workspace
+ * then ends with one more region:
+ *   states      fp32  [N, H, ns, ncp + 2, dv, dk]   the recorded states, the first pass's final
+ *                                                   state, the second pass's final state
+ *                                                   (segments it did not match)
  *   reran       int32 [N, H, max(1, dv/64), ns]     chunks the second pass computed for each
  *                                                   segment s >= 1 of each 64-column tile
  *                                                   (a diagnostic; unset for segments past

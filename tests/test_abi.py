@@ -90,7 +90,7 @@ def _fwd_base_bytes(B, T, H, d):
 
 def _seg_bytes(N, H, d, ns, sl):
     ncp = (sl - 1).bit_length()   # offsets 1, 2, 4, .. below sl
-    return N * H * ns * (ncp + 1) * d * d * 4 + N * H * max(1, d // 64) * ns * 4
+    return N * H * ns * (ncp + 2) * d * d * 4 + N * H * max(1, d // 64) * ns * 4
 
 
 def test_segment_plan_workspace(L, monkeypatch):
