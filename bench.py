@@ -136,11 +136,23 @@ def pcts(xs):
     return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
 
 
+def fwd_path(N, H, dk, dv, dtype):
+    """The path gdn_chunk_fwd takes for a shape, by the library's own rule: the one-kernel
+    forward for bf16 inputs with d_k = d_v = 128 and fewer than 64 (sequence, head) pairs, the
+    two stages (gdn_chunk_prepare, gdn_chunk_propagate) otherwise; GDN_FUSED=0/1 forces it."""
+    if dtype != "bf16" or dk != 128 or dv != 128:
+        return "staged"
+    env = os.environ.get("GDN_FUSED")
+    if env is not None:
+        return "fused" if int(env) != 0 else "staged"
+    return "fused" if N * H < 64 else "staged"
+
+
 def bench_forward(wid, steps, warmup, nsets, torch, gb, SY):
-    """gdn_chunk_prepare + gdn_chunk_propagate on forward workload `wid` (o in the input
-    dtype), nsets rotating input sets: `steps` back-to-back calls timed by the wall clock, then
-    as many calls (at least 10) each bracketed by HIP events on the launch stream for the
-    per-call and per-stage distributions."""
+    """gdn_chunk_fwd on forward workload `wid` (o in the input dtype), nsets rotating input sets:
+    `steps` back-to-back calls timed by the wall clock, then as many calls (at least 10) each
+    bracketed by HIP events on the launch stream. When the call runs the two stages, they are
+    also timed as gdn_chunk_prepare + gdn_chunk_propagate (checked equal to the call first)."""
     w = SY.WORKLOADS[wid]
     dev = torch.device("cuda:0")
     sets = []
@@ -156,40 +168,52 @@ def bench_forward(wid, steps, warmup, nsets, torch, gb, SY):
     cu0 = sets[0]["cu_seqlens"]
     need = gb.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, cu0 is not None, dtype=sets[0]["q"].dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    path = fwd_path(N, H, dk, dv, w.dtype)
 
-    def step(t, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def call(t):
+        gb.gdn_chunk_fwd(*(t[n] for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")), o=t["o"], hT=t["hT"],
+                         workspace=ws)
+
+    def stages(t, ev):
+        ev[0].record()
         gb.gdn_chunk_prepare(t["q"], t["k"], t["g"], t["beta"], ws, t["cu_seqlens"], dv=dv)
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         gb.gdn_chunk_propagate(t["q"], t["k"], t["v"], ws, t["h0"], t["cu_seqlens"], o=t["o"], hT=t["hT"])
-        if ev is not None:
-            ev[2].record()
-
-    # the two stage calls are exactly gdn_chunk_fwd
-    step(sets[0])
-    o_ref, h_ref = gb.gdn_chunk_fwd(*(sets[0][n] for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")),
-                                    o_dtype=sets[0]["q"].dtype)
-    torch.cuda.synchronize()
-    assert torch.equal(o_ref, sets[0]["o"]) and torch.equal(h_ref, sets[0]["hT"])
+        ev[2].record()
 
     for i in range(warmup):
-        step(sets[i % nsets])
+        call(sets[i % nsets])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(sets[i % nsets])
+        call(sets[i % nsets])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(10, steps))]
+    n_ev = max(10, steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
     for i, e in enumerate(evs):
-        step(sets[i % nsets], e)
+        e[0].record()
+        call(sets[i % nsets])
+        e[1].record()
     torch.cuda.synchronize()
-    return dict(wid=wid, name=w.name, B=B, T=T, H=H, dk=dk, dv=dv, N=N, dtype=w.dtype,
-                h0=sets[0]["h0"] is not None, tokens=B * T, ms=wall / steps * 1e3, steps=steps,
-                call_ms=[e[0].elapsed_time(e[2]) for e in evs], prep_ms=[e[0].elapsed_time(e[1]) for e in evs],
-                prop_ms=[e[1].elapsed_time(e[2]) for e in evs])
+    out = dict(wid=wid, name=w.name, B=B, T=T, H=H, dk=dk, dv=dv, N=N, dtype=w.dtype, path=path,
+               h0=sets[0]["h0"] is not None, tokens=B * T, ms=wall / steps * 1e3, steps=steps,
+               call_ms=[e[0].elapsed_time(e[1]) for e in evs], prep_ms=None, prop_ms=None)
+    if path == "staged":
+        # the two stage calls are exactly gdn_chunk_fwd on this path
+        t = sets[0]
+        call(t)
+        o_ref, h_ref = t["o"].clone(), t["hT"].clone()
+        stages(t, [torch.cuda.Event() for _ in range(3)])
+        torch.cuda.synchronize()
+        assert torch.equal(o_ref, t["o"]) and torch.equal(h_ref, t["hT"])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+        for i, e in enumerate(evs):
+            stages(sets[i % nsets], e)
+        torch.cuda.synchronize()
+        out["prep_ms"] = [e[0].elapsed_time(e[1]) for e in evs]
+        out["prop_ms"] = [e[1].elapsed_time(e[2]) for e in evs]
+    return out
 
 
 def forward_report(f):
@@ -212,8 +236,10 @@ def forward_report(f):
             "mfma_frac": flops / sec / peak, "mfma_peak_tflops": peak / 1e12,
             "hbm_GBps_algorithmic": byts / sec / 1e9, "hbm_frac": byts / sec / PEAK_HBM_BPS,
             "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": byts,
-            "stages_ms_median": {"chunk_prepare": pcts(f["prep_ms"])["median"],
-                                 "chunk_propagate": pcts(f["prop_ms"])["median"]},
+            "path": ("two stages (gdn_chunk_prepare, gdn_chunk_propagate)" if f["path"] == "staged"
+                     else "one kernel (chunk_fused_kernel)"),
+            "stages_ms_median": ({"chunk_prepare": pcts(f["prep_ms"])["median"],
+                                  "chunk_propagate": pcts(f["prop_ms"])["median"]} if f["prep_ms"] else None),
             "call_roofline": {"bound": "hbm" if hbm_bound else "mfma",
                               "achieved": byts / sec / 1e9 if hbm_bound else flops / sec / 1e12,
                               "peak": PEAK_HBM_BPS / 1e9 if hbm_bound else peak / 1e12,
@@ -502,27 +528,37 @@ def main():
             out["hbm_frac_algorithmic"] = r1["hbm_frac"]
             out["ms_per_step_events"] = r1["ms_per_call_events"]
             out["forward_call_roofline"] = r1["call_roofline"]
-            prep, prop = pcts(f1["prep_ms"])["median"], pcts(f1["prop_ms"])["median"]
-            out["stages_ms"] = {"chunk_prepare_median": prep, "chunk_propagate_median": prop,
-                                "chunk_prepare_mean": sum(f1["prep_ms"]) / len(f1["prep_ms"]),
-                                "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
+            out["forward_path"] = r1["path"]
             c = fwd_counts(f1["dk"], f1["dv"])
             th = f1["tokens"] * f1["H"]
-            mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
-            if mean_prop >= mean_prep:
-                ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
-                out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
+            if f1["path"] == "fused":
+                # one kernel family per call: the call's events time it
+                mean_call = sum(f1["call_ms"]) / len(f1["call_ms"])
+                ach = c["bytes"] * th / (mean_call / 1e3)
+                out["roofline"] = {"kernel": "chunk_fused_kernel", "bound": "hbm",
                                    "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                                   "frac": ach / PEAK_HBM_BPS,
-                                   "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
-                                   "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
+                                   "frac": ach / PEAK_HBM_BPS, "traffic": measured_traffic("chunk_fused_kernel"),
+                                   "algorithmic_bytes_per_launch": c["bytes"] * th}
             else:
-                ach = c["stage1_flops"] * th / (mean_prep / 1e3)
-                out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
-                                   "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
-                                   "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
-                                   "traffic": measured_traffic("chunk_prepare_kernel"),
-                                   "algorithmic_flops_per_launch": c["stage1_flops"] * th}
+                out["stages_ms"] = {"chunk_prepare_median": pcts(f1["prep_ms"])["median"],
+                                    "chunk_propagate_median": pcts(f1["prop_ms"])["median"],
+                                    "chunk_prepare_mean": sum(f1["prep_ms"]) / len(f1["prep_ms"]),
+                                    "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
+                mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
+                if mean_prop >= mean_prep:
+                    ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
+                    out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
+                                       "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                                       "frac": ach / PEAK_HBM_BPS,
+                                       "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
+                                       "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
+                else:
+                    ach = c["stage1_flops"] * th / (mean_prep / 1e3)
+                    out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
+                                       "achieved": ach / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                                       "unit": "TFLOP/s", "frac": ach / PEAK_BF16_FLOPS,
+                                       "traffic": measured_traffic("chunk_prepare_kernel"),
+                                       "algorithmic_flops_per_launch": c["stage1_flops"] * th}
         # the other forward workloads, one input set each (each exceeds the Infinity Cache but
         # the tiny one, which is latency-bound anyway)
         for wid, steps in ((0, args.steps), (2, max(5, args.steps // 3)), (3, max(5, args.steps // 3))):

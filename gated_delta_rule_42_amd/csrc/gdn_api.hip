@@ -194,6 +194,8 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* g_log_al
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = debug_check_offsets(cu_seqlens, N, T, s);
     if (st != GDN_OK) return st;
+    if (gdn::fused_wanted(p.N, p.H, p.dk, p.dv, p.bf16))
+        return gdn::launch_chunk_fused(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     if (gdn::launch_chunk_prepare(p, s) != hipSuccess) return GDN_ERR_HIP;
     if (gdn::launch_chunk_propagate(p, s) != hipSuccess) return GDN_ERR_HIP;
     return GDN_OK;

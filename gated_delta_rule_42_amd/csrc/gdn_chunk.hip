@@ -1061,6 +1061,9 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
 // work-groups on a 256-CU gfx950 part, with segments of at least kSegMinChunks chunks.
 constexpr int kSegTargetGroups = 256;
 constexpr int kSegMinChunks = 16;
+// the one-kernel forward (d_k = d_v = 128) splits down to 8-chunk segments: its fix-up passes
+// cost about one chunk's work per segment
+constexpr int kFusedMinChunks = 8;
 
 static long tiles_of(int N, int H, int dv, int cols) { return (long)N * H * (dv > cols ? dv / cols : 1); }
 
@@ -1078,6 +1081,11 @@ SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16) {
     if (const char* env = std::getenv("GDN_SEGMENT_CHUNKS")) {
         len = std::atol(env);
         if (len <= 0) return sp;
+    } else if (fused_wanted(N, H, dk, dv, bf16)) {   // the one-kernel forward: one work-group per pair
+        const long pairs = (long)N * H;
+        const long g = std::min((long)kSegTargetGroups / pairs, nmax / kFusedMinChunks);
+        if (g < 2) return sp;
+        len = (nmax + g - 1) / g;
     } else {
         if (prop_cols(N, H, dv) != 64) return sp;
         const long g = std::min((long)kSegTargetGroups / tiles, nmax / kSegMinChunks);

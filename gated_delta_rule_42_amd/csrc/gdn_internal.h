@@ -144,6 +144,11 @@ struct SegPlan {
 SegPlan segment_plan(int T, int H, int dk, int dv, int N, int bf16);
 
 hipError_t launch_chunk_base(const ChunkProblem& p, hipStream_t s);   // chunk_base (packed only)
+// The one-kernel forward (gdn_fused.hip): whether gdn_chunk_fwd takes it for a shape (bf16
+// inputs, d_k = d_v = 128, fewer than 64 (sequence, head) pairs; GDN_FUSED=0 or 1 in the
+// environment forces the choice for the shapes it supports), and its launch
+bool fused_wanted(int N, int H, int dk, int dv, int bf16);
+hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s);
 hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s);

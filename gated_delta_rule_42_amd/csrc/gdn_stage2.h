@@ -103,4 +103,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same without the fences, whose release half makes the compiler wait for every outstanding
+// vector memory operation of the wave, global loads and stores included: this barrier waits for
+// the wave's LDS accesses only and keeps the compiler from moving memory accesses across it. For
+// kernels that copy nothing into LDS; their global loads are waited for where used.
+__device__ __forceinline__ void lds_barrier_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace gdn

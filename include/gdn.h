@@ -45,6 +45,9 @@
  *    of the long-chain split of the bf16 forward pass to L chunks; 0 turns the split off.
  *    Without it the split is chosen from the shape (see gdn_chunk_fwd_workspace_bytes). The
  *    setting must not change between a workspace size query and the call that uses it.
+ *  - GDN_FUSED=0 or 1 in the environment (for tests and tuning) forces gdn_chunk_fwd's path for
+ *    bf16 inputs with dk = dv = 128: 0 the two stages, 1 the one-kernel forward (see
+ *    gdn_chunk_fwd). It also selects the split plan, so the same rule about size queries holds.
  *  - Alignment: q, k, v, o, h0, hT and the decode state 16 bytes; g, beta and cu_seqlens
  *    4 bytes; the workspace 256 bytes. A misaligned pointer gives GDN_ERR_ALIGN.
  */
@@ -107,7 +110,9 @@ const char *gdn_status_string(int status);
  * neither fills the device (N*H*(dv/64) at most 128) and a sequence can span at least 32
  * chunks, it cuts every sequence into `ns` segments of `sl` chunks (about 256 / (N*H*dv/64)
  * segments, each at least 16 chunks; the longest possible sequence, ceil(T/64) chunks, sets the
- * count). All segments run at once, segment 0 from h0 and the others from zero, recording
+ * count). The one-kernel forward (see gdn_chunk_fwd) runs one work-group per (sequence, head)
+ * and aims at about 256 / (N*H) segments of at least 8 chunks instead (a sequence that can span
+ * 16 chunks or more). All segments run at once, segment 0 from h0 and the others from zero, recording
  * their final states and (segments past the first) their states at segment offsets 1, 2, 4, ..
  * below sl (`ncp` of them). A second pass reruns every segment at once from the final state
  * the first pass left for the segment before it, and stops at the first recorded offset where
@@ -129,7 +134,13 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
 /*
  * Chunkwise-parallel forward pass (WY representation / UT transform carrying the
  * gate): computes o for every token and, optionally, the final state of every
- * sequence. Equals gdn_chunk_prepare followed by gdn_chunk_propagate on `stream`.
+ * sequence. Runs gdn_chunk_prepare followed by gdn_chunk_propagate on `stream` (bitwise the
+ * same results), except for bf16 inputs with dk = dv = 128 and fewer than 64 (sequence, head)
+ * pairs (or under GDN_FUSED=1): there one kernel builds each chunk's operators in LDS one chunk
+ * ahead of the state propagation, reading q, k, v, g and beta once and writing only o, hT and
+ * (long chains) the split's records. The two paths compute the same products in a different
+ * order and agree to rounding; the stage-1 regions of the workspace are left untouched by the
+ * one-kernel path.
  *
  *   q, k        [B, T, H, dk]  dtype                     (required)
  *   v           [B, T, H, dv]  dtype                     (required)

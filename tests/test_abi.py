@@ -94,32 +94,46 @@ def _seg_bytes(N, H, d, ns, sl):
 
 
 def test_segment_plan_workspace(L, monkeypatch):
-    """The long-chain split's plan, read from the workspace size: the long-context shape
-    (B1 H16 T32768 d128 bf16: 32 tiles of 64 columns) gets 8 segments of 64 chunks (6 records
-    each); B2 H16 T2048 (64 tiles of 64 columns, 128 of 32) 2 of 16; the training shape
-    (B4 H16 T2048: 256 tiles of 32 columns), 256 tiles of 64 columns and fp32 inputs get none;
+    """The long-chain split's plan, read from the workspace size.
+
+    Two-stage path (GDN_FUSED=0, and the default from 64 (sequence, head) pairs on): about 256
+    work-groups of 64-column tiles with segments of at least 16 chunks, so the long-context shape
+    (B1 H16 T32768 d128 bf16: 32 tiles) gets 8 segments of 64 chunks (6 records each), B2 H16
+    T2048 (64 tiles) 2 of 16, the training shape (B4 H16 T2048: 256 tiles of 32 columns) and
+    B8 none. One-kernel path (bf16 d128, the default below 64 pairs, GDN_FUSED=1): one
+    work-group per pair, segments of at least 8 chunks: the long-context shape gets 16 of 32,
+    B2 H16 T2048 4 of 8 and, forced, the training shape 4 of 8. fp32 inputs are never split;
     GDN_SEGMENT_CHUNKS forces a length or turns the split off."""
     import torch
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     monkeypatch.delenv("GDN_SEGMENT_CHUNKS", raising=False)
-    base = _fwd_base_bytes(1, 32768, 16, 128)
-    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == al(base) + _seg_bytes(1, 16, 128, 8, 64)
-    base = _fwd_base_bytes(2, 2048, 16, 128)
-    assert gb.gdn_chunk_fwd_workspace_bytes(2, 2048, 16, 128, 128, 2, False) == al(base) + _seg_bytes(2, 16, 128, 2, 16)
+    monkeypatch.delenv("GDN_FUSED", raising=False)
+    ws = gb.gdn_chunk_fwd_workspace_bytes
+    # default paths: one kernel for the long-context shape and B2, two stages for B4 and B8
+    assert ws(1, 32768, 16, 128, 128, 1, False) == al(_fwd_base_bytes(1, 32768, 16, 128)) + _seg_bytes(1, 16, 128, 16, 32)
+    assert ws(2, 2048, 16, 128, 128, 2, False) == al(_fwd_base_bytes(2, 2048, 16, 128)) + _seg_bytes(2, 16, 128, 4, 8)
     for B in (4, 8):
-        assert gb.gdn_chunk_fwd_workspace_bytes(B, 2048, 16, 128, 128, B, False) == _fwd_base_bytes(B, 2048, 16, 128)
-    f32 = gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False, dtype=torch.float32)
-    assert f32 == gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 256, 128, 128, 1, False, dtype=torch.float32) // 16
+        assert ws(B, 2048, 16, 128, 128, B, False) == _fwd_base_bytes(B, 2048, 16, 128)
+    monkeypatch.setenv("GDN_FUSED", "0")
+    assert ws(1, 32768, 16, 128, 128, 1, False) == al(_fwd_base_bytes(1, 32768, 16, 128)) + _seg_bytes(1, 16, 128, 8, 64)
+    assert ws(2, 2048, 16, 128, 128, 2, False) == al(_fwd_base_bytes(2, 2048, 16, 128)) + _seg_bytes(2, 16, 128, 2, 16)
+    monkeypatch.setenv("GDN_FUSED", "1")
+    assert ws(4, 2048, 16, 128, 128, 4, False) == al(_fwd_base_bytes(4, 2048, 16, 128)) + _seg_bytes(4, 16, 128, 4, 8)
+    # fewer than 16 chunks: no split on the one-kernel path
+    assert ws(1, 15 * 64, 2, 128, 128, 1, False) == _fwd_base_bytes(1, 15 * 64, 2, 128)
+    monkeypatch.delenv("GDN_FUSED")
+    f32 = ws(1, 32768, 16, 128, 128, 1, False, dtype=torch.float32)
+    assert f32 == ws(1, 32768, 256, 128, 128, 1, False, dtype=torch.float32) // 16
     # one head of d 64 (one tile): 256 segments wanted, but at least 16 chunks each: 32 x 16
     base = _fwd_base_bytes(1, 32768, 1, 64)
-    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 1, 64, 64, 1, False) == al(base) + _seg_bytes(1, 1, 64, 32, 16)
+    assert ws(1, 32768, 1, 64, 64, 1, False) == al(base) + _seg_bytes(1, 1, 64, 32, 16)
     # fewer than 32 chunks: no split
-    assert gb.gdn_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 64, 64, 1, False) == _fwd_base_bytes(1, 31 * 64, 1, 64)
+    assert ws(1, 31 * 64, 1, 64, 64, 1, False) == _fwd_base_bytes(1, 31 * 64, 1, 64)
     monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "3")
     base = _fwd_base_bytes(2, 849, 2, 128)   # 14 chunks per sequence: 5 segments of 3
-    assert gb.gdn_chunk_fwd_workspace_bytes(2, 849, 2, 128, 128, 2, False) == al(base) + _seg_bytes(2, 2, 128, 5, 3)
+    assert ws(2, 849, 2, 128, 128, 2, False) == al(base) + _seg_bytes(2, 2, 128, 5, 3)
     monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "0")
-    assert gb.gdn_chunk_fwd_workspace_bytes(1, 32768, 16, 128, 128, 1, False) == _fwd_base_bytes(1, 32768, 16, 128)
+    assert ws(1, 32768, 16, 128, 128, 1, False) == _fwd_base_bytes(1, 32768, 16, 128)
 
 
 def test_bwd_workspace_bytes(L):

@@ -109,6 +109,27 @@ def test_fwd_small(B, T, H, dk, dv, dtype, h0, gs):
     check_fwd(SY.make_forward_inputs(w, seed=1000 + T + dk + dv, gate_scale=gs, h0=h0))
 
 
+# bf16 with d_k = d_v = 128 has two forward paths (GDN_FUSED: 0 two stages, 1 one kernel; the
+# default takes the one kernel below 64 (sequence, head) pairs); the small cases run on both
+D128 = [c for c in SMALL if c[3] == c[4] == 128 and c[5] == "bf16"]
+
+
+@pytest.mark.parametrize("path", ["0", "1"])
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,h0,gs", D128)
+def test_fwd_small_each_path(B, T, H, dk, dv, dtype, h0, gs, path, monkeypatch):
+    monkeypatch.setenv("GDN_FUSED", path)
+    w = SY.Workload(99, f"small_{dtype}_path{path}", H=H, dk=dk, dv=dv, dtype=dtype, B=B, T=T)
+    check_fwd(SY.make_forward_inputs(w, seed=1000 + T + dk + dv, gate_scale=gs, h0=h0))
+
+
+@pytest.mark.parametrize("path", ["0", "1"])
+def test_fwd_varlen_beta_to_2_each_path(path, monkeypatch):
+    monkeypatch.setenv("GDN_FUSED", path)
+    w = SY.Workload(90, f"beta2_varlen_path{path}", H=3, dk=128, dv=128, dtype="bf16")
+    check_fwd(SY.make_forward_inputs(w, seed=33, lengths=[65, 1, 200, 0, 130], gate_scale=0.1, h0=True,
+                                     beta_scale=2.0))
+
+
 @pytest.mark.parametrize("dtype,dk,dv,T,gs", [("bf16", 128, 128, 300, 0.05), ("bf16", 64, 128, 130, 1.0),
                                                ("f32", 128, 128, 200, 0.05), ("f32", 64, 64, 150, 1.0)])
 def test_fwd_beta_to_2(dtype, dk, dv, T, gs):
@@ -401,6 +422,35 @@ def test_workload_train_1p3b_slow_decay_sampled_heads():
 def test_workload_long_context_sampled_heads():
     """B1 H16 T32768 d128 bf16, h0 ~ N(0, 0.02^2); heads 5 and 14."""
     check_fwd(SY.make_forward_inputs(2), heads=[5, 14])
+
+
+def test_workload_train_1p3b_one_kernel_sampled_heads(monkeypatch):
+    """The training shape on the one-kernel path (GDN_FUSED=1; by default it takes the two
+    stages): heads 2 and 9."""
+    monkeypatch.setenv("GDN_FUSED", "1")
+    check_fwd(SY.make_forward_inputs(1), heads=[2, 9])
+
+
+def test_workload_long_context_two_stages_sampled_heads(monkeypatch):
+    """The long-context shape on the two-stage path (GDN_FUSED=0; by default it takes the one
+    kernel): heads 1 and 10."""
+    monkeypatch.setenv("GDN_FUSED", "0")
+    check_fwd(SY.make_forward_inputs(2), heads=[1, 10])
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_forward_paths_agree(wid, monkeypatch):
+    """Both bf16 d128 forward paths on a full workload agree with each other within the parity
+    tolerance, on every head (the oracle pins each of them on sampled heads)."""
+    x = SY.make_forward_inputs(wid)
+    h0 = x["h0"]
+    monkeypatch.setenv("GDN_FUSED", "0")
+    o0, h0T = gpu_fwd(x, h0)
+    monkeypatch.setenv("GDN_FUSED", "1")
+    o1, h1T = gpu_fwd(x, h0)
+    eo, eh = err(o1, o0, "bf16"), err(h1T, h0T, "bf16")
+    print(f"[gpu] paths agree on workload {wid}: o {eo:.3e} hT {eh:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eh <= TOL_BF16
 
 
 def test_workload_varlen_packed_sampled_heads():

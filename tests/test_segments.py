@@ -12,9 +12,12 @@ unsplit pass, for every segment length, with and without matches:
     state, tiny but not zero, and a few sums round the other way);
   * slow decay: no record ever matches and the second pass recomputes every segment;
   * medium decay: a match at a later record in some tiles (last-bit differences fade slowly
-    once the decayed state is no longer negligible in the accumulate; where is data-dependent).
+    once the decayed state is no longer negligible in the accumulate; where is data-dependent:
+    the one-kernel path compares all 128 columns of a head at once, the two-stage path each
+    64-column tile on its own).
 GDN_SEGMENT_CHUNKS forces the segment length; the workspace's last region tells how many
-chunks the second pass computed per segment.
+chunks the second pass computed per segment. Cases with d_k = d_v = 128 run on both bf16 forward
+paths (GDN_FUSED=0: two stages; 1: one kernel), each against its own unsplit pass.
 """
 import numpy as np
 import pytest
@@ -104,32 +107,43 @@ CASES = [
     (1, 849, 2, 128, 128, 3, 1.0, 2.0, "quick"),
     (2, 849, 2, 128, 128, 5, 1.0, 1.0, "quick"),
     (2, 849, 2, 128, 128, 5, 0.001, 2.0, "full"),    # no match anywhere
-    (1, 6400, 2, 128, 128, 32, 0.05, 1.0, "early"),  # matches at a later record
+    (1, 6400, 2, 128, 128, 32, 0.1, 1.0, "early"),   # matches at a later record
     (1, 1000, 2, 64, 64, 3, 1.0, 2.0, "quick"),
     (1, 1000, 3, 64, 128, 2, 0.001, 1.0, "full"),
     (1, 1000, 2, 128, 64, 4, 1.0, 2.0, "quick"),
 ]
+PATHS = ["0", "1"]   # GDN_FUSED: two stages, one kernel
 
 
-@pytest.mark.parametrize("B,T,H,dk,dv,L,gs,bs,expect", CASES)
-def test_split_equals_unsplit(B, T, H, dk, dv, L, gs, bs, expect, monkeypatch):
+def paths_of(dk, dv):
+    return PATHS if dk == dv == 128 else ["0"]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,L,gs,bs,expect,path",
+                         [c + (pth,) for c in CASES for pth in paths_of(c[3], c[4])])
+def test_split_equals_unsplit(B, T, H, dk, dv, L, gs, bs, expect, path, monkeypatch):
+    monkeypatch.setenv("GDN_FUSED", path)
     w = SY.Workload(95, "split", H=H, dk=dk, dv=dv, dtype="bf16", B=B, T=T)
     x = SY.make_forward_inputs(w, seed=500 + T + L, gate_scale=gs, h0=True, beta_scale=bs)
     check_split(x, L, monkeypatch, expect)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("L,gs,expect", [(3, 1.0, "quick"), (2, 0.001, "full")])
-def test_split_varlen(L, gs, expect, monkeypatch):
+def test_split_varlen(L, gs, expect, path, monkeypatch):
     """Packed sequences of 700, 64, 0, 300 and 1 tokens: segments past a sequence's end are
     empty, a one-chunk sequence never reaches the second pass."""
+    monkeypatch.setenv("GDN_FUSED", path)
     w = SY.Workload(95, "split_varlen", H=2, dk=128, dv=128, dtype="bf16")
     x = SY.make_forward_inputs(w, seed=77, lengths=[700, 64, 0, 300, 1], gate_scale=gs, h0=True,
                                beta_scale=2.0)
     check_split(x, L, monkeypatch, expect)
 
 
-def test_split_bf16_output_and_no_final_state(monkeypatch):
+@pytest.mark.parametrize("path", PATHS)
+def test_split_bf16_output_and_no_final_state(path, monkeypatch):
     """bf16 o through the split equals the unsplit bf16 o; hT not requested."""
+    monkeypatch.setenv("GDN_FUSED", path)
     w = SY.Workload(95, "split_bf16o", H=2, dk=128, dv=128, dtype="bf16", B=1, T=1500)
     x = SY.make_forward_inputs(w, seed=78, h0=True)
     o0, _, _ = run(x, 0, monkeypatch, o_dtype=torch.bfloat16)
@@ -137,10 +151,13 @@ def test_split_bf16_output_and_no_final_state(monkeypatch):
     assert o1.dtype == torch.bfloat16 and torch.equal(o0, o1)
 
 
-def test_long_context_split_equals_unsplit(monkeypatch):
-    """B1 H16 T32768 d128: the shape-chosen plan (8 segments of 64 chunks) against the unsplit
-    pass, bit for bit; with the workloads' decay the second pass stops at offset 1 or 2."""
+@pytest.mark.parametrize("path,ns", [("0", 8), ("1", 16)])
+def test_long_context_split_equals_unsplit(path, ns, monkeypatch):
+    """B1 H16 T32768 d128: the shape-chosen plan (two stages: 8 segments of 64 chunks; one
+    kernel: 16 of 32) against the unsplit pass, bit for bit; with the workloads' decay the
+    second pass stops at offset 1 or 2."""
     monkeypatch.delenv("GDN_SEGMENT_CHUNKS", raising=False)
+    monkeypatch.setenv("GDN_FUSED", path)
     x = SY.make_forward_inputs(2)
     dev = "cuda"
     t = [x[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
@@ -149,7 +166,7 @@ def test_long_context_split_equals_unsplit(monkeypatch):
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     o1, h1 = gb.gdn_chunk_fwd(*t, h0, workspace=ws)
     torch.cuda.synchronize()
-    reran = ws[need - 4 * 16 * 2 * 8:].cpu().view(torch.int32).numpy().reshape(16, 2, 8)
+    reran = ws[need - 4 * 16 * 2 * ns:].cpu().view(torch.int32).numpy().reshape(16, 2, ns)
     monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "0")
     o0, h0r = gb.gdn_chunk_fwd(*t, h0)
     torch.cuda.synchronize()
