@@ -57,13 +57,16 @@ __device__ __forceinline__ Frag<TM> load_kt(const TM* K, int t0, int t1, int j) 
 // copies them with plain 1 KB DMA blocks. A row is cut into 16-byte pieces; piece pc holds
 // the 8 contraction indices one lane feeds to a 16x16x32 product, columns
 // 32(pc>>2) + 4(pc&3) + 0..3 then the same + 16, and sits at position pc ^ img_swz<W>(r)
-// of row r. With that permutation the row-fragment reads (16 rows x 16 bytes per quarter
-// wave) and the transposing reads of K (4 rows x 32 bytes per quarter wave) touch distinct
-// banks.
+// of row r. LDS serves a 16-byte read 8 lanes (128 bytes) at a time and an 8-byte read 16 lanes
+// at a time; the permutation is chosen so that the 8 rows of a row-fragment read (W = 128: one
+// row per 256 bytes, so only the position within the row can separate them) fall on 8 distinct
+// 16-byte positions modulo 128, and so that the transposing reads of K (4 rows x 32 bytes per
+// 16 lanes) meet the least bank sharing their shape allows (they are read as 8-byte halves of
+// 16-byte positions, so 16 lanes can use at most 8 of the 16 half-positions in 128 bytes).
 template <int W>
 __device__ __forceinline__ int img_swz(int r) {
-    if constexpr (W == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-    else return (r >> 1) & 7;  // W = 64: two rows per 256-byte bank line
+    if constexpr (W == 128) return (4 * (r & 3) + ((r >> 2) & 3)) ^ (r & 2);
+    else return (r >> 1) & 7;  // W = 64: two rows per 256 bytes
 }
 // element offset, in a [64, W] image, of the 4-element run at column c (c % 4 == 0) of row r
 template <int W>

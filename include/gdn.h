@@ -102,7 +102,7 @@ const char *gdn_status_string(int status);
  * ones (Mmat, P, K16, Q16: W = 64 or dk columns) are stored as the LDS images the propagate
  * kernel reads: each row is W/8 pieces of 8 values, the piece at position pos of row r holds
  * columns 32(pc>>2) + 4(pc&3) + {0..3, 16..19} with pc = pos ^ swz(r), where
- * swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64.
+ * swz(r) = (4(r&3) + ((r>>2)&3)) ^ (r&2) for W = 128 and (r>>1)&7 for W = 64.
  * where A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
  *
  * Long chains, bf16 inputs: the state propagation runs one work-group per (sequence, head,

@@ -260,10 +260,10 @@ def from_image(img, W):
     """Row-major [.., 64, W] from the fp16 operand image stage 1 writes for bf16 inputs: each
     row holds W/8 16-byte pieces; the piece at position pos of row r carries the source piece
     pc = pos ^ swz(r), whose 8 values are columns 32(pc>>2) + 4(pc&3) + 0..3 and the same + 16;
-    swz(r) = 4(r&3) + ((r>>2)&3) for W = 128 and (r>>1)&7 for W = 64."""
+    swz(r) = (4(r&3) + ((r>>2)&3)) ^ (r&2) for W = 128 and (r>>1)&7 for W = 64."""
     out = np.full_like(img, np.nan)
     for r in range(64):
-        swz = 4 * (r & 3) + ((r >> 2) & 3) if W == 128 else (r >> 1) & 7
+        swz = (4 * (r & 3) + ((r >> 2) & 3)) ^ (r & 2) if W == 128 else (r >> 1) & 7
         for pos in range(W // 8):
             pc = pos ^ swz
             c0 = 32 * (pc >> 2) + 4 * (pc & 3)
