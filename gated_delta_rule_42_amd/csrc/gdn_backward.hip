@@ -730,7 +730,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad_kernel(BwdProblem bp) {
 // accumulator tiles (4lq + 0..3, then 16 + 4lq + 0..3 of each 32-wide k slice): an operand
 // stored along k is read as two 8-byte runs (load_frag2), one stored across k with the
 // transposing read (load_frag_t). d_v is processed in 32-column slices so that the d_v
-// contractions fill whole 32-wide k slices.
+// contractions fill whole 32-wide k slices. Eight waves, two per SIMD (the LDS use admits one
+// work-group per CU): wave w % 4 owns the 16-row block w % 4 of every product and wave w / 4 one
+// half of its output columns (the slice's 16-column tile w / 4, column blocks 2(w/4), 2(w/4)+1 of
+// dP, dMmat and the T products, d_k blocks 4(w/4) .. +3 of dQ and dK), so no product is split
+// along its contraction; only the row sums of dgamma and dbeta are added across the two halves.
 template <int DK>
 struct alignas(16) Grad16Smem {
     static constexpr int PK = DK + 8, PT = 72, PS = DK + 8, PV = 40;
@@ -753,18 +757,20 @@ struct alignas(16) Grad16Smem {
         } cc;
     } u;
     float gam[64], eg[64], ed[64], beta[64];
-    float colg[4][64], colb[4][64];
-    float rowg[64], rowb[64];
-    float tailw[4];
+    float colg[4][64], colb[4][64];   // [row block][column]: column sums of the block's rows
+    float rowg[2][64], rowb[2][64];   // [half][row]: row sums over that half's columns
+    float tailw[8];
 };
 
 template <typename TO, int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
+__global__ __launch_bounds__(512) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     using SM = Grad16Smem<DK>;
     constexpr int PK = SM::PK, PT = SM::PT, PS = SM::PS, PV = SM::PV, NKB = DK / 16, NKS = DK / 32;
     __shared__ SM sm;
     const ChunkProblem& p = bp.f;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // eight waves: wave w % 4 owns row block w % 4 (`wave`), w / 4 (`half`) the half of every
+    // product's output columns it forms (see the struct comment)
+    const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, half = tid >> 8;
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
     const long unit = blockIdx.x, c = unit / H;
@@ -795,7 +801,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     // The unit's first loads are all issued before any is used (one memory latency instead of
     // one per group): K, Q (rows past the chunk's end read as zeros through resources sized to
     // the valid rows), T and P, the gates and, further below, the first d_v slice.
-    constexpr int NKQ = 64 * DK / 8 / 256;
+    constexpr int NKQ = 64 * DK / 8 / 512;
     u32x4_t kin[NKQ], qin[NKQ];
     {
         const unsigned kbytes = (unsigned)((len - 1) * H * DK + DK) * 2;
@@ -803,22 +809,22 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         const auto qr = make_rsrc(qp + (bos * H + h) * DK, kbytes);
 #pragma unroll
         for (int it = 0; it < NKQ; ++it) {
-            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8)), off = (r * H * DK + cc) * 2;
+            const int i = tid + 512 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8)), off = (r * H * DK + cc) * 2;
             kin[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
             qin[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
         }
     }
     // T fp16 row-major; P as fp16 hi + lo, two images (piece i: row r, columns c0..+3, c0+16..+19)
-    u32x4_t tin[2], phi[2], plo[2];
+    u32x4_t tin[1], phi[1], plo[1];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
+    for (int it = 0; it < 1; ++it) {
+        const int i = tid + 512 * it, r = i / 8, cc = 8 * (i % 8);
         tin[it] = *reinterpret_cast<const u32x4_t*>(p.tmat16 + widx * 4096 + r * 64 + cc);
         phi[it] = reinterpret_cast<const u32x4_t*>(p.pimg16 + widx * 4096)[i];
         plo[it] = reinterpret_cast<const u32x4_t*>(p.plo16 + widx * 4096)[i];
     }
     float gin = 0.f, bin = 0.f, egin = 0.f, edin = 0.f;
-    if (wave == 0) {
+    if (tid < 64) {
         const unsigned gbytes = (unsigned)(((len - 1) * H + 1) * 4);
         gin = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.g + bos * H + h, gbytes), lane * H * 4, 0, 0));
         bin = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.beta + bos * H + h, gbytes), lane * H * 4, 0, 0));
@@ -838,11 +844,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     auto colc = [&](const _Float16* t, int pitch, int k0, int c0) {
         return load_frag_t<_Float16>(&t[(k0 + 8 * lq) * pitch + c0], &t[(k0 + 8 * lq + 4) * pitch + c0], pitch);
     };
-    f32x4_t dP[4], dM[4], dQ1[NKB], dK1[NKB];
+    f32x4_t dP[2], dM[2], dQ1[NKB / 2], dK1[NKB / 2];   // the wave's column blocks 2 half + cl, d_k blocks NKB/2 half + jl
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dP[t] = dM[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) dP[t] = dM[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) dQ1[j] = dK1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jl = 0; jl < NKB / 2; ++jl) dQ1[jl] = dK1[jl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float gacc[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma of rows 16 wave + 4 lq + m
     float tail = 0.f;                       // lam (dS' : S) + sum z, this thread's share
     auto& sl = sm.u.sl;
@@ -851,39 +857,39 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     // registers: slice js+1 is loaded while slice js is computed. Native vector types (a
     // struct-typed copy would go through memory); every load is issued (past the last slice
     // they reload it), V and dO rows past the chunk's end read as zeros through buffer resources.
-    constexpr int NSI = 32 * DK / 8 / 256;
+    constexpr int NSP = 32 * DK / 8, NSI = (NSP + 511) / 512;   // 16-byte pieces of a slice's rows
     u32x4_t rs[NSI];
     f32x4_t rd[NSI][2];
-    u32x4_t rv, ro;
+    u32x4_t rvo;   // V (half 0) or dO (half 1) rows
     const unsigned vrow_bytes = (unsigned)((len - 1) * H * DV + 32) * 2;
     auto load_slice = [&](int js) __attribute__((always_inline)) {
         const int dv0 = 32 * js;
 #pragma unroll
         for (int it = 0; it < NSI; ++it) {
-            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const int i = tid + 512 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            if (i >= NSP) break;
             const _Float16* sp = p.states16 + (widx * DV + dv0 + r) * DK + cc;
             const float* dp = bp.dstates + (widx * DV + dv0 + r) * DK + cc;
             rs[it] = *reinterpret_cast<const u32x4_t*>(sp);
             rd[it][0] = *reinterpret_cast<const f32x4_t*>(dp);
             rd[it][1] = *reinterpret_cast<const f32x4_t*>(dp + 4);
         }
-        const int r = tid >> 2, cc = 8 * (tid & 3), off = (r * H * DV + cc) * 2;
-        rv = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(vp + (bos * H + h) * DV + dv0, vrow_bytes), off, 0, 0);
-        ro = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(dop + (bos * H + h) * DV + dv0, vrow_bytes), off, 0, 0);
+        const int r = (tid & 255) >> 2, cc = 8 * (tid & 3), off = (r * H * DV + cc) * 2;
+        rvo = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc((half ? dop : vp) + (bos * H + h) * DV + dv0, vrow_bytes), off, 0, 0);
     };
     auto f4 = [](f32x4_t x) { return make_float4(x[0], x[1], x[2], x[3]); };
     load_slice(0);
 #pragma unroll
     for (int it = 0; it < NKQ; ++it) {
-        const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+        const int i = tid + 512 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
         *reinterpret_cast<uint4*>(&sm.K[r * PK + cc]) =
             to_operand16<uint16_t>(make_uint4(kin[it][0], kin[it][1], kin[it][2], kin[it][3]));
         *reinterpret_cast<uint4*>(&sm.Q[r * PK + cc]) =
             to_operand16<uint16_t>(make_uint4(qin[it][0], qin[it][1], qin[it][2], qin[it][3]));
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int i = tid + 256 * it, r = i / 8, cc = 8 * (i % 8);
+    for (int it = 0; it < 1; ++it) {
+        const int i = tid + 512 * it, r = i / 8, cc = 8 * (i % 8);
         *reinterpret_cast<uint4*>(&sm.T[r * PT + cc]) = make_uint4(tin[it][0], tin[it][1], tin[it][2], tin[it][3]);
         int pr, pc0;
         img_piece<64>(i, pr, pc0);
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         *reinterpret_cast<uint2*>(&sm.Plo[pr * PT + pc0]) = make_uint2(plo[it][0], plo[it][1]);
         *reinterpret_cast<uint2*>(&sm.Plo[pr * PT + pc0 + 16]) = make_uint2(plo[it][2], plo[it][3]);
     }
-    if (wave == 0) {
+    if (tid < 64) {
         sm.beta[lane] = bin;
         sm.gam[lane] = wave_inclusive_sum(gin);
         sm.eg[lane] = egin;
@@ -905,7 +911,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         const float lam = sm.eg[63];
 #pragma unroll
         for (int it = 0; it < NSI; ++it) {
-            const int i = tid + 256 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            const int i = tid + 512 * it, r = i / (DK / 8), cc = 8 * (i % (DK / 8));
+            if (i >= NSP) break;
             const uint4 sh = make_uint4(rs[it][0], rs[it][1], rs[it][2], rs[it][3]);
             const f16x8_t s8 = __builtin_bit_cast(f16x8_t, sh);
             const float4 s0 = make_float4((float)s8[0], (float)s8[1], (float)s8[2], (float)s8[3]),
@@ -919,84 +926,91 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                            s1.x * d1.x + s1.y * d1.y + s1.z * d1.z + s1.w * d1.w);
         }
         {
-            const int r = tid >> 2, cc = 8 * (tid & 3);
-            const uint4 v = make_uint4(rv[0], rv[1], rv[2], rv[3]), d = make_uint4(ro[0], ro[1], ro[2], ro[3]);
-            const uint4 d16 = to_operand16<uint16_t>(d);
-            *reinterpret_cast<uint4*>(&sl.V[r * PV + cc]) = to_operand16<uint16_t>(v);
-            *reinterpret_cast<uint4*>(&sl.dO[r * PV + cc]) = d16;
-            const f16x8_t dh = __builtin_bit_cast(f16x8_t, d16);
-            const float e = sm.eg[r];
-            *reinterpret_cast<uint4*>(&sl.EdO[r * PV + cc]) =
-                pack8(make_float4(e * (float)dh[0], e * (float)dh[1], e * (float)dh[2], e * (float)dh[3]),
-                      make_float4(e * (float)dh[4], e * (float)dh[5], e * (float)dh[6], e * (float)dh[7]));
+            const int r = (tid & 255) >> 2, cc = 8 * (tid & 3);
+            const uint4 x16 = to_operand16<uint16_t>(make_uint4(rvo[0], rvo[1], rvo[2], rvo[3]));
+            if (half == 0) {
+                *reinterpret_cast<uint4*>(&sl.V[r * PV + cc]) = x16;
+            } else {
+                *reinterpret_cast<uint4*>(&sl.dO[r * PV + cc]) = x16;
+                const f16x8_t dh = __builtin_bit_cast(f16x8_t, x16);
+                const float e = sm.eg[r];
+                *reinterpret_cast<uint4*>(&sl.EdO[r * PV + cc]) =
+                    pack8(make_float4(e * (float)dh[0], e * (float)dh[1], e * (float)dh[2], e * (float)dh[3]),
+                          make_float4(e * (float)dh[4], e * (float)dh[5], e * (float)dh[6], e * (float)dh[7]));
+            }
         }
         __syncthreads();
         load_slice(js + 1 < DV / 32 ? js + 1 : js);
         const auto dvr = make_rsrc(static_cast<TO*>(bp.dv) + (bos * H + h) * DV + dv0,
                                    (unsigned)(((len - 1) * H * DV + 32) * (int)sizeof(TO)));
 
-        // X = K S^T, Y = Q S^T, Z = K dS'^T for this wave's rows and the slice's two column tiles
-        f32x4_t X[2], Y[2], Z[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) X[nt] = Y[nt] = Z[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // X = K S^T, Y = Q S^T, Z = K dS'^T for this wave's rows and its column tile nt = half of
+        // the slice
+        f32x4_t X[1], Y[1], Z[1];
+        X[0] = Y[0] = Z[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const Frag<_Float16> ak = rowc(sm.K, PK, row, 32 * s), aq = rowc(sm.Q, PK, row, 32 * s);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt0 = 0; nt0 < 1; ++nt0) {
+                const int nt = half;
                 const Frag<_Float16> bs = rowc(sl.S, PS, 16 * nt + l16, 32 * s), bd = rowc(sl.dS, PS, 16 * nt + l16, 32 * s);
-                mma_k32(X[nt], ak, bs);
-                mma_k32(Y[nt], aq, bs);
-                mma_k32(Z[nt], ak, bd);
-                mma_k32(Z[nt], ak, rowc(sl.dSlo, PS, 16 * nt + l16, 32 * s));
+                mma_k32(X[nt0], ak, bs);
+                mma_k32(Y[nt0], aq, bs);
+                mma_k32(Z[nt0], ak, bd);
+                mma_k32(Z[nt0], ak, rowc(sl.dSlo, PS, 16 * nt + l16, 32 * s));
             }
         }
-        float EX[2][4];
+        float EX[1][4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt0 = 0; nt0 < 1; ++nt0)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                const int nt = half;
                 const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
-                EX[nt][m] = sm.eg[r] * X[nt][m];
-                const float rv = (float)sl.V[r * PV + v] - EX[nt][m];
+                EX[nt0][m] = sm.eg[r] * X[nt0][m];
+                const float rv = (float)sl.V[r * PV + v] - EX[nt0][m];
                 sl.R[r * PV + v] = (_Float16)rv;
                 split(sm.beta[r] * rv, sl.BR, sl.BRlo, r * PV + v);
-                gacc[m] += (float)sl.EdO[r * PV + v] * Y[nt][m];
+                gacc[m] += (float)sl.EdO[r * PV + v] * Y[nt0][m];
             }
         __syncthreads();
 
         // Delta = T (beta R), dDelta = P^T dO + Ed Z
-        f32x4_t Dl[2], dDl[2];
+        f32x4_t Dl[1], dDl[1];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            Dl[nt] = dDl[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt0 = 0; nt0 < 1; ++nt0) {
+            const int nt = half;
+            Dl[nt0] = dDl[nt0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32) {
                 const Frag<_Float16> at = rowc(sm.T, PT, row, k0), bo = colc(sl.dO, PV, k0, 16 * nt);
-                mma_k32(Dl[nt], at, colc(sl.BR, PV, k0, 16 * nt));
-                mma_k32(Dl[nt], at, colc(sl.BRlo, PV, k0, 16 * nt));
-                mma_k32(dDl[nt], colc(sm.P, PT, k0, 16 * wave), bo);
-                mma_k32(dDl[nt], colc(sm.Plo, PT, k0, 16 * wave), bo);
+                mma_k32(Dl[nt0], at, colc(sl.BR, PV, k0, 16 * nt));
+                mma_k32(Dl[nt0], at, colc(sl.BRlo, PV, k0, 16 * nt));
+                mma_k32(dDl[nt0], colc(sm.P, PT, k0, 16 * wave), bo);
+                mma_k32(dDl[nt0], colc(sm.Plo, PT, k0, 16 * wave), bo);
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt0 = 0; nt0 < 1; ++nt0)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                const int nt = half;
                 const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
-                const float z = sm.ed[r] * Dl[nt][m] * Z[nt][m];
-                dDl[nt][m] += sm.ed[r] * Z[nt][m];
+                const float z = sm.ed[r] * Dl[nt0][m] * Z[nt0][m];
+                dDl[nt0][m] += sm.ed[r] * Z[nt0][m];
                 gacc[m] -= z;
                 tail += z;
-                split(Dl[nt][m], sl.D, sl.Dlo, r * PV + v);
-                split(sm.ed[r] * Dl[nt][m], sl.EdD, sl.EdDlo, r * PV + v);
-                split(dDl[nt][m], sl.dD, sl.dDlo, r * PV + v);
+                split(Dl[nt0][m], sl.D, sl.Dlo, r * PV + v);
+                split(sm.ed[r] * Dl[nt0][m], sl.EdD, sl.EdDlo, r * PV + v);
+                split(dDl[nt0][m], sl.dD, sl.dDlo, r * PV + v);
             }
         __syncthreads();
 
         // dR = diag(beta) T^T dDelta (= dV)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt0 = 0; nt0 < 1; ++nt0) {
+            const int nt = half;
             f32x4_t dRl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32) {
@@ -1008,7 +1022,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * wave + 4 * lq + m, v = 16 * nt + l16;
                 const float d = sm.beta[r] * dRl[m];
-                gacc[m] -= d * EX[nt][m];
+                gacc[m] -= d * EX[nt0][m];
                 sl.EdR[r * PV + v] = (_Float16)(-sm.eg[r] * d);
                 const int off = (r * H * DV + v) * (int)sizeof(TO);   // rows past the end fall outside dvr
                 if constexpr (sizeof(TO) == 2)
@@ -1023,21 +1037,23 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         {
             const Frag<_Float16> ao = rowc(sl.dO, PV, row, 0), ad = rowc(sl.dD, PV, row, 0);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                mma_k32(dP[ct], ao, rowc(sl.D, PV, 16 * ct + l16, 0));
-                mma_k32(dP[ct], ao, rowc(sl.Dlo, PV, 16 * ct + l16, 0));
-                mma_k32(dM[ct], ad, rowc(sl.R, PV, 16 * ct + l16, 0));
+            for (int cl = 0; cl < 2; ++cl) {
+                const int ct = 2 * half + cl;
+                mma_k32(dP[cl], ao, rowc(sl.D, PV, 16 * ct + l16, 0));
+                mma_k32(dP[cl], ao, rowc(sl.Dlo, PV, 16 * ct + l16, 0));
+                mma_k32(dM[cl], ad, rowc(sl.R, PV, 16 * ct + l16, 0));
             }
             const Frag<_Float16> a1 = rowc(sl.EdO, PV, row, 0), a2 = rowc(sl.EdR, PV, row, 0),
                                  a3 = rowc(sl.EdD, PV, row, 0), a3l = rowc(sl.EdDlo, PV, row, 0);
 #pragma unroll
-            for (int j = 0; j < NKB; ++j) {
+            for (int jl = 0; jl < NKB / 2; ++jl) {
+                const int j = half * (NKB / 2) + jl;
                 const Frag<_Float16> bS = colc(sl.S, PS, 0, 16 * j), bdS = colc(sl.dS, PS, 0, 16 * j);
-                mma_k32(dQ1[j], a1, bS);
-                mma_k32(dK1[j], a2, bS);
-                mma_k32(dK1[j], a3, bdS);
-                mma_k32(dK1[j], a3l, bdS);
-                mma_k32(dK1[j], a3, colc(sl.dSlo, PS, 0, 16 * j));
+                mma_k32(dQ1[jl], a1, bS);
+                mma_k32(dK1[jl], a2, bS);
+                mma_k32(dK1[jl], a3, bdS);
+                mma_k32(dK1[jl], a3l, bdS);
+                mma_k32(dK1[jl], a3, colc(sl.dSlo, PS, 0, 16 * j));
             }
         }
     }
@@ -1045,30 +1061,32 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
 
     // -- dPg (X3) and the P terms of dgamma; dT (X1) and the Mmat term of dbeta
     float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, dbrow[4] = {0.f, 0.f, 0.f, 0.f};
-    float colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};   // column 16 ct + l16
+    float colg[2] = {0.f, 0.f}, colb[2] = {0.f, 0.f};   // column 16 ct + l16, ct = 2 half + cl
     auto& cc = sm.u.cc;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * half + cl;
         const int col = 16 * ct + l16;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = 16 * wave + 4 * lq + m;
             float dpg = 0.f;
             if (col <= r) {
-                const float x = dP[ct][m] * ((float)sm.P[r * PT + col] + (float)sm.Plo[r * PT + col]);
+                const float x = dP[cl][m] * ((float)sm.P[r * PT + col] + (float)sm.Plo[r * PT + col]);
                 rowacc[m] += x;
-                colg[ct] -= x;
-                dpg = dP[ct][m] * __expf(sm.gam[r] - sm.gam[col]);
+                colg[cl] -= x;
+                dpg = dP[cl][m] * __expf(sm.gam[r] - sm.gam[col]);
             }
             split(dpg, cc.X3, cc.X3lo, r * PT + col);
-            colb[ct] += dM[ct][m] * (float)sm.T[r * PT + col];
-            cc.X1[r * PT + col] = (_Float16)(dM[ct][m] * sm.beta[col]);
+            colb[cl] += dM[cl][m] * (float)sm.T[r * PT + col];
+            cc.X1[r * PT + col] = (_Float16)(dM[cl][m] * sm.beta[col]);
         }
     }
     __syncthreads();
     // -- X2 = dT T^T
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * half + cl;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(acc, rowc(cc.X1, PT, row, k0), rowc(sm.T, PT, 16 * ct + l16, k0));
@@ -1078,7 +1096,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     __syncthreads();
     // -- dA = strict_lower(-T^T X2); with G = K K^T: the A terms of dbeta and dgamma, dG into X1
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * half + cl;
         f32x4_t ta = {0.f, 0.f, 0.f, 0.f}, G = ta;
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32) mma_k32(ta, colc(sm.T, PT, k0, 16 * wave), colc(cc.X2, PT, k0, 16 * ct));
@@ -1095,15 +1114,16 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
                 dbrow[m] += da * ag;
                 const float aa = da * sm.beta[r] * ag;
                 rowacc[m] += aa;
-                colg[ct] -= aa;
+                colg[cl] -= aa;
                 dg = da * sm.beta[r] * gm;
             }
             cc.X1[r * PT + col] = (_Float16)dg;
         }
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const float g = sum_lq(colg[ct]), b = sum_lq(colb[ct]);
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * half + cl;
+        const float g = sum_lq(colg[cl]), b = sum_lq(colb[cl]);
         if (lq == 0) {
             sm.colg[wave][16 * ct + l16] = g;
             sm.colb[wave][16 * ct + l16] = b;
@@ -1113,20 +1133,21 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
     for (int m = 0; m < 4; ++m) {
         const float g = sum_l16(gacc[m] + rowacc[m]), b = sum_l16(dbrow[m]);
         if (l16 == 0) {
-            sm.rowg[16 * wave + 4 * lq + m] = g;
-            sm.rowb[16 * wave + 4 * lq + m] = b;
+            sm.rowg[half][16 * wave + 4 * lq + m] = g;
+            sm.rowb[half][16 * wave + 4 * lq + m] = b;
         }
     }
     {
         const float t = sum_l16(sum_lq(tail));
-        if (lane == 0) sm.tailw[wave] = t;
+        if (lane == 0) sm.tailw[tid >> 6] = t;
     }
     __syncthreads();
 
     // -- dQ = dQ1 + dPg K, dK = dK1 + dPg^T Q + dG K + dG^T K
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-        f32x4_t aq = dQ1[j], ak = dK1[j];
+    for (int jl = 0; jl < NKB / 2; ++jl) {
+        const int j = half * (NKB / 2) + jl;
+        f32x4_t aq = dQ1[jl], ak = dK1[jl];
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32) {
             const Frag<_Float16> bK = colc(sm.K, PK, k0, 16 * j), bQ = colc(sm.Q, PK, k0, 16 * j);
@@ -1148,15 +1169,17 @@ __global__ __launch_bounds__(256) void chunk_bwd_grad16_kernel(BwdProblem bp) {
         }
     }
     // -- dg = reverse cumulative sum of dgamma; dbeta
-    if (wave == 0) {
+    if (tid < 64) {
         const int r = 63 - lane;
-        float dgam = sm.rowg[r] + ((sm.colg[0][r] + sm.colg[1][r]) + (sm.colg[2][r] + sm.colg[3][r]));
-        if (r == 63) dgam += (sm.tailw[0] + sm.tailw[1]) + (sm.tailw[2] + sm.tailw[3]);
+        float dgam = (sm.rowg[0][r] + sm.rowg[1][r]) + ((sm.colg[0][r] + sm.colg[1][r]) + (sm.colg[2][r] + sm.colg[3][r]));
+        if (r == 63)
+            dgam += ((sm.tailw[0] + sm.tailw[1]) + (sm.tailw[2] + sm.tailw[3])) +
+                    ((sm.tailw[4] + sm.tailw[5]) + (sm.tailw[6] + sm.tailw[7]));
         const float x = wave_inclusive_sum(dgam);
         if (r < len) {
             bp.dg[(bos + r) * H + h] = x;
             bp.dbeta[(bos + r) * H + h] =
-                sm.rowb[r] + ((sm.colb[0][r] + sm.colb[1][r]) + (sm.colb[2][r] + sm.colb[3][r]));
+                (sm.rowb[0][r] + sm.rowb[1][r]) + ((sm.colb[0][r] + sm.colb[1][r]) + (sm.colb[2][r] + sm.colb[3][r]));
         }
     }
 }
@@ -1198,7 +1221,7 @@ static hipError_t bwd_launch(const BwdProblem& b, hipStream_t s) {
     const long units = p.nc_bound * p.H;
     if (e == hipSuccess && units > 0) {
         if (p.mimg16)
-            e = launch(chunk_bwd_grad16_kernel<TO, DK, DV>, dim3((unsigned)units), dim3(256), s, b);
+            e = launch(chunk_bwd_grad16_kernel<TO, DK, DV>, dim3((unsigned)units), dim3(512), s, b);
         else
             e = launch(chunk_bwd_grad_kernel<TO, DK, DV>, dim3((unsigned)units), dim3(256), s, b);
     }
