@@ -33,6 +33,14 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(uint16_t bf16_bits) { return __uint_as_float((uint32_t)bf16_bits << 16); }
 
+// x, with the compiler made to assume it may have changed: lane-dependent values derived from it
+// inside a loop are recomputed where used instead of being hoisted out of the loop and kept
+// (or spilled) for its whole length.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // fp32 -> bf16, round to nearest even (the conversion instruction of gfx950; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);

@@ -86,14 +86,6 @@ struct ORaw {
     float g, b;
 };
 
-// x, with the compiler made to assume it may have changed: lane-dependent values derived from it
-// inside a loop are recomputed where used instead of being hoisted out of the loop and kept
-// (or spilled) for its whole length.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // The loads take the lane's row and column as their vector offset and the rows' block as their
 // scalar offset, so that no per-load address lives in a vector register across the chunk loop.
 template <int U>

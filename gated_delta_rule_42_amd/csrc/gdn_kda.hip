@@ -38,6 +38,8 @@
 #include "gdn_stage2.h"
 #include "gdn_ut.h"
 
+#include <type_traits>
+
 namespace gdn {
 
 // Four consecutive input elements as fp32.
@@ -62,16 +64,22 @@ struct alignas(16) KdaPrepSmem {
     float Q[64 * PK];
     float G[64 * PK];   // g, then gamma (in-chunk inclusive cumulative sum, per channel)
     float A[64 * PF];
-    float T[64 * PF];
-    float P[64 * PF];
+    float T[64 * PF];   // before the Gram products: per row block of the gamma scan, the
+                        // block's sum of g per channel; during them, their scratch
+    float P[64 * PF];   // with decoupled gates, until A is formed: the raw Q tile
     float beta[64];
-    float tot[1024];    // per row block of the gamma scan: the block's sum of g, per channel
 };
 
-// Rows of row block I = wave of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}], i < 16 (I + 1),
+// Threads of the stage-1 work-group: eight waves, two per SIMD, so that one wave's LDS and
+// transcendental latencies hide behind the other's work.
+constexpr int kKdaPrepThreads = 512;
+
+// Rows of row block I of [sum_c L[r][c] K[i][c] e^{gamma_r[c] - gamma_i[c]}], i < 16 (I + 1),
 // for one or two left operands L1, L2 (sharing the right operand K and the exponentials), into
 // O1 (times rs1[r] when rs1 is set; strictly lower when strict1) and O2 (lower including the
-// diagonal). Column blocks on the fp32 matrix core with the reference gamma of row 16 I:
+// diagonal). Two waves share a row block, each summing half of the d_k channels (HF = 0: the
+// first half); the first writes its partial sums, the second adds its own after a barrier.
+// Column blocks on the fp32 matrix core with the reference gamma of row 16 I:
 // left factor L[r] e^{gamma_r - gamma_ref} (<= |L|: r >= ref), right factor
 // K[i] e^{gamma_ref - gamma_i}, which is <= |K| below the diagonal block (i < ref) and, in the
 // diagonal block, grows with the channel's decay over the block's rows. A channel whose decay
@@ -84,8 +92,9 @@ struct alignas(16) KdaPrepSmem {
 // and the right factor K[i] e^{gamma_last(J) - gamma_i} are both <= |L|, |K| (rows r > last(J)
 // >= i, and gamma does not increase down the chunk), so nothing overflows fp16; a factor that
 // underflows belongs to a term below fp16's resolution of the entry. The right factors depend
-// on J alone: wave J forms them once as fp16 fragments (zf) for the waves below it, and wave I
-// forms its channel scalars e^{gamma_ref - gamma_last(J)} (ss); see gram_offdiag_prep. The
+// on J alone: the waves of row block J form them once as fp16 fragments (zf) for the waves
+// below, and those of row block I form its channel scalars e^{gamma_ref - gamma_last(J)} (ss);
+// see gram_offdiag_prep. The
 // diagonal block (F16) runs on the bf16 matrix core with each factor as a bf16 hi + lo pair.
 constexpr float kMaxRange = 60.f;
 
@@ -103,17 +112,18 @@ struct KdaOffdiag {
         : zf(reinterpret_cast<uint4*>(base)), ss(base + 3 * NS * 64 * 4) {}
 };
 
-// Wave I's share of the scratch: the right-operand fragments of column block I (I < 3; lane
-// (l16, lq) holds row 16 I + l16, channels 32 s + 4 lq + 0..3 and 32 s + 16 + 4 lq + 0..3, the
-// k-slot order of the products) and the channel scalars of its pairs (I > 0).
-template <int DK, int I>
+// A wave's share of the scratch of row block I, the channel half HF of: the right-operand
+// fragments of column block I (I < 3; lane (l16, lq) holds row 16 I + l16, channels
+// 32 s + 4 lq + 0..3 and 32 s + 16 + 4 lq + 0..3, the k-slot order of the products) and the
+// channel scalars of its pairs (I > 0).
+template <int DK, int I, int HF>
 __device__ __forceinline__ void gram_offdiag_prep(const KdaPrepSmem<DK>& sm, KdaOffdiag<DK> od, int lane) {
     constexpr int PK = KdaPrepSmem<DK>::PK, NS = KdaOffdiag<DK>::NS;
     const int l16 = lane & 15, lq = lane >> 4;
     if constexpr (I < 3) {
         const int i = 16 * I + l16, last = 16 * I + 15;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int s = HF * NS / 2; s < (HF + 1) * NS / 2; ++s) {
             const int c0 = 32 * s + 4 * lq;
             uint32_t w[4];
 #pragma unroll
@@ -130,11 +140,13 @@ __device__ __forceinline__ void gram_offdiag_prep(const KdaPrepSmem<DK>& sm, Kda
 #pragma unroll
     for (int J = 0; J < I; ++J)
 #pragma unroll
-        for (int c = lane; c < DK; c += 64)
+        for (int c0 = 64 * HF; c0 < DK; c0 += 128) {
+            const int c = c0 + lane;
             od.ss[(I * (I - 1) / 2 + J) * DK + c] = __expf(sm.G[16 * I * PK + c] - sm.G[(16 * J + 15) * PK + c]);
+        }
 }
 
-template <int DK, bool TWO, int I, bool F16>
+template <int DK, bool TWO, int I, bool F16, int HF>
 __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
                                              float* O1, float* O2, const float* rs1, bool strict1,
                                              KdaOffdiag<DK> od, int lane) {
@@ -156,7 +168,7 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
         constexpr int NS = KdaOffdiag<DK>::NS;
         const int r = 16 * I + l16;
 #pragma unroll 1
-        for (int s = 0; s < NS; ++s) {
+        for (int s = HF * NS / 2; s < (HF + 1) * NS / 2; ++s) {
             const int c0 = 32 * s + 4 * lq;
             f32x4_t x1[2], x2[2], y[2];
 #pragma unroll
@@ -209,7 +221,7 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
         // fp32 products: lane (l16, lq) takes channels 16 u + 4 lq + e, e = 0..3, in product (u, e),
         // so its operands arrive as 16-byte reads
         constexpr int J0 = 0;
-        for (int u = 0; u < DK / 16; ++u) {
+        for (int u = HF * DK / 32; u < (HF + 1) * DK / 32; ++u) {
             const int c = 16 * u + 4 * lq;
             const f32x4_t gref = *reinterpret_cast<const f32x4_t*>(&sm.G[16 * I * PK + c]);
             const f32x4_t glast = *reinterpret_cast<const f32x4_t*>(&sm.G[(16 * I + 15) * PK + c]);
@@ -238,18 +250,33 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
             }
         }
     }
+    if constexpr (HF == 0) {
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
+                const bool k1 = J < I || (strict1 ? i < r : i <= r), k2 = J < I || i <= r;
+                O1[r * PF + i] = k1 ? (rs1 ? rs1[r] : 1.f) * a1[J][m] : 0.f;
+                if constexpr (TWO) O2[r * PF + i] = k2 ? a2[J][m] : 0.f;
+            }
+        }
+    }
+    __syncthreads();  // the first half's sums are in O1, O2
+    if constexpr (HF == 0) return;
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = 16 * I + 4 * lq + m, i = 16 * J + l16;
             const bool k1 = J < I || (strict1 ? i < r : i <= r), k2 = J < I || i <= r;
-            O1[r * PF + i] = k1 ? (rs1 ? rs1[r] : 1.f) * a1[J][m] : 0.f;
-            if constexpr (TWO) O2[r * PF + i] = k2 ? a2[J][m] : 0.f;
+            if (k1) O1[r * PF + i] += (rs1 ? rs1[r] : 1.f) * a1[J][m];
+            if constexpr (TWO)
+                if (k2) O2[r * PF + i] += a2[J][m];
         }
     }
     // channels left out of the diagonal block's product: exact sums over them (each lane adds to
-    // the entries it wrote above)
+    // the entries it added to above)
     for (int c0 = 0; c0 < DK; c0 += 64) {
         const int ch = c0 + lane;
         const bool out = ch < DK && sm.G[16 * I * PK + ch] - sm.G[(16 * I + 15) * PK + ch] > kMaxRange;
@@ -270,28 +297,35 @@ __device__ __forceinline__ void gram_rows_of(const KdaPrepSmem<DK>& sm, const fl
     }
 }
 
-// gram_rows_of for the row block of this wave (the row block is a compile-time constant of each
-// wave's code, so its loops are static)
-// (F16: the scratch is filled first, then a barrier.) Called by all 256 threads.
+// gram_rows_of for the (row block, channel half) of this wave; both are compile-time constants
+// of each wave's code, so its loops are static. Wave w and w + 4 share a SIMD; the pairing puts
+// the longest and the shortest row block (3 and 0), or 2 and 1, on each SIMD, so that every SIMD
+// gets the same work: waves 0-3 take row blocks 3, 3, 2, 2 and waves 4-7 row blocks 0, 0, 1, 1,
+// halves alternating. (F16: the scratch is filled first, then a barrier.) Called by all
+// kKdaPrepThreads threads; takes two barriers (one without F16).
 template <int DK, bool TWO, bool F16>
 __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float* L1, const float* L2,
                                           float* O1, float* O2, const float* rs1, bool strict1,
                                           float* scratch, int wave, int lane) {
     const KdaOffdiag<DK> od(scratch);
-    if constexpr (F16) {
-        switch (wave) {
-            case 0: gram_offdiag_prep<DK, 0>(sm, od, lane); break;
-            case 1: gram_offdiag_prep<DK, 1>(sm, od, lane); break;
-            case 2: gram_offdiag_prep<DK, 2>(sm, od, lane); break;
-            default: gram_offdiag_prep<DK, 3>(sm, od, lane); break;
+    auto run = [&](auto ib, auto hf) {
+        constexpr int I = decltype(ib)::value, HF = decltype(hf)::value;
+        if constexpr (F16) {
+            gram_offdiag_prep<DK, I, HF>(sm, od, lane);
+            __syncthreads();
         }
-        __syncthreads();
-    }
+        gram_rows_of<DK, TWO, I, F16, HF>(sm, L1, L2, O1, O2, rs1, strict1, od, lane);
+    };
+    using std::integral_constant;
     switch (wave) {
-        case 0: gram_rows_of<DK, TWO, 0, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
-        case 1: gram_rows_of<DK, TWO, 1, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
-        case 2: gram_rows_of<DK, TWO, 2, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
-        default: gram_rows_of<DK, TWO, 3, F16>(sm, L1, L2, O1, O2, rs1, strict1, od, lane); break;
+        case 0: run(integral_constant<int, 3>{}, integral_constant<int, 0>{}); break;
+        case 1: run(integral_constant<int, 3>{}, integral_constant<int, 1>{}); break;
+        case 2: run(integral_constant<int, 2>{}, integral_constant<int, 0>{}); break;
+        case 3: run(integral_constant<int, 2>{}, integral_constant<int, 1>{}); break;
+        case 4: run(integral_constant<int, 0>{}, integral_constant<int, 0>{}); break;
+        case 5: run(integral_constant<int, 0>{}, integral_constant<int, 1>{}); break;
+        case 6: run(integral_constant<int, 1>{}, integral_constant<int, 0>{}); break;
+        default: run(integral_constant<int, 1>{}, integral_constant<int, 1>{}); break;
     }
 }
 
@@ -301,10 +335,14 @@ __device__ __forceinline__ void gram_rows(const KdaPrepSmem<DK>& sm, const float
 // arrays use native vector types (a struct-typed copy would go through memory).
 template <typename TIn, int DK, bool DEC>
 struct KdaPrepStage {
-    static constexpr int NP = 64 * DK / 4 / 256;   // groups of 4 values per thread
+    static constexpr int NP = 64 * DK / 4 / kKdaPrepThreads;   // groups of 4 values per thread
     // thread tid holds channels 4 (tid % NG) .. +3 of the NP consecutive rows NP (tid / NG) + it
-    static constexpr int NG = DK / 4, RB = 256 / NG;
+    static constexpr int NG = DK / 4, RB = kKdaPrepThreads / NG;
     static constexpr int EB = (int)sizeof(TIn);    // bytes of an input element
+    // with decoupled gates Q is staged too when its raw tile fits in the P buffer (all shapes
+    // but fp32 d_k = 128, which loads it when needed)
+    static constexpr bool QPRE = !DEC || 64 * DK * EB <= (int)sizeof(KdaPrepSmem<DK>::P);
+    static_assert(RB * DK <= (int)sizeof(KdaPrepSmem<DK>::T) / 4, "the scan's block sums fit in T");
     u32x4_t k[NP], q[NP];                         // raw groups (bf16: the low 8 bytes)
     f32x4_t g[NP], e[NP];
     float beta;
@@ -330,7 +368,7 @@ struct KdaPrepStage {
         const long o = (bos * H + h) * DK;
         const unsigned rows = (unsigned)((len - 1) * H * DK + DK);
         const auto kr = make_rsrc(static_cast<const TIn*>(p.k) + o, rows * EB);
-        const auto qr = make_rsrc(static_cast<const TIn*>(p.q) + o, DEC ? 0u : rows * EB);
+        const auto qr = make_rsrc(static_cast<const TIn*>(p.q) + o, QPRE ? rows * EB : 0u);
         const auto gr = make_rsrc(p.g + o, rows * 4);
         const auto er = make_rsrc(DEC ? p.erase + o : p.g, DEC ? rows * 4 : 0u);
 #pragma unroll
@@ -345,8 +383,9 @@ struct KdaPrepStage {
         beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, tid * H * 4, 0, 0));
     }
 
-    // K and (Q, or E * K with decoupled gates) into LDS as fp32; g scanned down the thread's
-    // rows in registers, the row block's sum into tot
+    // K and (Q, or E * K with decoupled gates) into LDS as fp32, and with decoupled gates the raw
+    // Q tile into P ([64, DK] row-major input elements); g scanned down the thread's rows in
+    // registers, the row block's sum into T
     __device__ __forceinline__ void store(KdaPrepSmem<DK>& sm, int tid) {
         constexpr int PK = KdaPrepSmem<DK>::PK;
 #pragma unroll
@@ -357,10 +396,32 @@ struct KdaPrepStage {
                                   : widen(q[it]);
             *reinterpret_cast<float4*>(&sm.K[r * PK + cc]) = kv;
             *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+            if constexpr (DEC && QPRE) {
+                char* dst = reinterpret_cast<char*>(sm.P) + (r * DK + cc) * EB;
+                if constexpr (EB == 2) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{q[it][0], q[it][1]};
+                else *reinterpret_cast<u32x4_t*>(dst) = q[it];
+            }
             if (it > 0) g[it] += g[it - 1];
         }
-        *reinterpret_cast<f32x4_t*>(&sm.tot[(tid / NG) * DK + 4 * (tid % NG)]) = g[NP - 1];
+        *reinterpret_cast<f32x4_t*>(&sm.T[(tid / NG) * DK + 4 * (tid % NG)]) = g[NP - 1];
         if (tid < 64) sm.beta[tid] = beta;
+    }
+    // with decoupled gates: the raw Q tile in P to fp32 in Q (rows past the chunk's end are zero,
+    // as loaded)
+    __device__ __forceinline__ static void q_from_raw(KdaPrepSmem<DK>& sm, int tid) {
+        constexpr int PK = KdaPrepSmem<DK>::PK;
+        for (int i = tid; i < 64 * DK / 4; i += kKdaPrepThreads) {
+            const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+            const char* src = reinterpret_cast<const char*>(sm.P) + (r * DK + cc) * EB;
+            u32x4_t x;
+            if constexpr (EB == 2) {
+                const u32x2_t h = *reinterpret_cast<const u32x2_t*>(src);
+                x = u32x4_t{h[0], h[1], 0u, 0u};
+            } else {
+                x = *reinterpret_cast<const u32x4_t*>(src);
+            }
+            *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = widen(x);
+        }
     }
     // gamma (the in-chunk inclusive cumulative sum of g, per channel) into LDS: the thread's
     // rows plus the sums of the row blocks above them; and the scaled operators of those rows
@@ -376,7 +437,7 @@ struct KdaPrepStage {
         f32x4_t pre = {0.f, 0.f, 0.f, 0.f}, last = pre;   // rows above the block; gamma_last
         for (int b = 0; b < RB; ++b) {
             if (b == rb) pre = last;
-            last += *reinterpret_cast<const f32x4_t*>(&sm.tot[b * DK + cc]);
+            last += *reinterpret_cast<const f32x4_t*>(&sm.T[b * DK + cc]);
         }
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
@@ -404,12 +465,12 @@ struct KdaPrepStage {
 // Persistent work-groups: each walks (chunk, head) units with a stride of the grid, keeping the
 // next unit's inputs in flight in registers while the current one is computed (the loads are
 // issued on every pass, for the current unit again past the last one, which keeps the
-// compiler's waits for them exact). Wave w owns row block w of A and P. With
+// compiler's waits for them exact). Two waves share each row block of A and P (gram_rows). With
 // decoupled gates (DEC) the erased read runs along E * K, so A's left operand is E * K (held
-// in the Q buffer until A is formed, then Q is loaded), Kh is E * K * e^gamma, V is scaled by
-// the write gate in stage 2 and Mmat is T itself.
+// in the Q buffer until A is formed, then Q is moved there from its raw copy in P), Kh is
+// E * K * e^gamma, V is scaled by the write gate in stage 2 and Mmat is T itself.
 template <typename TIn, int DK, bool DEC>
-__global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
+__global__ __launch_bounds__(kKdaPrepThreads) void kda_prepare_kernel(ChunkProblem p) {
     using SM = KdaPrepSmem<DK>;
     constexpr int PK = SM::PK, PF = SM::PF;
     constexpr bool F16 = sizeof(TIn) == 2;  // off-diagonal Gram blocks on the fp16 matrix core
@@ -444,18 +505,23 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
         }
         const int h = (int)(unit % H);
         const long widx = unit;   // (chunk, head) = (unit / H, unit % H)
+        // Every phase takes the thread's index through opaque(), so that the per-thread addresses
+        // of one phase are formed there instead of being hoisted out of the unit loop and held
+        // (or spilled) through the others.
         __syncthreads();  // the previous unit is done with LDS
-        stage.store(sm, tid);
+        stage.store(sm, opaque(tid));
         __syncthreads();
         // gamma (rows past the chunk's end add 0) and Kh, Qh, Kd, lam to the workspace
-        stage.template finish_scan<IMG>(sm, tid, khat, qhat, kdec, p.lam, widx);
-        if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), tid);
-        else stage.load(p, bos, len, h, tid);
+        stage.template finish_scan<IMG>(sm, opaque(tid), khat, qhat, kdec, p.lam, widx);
         __syncthreads();
+        // the next unit's loads, issued past the barrier so that no wave waits there for another
+        // wave's loads to be accepted behind the stores above; the Gram products hide them
+        if (nok) stage.load(p, nbos, nlen, (int)(nxt % H), opaque(tid));
+        else stage.load(p, bos, len, h, opaque(tid));
 
         // -- Qh with decoupled gates (Q is loaded after A is formed)
         auto write_qhat = [&]() {
-            for (int i = tid; i < 64 * DK / 4; i += 256) {
+            for (int i = opaque(tid); i < 64 * DK / 4; i += kKdaPrepThreads) {
                 const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
                 const float4 g = *reinterpret_cast<const float4*>(&sm.G[r * PK + cc]);
                 const float4 q = *reinterpret_cast<const float4*>(&sm.Q[r * PK + cc]);
@@ -466,46 +532,46 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(ChunkProblem p) {
 
         // -- A and P
         if constexpr (DEC) {
-            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, sm.T, wave, lane);
-            __syncthreads();  // E * K is dead: load Q in its place
-            for (int i = tid; i < 64 * DK / 4; i += 256) {
-                const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
-                float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < len) qv = load4_in(qp + ((bos + r) * H + h) * DK + cc);
-                *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.A, nullptr, nullptr, true, sm.T, wave, opaque(lane));
+            __syncthreads();  // E * K is dead: Q in its place
+            if constexpr (KdaPrepStage<TIn, DK, DEC>::QPRE) {
+                KdaPrepStage<TIn, DK, DEC>::q_from_raw(sm, opaque(tid));
+            } else {
+                for (int i = opaque(tid); i < 64 * DK / 4; i += kKdaPrepThreads) {
+                    const int r = i / (DK / 4), cc = 4 * (i % (DK / 4));
+                    float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (r < len) qv = load4_in(qp + ((bos + r) * H + h) * DK + cc);
+                    *reinterpret_cast<float4*>(&sm.Q[r * PK + cc]) = qv;
+                }
             }
             __syncthreads();
             write_qhat();
-            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, sm.T, wave, lane);
+            gram_rows<DK, false, F16>(sm, sm.Q, nullptr, sm.P, nullptr, nullptr, false, sm.T, wave, opaque(lane));
         } else {
-            gram_rows<DK, true, F16>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, sm.T, wave, lane);
+            gram_rows<DK, true, F16>(sm, sm.K, sm.Q, sm.A, sm.P, sm.beta, true, sm.T, wave, opaque(lane));
         }
         __syncthreads();
 
-        ut_inverse64<PF>(sm.A, sm.T, wave, lane);
+        ut_inverse64<PF>(sm.A, sm.T, wave, opaque(lane));
 
         // -- Mmat = T diag(beta) (T with decoupled gates) and P (lower incl. diagonal), fp32 row-major
         {
-            const int r = tid >> 2, c0 = (tid & 3) * 16;
-            float mv[16], pv[16];
-    #pragma unroll
-            for (int e = 0; e < 16; ++e) {
+            constexpr int NE = 64 * 64 / kKdaPrepThreads;   // entries of one row per thread
+            const int t = opaque(tid), r = t / (64 / NE), c0 = (t % (64 / NE)) * NE;
+            float mv[NE], pv[NE];
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
                 const int ci = c0 + e;
                 mv[e] = ((ci >> 4) <= (r >> 4)) ? sm.T[r * PF + ci] * (DEC ? 1.f : sm.beta[ci]) : 0.f;
                 pv[e] = ci <= r ? sm.P[r * PF + ci] : 0.f;
             }
-            if constexpr (IMG) {
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int o = img_off<64>(r, c0 + 4 * q4);
-                    put4(static_cast<TM*>(p.mmat) + widx * 4096 + o,
-                         make_float4(mv[4 * q4], mv[4 * q4 + 1], mv[4 * q4 + 2], mv[4 * q4 + 3]));
-                    put4(static_cast<TM*>(p.pmat) + widx * 4096 + o,
-                         make_float4(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]));
-                }
-            } else {
-                store16<TM>(static_cast<TM*>(p.mmat) + widx * 4096 + r * 64 + c0, mv);
-                store16<TM>(static_cast<TM*>(p.pmat) + widx * 4096 + r * 64 + c0, pv);
+            for (int q4 = 0; q4 < NE / 4; ++q4) {
+                const int o = IMG ? img_off<64>(r, c0 + 4 * q4) : r * 64 + c0 + 4 * q4;
+                put4(static_cast<TM*>(p.mmat) + widx * 4096 + o,
+                     make_float4(mv[4 * q4], mv[4 * q4 + 1], mv[4 * q4 + 2], mv[4 * q4 + 3]));
+                put4(static_cast<TM*>(p.pmat) + widx * 4096 + o,
+                     make_float4(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3]));
             }
         }
         unit = nxt; ok = nok; bos = nbos; len = nlen;
@@ -987,8 +1053,8 @@ static hipError_t kda_launch(const ChunkProblem& p, hipStream_t s) {
     if (units > 0) {
         // persistent grid: as many work-groups as the device holds at once
         auto go = [&](auto kern, std::atomic<int> (&resident)[64]) {
-            const long cap = resident_blocks(kern, 256, resident, 1);
-            return launch(kern, dim3((unsigned)(units < cap ? units : cap)), dim3(256), s, p);
+            const long cap = resident_blocks(kern, kKdaPrepThreads, resident, 1);
+            return launch(kern, dim3((unsigned)(units < cap ? units : cap)), dim3(kKdaPrepThreads), s, p);
         };
         static std::atomic<int> resident_erase[64], resident_beta[64];
         e = p.erase ? go(kda_prepare_kernel<TIn, DK, true>, resident_erase)

@@ -1,4 +1,4 @@
-// The UT transform of one 64-token chunk on a work-group of four waves: T = (I + A)^{-1} for a
+// The UT transform of one 64-token chunk on the first four waves of a work-group: T = (I + A)^{-1} for a
 // strictly lower triangular A (so I + A is unit lower triangular and needs no pivoting).
 #pragma once
 
@@ -46,11 +46,12 @@ __device__ __forceinline__ void ut_block(const float* At, float* Tt, int lane) {
 // with the block's strictly lower entries held in registers. Then, after one barrier, wave w
 // walks block column w downwards (ut_block): each block needs only the diagonal blocks and the
 // blocks above it in its column, which the same wave wrote just before, so no further barrier
-// is needed until the end. Called by all 256 threads; ends with a barrier.
+// is needed until the end. Called by all threads of the work-group (waves past the fourth only
+// take part in the barriers); ends with a barrier.
 template <int PF>
 __device__ __forceinline__ void ut_inverse64(const float* At, float* Tt, int wave, int lane) {
     const int l16 = lane & 15, lq = lane >> 4;
-    {
+    if (wave < 4) {
         const float* Ab = At + 16 * wave * PF + 16 * wave;
         float a[16][16];
 #pragma unroll
