@@ -614,8 +614,9 @@ struct alignas(16) MPVChunk {
 };
 
 // The DMA wave's copies for one chunk, as 1 KB DMA blocks: the Q image (copy_kq), and the K
-// image, Mmat, P, the gate tables and V (copy_mpv; V rows gathered from the input, rows past the
-// chunk's end read as zeros). copy_mpv issues kMpvCopies instructions.
+// image, Mmat, P (not when WP is false: the state chain alone needs no P), the gate tables and
+// V (copy_mpv; V rows gathered from the input, rows past the chunk's end read as zeros).
+// copy_mpv issues kMpvCopies instructions.
 template <int DK>
 __device__ __forceinline__ void copy_kq(KQChunk<DK>& dst, const ChunkProblem& p, long widx, int lane) {
     constexpr int NB_KQ = 64 * DK * 2 / 1024;
@@ -624,9 +625,9 @@ __device__ __forceinline__ void copy_kq(KQChunk<DK>& dst, const ChunkProblem& p,
 #pragma unroll
     for (int b = 0; b < NB_KQ; ++b) dma16g(qimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.Q) + 1024 * b);
 }
-template <int DK, int DVT>
-constexpr int kMpvCopies = 64 * DK * 2 / 1024 + 8 + 8 + 64 * DVT * 2 / 1024 + 1;
-template <int DK, int DV, int DVT>
+template <int DK, int DVT, bool WP = true>
+constexpr int kMpvCopies = 64 * DK * 2 / 1024 + 8 + (WP ? 8 : 0) + 64 * DVT * 2 / 1024 + 1;
+template <int DK, int DV, int DVT, bool WP = true>
 __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProblem& p, long bos, int len,
                                          long widx, int h, int dv0, int lane) {
     constexpr int NB_KQ = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
@@ -648,7 +649,7 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
-        dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+        if constexpr (WP) dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
     }
 }
 
@@ -687,8 +688,11 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
 //   o and hT equal those of the unsplit kernel bit for bit. The saving comes from decay: a
 //   segment's dependence on its entering state shrinks by the product of its gates, and once
 //   that falls under fp32 rounding the two states agree and all segments are fixed at once.
-template <typename TO, int DK, int DV, int DVT, int SEG>
+// OUT = false (the backward pass's state recompute, SEG = 0): the state chain alone; the
+// products that only form o (Q S^T, P Delta) and their LDS reads are left out.
+template <typename TO, int DK, int DV, int DVT, int SEG, bool OUT = true>
 __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kernel(ChunkProblem p) {
+    static_assert(OUT || SEG == 0, "the state recompute runs unsplit");
     using KQ = KQChunk<DK>;
     using MPV = MPVChunk<DK, DVT>;
     constexpr int NW = DVT / 16;   // compute waves
@@ -769,28 +773,29 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
 
     if (wave == NW) {
         // ------------------------------------------------------------------- DMA wave
-        // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2). Loads complete
-        // in issue order, so at the top of chunk c only MPV(c+1) may still be in flight.
+        // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2) (no KQ without
+        // OUT). Loads complete in issue order, so at the top of chunk c only MPV(c+1) may still
+        // be in flight.
         auto run = [&](long c0, long len) -> int {
             auto mpv_copy = [&](int i) {
                 const long jc = c0 + i;
-                copy_mpv<DK, DV, DVT>(mpv[i % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
+                copy_mpv<DK, DV, DVT, OUT>(mpv[i % 3], p, sbos + jc * kChunk, chunk_len(jc), (cbase + jc) * H + h, h,
                                       dv0, lane);
             };
             if (len > 0) {
-                copy_kq<DK>(kq[0], p, (cbase + c0) * H + h, lane);
+                if constexpr (OUT) copy_kq<DK>(kq[0], p, (cbase + c0) * H + h, lane);
                 mpv_copy(0);
             }
             if (len > 1) mpv_copy(1);
             for (int i = 0;; ++i) {
-                if (i + 1 < len) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
+                if (i + 1 < len) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT, OUT>));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 lds_barrier();  // chunk i's operands are in LDS; chunk i-1's buffers are free
                 if (range_done(i, len)) {
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // copies of an abandoned chunk
                     return i;
                 }
-                if (i + 1 < len) copy_kq<DK>(kq[(i + 1) & 1], p, (cbase + c0 + i + 1) * H + h, lane);
+                if (OUT && i + 1 < len) copy_kq<DK>(kq[(i + 1) & 1], p, (cbase + c0 + i + 1) * H + h, lane);
                 if (i + 2 < len) mpv_copy(i + 2);
             }
         };
@@ -868,7 +873,7 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
             for (int t = 0; t < 4; ++t) {
                 const int row = 16 * t + l16, c0 = 32 * s + 4 * lq;
                 kf[t] = *reinterpret_cast<const uint4*>(&cm.K[img_off<DK>(row, c0)]);
-                qf[t] = *reinterpret_cast<const uint4*>(&ck.Q[img_off<DK>(row, c0)]);
+                if constexpr (OUT) qf[t] = *reinterpret_cast<const uint4*>(&ck.Q[img_off<DK>(row, c0)]);
             }
         };
         load_xy(0, KF[0], QF[0]);
@@ -890,13 +895,13 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 X[t] = mfma_f16(KF[b][t], BS[s], X[t]);
-                Y[t] = mfma_f16(BS[s], QF[b][t], Y[t]);
+                if constexpr (OUT) Y[t] = mfma_f16(BS[s], QF[b][t], Y[t]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 
         // R = V - e^gamma X
-        load_mp(cm.P, PF);
+        if constexpr (OUT) load_mp(cm.P, PF);
         f32x4_t R[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -926,21 +931,23 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
 
         // O^T = e^gamma S Q^T + Delta^T P^T (lane: token 16t + l16, columns 16 wave + 4 lq .. +3),
         // stored through a resource that ends at the chunk's last token row
-        const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
-        f32x4_t O[4];
+        if constexpr (OUT) {
+            const uint4 BD[2] = {pack_f16_frag(D[0], D[1]), pack_f16_frag(D[2], D[3])};
+            f32x4_t O[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) O[t] = Y[t];
+            for (int t = 0; t < 4; ++t) O[t] = Y[t];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
-        if (p.o) {
-            constexpr int E = (int)sizeof(TO);
-            const long obos = sbos + jc * kChunk;
-            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dvw,
-                                       (unsigned)(((chunk_len(jc) - 1) * H * DV + 16) * E));
+                for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+            if (p.o) {
+                constexpr int E = (int)sizeof(TO);
+                const long obos = sbos + jc * kChunk;
+                const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dvw,
+                                           (unsigned)(((chunk_len(jc) - 1) * H * DV + 16) * E));
 #pragma unroll
-            for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + 4 * lq) * E, O[t]);
+                for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + 4 * lq) * E, O[t]);
+            }
         }
 
         // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
@@ -1132,11 +1139,13 @@ hipError_t launch_chunk_prepare(const ChunkProblem& p, hipStream_t s) {
     return e;
 }
 
-// bf16: DVT/16 compute waves and a DMA wave per work-group
-template <typename TO, int DK, int DV, int DVT>
+// bf16: DVT/16 compute waves and a DMA wave per work-group (OUT = false: the state chain alone,
+// unsplit)
+template <typename TO, int DK, int DV, int DVT, bool OUT = true>
 static hipError_t prop_launch_bf16(const ChunkProblem& p, hipStream_t s) {
     const long blocks = (long)p.N * p.H * (DV / DVT);
     const dim3 block((DVT / 16 + 1) * 64);
+    if constexpr (!OUT) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0, false>, dim3((unsigned)blocks), block, s, p);
     if (p.seg_n <= 1) return launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 0>, dim3((unsigned)blocks), block, s, p);
     hipError_t e = launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 1>, dim3((unsigned)(blocks * p.seg_n)), block, s, p);
     if (e == hipSuccess)
@@ -1144,12 +1153,13 @@ static hipError_t prop_launch_bf16(const ChunkProblem& p, hipStream_t s) {
     return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 3>, dim3((unsigned)blocks), block, s, p);
 }
 
-template <typename TIn, typename TO, int DK, int DV>
+template <typename TIn, typename TO, int DK, int DV, bool OUT = true>
 static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
     if constexpr (sizeof(TIn) == 2) {
-        if (p.seg_n <= 1 && prop_cols(p.N, p.H, DV) == 32) return prop_launch_bf16<TO, DK, DV, 32>(p, s);
-        return prop_launch_bf16<TO, DK, DV, (DV < 64 ? DV : 64)>(p, s);
-    } else {                            // two waves of 16 columns (LDS size)
+        if (p.seg_n <= 1 && prop_cols(p.N, p.H, DV) == 32) return prop_launch_bf16<TO, DK, DV, 32, OUT>(p, s);
+        return prop_launch_bf16<TO, DK, DV, (DV < 64 ? DV : 64), OUT>(p, s);
+    } else {
+        static_assert(OUT, "the fp32 state propagation always writes o");                            // two waves of 16 columns (LDS size)
         constexpr int DVT = 32;
         const long blocks = (long)p.N * p.H * (DV / DVT);
         return launch(chunk_propagate_kernel<TIn, TO, DK, DV, DVT>, dim3((unsigned)blocks),
@@ -1157,11 +1167,11 @@ static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
     }
 }
 
-template <typename TIn, typename TO>
+template <typename TIn, typename TO, bool OUT = true>
 static hipError_t prop_dispatch(const ChunkProblem& p, hipStream_t s) {
     if (p.dk == 64)
-        return p.dv == 64 ? prop_launch<TIn, TO, 64, 64>(p, s) : prop_launch<TIn, TO, 64, 128>(p, s);
-    return p.dv == 64 ? prop_launch<TIn, TO, 128, 64>(p, s) : prop_launch<TIn, TO, 128, 128>(p, s);
+        return p.dv == 64 ? prop_launch<TIn, TO, 64, 64, OUT>(p, s) : prop_launch<TIn, TO, 64, 128, OUT>(p, s);
+    return p.dv == 64 ? prop_launch<TIn, TO, 128, 64, OUT>(p, s) : prop_launch<TIn, TO, 128, 128, OUT>(p, s);
 }
 
 // The state recompute of the backward pass for bf16 inputs: the DMA-fed stage 2 on the fp16
@@ -1174,7 +1184,7 @@ hipError_t launch_chunk_propagate_states16(const ChunkProblem& p, hipStream_t s)
     q.pmat = p.pimg16;
     q.o = nullptr;
     q.hT = nullptr;
-    return (long)p.N * p.H > 0 ? prop_dispatch<uint16_t, float>(q, s) : hipSuccess;
+    return (long)p.N * p.H > 0 ? prop_dispatch<uint16_t, float, false>(q, s) : hipSuccess;
 }
 
 hipError_t launch_chunk_propagate(const ChunkProblem& p, hipStream_t s) {
