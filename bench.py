@@ -77,20 +77,33 @@ def decode_bytes(dk, dv, elem=2, o_elem=4):
     return 2 * dk * dv * 4 + (2 * dk + dv) * elem + dv * o_elem + 8
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, instance=None):
     """HBM bytes per launch (read + write) that rocprofv3 counters measured for `kernel` on
     the benchmark workload (profiles/traffic.json), or None when the kernel's sources have
-    changed since the counters were taken."""
+    changed since the counters were taken (or, with `instance`, when the record is of another
+    template instance than the one whose name contains it)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel)
-    if not rec:
+    if not rec or (instance is not None and instance not in rec["kernel"]):
         return None
     csrc = os.path.join(ROOT, "gated_delta_rule_42_amd", "csrc")
     h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in rec["sources"])).hexdigest()
     return rec["read_bytes"] + rec["write_bytes"] if h == rec["source_sha256"] else None
+
+
+def call_traffic(launches):
+    """Measured HBM bytes of one call that makes the given launches ((traffic.json key, instance
+    name fragment or None) each once), or None unless every launch has a current record."""
+    total = 0.0
+    for key, inst in launches:
+        t = measured_traffic(key, inst)
+        if t is None:
+            return None
+        total += t
+    return total
 
 
 def parse():
@@ -610,7 +623,11 @@ def main():
                       # (algorithmic bytes at peak take longer than algorithmic FLOP at peak)
                       "roofline": {"kernel": "gdn_chunk_bwd (whole call)", "bound": "hbm",
                                    "achieved": bb / (ms / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
-                                   "unit": "GB/s", "frac": bb / (ms / 1e3) / PEAK_HBM_BPS, "traffic": None,
+                                   "unit": "GB/s", "frac": bb / (ms / 1e3) / PEAK_HBM_BPS,
+                                   "traffic": call_traffic([("chunk_prepare_kernel@bwd", "128, true>"),
+                                                            ("chunk_propagate_bf16_kernel@bwd", "false>"),
+                                                            ("chunk_bwd_state16_kernel@bwd", None),
+                                                            ("chunk_bwd_grad16_kernel@bwd", None)]),
                                    "algorithmic_bytes_per_call": bb}}
         if args.cpu_seconds > 0:
             out["bwd"]["cpu_baseline"] = cpu_baseline_slices("bwd", args.cpu_seconds / 2)
@@ -641,7 +658,10 @@ def main():
         out["kda"]["roofline"] = {"kernel": "gdn_kda_chunk_fwd (whole call)", "bound": "hbm",
                                   "achieved": kb / (k["fwd_ms"] / 1e3) / 1e9, "peak": PEAK_HBM_BPS / 1e9,
                                   "unit": "GB/s", "frac": kb / (k["fwd_ms"] / 1e3) / PEAK_HBM_BPS,
-                                  "traffic": None, "algorithmic_bytes_per_call": kb}
+                                  # the instances without decoupled gates (template flag false)
+                                  "traffic": call_traffic([("kda_prepare_kernel@kda", "128, false>"),
+                                                           ("kda_propagate_dma_kernel@kda", "false>")]),
+                                  "algorithmic_bytes_per_call": kb}
         if args.cpu_seconds > 0:
             out["kda"]["cpu_baseline"] = cpu_baseline_slices("kda", args.cpu_seconds / 2)
         if args.only == "kda":
