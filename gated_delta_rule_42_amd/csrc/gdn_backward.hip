@@ -298,7 +298,10 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_bwd_state16_kernel(
         for (long i = 0; i < nchunks; ++i) {
             if (i + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWalkCopies<DK, DVT>));
             else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            lds_barrier();  // pass i's operands are in LDS; pass i-1's buffers are free
+            // pass i's operands are in LDS; pass i-1's buffers are free. The barrier has no fence:
+            // a release fence would make the compiler wait here for every copy in flight (copies
+            // write LDS), where the counts above wait for exactly the ones pass i needs
+            lds_barrier_lgkm();
             if (i + 2 < nchunks) copy(i + 2);
         }
         return;

@@ -790,7 +790,10 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
             for (int i = 0;; ++i) {
                 if (i + 1 < len) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT, OUT>));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                lds_barrier();  // chunk i's operands are in LDS; chunk i-1's buffers are free
+                // chunk i's operands are in LDS; chunk i-1's buffers are free. The barrier has no
+                // fence: a release fence would make the compiler wait here for every copy in flight
+                // (copies write LDS), where the counts above wait for exactly the ones chunk i needs
+                lds_barrier_lgkm();
                 if (range_done(i, len)) {
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // copies of an abandoned chunk
                     return i;

@@ -109,7 +109,8 @@ __device__ __forceinline__ void lds_barrier() {
 // The same without the fences, whose release half makes the compiler wait for every outstanding
 // vector memory operation of the wave, global loads and stores included: this barrier waits for
 // the wave's LDS accesses only and keeps the compiler from moving memory accesses across it. For
-// kernels that copy nothing into LDS; their global loads are waited for where used.
+// waves that copy nothing into LDS (their global loads are waited for where used), or that wait
+// for their copies into LDS themselves, with explicit counts, before it.
 __device__ __forceinline__ void lds_barrier_lgkm() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
