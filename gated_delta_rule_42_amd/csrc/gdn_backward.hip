@@ -69,9 +69,13 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_bwd_state_kernel(ChunkPro
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
-    const long pair = blockIdx.x / NTILE;
+    const long slot = blockIdx.x / NTILE;
     const int tile = (int)(blockIdx.x % NTILE);
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order)
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
 
     long sbos, seos;
@@ -264,17 +268,21 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_bwd_state16_kernel(
     // pair get block ids equal modulo 8 (same XCD, shared L2 for the pair's operands)
     const long NP = (long)p.N * H;
     const long bid = blockIdx.x;
-    long pair;
+    long slot;
     int tile;
     if (NP % 8 == 0) {
         const long x = bid % 8, i = bid / 8;
         tile = (int)(i % NTILE);
-        pair = (i / NTILE) * 8 + x;
+        slot = (i / NTILE) * 8 + x;
     } else {
-        pair = bid / NTILE;
+        slot = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order)
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT;
 
     long sbos, seos;

@@ -32,10 +32,14 @@ namespace gdn {
 // ------------------------------------------------------------------ chunk table
 // base[n] = number of chunks in sequences 0..n-1 (each sequence is cut into 64-token
 // chunks from its own start); base[N] = total. Token ranges are clamped to [0, T] so a
-// malformed offset array cannot move any later access out of bounds.
+// malformed offset array cannot move any later access out of bounds. Then base[N + 1 + k] =
+// the k-th sequence in order of decreasing chunk count (ties by index; the identity order
+// above 1024 sequences): the state propagation takes the sequences' chains longest first, so
+// that a long chain does not start last and extend the launch (its work-groups run one per CU).
 __global__ __launch_bounds__(1024) void chunk_base_kernel(const int32_t* __restrict__ cu, int N,
                                                           int T, int32_t* __restrict__ base) {
     __shared__ int32_t part[1024];
+    __shared__ int32_t cnt[1024];
     const int tid = threadIdx.x;
     const int per = (N + 1023) / 1024;
     const int s0 = min(N, tid * per), s1 = min(N, s0 + per);
@@ -60,6 +64,19 @@ __global__ __launch_bounds__(1024) void chunk_base_kernel(const int32_t* __restr
         run += nchunks(m);
     }
     if (tid == 1023) base[N] = part[1023];
+    int32_t* order = base + N + 1;
+    if (N > 1024) {
+        for (int m = s0; m < s1; ++m) order[m] = m;
+        return;
+    }
+    const int c = tid < N ? nchunks(tid) : 0;
+    cnt[tid] = c;
+    __syncthreads();
+    if (tid < N) {
+        int rank = 0;
+        for (int m = 0; m < N; ++m) rank += (cnt[m] > c) || (cnt[m] == c && m < tid);
+        order[rank] = tid;
+    }
 }
 
 // ------------------------------------------------------------------- stage 1
@@ -439,17 +456,21 @@ __global__ __launch_bounds__(DVT / 16 * 64) void chunk_propagate_kernel(ChunkPro
     // share its L2 for K, Q, Mmat and P.
     const long NP = (long)p.N * H;
     const long bid = blockIdx.x;
-    long pair;
+    long slot;
     int tile;
     if (NP % 8 == 0) {
         const long x = bid % 8, i = bid / 8;
         tile = (int)(i % NTILE);
-        pair = (i / NTILE) * 8 + x;
+        slot = (i / NTILE) * 8 + x;
     } else {
-        pair = bid / NTILE;
+        slot = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order)
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT;
     const int dvw = dv0 + 16 * wave;  // this wave's first d_v column
 
@@ -724,9 +745,13 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         unit = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
-    const long pair = SEG == 1 ? unit / p.seg_n : SEG == 2 ? unit / (p.seg_n - 1) : unit;
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order; every pass of the split maps its slots the same way)
+    const long slot = SEG == 1 ? unit / p.seg_n : SEG == 2 ? unit / (p.seg_n - 1) : unit;
     const int seg = SEG == 1 ? (int)(unit % p.seg_n) : SEG == 2 ? 1 + (int)(unit % (p.seg_n - 1)) : 0;
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT;
 
     long sbos, seos;
@@ -1049,7 +1074,7 @@ WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen,
                         : (long)B * (((long)T + kChunk - 1) / kChunk);
     const size_t units = (size_t)w.nc_bound * H;
     w.off_base = 0;
-    const size_t base_bytes = varlen ? (size_t)(N + 1) * 4 : 0;
+    const size_t base_bytes = varlen ? (size_t)(2 * N + 1) * 4 : 0;   // chunk_base, then the chain order
     w.off_gates = al(base_bytes);
     w.off_m = al(w.off_gates + units * 128 * 4);
     w.off_p = al(w.off_m + units * 4096 * elem_bytes);

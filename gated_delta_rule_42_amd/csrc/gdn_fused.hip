@@ -367,6 +367,8 @@ __global__ __launch_bounds__(FNT) void chunk_fused_kernel(ChunkProblem p) {
 
     const long NP = (long)p.N * H;
     const long unit = blockIdx.x;
+    // (sequence, head) pair in index order: this path runs no chunk-table kernel, so it takes no
+    // chain order from the workspace
     const long pair = SEG == 1 ? unit / p.seg_n : SEG == 2 ? unit / (p.seg_n - 1) : unit;
     const int seg = SEG == 1 ? (int)(unit % p.seg_n) : SEG == 2 ? 1 + (int)(unit % (p.seg_n - 1)) : 0;
     const int n = (int)(pair / H), h = (int)(pair % H);

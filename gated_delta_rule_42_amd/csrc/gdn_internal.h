@@ -58,7 +58,7 @@ struct ChunkProblem {
     long nc_bound;               // upper bound on the number of chunks (workspace rows)
     int nc_per_seq;              // chunks per row when cu_seqlens is NULL
     // workspace regions
-    int32_t* chunk_base;         // [N + 1] (varlen only)
+    int32_t* chunk_base;         // [2N + 1] (varlen only): chunk bases, total, chain order
     float* gates;                // [nc_bound, H, 128]: e^gamma (64), e^{gamma_last - gamma} (64)
     void* mmat;                  // [nc_bound, H, 64, 64] operand type (fp16 or fp32)
     void* pmat;                  // [nc_bound, H, 64, 64] operand type

@@ -602,9 +602,13 @@ __global__ __launch_bounds__(DVT / 16 * 64) void kda_propagate_kernel(ChunkProbl
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const int H = p.H;
-    const long pair = blockIdx.x / NTILE;
+    const long slot = blockIdx.x / NTILE;
     const int tile = (int)(blockIdx.x % NTILE);
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order)
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT, dvw = dv0 + 16 * wave;
 
     long sbos, seos;
@@ -813,17 +817,21 @@ __global__ __launch_bounds__((DVT / 16 + (WG ? 1 : 2)) * 64) void kda_propagate_
     // pair get block ids equal modulo 8 (same XCD, shared L2 for the pair's operators)
     const long NP = (long)p.N * H;
     const long bid = blockIdx.x;
-    long pair;
+    long slot;
     int tile;
     if (NP % 8 == 0) {
         const long x = bid % 8, i = bid / 8;
         tile = (int)(i % NTILE);
-        pair = (i / NTILE) * 8 + x;
+        slot = (i / NTILE) * 8 + x;
     } else {
-        pair = bid / NTILE;
+        slot = bid / NTILE;
         tile = (int)(bid % NTILE);
     }
-    const int n = (int)(pair / H), h = (int)(pair % H);
+    // the work-group's (sequence, head) pair: packed sequences are taken longest first (the chunk
+    // table's order)
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(slot / H)] : (int)(slot / H);
+    const int h = (int)(slot % H);
+    const long pair = (long)n * H + h;
     const int dv0 = tile * DVT;
 
     long sbos, seos;
@@ -1034,14 +1042,14 @@ KdaLayout kda_workspace_layout(int B, int T, int H, int dk, int N, int varlen, i
     w.nc_bound = varlen ? ((long)T + (long)N * 63) / 64 : (long)B * (((long)T + 63) / 64);
     const size_t units = (size_t)w.nc_bound * H;
     w.off_base = 0;
-    w.off_m = al(varlen ? (size_t)(N + 1) * 4 : 0);
+    w.off_m = al(varlen ? (size_t)(2 * N + 1) * 4 : 0);   // chunk_base, then the chain order
     w.off_p = al(w.off_m + units * 4096 * elem);
     w.off_kh = al(w.off_p + units * 4096 * elem);
     w.off_qh = al(w.off_kh + units * 64 * dk * elem);
     w.off_kd = al(w.off_qh + units * 64 * dk * elem);
     w.off_lam = al(w.off_kd + units * 64 * dk * elem);
     w.total = w.off_lam + units * dk * 4;
-    if (w.nc_bound == 0) w.total = al(varlen ? (size_t)(N + 1) * 4 : 0);
+    if (w.nc_bound == 0) w.total = al(varlen ? (size_t)(2 * N + 1) * 4 : 0);
     return w;
 }
 

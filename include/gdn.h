@@ -90,7 +90,8 @@ const char *gdn_status_string(int status);
  * Workspace contents (all regions 256-byte aligned, in this order; `nc` is an upper
  * bound on the number of chunks, ceil(T/64)*B without cu_seqlens and
  * floor((T + N*63)/64) with them):
- *   chunk_base  int32 [N + 1]         first chunk index of each sequence (varlen only)
+ *   chunk_base  int32 [2N + 1]        first chunk index of each sequence, the total, then the
+ *                                     sequences by decreasing chunk count (varlen only)
  *   gates       fp32  [nc, H, 128]    exp(gamma_r) for r < 64, then exp(gamma_last - gamma_r),
  *                                     gamma = in-chunk inclusive cumulative sum of g
  *   Mmat        op    [nc, H, 64, 64] T diag(beta), T = (I + A)^{-1} (UT transform)
@@ -307,7 +308,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g_
  * gdn_kda_chunk_fwd: chunkwise forward pass, arguments as in gdn_chunk_fwd except
  *   g_log_alpha [B, T, H, dk] fp32 (16-byte aligned), log of the per-channel decay, <= 0
  *   workspace   at least gdn_kda_chunk_fwd_workspace_bytes(...) bytes: chunk_base (packed
- *               only), then op [nc, H, 64, 64] Mmat and P, op [nc, H, 64, dk] K * e^gamma,
+ *               only; as in gdn_chunk_fwd's workspace), then op [nc, H, 64, 64] Mmat and P, op [nc, H, 64, dk] K * e^gamma,
  *               Q * e^gamma and K * e^{gamma_last - gamma}, fp32 [nc, H, dk] e^{gamma_last}
  *               (gamma: per-channel in-chunk cumulative sum of g), with op = fp32 for fp32
  *               inputs and fp16 for bf16 inputs; row-major, except that for bf16 inputs the

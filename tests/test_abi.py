@@ -70,7 +70,7 @@ def test_workspace_bytes(L, monkeypatch):
     # packed: bound floor((T + N*63)/64), plus the chunk table
     T, N, H = 1000, 5, 2
     ncb = (T + N * 63) // 64
-    expect = al((N + 1) * 4) + al(ncb * H * 128 * 4) + al(ncb * H * 4096 * 4) + ncb * H * 4096 * 4
+    expect = al((2 * N + 1) * 4) + al(ncb * H * 128 * 4) + al(ncb * H * 4096 * 4) + ncb * H * 4096 * 4
     import torch
     assert gb.gdn_chunk_fwd_workspace_bytes(1, T, H, 64, 64, N, True, dtype=torch.float32) == expect
     assert gb.gdn_chunk_fwd_workspace_bytes(1, 0, 2, 64, 64, 1, False) == 0
@@ -144,7 +144,7 @@ def test_bwd_workspace_bytes(L):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
 
     def expect(nc, H, dk, dv, bf16, varlen_n=None):
-        fwd = (al((varlen_n + 1) * 4) if varlen_n else 0) + al(nc * H * 128 * 4) \
+        fwd = (al((2 * varlen_n + 1) * 4) if varlen_n else 0) + al(nc * H * 128 * 4) \
             + al(nc * H * 4096 * 4) + nc * H * 4096 * 4
         e16 = 2 if bf16 else 4
         off = al(al(al(fwd) + nc * H * 4096 * e16) + nc * H * dv * dk * e16)
