@@ -86,8 +86,14 @@ def measured_traffic(kernel, instance=None):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel)
-    if not rec or (instance is not None and instance not in rec["kernel"]):
+    recs = json.load(open(path))
+    rec = recs.get(kernel)
+    if instance is not None and (not rec or instance not in rec["kernel"]):
+        # another instance of the family measured on the same workload (key kernel<...>@workload)
+        fam, _, wl = kernel.partition("@")
+        rec = next((r for r in recs.values() if r["kernel"].startswith(fam + "<") and r.get("workload") == wl
+                    and instance in r["kernel"]), None)
+    if not rec:
         return None
     csrc = os.path.join(ROOT, "gated_delta_rule_42_amd", "csrc")
     h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in rec["sources"])).hexdigest()
