@@ -829,12 +829,13 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         };
         if constexpr (SEG == 3) {   // the same walk as the compute waves'
             bool ok = true;
+            SegCounts rc(reran, p.seg_n);
             for (int g = 1; g < p.seg_n; ++g) {
                 long c0, len;
                 seg_range(g, c0, len);
                 if (len == 0) break;
                 if (ok) {
-                    ok = reran[g] < len;
+                    ok = rc.get(g) < len;
                     continue;
                 }
                 ok = run(c0, len) < len;
@@ -1039,13 +1040,14 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
         // true state entering segment g
         bool ok = true;
         int glast = 0;
+        SegCounts rc(reran, p.seg_n);
         for (int g = 1; g < p.seg_n; ++g) {
             long c0, len;
             seg_range(g, c0, len);
             if (len == 0) break;
             glast = g;
             if (ok) {   // the same test as the DMA wave's: both take the same barriers
-                ok = reran[g] < len;
+                ok = rc.get(g) < len;
                 if (!ok) load_state(seg_state(g, p.seg_ncp + 1));   // no match: SEG = 2's final state is the true one
                 continue;
             }

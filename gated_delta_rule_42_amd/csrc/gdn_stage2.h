@@ -115,4 +115,24 @@ __device__ __forceinline__ void lds_barrier_lgkm() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The chunk counts the second pass of the long-chain split left per segment, as the ordered walk
+// reads them: wave-wide, 64 segments per vector load (lane l holds segment base + l), so that the
+// walk waits for one load latency per 64 segments instead of one per segment. get(g) takes a
+// wave-uniform g in increasing order; segments at or past n read as 0.
+struct SegCounts {
+    const int* src;
+    int n;
+    int base = -64;
+    int v = 0;
+    __device__ __forceinline__ SegCounts(const int* s, int count) : src(s), n(count) {}
+    __device__ __forceinline__ int get(int g) {
+        if (g - base >= 64) {
+            base = g & ~63;
+            const int i = base + (int)(threadIdx.x & 63);
+            v = i < n ? src[i] : 0;
+        }
+        return __builtin_amdgcn_readlane(v, g - base);
+    }
+};
+
 }  // namespace gdn
