@@ -550,14 +550,17 @@ def main():
             out["forward_path"] = r1["path"]
             c = fwd_counts(f1["dk"], f1["dv"])
             th = f1["tokens"] * f1["H"]
+            # the method's algorithmic bytes per call (q, k, v, o, g, beta per token-head; hT),
+            # charged to the dominant kernel's launch
+            alg = r1["algorithmic_bytes_per_call"]
             if f1["path"] == "fused":
                 # one kernel family per call: the call's events time it
                 mean_call = sum(f1["call_ms"]) / len(f1["call_ms"])
-                ach = c["bytes"] * th / (mean_call / 1e3)
+                ach = alg / (mean_call / 1e3)
                 out["roofline"] = {"kernel": "chunk_fused_kernel", "bound": "hbm",
                                    "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                                    "frac": ach / PEAK_HBM_BPS, "traffic": measured_traffic("chunk_fused_kernel"),
-                                   "algorithmic_bytes_per_launch": c["bytes"] * th}
+                                   "algorithmic_bytes_per_launch": alg}
             else:
                 out["stages_ms"] = {"chunk_prepare_median": pcts(f1["prep_ms"])["median"],
                                     "chunk_propagate_median": pcts(f1["prop_ms"])["median"],
@@ -565,12 +568,12 @@ def main():
                                     "chunk_propagate_mean": sum(f1["prop_ms"]) / len(f1["prop_ms"])}
                 mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
                 if mean_prop >= mean_prep:
-                    ach = c["stage2_bytes"] * th / (mean_prop / 1e3)
+                    ach = alg / (mean_prop / 1e3)
                     out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
                                        "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                                        "frac": ach / PEAK_HBM_BPS,
                                        "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
-                                       "algorithmic_bytes_per_launch": c["stage2_bytes"] * th}
+                                       "algorithmic_bytes_per_launch": alg}
                 else:
                     ach = c["stage1_flops"] * th / (mean_prep / 1e3)
                     out["roofline"] = {"kernel": "chunk_prepare_kernel", "bound": "mfma",
