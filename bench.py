@@ -569,10 +569,14 @@ def main():
                 mean_prep, mean_prop = out["stages_ms"]["chunk_prepare_mean"], out["stages_ms"]["chunk_propagate_mean"]
                 if mean_prop >= mean_prep:
                     ach = alg / (mean_prop / 1e3)
-                    out["roofline"] = {"kernel": "chunk_propagate_bf16_kernel", "bound": "hbm",
+                    # the training shape's 32-column tiles run on chain and output waves unless
+                    # GDN_SPLIT_OUT=0 selects the four-wave kernel
+                    kname = ("chunk_propagate_bf16_kernel" if os.environ.get("GDN_SPLIT_OUT", "1") == "0"
+                             else "chunk_propagate_split_kernel")
+                    out["roofline"] = {"kernel": kname, "bound": "hbm",
                                        "achieved": ach / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                                        "frac": ach / PEAK_HBM_BPS,
-                                       "traffic": measured_traffic("chunk_propagate_bf16_kernel"),
+                                       "traffic": measured_traffic(kname),
                                        "algorithmic_bytes_per_launch": alg}
                 else:
                     ach = c["stage1_flops"] * th / (mean_prep / 1e3)

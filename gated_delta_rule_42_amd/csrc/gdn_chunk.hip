@@ -21,6 +21,7 @@
 // writes O. Every gate factor is exp of a non-positive difference, masked before the exp.
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -648,7 +649,9 @@ __device__ __forceinline__ void copy_kq(KQChunk<DK>& dst, const ChunkProblem& p,
 }
 template <int DK, int DVT, bool WP = true>
 constexpr int kMpvCopies = 64 * DK * 2 / 1024 + 8 + (WP ? 8 : 0) + 64 * DVT * 2 / 1024 + 1;
-template <int DK, int DV, int DVT, bool WP = true>
+// PART selects the instructions issued: 0 all, 1 the gate tables, V and the K image, 2 Mmat and
+// P (issued in that order, PART 1 then PART 2 is the same sequence as PART 0).
+template <int DK, int DV, int DVT, bool WP = true, int PART = 0>
 __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProblem& p, long bos, int len,
                                          long widx, int h, int dv0, int lane) {
     constexpr int NB_KQ = 64 * DK * 2 / 1024, NB_V = 64 * DVT * 2 / 1024, ROW_V = DVT * 2;
@@ -659,18 +662,22 @@ __device__ __forceinline__ void copy_mpv(MPVChunk<DK, DVT>& dst, const ChunkProb
     const unsigned vbytes = (unsigned)((len - 1) * H * DV + DVT) * 2;
     const auto vr = make_rsrc(static_cast<const uint16_t*>(p.v) + (bos * H + h) * DV + dv0, vbytes);
     const char* kimg = reinterpret_cast<const char*>(p.k16 + widx * 64 * DK);
-    if (lane < 32) dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
+    if constexpr (PART != 2) {
+        if (lane < 32) dma16g(reinterpret_cast<const char*>(p.gates + widx * 128), lo, dst.eg);
 #pragma unroll
-    for (int b = 0; b < NB_V; ++b) {
-        const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
-        dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
+        for (int b = 0; b < NB_V; ++b) {
+            const int byte = 1024 * b + 16 * lane, r = byte / ROW_V;
+            dma16(vr, reinterpret_cast<const char*>(dst.V) + 1024 * b, r * H * DV * 2 + 16 * ((byte % ROW_V) >> 4));
+        }
+#pragma unroll
+        for (int b = 0; b < NB_KQ; ++b) dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
     }
+    if constexpr (PART != 1) {
 #pragma unroll
-    for (int b = 0; b < NB_KQ; ++b) dma16g(kimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.K) + 1024 * b);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
-        if constexpr (WP) dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+        for (int b = 0; b < 8; ++b) {
+            dma16g(mimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.M) + 1024 * b);
+            if constexpr (WP) dma16g(pimg, 1024u * b + lo, reinterpret_cast<const char*>(dst.P) + 1024 * b);
+        }
     }
 }
 
@@ -1068,6 +1075,267 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
     }
 }
 
+// ----------------------------------------- stage 2, bf16 inputs, chain and output waves
+// The chunk step of chunk_propagate_bf16_kernel for 32-column tiles of unsplit chains, with the
+// products that only form o taken off the state chain. Per chunk the state depends on the chain
+// X = K S^T -> R = V - diag(e^gamma) X -> Delta = Mmat R -> S' = e^{gamma_last} S + Delta^T
+// diag(e^{gamma_last - gamma}) K; the output O^T = e^gamma S Q^T + Delta^T P^T needs S and Delta
+// but feeds nothing back. Chain wave w (w < 2) owns columns dv0 + 16w .. +15 and steps the
+// state; output wave 2 + w forms o for the same columns from the fp16 operands the chain wave
+// leaves in LDS: the state entering the chunk (written at the end of the previous chunk, read
+// after the chunk's first barrier) and Delta (written before the chunk's second barrier, read
+// after it). The DMA wave (wave 4) copies the operands as in chunk_propagate_bf16_kernel. Two
+// barriers per chunk; each wave is on its own SIMD, the DMA wave beside chain wave 0.
+template <typename TO, int DK, int DV>
+__global__ __launch_bounds__(5 * 64) void chunk_propagate_split_kernel(ChunkProblem p) {
+    constexpr int DVT = 32, NW = DVT / 16;   // chain waves; output waves NW .. 2NW-1; DMA wave 2NW
+    using KQ = KQChunk<DK>;
+    using MPV = MPVChunk<DK, DVT>;
+    constexpr int NKB = DK / 16, NKS = DK / 32, NTILE = DV / DVT;
+    __shared__ KQ kq[2];
+    __shared__ MPV mpv[3];
+    __shared__ uint4 xs[NW][NKS][64];   // per chain wave: S^T entering the chunk, fp16 right operands
+    __shared__ uint4 xd[NW][2][64];     // per chain wave: Delta^T, fp16 left operands
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+
+    // (sequence, head) pair and column tile, mapped as in chunk_propagate_bf16_kernel
+    const long NP = (long)p.N * H;
+    const long bid = blockIdx.x;
+    long unit;
+    int tile;
+    if (NP % 8 == 0) {
+        const long x = bid % 8, i = bid / 8;
+        tile = (int)(i % NTILE);
+        unit = (i / NTILE) * 8 + x;
+    } else {
+        unit = bid / NTILE;
+        tile = (int)(bid % NTILE);
+    }
+    const int n = p.cu_seqlens ? p.chunk_base[p.N + 1 + (int)(unit / H)] : (int)(unit / H);
+    const int h = (int)(unit % H);
+    const long pair = (long)n * H + h;
+    const int dv0 = tile * DVT;
+
+    long sbos, seos;
+    seq_range(p, n, sbos, seos);
+    const long cbase = (p.cu_seqlens == nullptr) ? (long)n * p.nc_per_seq : (long)p.chunk_base[n];
+    long nchunks = (seos - sbos + kChunk - 1) / kChunk;
+    if (cbase + nchunks > p.nc_bound) nchunks = max(0L, p.nc_bound - cbase);
+    auto chunk_len = [&](long jc) {
+        const long l = seos - (sbos + jc * kChunk);
+        return (int)(l < kChunk ? l : kChunk);
+    };
+
+    if (wave == 2 * NW) {
+        // ------------------------------------------------------------------- DMA wave
+        // Issue order: KQ(0) MPV(0) MPV(1), then per chunk c: KQ(c+1) MPV(c+2); at the top of
+        // chunk c only MPV(c+1) may still be in flight.
+        // Issuing a chunk's 53 copies takes about as long as the chain's work before the second
+        // barrier, so Mmat and P of chunk c+2 are issued after it (same order, same counts).
+        auto mpv_copy = [&](long jc, auto part) {
+            copy_mpv<DK, DV, DVT, true, decltype(part)::value>(mpv[jc % 3], p, sbos + jc * kChunk, chunk_len(jc),
+                                                               (cbase + jc) * H + h, h, dv0, lane);
+        };
+        if (nchunks > 0) {
+            copy_kq<DK>(kq[0], p, cbase * H + h, lane);
+            mpv_copy(0, std::integral_constant<int, 0>{});
+        }
+        if (nchunks > 1) mpv_copy(1, std::integral_constant<int, 0>{});
+        for (long i = 0;; ++i) {
+            if (i + 1 < nchunks) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMpvCopies<DK, DVT>));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            lds_barrier_lgkm();   // chunk i's operands are in LDS (fence-free: see chunk_propagate_bf16_kernel)
+            if (i == nchunks) return;
+            if (i + 1 < nchunks) copy_kq<DK>(kq[(i + 1) & 1], p, (cbase + i + 1) * H + h, lane);
+            if (i + 2 < nchunks) mpv_copy(i + 2, std::integral_constant<int, 1>{});
+            lds_barrier_lgkm();   // Delta of chunk i written
+            if (i + 2 < nchunks) mpv_copy(i + 2, std::integral_constant<int, 2>{});
+        }
+    }
+
+    if (wave < NW) {
+        // ----------------------------------------------------------------- chain waves
+        const int dvw = dv0 + 16 * wave;
+        f32x4_t ST[NKB];
+        const long scol = (dvw + l16) * DK + 4 * lq;   // this lane's offset in a [dv, dk] state
+        if (p.h0) {
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) {
+                const float4 x = *reinterpret_cast<const float4*>(p.h0 + pair * DV * DK + scol + 16 * j);
+                ST[j] = f32x4_t{x.x, x.y, x.z, x.w};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) ST[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        uint4 BS[NKS];
+        auto put_state = [&]() {   // S^T as fp16 right operands, kept and left for the output wave
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                BS[s] = pack_f16_frag(ST[2 * s], ST[2 * s + 1]);
+                xs[wave][s][lane] = BS[s];
+            }
+        };
+        put_state();
+        for (long i = 0;; ++i) {
+            lds_barrier();   // chunk i's operands (and the output wave's reads of the last state) done
+            if (i == nchunks) break;
+            const MPV& cm = mpv[i % 3];
+            uint4 MF[4][2];
+            float4 V4[4], EG4[4];
+            // X = K S^T [64 tokens x 16 columns], the K fragments one 32-wide slice ahead; Mmat
+            // and the residual terms read during the last slice
+            uint4 KF[2][4];
+            auto load_k = [&](int s, uint4 (&kf)[4]) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    kf[t] = *reinterpret_cast<const uint4*>(&cm.K[img_off<DK>(16 * t + l16, 32 * s + 4 * lq)]);
+            };
+            load_k(0, KF[0]);
+            f32x4_t X[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) X[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const int b = s & 1;
+                if (s + 1 < NKS) {
+                    load_k(s + 1, KF[b ^ 1]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        V4[t] = load4_t<uint16_t>(&cm.V[(16 * t + 4 * lq) * DVT + 16 * wave], DVT);
+                        EG4[t] = *reinterpret_cast<const float4*>(&cm.eg[16 * t + 4 * lq]);
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf)
+                            MF[t][hf] = *reinterpret_cast<const uint4*>(&cm.M[img_off<64>(16 * t + l16, 32 * hf + 4 * lq)]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) X[t] = mfma_f16(KF[b][t], BS[s], X[t]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // R = V - e^gamma X;  Delta = Mmat R
+            f32x4_t R[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                R[t] = f32x4_t{V4[t].x - EG4[t].x * X[t][0], V4[t].y - EG4[t].y * X[t][1],
+                               V4[t].z - EG4[t].z * X[t][2], V4[t].w - EG4[t].w * X[t][3]};
+            const uint4 BR[2] = {pack_f16_frag(R[0], R[1]), pack_f16_frag(R[2], R[3])};
+            f32x4_t D[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) D[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) D[t] = mfma_f16(MF[t][hf], BR[hf], D[t]);
+            __builtin_amdgcn_sched_barrier(0);
+            xd[wave][0][lane] = pack_f16_frag(D[0], D[1]);
+            xd[wave][1][lane] = pack_f16_frag(D[2], D[3]);
+            // K^T fragments for the state update, read while Delta is handed over
+            const int tr = l16 >> 2, tc = 4 * (l16 & 3);
+            uint4 KT[NKB][2];
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) {
+                const int c = 16 * j + tc;
+                KT[j][0] = lds_frag2_t(&cm.K[img_off<DK>(4 * lq + tr, c)], &cm.K[img_off<DK>(16 + 4 * lq + tr, c)]);
+                KT[j][1] = lds_frag2_t(&cm.K[img_off<DK>(32 + 4 * lq + tr, c)], &cm.K[img_off<DK>(48 + 4 * lq + tr, c)]);
+            }
+            lds_barrier();   // Delta handed over
+            // S^T <- e^{gamma_last} S^T + K^T diag(e^{gamma_last - gamma}) Delta
+            f32x4_t Dd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float4 ed = *reinterpret_cast<const float4*>(&cm.ed[16 * t + 4 * lq]);
+                Dd[t] = f32x4_t{ed.x * D[t][0], ed.y * D[t][1], ed.z * D[t][2], ed.w * D[t][3]};
+            }
+            const float elast = cm.eg[63];
+            const uint4 BT[2] = {pack_f16_frag(Dd[0], Dd[1]), pack_f16_frag(Dd[2], Dd[3])};
+#pragma unroll
+            for (int j = 0; j < NKB; ++j) ST[j] *= elast;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int j = 0; j < NKB; ++j) ST[j] = mfma_f16(KT[j][hf], BT[hf], ST[j]);
+            put_state();
+        }
+        if (p.hT) {
+#pragma unroll
+            for (int j = 0; j < NKB; ++j)
+                *reinterpret_cast<float4*>(p.hT + pair * DV * DK + scol + 16 * j) =
+                    make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+        }
+        return;
+    }
+
+    // ------------------------------------------------------------------- output waves
+    const int w = wave - NW;
+    const int dvw = dv0 + 16 * w;
+    for (long i = 0;; ++i) {
+        lds_barrier();   // chunk i's operands and the state entering it are in LDS
+        if (i == nchunks) break;
+        const long jc = i;
+        const KQ& ck = kq[i & 1];
+        const MPV& cm = mpv[i % 3];
+        uint4 BS[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) BS[s] = xs[w][s][lane];
+        // Y^T = S (diag(e^gamma) Q)^T [16 columns x 64 tokens], Q fragments one slice ahead; P
+        // read during the last slice
+        uint4 QF[2][4], PF[4][2];
+        auto load_q = [&](int s, uint4 (&qf)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                qf[t] = *reinterpret_cast<const uint4*>(&ck.Q[img_off<DK>(16 * t + l16, 32 * s + 4 * lq)]);
+        };
+        load_q(0, QF[0]);
+        f32x4_t Y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) Y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int b = s & 1;
+            if (s + 1 < NKS) {
+                load_q(s + 1, QF[b ^ 1]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        PF[t][hf] = *reinterpret_cast<const uint4*>(&cm.P[img_off<64>(16 * t + l16, 32 * hf + 4 * lq)]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Y[t] = mfma_f16(BS[s], QF[b][t], Y[t]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_barrier();   // Delta of chunk i is in LDS
+        const uint4 BD[2] = {xd[w][0][lane], xd[w][1][lane]};
+        // O^T = Y^T + Delta^T P^T (lane: token 16t + l16, columns 16 w + 4 lq .. +3), stored
+        // through a resource that ends at the chunk's last token row
+        f32x4_t O[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) O[t] = Y[t];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[t] = mfma_f16(BD[hf], PF[t][hf], O[t]);
+        if (p.o) {
+            constexpr int E = (int)sizeof(TO);
+            const long obos = sbos + jc * kChunk;
+            const auto orr = make_rsrc(static_cast<TO*>(p.o) + (obos * H + h) * DV + dvw,
+                                       (unsigned)(((chunk_len(jc) - 1) * H * DV + 16) * E));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) buf_store4<TO>(orr, ((16 * t + l16) * H * DV + 4 * lq) * E, O[t]);
+        }
+    }
+}
+
 // -------------------------------------------------------------------- launchers
 WorkspaceLayout workspace_layout(int B, int T, int H, int dk, int N, int varlen, int elem_bytes) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -1183,10 +1451,24 @@ static hipError_t prop_launch_bf16(const ChunkProblem& p, hipStream_t s) {
     return e != hipSuccess ? e : launch(chunk_propagate_bf16_kernel<TO, DK, DV, DVT, 3>, dim3((unsigned)blocks), block, s, p);
 }
 
+// 32-column tiles of unsplit chains: the chain and output waves of chunk_propagate_split_kernel
+// (GDN_SPLIT_OUT=0 selects the four-wave chunk_propagate_bf16_kernel instead)
+static bool split_out_wanted() {
+    const char* env = std::getenv("GDN_SPLIT_OUT");
+    return env ? std::atoi(env) != 0 : true;
+}
+
 template <typename TIn, typename TO, int DK, int DV, bool OUT = true>
 static hipError_t prop_launch(const ChunkProblem& p, hipStream_t s) {
     if constexpr (sizeof(TIn) == 2) {
-        if (p.seg_n <= 1 && prop_cols(p.N, p.H, DV) == 32) return prop_launch_bf16<TO, DK, DV, 32, OUT>(p, s);
+        if (p.seg_n <= 1 && prop_cols(p.N, p.H, DV) == 32) {
+            if constexpr (OUT && DV >= 32) {
+                if (split_out_wanted())
+                    return launch(chunk_propagate_split_kernel<TO, DK, DV>, dim3((unsigned)((long)p.N * p.H * (DV / 32))),
+                                  dim3(5 * 64), s, p);
+            }
+            return prop_launch_bf16<TO, DK, DV, 32, OUT>(p, s);
+        }
         return prop_launch_bf16<TO, DK, DV, (DV < 64 ? DV : 64), OUT>(p, s);
     } else {
         static_assert(OUT, "the fp32 state propagation always writes o");                            // two waves of 16 columns (LDS size)
