@@ -835,17 +835,21 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
             }
         };
         if constexpr (SEG == 3) {   // the same walk as the compute waves'
-            bool ok = true;
-            SegCounts rc(reran, p.seg_n);
-            for (int g = 1; g < p.seg_n; ++g) {
-                long c0, len;
-                seg_range(g, c0, len);
-                if (len == 0) break;
-                if (ok) {
-                    ok = rc.get(g) < len;
-                    continue;
+            // segments before the first stop were fixed by the second pass; from an unfixed one on,
+            // the walk reruns segments until one matches its record again
+            int g = walk_first_stop(reran, p.seg_n, [&](int gg) { long c0, len; seg_range(gg, c0, len); return len; });
+            long c0, len;
+            if (g < p.seg_n && (seg_range(g, c0, len), len > 0)) {
+                bool ok = false;
+                for (++g; g < p.seg_n; ++g) {
+                    seg_range(g, c0, len);
+                    if (len == 0) break;
+                    if (ok) {
+                        ok = reran[g] < len;
+                        continue;
+                    }
+                    ok = run(c0, len) < len;
                 }
-                ok = run(c0, len) < len;
             }
         } else {
             run(c_first, c_count);
@@ -1045,20 +1049,27 @@ __global__ __launch_bounds__((DVT / 16 + 1) * 64) void chunk_propagate_bf16_kern
     if constexpr (SEG == 3) {
         // ok: the state SEG = 2 started segment g from was the true one; otherwise ST holds the
         // true state entering segment g
+        // segments 1 .. g-1 were fixed by the second pass (the same test as the DMA wave's: both
+        // take the same barriers)
+        int g = walk_first_stop(reran, p.seg_n, [&](int gg) { long c0, len; seg_range(gg, c0, len); return len; });
         bool ok = true;
-        int glast = 0;
-        SegCounts rc(reran, p.seg_n);
-        for (int g = 1; g < p.seg_n; ++g) {
-            long c0, len;
-            seg_range(g, c0, len);
-            if (len == 0) break;
+        int glast = g - 1;
+        long c0, len;
+        if (g < p.seg_n && (seg_range(g, c0, len), len > 0)) {
             glast = g;
-            if (ok) {   // the same test as the DMA wave's: both take the same barriers
-                ok = rc.get(g) < len;
-                if (!ok) load_state(seg_state(g, p.seg_ncp + 1));   // no match: SEG = 2's final state is the true one
-                continue;
+            ok = false;
+            load_state(seg_state(g, p.seg_ncp + 1));   // no match: SEG = 2's final state is the true one
+            for (++g; g < p.seg_n; ++g) {
+                seg_range(g, c0, len);
+                if (len == 0) break;
+                glast = g;
+                if (ok) {
+                    ok = reran[g] < len;
+                    if (!ok) load_state(seg_state(g, p.seg_ncp + 1));
+                    continue;
+                }
+                ok = run(c0, len, g) < len;   // matched: the true final state is SEG = 1's
             }
-            ok = run(c0, len, g) < len;   // matched: the true final state is SEG = 1's
         }
         if (ok) load_state(seg_state(glast, p.seg_ncp));
     } else {

@@ -115,24 +115,26 @@ __device__ __forceinline__ void lds_barrier_lgkm() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The chunk counts the second pass of the long-chain split left per segment, as the ordered walk
-// reads them: wave-wide, 64 segments per vector load (lane l holds segment base + l), so that the
-// walk waits for one load latency per 64 segments instead of one per segment. get(g) takes a
-// wave-uniform g in increasing order; segments at or past n read as 0.
-struct SegCounts {
-    const int* src;
-    int n;
-    int base = -64;
-    int v = 0;
-    __device__ __forceinline__ SegCounts(const int* s, int count) : src(s), n(count) {}
-    __device__ __forceinline__ int get(int g) {
-        if (g - base >= 64) {
-            base = g & ~63;
-            const int i = base + (int)(threadIdx.x & 63);
-            v = i < n ? src[i] : 0;
+// The ordered walk of the long-chain split accepts segment g >= 1 when the second pass fixed it
+// (counts[g] < its chunk count) and ends at the first segment with no chunks. This returns the
+// first g >= 1 where the walk stops accepting, because segment g is empty or was not fixed, or
+// seg_n when there is none: every lane tests one segment, 64 per step, so that a walk over
+// segments that were all fixed reads the counts once instead of one dependent load per segment.
+// chunks_of(g) gives segment g's chunk count; the result is uniform over the wave.
+template <typename F>
+__device__ __forceinline__ int walk_first_stop(const int* counts, int seg_n, F chunks_of) {
+    const int lane = (int)(threadIdx.x & 63);
+    for (int base = 1; base < seg_n; base += 64) {
+        const int g = base + lane;
+        bool stop = false;
+        if (g < seg_n) {
+            const long len = chunks_of(g);
+            stop = len == 0 || counts[g] >= len;
         }
-        return __builtin_amdgcn_readlane(v, g - base);
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(stop);
+        if (m) return base + (int)__builtin_ctzll(m);
     }
-};
+    return seg_n;
+}
 
 }  // namespace gdn
