@@ -34,6 +34,25 @@ def test_noalloc_matches_workspace_entry_point(dtype):
         assert torch.equal(o, o_ref) and torch.equal(h, h_ref)
 
 
+@pytest.mark.parametrize("path", ["0", "1"])   # GDN_FUSED: two stages, one kernel
+def test_noalloc_long_chain_split(path, monkeypatch):
+    """The long-chain split keeps its segment records and per-segment rerun counts in the
+    workspace, which here is the shared array holding the previous call's contents: forced
+    segments of 3 chunks, a long input then a shorter one, bitwise equal to gdn_chunk_fwd."""
+    monkeypatch.setenv("GDN_FUSED", path)
+    monkeypatch.setenv("GDN_SEGMENT_CHUNKS", "3")
+    big = SY.make_forward_inputs(SY.Workload(80, "noalloc_split_big", H=2, dk=128, dv=128, dtype="bf16", B=2, T=1300),
+                                 seed=43, h0=True, beta_scale=2.0)
+    small = SY.make_forward_inputs(SY.Workload(80, "noalloc_split_small", H=2, dk=128, dv=128, dtype="bf16"),
+                                   seed=44, lengths=[700, 64, 0, 300], gate_scale=0.001, h0=True)
+    for x in (big, small):
+        print(f"[gpu] noalloc split path={path} {x['meta']}", flush=True)
+        o_ref, h_ref = _run(x, gb.gdn_chunk_fwd)
+        o, h = _run(x, gb.gdn_chunk_fwd_noalloc)
+        assert torch.isfinite(o.float()).all()
+        assert torch.equal(o, o_ref) and torch.equal(h, h_ref)
+
+
 def test_noalloc_rejects_problems_beyond_its_scratch():
     """A problem whose workspace exceeds the array is refused with GDN_ERR_WORKSPACE before any
     work is enqueued (the call does not fall back to allocating)."""
